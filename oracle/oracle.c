@@ -1,0 +1,411 @@
+/*
+ * CPU oracle for one EXL3 trellis-coded MoE layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU
+ * baseline leg of the benchmark may load this library.  It shares no code,
+ * header, table or constant generator with the HIP library; it is a plain,
+ * slow, direct statement of what the layer computes.
+ *
+ * Sources (page titles; each function cites the passage it follows):
+ *   [p1] "GLM-5.3-Flash EXL3 (~2.1 bpw, SM70 tile order)", header paragraph:
+ *        EXL3 tensors are packed 16-bit trellis words holding 16/K weights each.
+ *   [p2] "GLM-5.3 Flash EXL3 for 2x DGX Sparks", "Cold prefill (E3 grouped MoE)"
+ *        (gather, gate/up + SwiGLU, down + scatter, device segment tables) and
+ *        "What runs" (packed trellis + suh + svh + mcg, codebook MCG).
+ *   [p3] "GLM-5.3-Flash EXL3 K2", "What is in the shards": per expert tensor
+ *        `suh`, `svh`, `trellis` and a (1,) int32 `mcg`.
+ *   [p4] "GLM-5.3-Flash . exlr8 (K2/K3/K4)": opening paragraph (round every
+ *        codebook value to FP8 E4M3, nearest-even, saturating, before the side
+ *        vectors) and "Loading" (4096 x 128 gate/up halves, 288 experts top-8,
+ *        one shared expert).
+ *   [p5] "GLM-5.3-Flash-EXL3-TR3-3.5bpw": shared expert left unquantized.
+ *
+ * Where the pages are silent the readings below are this project's own and
+ * are listed with their reasons in the design notes:
+ *   value map   h = (mcg * s) mod 2^32; v = sum_{i=0..3} ((h >> (8i+1)) & 127) - 254;
+ *               c = v / 64
+ *   stream      a tile's 16K words form a 256K-bit stream, most significant
+ *               bit of word 0 first; state j is the 16 bits starting at bit
+ *               j*K, read circularly (tail-biting) and first bit most significant
+ *   tile order  state j of a tile sits at input row 16*tk + (j % 16) and output
+ *               column 16*tn + (j / 16); tile (tk, tn) starts at word
+ *               (tk * (out/16) + tn) * 16K of the expert's [in/16][out/16] grid
+ *   side vecs   W[k][n] = suh[k] * c[k][n] * svh[n] (no rotation)
+ *   router      fp32 logits in a fixed order (64 lane partial sums, then a
+ *               halving tree), top-k by (logit desc, index asc), softmax over
+ *               the k chosen logits
+ *   segments    stable counting sort of a = t*k + j by expert
+ *   combine     out[t] = sum_j w[t][j] * y[t][j] + shared(x[t])
+ *
+ * Precision: routing decides integers, so logits are fp32 in the fixed order
+ * (every bf16*fp16 or fp16*fp16 product is exact in fp32).  Everything after
+ * routing is carried in fp64.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_DT_F32 0
+#define ORC_DT_F16 1
+#define ORC_DT_BF16 2
+#define ORC_CB_MCG 0
+#define ORC_CB_MCG_E4M3 1
+
+/* IEEE binary16 -> double, from the format definition (bias 15, 10-bit mantissa). */
+double orc_f16_to_double(uint16_t h)
+{
+    int sign = h >> 15, ex = (h >> 10) & 0x1F, man = h & 0x3FF;
+    double v;
+    if (ex == 0)
+        v = ldexp((double)man, -24);
+    else if (ex == 31)
+        v = man ? NAN : INFINITY;
+    else
+        v = ldexp((double)(man | 0x400), ex - 25);
+    return sign ? -v : v;
+}
+
+/* bfloat16 = the upper 16 bits of an IEEE binary32. */
+double orc_bf16_to_double(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+static double act_to_double(uint16_t bits, int dtype)
+{
+    return dtype == ORC_DT_BF16 ? orc_bf16_to_double(bits) : orc_f16_to_double(bits);
+}
+
+/* Codebook value map: multiplicative congruential hash of the 16-bit state
+ * with the tensor's `mcg` multiplier ([p3] "What is in the shards"; [p2]
+ * "What runs": codebook MCG), then the sum of four 7-bit fields of the hash,
+ * centred.  Returns v in [-254, 254]; the weight value is v / 64. */
+int orc_mcg_value(uint32_t state, uint32_t mcg)
+{
+    uint32_t h = (uint32_t)(((uint64_t)mcg * (uint64_t)state) & 0xFFFFFFFFu);
+    int sum = 0;
+    for (int i = 0; i < 4; ++i)
+        sum += (int)((h >> (8 * i + 1)) & 0x7Fu);
+    return sum - 254;
+}
+
+/* States of a tail-biting K-bit trellis stream held in `nwords` 16-bit words
+ * ([p1] header: each word holds 16/K weights).  There are 16*nwords/K states;
+ * state j is the 16-bit window starting at stream bit j*K, wrapping at the end
+ * of the stream, first bit most significant.  Stream bit p is bit 15 - p%16
+ * of word p/16. */
+void orc_stream_states(const uint16_t *words, int nwords, int K, uint16_t *states)
+{
+    int B = 16 * nwords, n = B / K;
+    for (int j = 0; j < n; ++j) {
+        uint32_t s = 0;
+        for (int t = 0; t < 16; ++t) {
+            int p = (j * K + t) % B;
+            uint32_t bit = (words[p / 16] >> (15 - p % 16)) & 1u;
+            s = (s << 1) | bit;
+        }
+        states[j] = (uint16_t)s;
+    }
+}
+
+/* OCP FP8 E4M3FN rounding ([p4] opening paragraph: nearest-even, saturating).
+ * E4M3FN has 3 mantissa bits, exponent bias 7, smallest normal 2^-6,
+ * subnormal spacing 2^-9, largest finite 448 and no infinities. */
+double orc_e4m3_rne(double x)
+{
+    if (x != x || x == 0.0)
+        return x;
+    double a = fabs(x);
+    int e2;
+    frexp(a, &e2);            /* a = f * 2^e2 with f in [0.5, 1) */
+    int ex = e2 - 1;          /* floor(log2 a) */
+    if (ex < -6)
+        ex = -6;              /* subnormal range shares the 2^-9 spacing */
+    double q = ldexp(1.0, ex - 3);
+    double r = rint(a / q) * q;   /* default rounding mode: ties to even */
+    if (r > 448.0)
+        r = 448.0;
+    return copysign(r, x);
+}
+
+/* Decoded weight value of one state, before the side vectors: c = v / 64, or
+ * its E4M3 rounding for the exlr8 codebook variant ([p4]). */
+double orc_codebook_value(uint32_t state, uint32_t mcg, int codebook)
+{
+    double c = (double)orc_mcg_value(state, mcg) / 64.0;
+    return codebook == ORC_CB_MCG_E4M3 ? orc_e4m3_rne(c) : c;
+}
+
+/* Decode one 16x16 tile (16K words) into 256 values indexed by state j. */
+void orc_decode_tile(const uint16_t *words, int K, uint32_t mcg, int codebook, float *vals)
+{
+    uint16_t st[256];
+    orc_stream_states(words, 16 * K, K, st);
+    for (int j = 0; j < 256; ++j)
+        vals[j] = (float)orc_codebook_value(st[j], mcg, codebook);
+}
+
+/* Decode a whole [in][out] projection stored as an [in/16][out/16] grid of
+ * tiles into a dense row-major fp32 matrix (every value is exact in fp32). */
+void orc_decode_matrix(const uint16_t *codes, int in, int out, int K, uint32_t mcg,
+                       int codebook, float *dst)
+{
+    int ntn = out / 16, ntk = in / 16;
+#pragma omp parallel for schedule(static)
+    for (int tk = 0; tk < ntk; ++tk) {
+        float vals[256];
+        for (int tn = 0; tn < ntn; ++tn) {
+            const uint16_t *w = codes + ((size_t)tk * ntn + tn) * 16 * (size_t)K;
+            orc_decode_tile(w, K, mcg, codebook, vals);
+            for (int j = 0; j < 256; ++j) {
+                int r = j % 16, c = j / 16;
+                dst[(size_t)(16 * tk + r) * out + 16 * tn + c] = vals[j];
+            }
+        }
+    }
+}
+
+/* Router logits in fp32 ([p1] "Recipe" and [p4] "Intended use": routers stay
+ * in source precision because routing is sensitive).  For each (t, e): 64
+ * partial sums p[l] accumulate x[t][64i+l] * Wr[e][64i+l] for i = 0, 1, ...
+ * in order; then p[l] += p[l+d] for d = 32, 16, 8, 4, 2, 1; logit = p[0]
+ * (+ bias[e]).  Each product is exact in fp32. */
+void orc_router_logits(const uint16_t *x, int x_dtype, int64_t T, int H, const uint16_t *Wr,
+                       const float *bias, int E, float *logits)
+{
+    for (int64_t t = 0; t < T; ++t) {
+        for (int e = 0; e < E; ++e) {
+            float p[64];
+            for (int l = 0; l < 64; ++l)
+                p[l] = 0.0f;
+            for (int i = 0; i < H / 64; ++i) {
+                for (int l = 0; l < 64; ++l) {
+                    float a = (float)act_to_double(x[t * H + 64 * i + l], x_dtype);
+                    float b = (float)orc_f16_to_double(Wr[(size_t)e * H + 64 * i + l]);
+                    float prod = a * b;
+                    p[l] = p[l] + prod;
+                }
+            }
+            for (int d = 32; d >= 1; d /= 2)
+                for (int l = 0; l < d; ++l)
+                    p[l] = p[l] + p[l + d];
+            logits[t * E + e] = bias ? p[0] + bias[e] : p[0];
+        }
+    }
+}
+
+/* Top-k of each token's logits by (logit descending, expert ascending), and
+ * softmax weights over the k chosen logits ([p4] "Loading": 288 experts with
+ * top-8 routing), computed in fp64 from the fp32 logits. */
+void orc_topk_softmax(const float *logits, int64_t T, int E, int k, int32_t *idx, double *w)
+{
+    char *chosen = (char *)malloc((size_t)E);
+    for (int64_t t = 0; t < T; ++t) {
+        const float *l = logits + t * E;
+        memset(chosen, 0, (size_t)E);
+        for (int j = 0; j < k; ++j) {
+            int best = -1;
+            for (int e = 0; e < E; ++e)
+                if (!chosen[e] && (best < 0 || l[e] > l[best]))
+                    best = e;
+            chosen[best] = 1;
+            idx[t * k + j] = best;
+        }
+        double l0 = l[idx[t * k]], sum = 0.0;
+        for (int j = 0; j < k; ++j)
+            sum += exp((double)l[idx[t * k + j]] - l0);
+        for (int j = 0; j < k; ++j)
+            w[t * k + j] = exp((double)l[idx[t * k + j]] - l0) / sum;
+    }
+    free(chosen);
+}
+
+/* Segment tables ([p2] "Cold prefill (E3 grouped MoE)": device-side segment
+ * tables in place of a per-expert host loop): counts per expert, exclusive
+ * offsets (E+1 entries), the slots a = t*k + j grouped by expert ascending and
+ * by a ascending within an expert, and pos[a], the inverse permutation. */
+void orc_segments(const int32_t *idx, int64_t T, int k, int E, int32_t *counts,
+                  int32_t *offsets, int32_t *sorted_ids, int32_t *pos)
+{
+    int64_t n = T * k;
+    int32_t *fill = (int32_t *)malloc(sizeof(int32_t) * (size_t)E);
+    for (int e = 0; e < E; ++e)
+        counts[e] = 0;
+    for (int64_t a = 0; a < n; ++a)
+        counts[idx[a]]++;
+    offsets[0] = 0;
+    for (int e = 0; e < E; ++e)
+        offsets[e + 1] = offsets[e] + counts[e];
+    for (int e = 0; e < E; ++e)
+        fill[e] = offsets[e];
+    for (int64_t a = 0; a < n; ++a) {
+        int32_t p = fill[idx[a]]++;
+        sorted_ids[p] = (int32_t)a;
+        pos[a] = p;
+    }
+    free(fill);
+}
+
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+/*
+ * The layer for a subset of tokens, in fp64 after routing.
+ *
+ *   codes[p*E + e]  words of expert e, projection p (0 gate, 1 up, 2 down);
+ *                   may be NULL for experts no selected token routes to
+ *   suh[p], svh[p]  fp16 [E][in], [E][out]
+ *   shared[p]       fp16 nn.Linear weights (gate/up [I][H], down [H][I]) or NULL
+ *
+ * For each selected token t and each chosen expert e = idx[t][j]
+ * ([p2] "Cold prefill": gate/up + SwiGLU, then down + scatter):
+ *   g[n] = svh_g[n] * sum_k x[t][k] suh_g[k] c_g[k][n]       (u likewise)
+ *   h[n] = silu(g[n]) * u[n]
+ *   y[m] = svh_d[m] * sum_n h[n] suh_d[n] c_d[n][m]
+ *   out[t] += w[t][j] * y
+ * and the unquantized shared expert ([p1] "Recipe"; [p5]) is added with
+ * weight 1: out[t] += Wd (silu(Wg x) * (Wu x)).
+ *
+ * Returns 0, or -1 if a needed expert's codes are NULL.
+ */
+int orc_layer(int H, int I, int E, int k, int K, uint32_t mcg, int codebook, int x_dtype,
+              const uint16_t *x, const int64_t *tok, int64_t n_tok, const uint16_t *router_w,
+              const float *bias, const uint16_t *const *codes, const uint16_t *const *suh,
+              const uint16_t *const *svh, const uint16_t *const *shared, int32_t *idx_out,
+              double *w_out, double *out, int nthreads)
+{
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    float *lg = (float *)malloc(sizeof(float) * (size_t)E);
+    for (int64_t i = 0; i < n_tok; ++i) {
+        orc_router_logits(x + tok[i] * H, x_dtype, 1, H, router_w, bias, E, lg);
+        orc_topk_softmax(lg, 1, E, k, idx_out + i * k, w_out + i * k);
+    }
+    free(lg);
+    memset(out, 0, sizeof(double) * (size_t)n_tok * H);
+
+    float *cg = (float *)malloc(sizeof(float) * (size_t)H * I);
+    float *cu = (float *)malloc(sizeof(float) * (size_t)H * I);
+    float *cd = (float *)malloc(sizeof(float) * (size_t)I * H);
+    double *xs_g = (double *)malloc(sizeof(double) * H);
+    double *xs_u = (double *)malloc(sizeof(double) * H);
+    double *g = (double *)malloc(sizeof(double) * I);
+    double *u = (double *)malloc(sizeof(double) * I);
+    double *hs = (double *)malloc(sizeof(double) * I);
+    double *y = (double *)malloc(sizeof(double) * H);
+    int rc = 0;
+
+    for (int e = 0; e < E && rc == 0; ++e) {
+        int used = 0;
+        for (int64_t a = 0; a < n_tok * k; ++a)
+            used |= idx_out[a] == e;
+        if (!used)
+            continue;
+        if (!codes[0 * E + e] || !codes[1 * E + e] || !codes[2 * E + e]) {
+            rc = -1;
+            break;
+        }
+        orc_decode_matrix(codes[0 * E + e], H, I, K, mcg, codebook, cg);
+        orc_decode_matrix(codes[1 * E + e], H, I, K, mcg, codebook, cu);
+        orc_decode_matrix(codes[2 * E + e], I, H, K, mcg, codebook, cd);
+        const uint16_t *suh_g = suh[0] + (size_t)e * H, *suh_u = suh[1] + (size_t)e * H;
+        const uint16_t *svh_g = svh[0] + (size_t)e * I, *svh_u = svh[1] + (size_t)e * I;
+        const uint16_t *suh_d = suh[2] + (size_t)e * I, *svh_d = svh[2] + (size_t)e * H;
+        for (int64_t a = 0; a < n_tok * k; ++a) {
+            if (idx_out[a] != e)
+                continue;
+            int64_t ti = a / k;
+            const uint16_t *xt = x + tok[ti] * H;
+            for (int kk = 0; kk < H; ++kk) {
+                double xv = act_to_double(xt[kk], x_dtype);
+                xs_g[kk] = xv * orc_f16_to_double(suh_g[kk]);
+                xs_u[kk] = xv * orc_f16_to_double(suh_u[kk]);
+            }
+            /* columns in blocks of 64 so that each pass over k reads rows */
+#pragma omp parallel for schedule(static)
+            for (int n0 = 0; n0 < I; n0 += 64) {
+                int nn = I - n0 < 64 ? I - n0 : 64;
+                double sg[64], su[64];
+                for (int c = 0; c < nn; ++c)
+                    sg[c] = su[c] = 0.0;
+                for (int kk = 0; kk < H; ++kk) {
+                    const float *rg = cg + (size_t)kk * I + n0, *ru = cu + (size_t)kk * I + n0;
+                    for (int c = 0; c < nn; ++c) {
+                        sg[c] += xs_g[kk] * (double)rg[c];
+                        su[c] += xs_u[kk] * (double)ru[c];
+                    }
+                }
+                for (int c = 0; c < nn; ++c) {
+                    int n = n0 + c;
+                    g[n] = sg[c] * orc_f16_to_double(svh_g[n]);
+                    u[n] = su[c] * orc_f16_to_double(svh_u[n]);
+                    hs[n] = silu(g[n]) * u[n] * orc_f16_to_double(suh_d[n]);
+                }
+            }
+#pragma omp parallel for schedule(static)
+            for (int m0 = 0; m0 < H; m0 += 64) {
+                int mm = H - m0 < 64 ? H - m0 : 64;
+                double s[64];
+                for (int c = 0; c < mm; ++c)
+                    s[c] = 0.0;
+                for (int n = 0; n < I; ++n) {
+                    const float *rd = cd + (size_t)n * H + m0;
+                    for (int c = 0; c < mm; ++c)
+                        s[c] += hs[n] * (double)rd[c];
+                }
+                for (int c = 0; c < mm; ++c)
+                    y[m0 + c] = s[c] * orc_f16_to_double(svh_d[m0 + c]);
+            }
+            double wj = w_out[a];
+            for (int m = 0; m < H; ++m)
+                out[ti * H + m] += wj * y[m];
+        }
+    }
+
+    if (rc == 0 && shared && shared[0] && shared[1] && shared[2]) {
+        for (int64_t ti = 0; ti < n_tok; ++ti) {
+            const uint16_t *xt = x + tok[ti] * H;
+            for (int kk = 0; kk < H; ++kk)
+                xs_g[kk] = act_to_double(xt[kk], x_dtype);
+#pragma omp parallel for schedule(static)
+            for (int n = 0; n < I; ++n) {
+                double sg = 0.0, su = 0.0;
+                const uint16_t *wg = shared[0] + (size_t)n * H, *wu = shared[1] + (size_t)n * H;
+                for (int kk = 0; kk < H; ++kk) {
+                    sg += orc_f16_to_double(wg[kk]) * xs_g[kk];
+                    su += orc_f16_to_double(wu[kk]) * xs_g[kk];
+                }
+                hs[n] = silu(sg) * su;
+            }
+#pragma omp parallel for schedule(static)
+            for (int m = 0; m < H; ++m) {
+                double s = 0.0;
+                const uint16_t *wd = shared[2] + (size_t)m * I;
+                for (int n = 0; n < I; ++n)
+                    s += orc_f16_to_double(wd[n]) * hs[n];
+                out[ti * H + m] += s;
+            }
+        }
+    }
+
+    free(cg);
+    free(cu);
+    free(cd);
+    free(xs_g);
+    free(xs_u);
+    free(g);
+    free(u);
+    free(hs);
+    free(y);
+    return rc;
+}
