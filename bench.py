@@ -1,0 +1,223 @@
+"""Benchmark of the EXL3 trellis-coded MoE layer on one MI355X.
+
+Workload (one step = one whole layer, every launch of the hot path): the
+7168-token prefill chunk at GLM-5.3-Flash shapes (hidden 4096, expert
+intermediate 2048, 288 experts top-8 with a skewing router bias, K = 2 mcg
+codes, fp16 shared expert), seeded synthetic inputs already resident in HBM.
+`value` is tokens per second of that layer.  The 8-token decode step is timed
+as well (code HBM GB/s and us per layer, with rotating copies of the codes so
+the 256 MB last-level cache cannot hold them).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes as C
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP16_TFLOPS = 2500.0      # MI355X dense fp16/bf16 MFMA
+PEAK_HBM_GBPS = 8000.0
+
+
+def _dev(a):
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype in (np.uint16, np.float16):
+        a = a.view(np.int16)
+    return torch.from_numpy(a).cuda()
+
+
+class Hip:
+    """hipEvent helpers through the HIP runtime (events on the library's stream)."""
+
+    def __init__(self):
+        self.l = C.CDLL("libamdhip64.so")
+        self.l.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        self.l.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        self.l.hipEventDestroy.argtypes = [C.c_void_p]
+
+    def event(self):
+        e = C.c_void_p()
+        assert self.l.hipEventCreate(C.byref(e)) == 0
+        return e.value
+
+    def ms(self, a, b) -> float:
+        f = C.c_float()
+        assert self.l.hipEventElapsedTime(C.byref(f), a, b) == 0
+        return f.value
+
+    def destroy(self, e):
+        self.l.hipEventDestroy(e)
+
+
+def setup(cfg, copies=1, shared=True):
+    import trellis_quantized_moe_exl3_amd as M
+    import workloads as W
+    inp = W.gen_layer(cfg)
+    codes = [[_dev(c) for c in inp.codes] for _ in range(copies)]
+    suh = [_dev(s) for s in inp.suh]
+    svh = [_dev(s) for s in inp.svh]
+    rw = _dev(inp.router_w)
+    bias = _dev(inp.router_bias) if inp.router_bias is not None else None
+    sh = [_dev(s) for s in inp.shared] if (shared and inp.shared is not None) else None
+    flags = (M.HAS_SHARED if sh is not None else 0) | (M.HAS_ROUTER_BIAS if bias is not None else 0)
+    desc = M.make_desc(cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k, cfg.K, cfg.codebook,
+                       cfg.mcg, cfg.act_dtype, flags, 0)
+    weights = [M.make_weights(c, suh, svh, rw, bias, sh) for c in codes]
+    keep = (codes, suh, svh, rw, bias, sh)
+    return inp, desc, weights, keep
+
+
+def time_layer(desc, weights_list, x, steps, warmup, hip):
+    """Returns (ms per step from host clocks, per-step-kind event ms arrays)."""
+    import torch
+    import trellis_quantized_moe_exl3_amd as M
+    out = torch.empty_like(x)
+    ws = torch.empty(M.workspace_size(desc, x.shape[0]), dtype=torch.uint8, device="cuda")
+    nw = len(weights_list)
+    for i in range(warmup):
+        M.layer(desc, weights_list[i % nw], x, out, ws)
+    evs = [[hip.event() for _ in range(M.STEP_END + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        M.layer_profiled(desc, weights_list[i % nw], x, out, ws, evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    per = np.array([[hip.ms(e[j], e[j + 1]) for j in range(M.STEP_END)] for e in evs])
+    total = np.array([hip.ms(e[0], e[M.STEP_END]) for e in evs])
+    for e in evs:
+        for x_ in e:
+            hip.destroy(x_)
+    return (t1 - t0) * 1000.0 / steps, per, total, out, ws
+
+
+def routing_counts(desc, weights, x, cfg):
+    import torch
+    import trellis_quantized_moe_exl3_amd as M
+    T = x.shape[0]
+    idx = torch.empty(T * cfg.top_k, dtype=torch.int32, device="cuda")
+    counts = torch.empty(cfg.n_experts, dtype=torch.int32, device="cuda")
+    ws = torch.empty(M.workspace_size(desc, T), dtype=torch.uint8, device="cuda")
+    M.route(desc, weights, x, idx, None, counts, None, None, None, ws)
+    torch.cuda.synchronize()
+    return counts.cpu().numpy()
+
+
+def cpu_baseline(cfg, n_tokens):
+    import oracle
+    import workloads as W
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    inp = W.gen_layer(cfg, experts=[])
+    sample = list(range(n_tokens))
+    idx, _ = oracle.route_tokens(inp, sample)
+    ex = sorted(set(idx.ravel().tolist()))
+    codes = [W.gen_codes(cfg, p, ex) for p in range(3)]
+    t0 = time.perf_counter()
+    oracle.layer(inp, sample, nthreads=threads, codes=codes, present=set(ex))
+    dt = time.perf_counter() - t0
+    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n_tokens} tokens of the 7168-token prefill layer "
+                      f"({len(ex)} distinct experts decoded), fp64 oracle, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=50)
+    ap.add_argument("--cpu-tokens", type=int, default=16)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only; multi-GPU scaling is not part of it "
+              "(see the sharding notes in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import trellis_quantized_moe_exl3_amd as M
+    import workloads as W
+    torch.cuda.set_device(0)
+    hip = Hip()
+
+    # ---- prefill: the headline workload
+    cfg = W.BY_NAME["prefill"]
+    inp, desc, weights, keep = setup(cfg)
+    x = _dev(inp.x)
+    print(f"[bench] prefill inputs ready (T={cfg.tokens})", file=sys.stderr, flush=True)
+    ms, per, total, _, _ = time_layer(desc, weights, x, args.steps, args.warmup, hip)
+    counts = routing_counts(desc, weights[0], x, cfg)
+    g = 4
+    mfma_rows = int(counts[counts > g].sum())
+    step_ms = {n: float(per[:, i].mean()) for i, n in enumerate(M.STEPS)}
+    gu_ms = step_ms["mfma_gateup"]
+    gu_flops = 2.0 * 2 * cfg.hidden * cfg.inter * mfma_rows
+    achieved = gu_flops / (gu_ms * 1e-3) / 1e12
+    print(f"[bench] prefill {ms:.3f} ms/step; steps {json.dumps({k: round(v, 4) for k, v in step_ms.items()})}",
+          file=sys.stderr, flush=True)
+    del keep, weights, x
+    torch.cuda.empty_cache()
+
+    # ---- decode: 8 tokens, rotating code copies
+    dcfg = W.BY_NAME["decode"]
+    dinp, ddesc, dweights, dkeep = setup(dcfg, copies=4)
+    dx = _dev(dinp.x)
+    dms, dper, dtotal, _, _ = time_layer(ddesc, dweights, dx, args.decode_steps, 5, hip)
+    dcounts = routing_counts(ddesc, dweights[0], dx, dcfg)
+    touched = int((dcounts > 0).sum())
+    code_bytes = touched * 3 * (dcfg.hidden * dcfg.inter * dcfg.K // 8)
+    dstep = {n: float(dper[:, i].mean()) for i, n in enumerate(M.STEPS)}
+    routed_ms = dstep["gemv_gateup"] + dstep["mfma_gateup"] + dstep["gemv_down"] + dstep["mfma_down"]
+    code_gbps = code_bytes / (routed_ms * 1e-3) / 1e9
+    print(f"[bench] decode {float(dtotal.mean()) * 1000:.1f} us/layer (events), code {code_gbps:.0f} GB/s; "
+          f"steps {json.dumps({k: round(v * 1000, 1) for k, v in dstep.items()})}", file=sys.stderr, flush=True)
+    del dkeep, dweights
+    torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, args.cpu_tokens)
+
+    rec = {
+        "metric": "MoE-layer tokens/s @7168-tok prefill; us/layer @8-tok decode; code HBM GB/s",
+        "value": cfg.tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16/bf16 MFMA, fp32 accumulate (K=2 trellis codes)",
+        "data": "synthetic (seeded; uniform random codes, N(0,1) activations)",
+        "config": {"workload": "prefill-7168: one MoE layer, T=7168, H=4096, I=2048, E=288, top-8, "
+                               "K=2 mcg, router bias N(0,1), fp16 shared expert",
+                   "tokens": cfg.tokens, "parallelism": "single GPU"},
+        "roofline": {"kernel": "mfma_gateup (group_gemm_kernel<0,2,0>)", "bound": "mfma",
+                     "achieved": achieved, "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_FP16_TFLOPS, "traffic": None,
+                     "launch_ms": gu_ms, "flops_per_launch": gu_flops},
+        "step_ms": step_ms,
+        "decode": {"workload": "decode-8: T=8, same layer, no router bias", "us_per_layer": float(dtotal.mean()) * 1000,
+                   "host_ms_per_step": dms, "touched_experts": touched, "code_bytes": code_bytes,
+                   "routed_kernels_us": routed_ms * 1000, "code_GBps": code_gbps,
+                   "code_hbm_frac": code_gbps / PEAK_HBM_GBPS,
+                   "step_us": {k: v * 1000 for k, v in dstep.items()}},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,195 @@
+/*
+ * moe_exl3.h -- C ABI of the MI355X (gfx950) library for one MoE layer whose
+ * routed experts are EXL3 K-bit trellis codes.
+ *
+ * What the layer computes (page "GLM-5.3 Flash EXL3 for 2x DGX Sparks",
+ * section "Cold prefill (E3 grouped MoE)": gather, gate/up + SwiGLU, down +
+ * scatter, built from device-side segment tables with no host sync; page
+ * "GLM-5.3-Flash . exlr8 (K2/K3/K4)", section "Loading": 288 routed experts,
+ * top-8, hidden 4096, expert intermediate 2048, one shared expert):
+ *
+ *   logits[t][e] = sum_h x[t][h] * router_w[e][h] (+ router_bias[e])   (fp32,
+ *                  fixed order: 64 lane partial sums over h = 64i + l, added
+ *                  in order of i, then a halving tree over l)
+ *   idx[t][0..k) = top-k experts by (logit desc, expert asc)
+ *   w[t][j]      = softmax of the k chosen logits
+ *   for each (t, j), e = idx[t][j]:
+ *     g = (x[t] * suh_g[e]) C_g[e] * svh_g[e]        u likewise
+ *     y = ((silu(g) * u) * suh_d[e]) C_d[e] * svh_d[e]
+ *   out[t] = sum_j w[t][j] y[t][j]  +  Wd (silu(Wg x[t]) * (Wu x[t]))   (shared)
+ *
+ * C_p[e] is the dense [in][out] matrix of decoded codebook values c = v/64.
+ *
+ * Trellis code layout (page "GLM-5.3-Flash EXL3 (~2.1 bpw, SM70 tile order)",
+ * header: packed 16-bit words, 16/K weights each; page "GLM-5.3-Flash EXL3
+ * K2", "What is in the shards": trellis, suh, svh, (1,) int32 mcg):
+ *   codes[p]   uint16 [E][in/16][out/16][16*K]: one 16x16 tile per 16*K words,
+ *              tiles row-major over (input block, output block).
+ *   tile       a 256*K-bit stream, word 0 first, most significant bit first;
+ *              state j = the 16 bits starting at bit j*K, wrapping inside the
+ *              tile; state j is the weight at input row j % 16 and output
+ *              column j / 16 of the tile.
+ *   value      h = (mcg * state) mod 2^32;
+ *              v = sum_{i=0..3} ((h >> (8i+1)) & 127) - 254;  c = v / 64.
+ *   E4M3       with MOE_EXL3_CB_MCG_E4M3, c is rounded to OCP FP8 E4M3FN
+ *              (nearest-even, saturating) before the side vectors (page
+ *              "GLM-5.3-Flash . exlr8 (K2/K3/K4)", opening paragraph).
+ *   gate, up   in = hidden, out = inter;  down: in = inter, out = hidden.
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked "device" point to device memory of the current HIP
+ *     device, are owned by the caller and must stay valid until the work
+ *     queued on `stream` has finished.  The library never allocates, frees or
+ *     synchronises; it keeps no mutable global state, so calls on different
+ *     streams are independent as long as each call has its own workspace.
+ *   - `stream` is a hipStream_t (NULL = the null stream).
+ *   - Return value: 0 on success or a negative MOE_EXL3_ERR_* code.  All
+ *     argument checks run before the first launch; on error nothing is
+ *     launched.  Faults inside kernels surface at the caller's next
+ *     synchronisation, as HIP errors.
+ *   - Device pointers must be 16-byte aligned (MOE_EXL3_ERR_MISALIGNED).
+ */
+#ifndef MOE_EXL3_H
+#define MOE_EXL3_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_EXL3_ABI_VERSION 1
+
+/* error codes */
+#define MOE_EXL3_OK 0
+#define MOE_EXL3_ERR_INVALID_ARG (-1)   /* NULL pointer, negative size, shape rule broken */
+#define MOE_EXL3_ERR_UNSUPPORTED (-2)   /* K, dtype, codebook or size outside the kernels' range */
+#define MOE_EXL3_ERR_WORKSPACE (-3)     /* workspace smaller than moe_exl3_workspace_size() */
+#define MOE_EXL3_ERR_MISALIGNED (-4)    /* a device pointer is not 16-byte aligned */
+#define MOE_EXL3_ERR_HIP (-5)           /* a launch failed (hipGetLastError) */
+
+/* element types */
+#define MOE_EXL3_DT_F32 0
+#define MOE_EXL3_DT_F16 1
+#define MOE_EXL3_DT_BF16 2
+#define MOE_EXL3_DT_FP8 3   /* OCP E4M3FN bit patterns, one byte per value */
+
+/* codebooks */
+#define MOE_EXL3_CB_MCG 0
+#define MOE_EXL3_CB_MCG_E4M3 1
+
+/* desc.flags */
+#define MOE_EXL3_HAS_SHARED (1u << 0)       /* add the fp16 shared expert */
+#define MOE_EXL3_HAS_ROUTER_BIAS (1u << 1)  /* add router_bias to the logits */
+#define MOE_EXL3_FORCE_GEMV (1u << 2)       /* every routed expert on the decode-fused GEMV path */
+#define MOE_EXL3_FORCE_MFMA (1u << 3)       /* every routed expert on the MFMA path */
+#define MOE_EXL3_FP8_MFMA (1u << 4)         /* routed MFMA GEMMs in fp8 (needs CB_MCG_E4M3) */
+
+/*
+ * Layer description.  Shape rules: hidden is a multiple of 256, inter a
+ * multiple of 128, both at most 16384; n_experts is a multiple of 8 and at
+ * most 1024; 1 <= top_k <= min(n_experts, 16); K in {2, 3, 4}; act_dtype is
+ * F16 or BF16; T * top_k < 2^31.
+ */
+typedef struct moe_exl3_desc {
+    int32_t hidden;         /* H */
+    int32_t inter;          /* I, expert (and shared expert) intermediate size */
+    int32_t n_experts;      /* E */
+    int32_t top_k;          /* k */
+    int32_t K;              /* trellis bits per weight */
+    int32_t codebook;       /* MOE_EXL3_CB_* */
+    uint32_t mcg;           /* codebook multiplier (bit pattern of the int32 `mcg`) */
+    int32_t act_dtype;      /* dtype of x and out */
+    uint32_t flags;         /* MOE_EXL3_* flags */
+    int32_t gemv_max_rows;  /* experts with at most this many routed rows use the
+                               GEMV path; 0 selects the default (4) */
+} moe_exl3_desc;
+
+/* Layer weights.  All device pointers, contiguous, row-major. */
+typedef struct moe_exl3_weights {
+    const uint16_t *codes[3];   /* gate, up, down: [E][in/16][out/16][16K] */
+    const uint16_t *suh[3];     /* fp16 [E][in]  input-channel side vectors */
+    const uint16_t *svh[3];     /* fp16 [E][out] output-channel side vectors */
+    const uint16_t *router_w;   /* fp16 [E][H] */
+    const float *router_bias;   /* fp32 [E], read only with HAS_ROUTER_BIAS */
+    const uint16_t *shared_w[3];/* fp16 nn.Linear weights: gate/up [I][H], down [H][I];
+                                   read only with HAS_SHARED */
+} moe_exl3_weights;
+
+/* ABI version (MOE_EXL3_ABI_VERSION). */
+int moe_exl3_version(void);
+
+/* Static description of an error code; never NULL. */
+const char *moe_exl3_strerror(int code);
+
+/*
+ * Workspace bytes needed by moe_exl3_layer / moe_exl3_route for up to
+ * `max_tokens` tokens (page "GLM-5.3 Flash EXL3 for 2x DGX Sparks", "Cold
+ * prefill": the grouped path keeps a caller-visible scratch of gathered rows).
+ * Host-only; touches no device.
+ */
+int moe_exl3_workspace_size(const moe_exl3_desc *desc, int64_t max_tokens, size_t *bytes);
+
+/*
+ * One MoE layer.  x: device [T][H] act_dtype; out: device [T][H] act_dtype,
+ * must not overlap x.  T = 0 is a no-op.  The workspace is device memory of at
+ * least moe_exl3_workspace_size(desc, T) bytes, 256-byte aligned; its content
+ * on entry is ignored and on exit unspecified.
+ */
+int moe_exl3_layer(const moe_exl3_desc *desc, const moe_exl3_weights *weights, const void *x,
+                   int64_t T, void *out, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Routing and segment tables only (the layer's first steps, exposed for
+ * bit-exact checks).  Outputs are device buffers:
+ *   idx [T][k] int32, w [T][k] fp32 (softmax over the chosen logits),
+ *   counts [E], offsets [E+1] (exclusive scan of counts),
+ *   sorted_ids [T*k]: slots a = t*k + j grouped by expert ascending, and by a
+ *   ascending within an expert; pos [T*k]: the inverse (sorted_ids[pos[a]] = a).
+ * Any output pointer may be NULL except idx.
+ */
+int moe_exl3_route(const moe_exl3_desc *desc, const moe_exl3_weights *weights, const void *x,
+                   int64_t T, int32_t *idx, float *w, int32_t *counts, int32_t *offsets,
+                   int32_t *sorted_ids, int32_t *pos, void *workspace, size_t ws_bytes,
+                   void *stream);
+
+/*
+ * moe_exl3_layer with timing hooks, for benchmarks and profilers: events[i]
+ * (caller-created hipEvent_t handles) is recorded on `stream` right before
+ * launch step i, and events[MOE_EXL3_STEP_END] after the last step.  Steps
+ * skipped for this call are still recorded (at the same point).  n_events must
+ * be MOE_EXL3_STEP_END + 1 and every handle non-NULL (else INVALID_ARG).  With
+ * T = 0 nothing is launched or recorded.  Same contract as moe_exl3_layer
+ * otherwise.
+ */
+#define MOE_EXL3_STEP_ROUTE_LOGITS 0
+#define MOE_EXL3_STEP_TOPK 1
+#define MOE_EXL3_STEP_SEGMENTS 2
+#define MOE_EXL3_STEP_CONVERT_X 3
+#define MOE_EXL3_STEP_GEMV_GATEUP 4
+#define MOE_EXL3_STEP_MFMA_GATEUP 5
+#define MOE_EXL3_STEP_GEMV_DOWN 6
+#define MOE_EXL3_STEP_MFMA_DOWN 7
+#define MOE_EXL3_STEP_SHARED 8
+#define MOE_EXL3_STEP_COMBINE 9
+#define MOE_EXL3_STEP_END 10
+int moe_exl3_layer_profiled(const moe_exl3_desc *desc, const moe_exl3_weights *weights,
+                            const void *x, int64_t T, void *out, void *workspace, size_t ws_bytes,
+                            void *stream, void *const *events, int n_events);
+
+/*
+ * Dense decode of one trellis-coded [n_in][n_out] matrix (no side vectors):
+ * dst[k][n] = c (dst_dtype F32, F16, BF16: exact) or its E4M3FN bit pattern
+ * (FP8, exact for the E4M3 codebook; for CB_MCG values are rounded to E4M3).
+ * codes: device [n_in/16][n_out/16][16K] uint16; dst: device, row-major.
+ * n_in and n_out are positive multiples of 16.
+ */
+int moe_exl3_decode(const uint16_t *codes, int32_t n_in, int32_t n_out, int32_t K, uint32_t mcg,
+                    int32_t codebook, void *dst, int32_t dst_dtype, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_EXL3_H */

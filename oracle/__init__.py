@@ -156,9 +156,9 @@ def layer(inp, tokens: Optional[Sequence[int]] = None, nthreads: int = 0,
     """Layer output (fp64) for the given token subset of a `workloads.LayerInputs`.
 
     Returns (idx [n][k] int32, w [n][k] fp64, out [n][H] fp64).  `codes`
-    overrides inp.codes (3 arrays [E][words]); rows of experts that no
-    selected token uses may be left unfilled; with `present` given, only
-    those experts' rows are passed and a routed expert outside it is an error.
+    overrides inp.codes: 3 arrays [E][words] or 3 dicts {expert: words}.
+    Experts missing from a dict, or outside `present`, are passed as NULL and
+    routing a selected token to one of them is an error.
     """
     cfg = inp.cfg
     H, I, E, k = cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k
@@ -167,12 +167,22 @@ def layer(inp, tokens: Optional[Sequence[int]] = None, nthreads: int = 0,
     assert tok.size == 0 or (tok.min() >= 0 and tok.max() < T)
     cds = inp.codes if codes is None else codes
     ptrs = (C.c_void_p * (3 * E))()
+    keep = []
     for p in range(3):
         arr = cds[p]
-        assert arr.dtype == np.uint16 and arr.flags.c_contiguous and arr.shape[0] == E
         for e in range(E):
-            if present is None or e in present:
-                ptrs[p * E + e] = arr[e].ctypes.data
+            if present is not None and e not in present:
+                continue
+            if isinstance(arr, dict):
+                if e not in arr:
+                    continue
+                row = np.ascontiguousarray(arr[e], dtype=np.uint16)
+            else:
+                row = arr[e]
+                assert row.dtype == np.uint16 and row.flags.c_contiguous
+            assert row.size == cfg.words_per_expert(p)
+            keep.append(row)
+            ptrs[p * E + e] = row.ctypes.data
     suh = [np.ascontiguousarray(a) for a in inp.suh]
     svh = [np.ascontiguousarray(a) for a in inp.svh]
     suh_p = (C.c_void_p * 3)(*[a.ctypes.data for a in suh])

@@ -180,16 +180,23 @@ void orc_decode_matrix(const uint16_t *codes, int in, int out, int K, uint32_t m
 void orc_router_logits(const uint16_t *x, int x_dtype, int64_t T, int H, const uint16_t *Wr,
                        const float *bias, int E, float *logits)
 {
+    /* every bf16 / fp16 value is exact in fp32 */
+    float *wf = (float *)malloc(sizeof(float) * (size_t)E * H);
+    for (size_t i = 0; i < (size_t)E * H; ++i)
+        wf[i] = (float)orc_f16_to_double(Wr[i]);
+#pragma omp parallel for schedule(dynamic, 1)
     for (int64_t t = 0; t < T; ++t) {
+        float *xf = (float *)malloc(sizeof(float) * H);
+        for (int hh = 0; hh < H; ++hh)
+            xf[hh] = (float)act_to_double(x[t * H + hh], x_dtype);
         for (int e = 0; e < E; ++e) {
+            const float *we = wf + (size_t)e * H;
             float p[64];
             for (int l = 0; l < 64; ++l)
                 p[l] = 0.0f;
             for (int i = 0; i < H / 64; ++i) {
                 for (int l = 0; l < 64; ++l) {
-                    float a = (float)act_to_double(x[t * H + 64 * i + l], x_dtype);
-                    float b = (float)orc_f16_to_double(Wr[(size_t)e * H + 64 * i + l]);
-                    float prod = a * b;
+                    float prod = xf[64 * i + l] * we[64 * i + l];
                     p[l] = p[l] + prod;
                 }
             }
@@ -198,7 +205,9 @@ void orc_router_logits(const uint16_t *x, int x_dtype, int64_t T, int H, const u
                     p[l] = p[l] + p[l + d];
             logits[t * E + e] = bias ? p[0] + bias[e] : p[0];
         }
+        free(xf);
     }
+    free(wf);
 }
 
 /* Top-k of each token's logits by (logit descending, expert ascending), and

@@ -1,0 +1,109 @@
+"""Layer parity of the HIP path (moe_exl3_layer through the C ABI) with the
+fp64 oracle, max |out - ref| / max |ref| <= 2e-2.
+
+With the synthetic side vectors (~1/64 on both sides) the routed experts add
+about 1e-5 of what the shared expert adds, so a whole-output comparison would
+not see routed errors: the routed part is checked on its own (layer without
+the shared expert) and the full layer is checked as well.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import trellis_quantized_moe_exl3_amd as M
+import workloads as W
+from gpu_util import DevLayer, dev, rel_err
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+
+def _routed_only(inp):
+    import dataclasses
+    return dataclasses.replace(inp, shared=None)
+
+
+@pytest.mark.parametrize("flags", [0, M.FORCE_GEMV, M.FORCE_MFMA])
+def test_tiny_full(flags):
+    inp = W.gen_layer(W.BY_NAME["tiny"])
+    out = DevLayer(inp, flags=flags).run()
+    _, _, ref = oracle.layer(inp)
+    err = rel_err(out, ref)
+    print(f"tiny flags={flags} err={err:.3e}")
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("T", [1, 37, 300])
+@pytest.mark.parametrize("flags", [0, M.FORCE_MFMA])
+def test_tiny_ragged(T, flags):
+    inp = W.gen_layer(W.BY_NAME["tiny"].replace(tokens=T))
+    out = DevLayer(inp, flags=flags).run()
+    _, _, ref = oracle.layer(inp)
+    assert rel_err(out, ref) <= TOL
+
+
+def test_tiny_one_expert_takes_every_token():
+    # a huge bias on expert 3: all 600 slots of expert 3 -> three MFMA row tiles
+    cfg = W.BY_NAME["tiny"].replace(tokens=600, router_bias=True)
+    inp = W.gen_layer(cfg)
+    inp.router_bias = np.zeros(cfg.n_experts, dtype=np.float32)
+    inp.router_bias[3] = 100.0
+    dl = DevLayer(inp)
+    idx = dl.route()[0]
+    assert (idx[:, 0] == 3).all()
+    out = dl.run()
+    _, _, ref = oracle.layer(inp)
+    assert rel_err(out, ref) <= TOL
+
+
+def test_zero_tokens_is_noop():
+    inp = W.gen_layer(W.BY_NAME["tiny"])
+    dl = DevLayer(inp)
+    x = dl.x[:0]
+    out = torch.empty_like(x)
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    M.layer(dl.desc, dl.weights, x, out, ws)
+    torch.cuda.synchronize()
+
+
+def test_decode_step():
+    inp = W.gen_layer(W.BY_NAME["decode"])
+    routed = _routed_only(inp)
+    out_r = DevLayer(routed).run()
+    _, _, ref_r = oracle.layer(routed)
+    err_r = rel_err(out_r, ref_r)
+    out = DevLayer(inp).run()
+    _, _, ref = oracle.layer(inp)
+    err = rel_err(out, ref)
+    print(f"decode routed err={err_r:.3e} full err={err:.3e}")
+    assert err_r <= TOL and err <= TOL
+
+
+def _sampled(name, sample, flags=0):
+    cfg = W.BY_NAME[name]
+    inp = W.gen_layer(cfg)
+    routed = _routed_only(inp)
+    out_r = DevLayer(routed, flags=flags).run()
+    _, _, ref_r = oracle.layer(routed, sample)
+    err_r = rel_err(out_r[sample], ref_r)
+    out = DevLayer(inp, flags=flags).run()
+    _, _, ref = oracle.layer(inp, sample)
+    err = rel_err(out[sample], ref)
+    print(f"{name} sampled routed err={err_r:.3e} full err={err:.3e}")
+    assert err_r <= TOL and err <= TOL
+    assert np.isfinite(out).all() and np.isfinite(out_r).all()
+
+
+def test_prefill_sampled():
+    _sampled("prefill", [0, 1, 2, 1234, 3583, 7167])
+
+
+@pytest.mark.parametrize("name", ["mixed_k3", "mixed_k4"])
+def test_mixed_width_sampled(name):
+    _sampled(name, [0, 5, 1023, 2047])
+
+
+def test_e4m3_codebook_sampled():
+    _sampled("fp8", [0, 8191, 16383])

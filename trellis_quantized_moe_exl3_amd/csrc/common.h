@@ -1,0 +1,44 @@
+// Shared device/host definitions of the HIP library (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef _Float16 f16;
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+
+#define MOE_DEV __device__ __forceinline__
+
+MOE_DEV float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+MOE_DEV float f16_to_f32(uint16_t h) { return (float)__builtin_bit_cast(f16, h); }
+
+// Round-to-nearest-even fp32 -> bf16 bits (inputs are finite).
+MOE_DEV uint16_t f32_to_bf16_bits(float f)
+{
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+MOE_DEV uint16_t f32_to_f16_bits(float f)
+{
+    return __builtin_bit_cast(uint16_t, (f16)f);
+}
+
+// Activation element -> fp32 (activation dtype is fp16 or bf16).
+template <bool BF16>
+MOE_DEV float act_to_f32(uint16_t v)
+{
+    return BF16 ? bf16_to_f32(v) : f16_to_f32(v);
+}
+
+// Wavefront size on CDNA.
+constexpr int kWave = 64;
+
+MOE_DEV float silu_f(float z) { return z / (1.0f + __expf(-z)); }

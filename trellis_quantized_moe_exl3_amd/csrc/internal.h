@@ -1,0 +1,82 @@
+// Internal launchers shared by the host entry points (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Rows of one MFMA work tile (an expert's routed rows are cut into tiles of
+// this many rows) and columns of one gate/up (per projection) and down work
+// tile.
+constexpr int kTileM = 256;
+constexpr int kGateUpN = 128;
+constexpr int kDownN = 256;
+// Entries of the routing table handled by one segment-table block.
+constexpr int kSegChunk = 2048;
+// Largest per-expert row count the GEMV path accepts.
+constexpr int kGemvMaxRows = 8;
+constexpr int kGemvDefaultRows = 4;
+// Tokens up to which the shared expert runs as a GEMV.
+constexpr int kSharedGemvMaxTokens = 16;
+
+// Small header at the start of the workspace, written by the segment kernels.
+struct WsHeader {
+    int32_t n_gemv;    // experts on the GEMV path
+    int32_t n_tiles;   // MFMA work tiles
+    int32_t status;
+    int32_t pad[13];
+};
+
+struct Plan {
+    int64_t T;
+    int nblk;        // segment-table blocks
+    int max_tiles;   // upper bound on MFMA work tiles
+    size_t hdr, logits, idx, w, counts, offsets, bhist, sorted, pos, glist, tiles, x16, hbuf,
+        ybuf, sh, sy, total;
+};
+
+hipError_t launch_route_logits(const uint16_t *x, bool bf16, int64_t T, int H, const uint16_t *Wr,
+                               const float *bias, int E, float *logits, hipStream_t s);
+hipError_t launch_topk(const float *logits, int64_t T, int E, int k, int32_t *idx, float *w,
+                       hipStream_t s);
+hipError_t launch_segments(const int32_t *idx, int64_t T, int k, int E, int nblk, int gemv_rows,
+                           int tile_m, int32_t *bhist, int32_t *counts, int32_t *offsets,
+                           int32_t *sorted, int32_t *pos, int32_t *glist, int32_t *tiles,
+                           WsHeader *hdr, hipStream_t s);
+
+hipError_t launch_decode(const uint16_t *codes, int n_in, int n_out, int K, uint32_t mcg, int cb,
+                         void *dst, int dst_dtype, hipStream_t s);
+
+struct GroupArgs {
+    const uint16_t *codes[3];
+    const uint16_t *suh[3];
+    const uint16_t *svh[3];
+    int H, I, E, k, K, cb;
+    uint32_t mcg;
+    const int32_t *counts, *offsets, *sorted, *glist, *tiles;
+    const WsHeader *hdr;
+    const float *w;          // routing weights [T*k]
+    const uint16_t *x16;     // fp16 activations [T][H]
+    uint16_t *hbuf;          // bf16 [T*k][I], sorted order, h * suh_down
+    float *ybuf;             // fp32 [T*k][H], slot order, w * y
+};
+
+hipError_t launch_convert_x(const uint16_t *x, bool bf16, int64_t n, uint16_t *x16, hipStream_t s);
+hipError_t launch_gemv_gateup(const GroupArgs &a, int max_list, int rows_cap, hipStream_t s);
+hipError_t launch_gemv_down(const GroupArgs &a, int max_list, int rows_cap, hipStream_t s);
+hipError_t launch_mfma_gateup(const GroupArgs &a, int max_tiles, hipStream_t s);
+hipError_t launch_mfma_down(const GroupArgs &a, int max_tiles, hipStream_t s);
+
+hipError_t launch_shared_gateup(const uint16_t *x16, int64_t T, int H, int I, const uint16_t *wg,
+                                const uint16_t *wu, uint16_t *sh, hipStream_t s);
+hipError_t launch_shared_down(const uint16_t *sh, int64_t T, int H, int I, const uint16_t *wd,
+                              float *sy, hipStream_t s);
+hipError_t launch_shared_gemv(const uint16_t *x16, int T, int H, int I, const uint16_t *wg,
+                              const uint16_t *wu, const uint16_t *wd, uint16_t *sh, float *sy,
+                              hipStream_t s);
+hipError_t launch_combine(const float *ybuf, const float *sy, int64_t T, int H, int k, bool bf16,
+                          uint16_t *out, hipStream_t s);
+
+}  // namespace moe

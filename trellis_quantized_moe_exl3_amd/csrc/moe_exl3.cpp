@@ -1,0 +1,378 @@
+// Host side of the C ABI: argument checks, workspace plan, launch sequence.
+// Declarations and the full contract are in include/moe_exl3.h.
+#include "moe_exl3.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "internal.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int gemv_rows_of(const moe_exl3_desc &d)
+{
+    // the GEMV gate/up block keeps x * suh of its rows for both projections
+    // in LDS (2 * rows * hidden fp16 values) and the down block keeps its
+    // rows of h (rows * inter bf16 values), each within 64 KiB
+    const int lds_cap = std::max(1, std::min(16384 / d.hidden, 32768 / d.inter));
+    const int cap = std::min(kGemvMaxRows, lds_cap);
+    if (d.flags & MOE_EXL3_FORCE_MFMA)
+        return 0;
+    if (d.flags & MOE_EXL3_FORCE_GEMV)
+        return cap;
+    const int g = d.gemv_max_rows > 0 ? d.gemv_max_rows : kGemvDefaultRows;
+    return std::min(g, cap);
+}
+
+int check_desc(const moe_exl3_desc *d)
+{
+    if (!d)
+        return MOE_EXL3_ERR_INVALID_ARG;
+    if (d->hidden <= 0 || d->inter <= 0 || d->n_experts <= 0 || d->top_k <= 0)
+        return MOE_EXL3_ERR_INVALID_ARG;
+    if (d->hidden % 256 || d->inter % 128 || d->n_experts % 8)
+        return MOE_EXL3_ERR_INVALID_ARG;
+    if (d->hidden > 16384 || d->inter > 16384 || d->n_experts > 1024 || d->top_k > 16 ||
+        d->top_k > d->n_experts)
+        return MOE_EXL3_ERR_UNSUPPORTED;
+    if (d->K < 2 || d->K > 4)
+        return MOE_EXL3_ERR_UNSUPPORTED;
+    if (d->codebook != MOE_EXL3_CB_MCG && d->codebook != MOE_EXL3_CB_MCG_E4M3)
+        return MOE_EXL3_ERR_UNSUPPORTED;
+    if (d->act_dtype != MOE_EXL3_DT_F16 && d->act_dtype != MOE_EXL3_DT_BF16)
+        return MOE_EXL3_ERR_UNSUPPORTED;
+    if (d->gemv_max_rows < 0)
+        return MOE_EXL3_ERR_INVALID_ARG;
+    if (d->flags & MOE_EXL3_FP8_MFMA)
+        return MOE_EXL3_ERR_UNSUPPORTED;
+    if ((d->flags & MOE_EXL3_FORCE_GEMV) && (d->flags & MOE_EXL3_FORCE_MFMA))
+        return MOE_EXL3_ERR_INVALID_ARG;
+    return MOE_EXL3_OK;
+}
+
+int check_weights(const moe_exl3_desc &d, const moe_exl3_weights *w, bool routing_only)
+{
+    if (!w || !w->router_w)
+        return MOE_EXL3_ERR_INVALID_ARG;
+    if ((d.flags & MOE_EXL3_HAS_ROUTER_BIAS) && !w->router_bias)
+        return MOE_EXL3_ERR_INVALID_ARG;
+    if (!aligned16(w->router_w) || ((d.flags & MOE_EXL3_HAS_ROUTER_BIAS) && !aligned16(w->router_bias)))
+        return MOE_EXL3_ERR_MISALIGNED;
+    if (routing_only)
+        return MOE_EXL3_OK;
+    for (int p = 0; p < 3; ++p) {
+        if (!w->codes[p] || !w->suh[p] || !w->svh[p])
+            return MOE_EXL3_ERR_INVALID_ARG;
+        if (!aligned16(w->codes[p]) || !aligned16(w->suh[p]) || !aligned16(w->svh[p]))
+            return MOE_EXL3_ERR_MISALIGNED;
+        if (d.flags & MOE_EXL3_HAS_SHARED) {
+            if (!w->shared_w[p])
+                return MOE_EXL3_ERR_INVALID_ARG;
+            if (!aligned16(w->shared_w[p]))
+                return MOE_EXL3_ERR_MISALIGNED;
+        }
+    }
+    return MOE_EXL3_OK;
+}
+
+Plan make_plan(const moe_exl3_desc &d, int64_t T)
+{
+    Plan p{};
+    p.T = T;
+    const int64_t n = T * d.top_k;
+    const int E = d.n_experts;
+    p.nblk = (int)std::max<int64_t>(1, (n + kSegChunk - 1) / kSegChunk);
+    const int g = gemv_rows_of(d);
+    const int64_t heavy = std::min<int64_t>(E, n / (g + 1));
+    p.max_tiles = (int)std::max<int64_t>(0, std::min<int64_t>(n / kTileM + heavy, n));
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = o;
+        o = align_up(o + bytes);
+        return at;
+    };
+    p.hdr = take(sizeof(WsHeader));
+    p.logits = take(sizeof(float) * (size_t)T * E);
+    p.idx = take(sizeof(int32_t) * (size_t)n);
+    p.w = take(sizeof(float) * (size_t)n);
+    p.counts = take(sizeof(int32_t) * (size_t)E);
+    p.offsets = take(sizeof(int32_t) * (size_t)(E + 1));
+    p.bhist = take(sizeof(int32_t) * (size_t)p.nblk * E);
+    p.sorted = take(sizeof(int32_t) * (size_t)n);
+    p.pos = take(sizeof(int32_t) * (size_t)n);
+    p.glist = take(sizeof(int32_t) * (size_t)E);
+    p.tiles = take(sizeof(int32_t) * 2 * (size_t)std::max(1, p.max_tiles));
+    p.x16 = take(d.act_dtype == MOE_EXL3_DT_BF16 ? sizeof(uint16_t) * (size_t)T * d.hidden : 0);
+    p.hbuf = take(sizeof(uint16_t) * (size_t)n * d.inter);
+    p.ybuf = take(sizeof(float) * (size_t)n * d.hidden);
+    const bool sh = d.flags & MOE_EXL3_HAS_SHARED;
+    p.sh = take(sh ? sizeof(uint16_t) * (size_t)T * d.inter : 0);
+    p.sy = take(sh ? sizeof(float) * (size_t)T * d.hidden : 0);
+    p.total = o;
+    return p;
+}
+
+template <class T>
+T *at(void *ws, size_t off)
+{
+    return (T *)((char *)ws + off);
+}
+
+// Records events[step] when timing hooks were given.
+struct Marks {
+    void *const *ev = nullptr;
+    hipStream_t s = nullptr;
+    bool mark(int step) const
+    {
+        return !ev || hipEventRecord((hipEvent_t)ev[step], s) == hipSuccess;
+    }
+};
+
+int run_route(const moe_exl3_desc &d, const moe_exl3_weights &w, const void *x, int64_t T,
+              void *ws, const Plan &p, hipStream_t s, const Marks &mk = Marks())
+{
+    const bool bf16 = d.act_dtype == MOE_EXL3_DT_BF16;
+    const float *bias = (d.flags & MOE_EXL3_HAS_ROUTER_BIAS) ? w.router_bias : nullptr;
+    if (!mk.mark(MOE_EXL3_STEP_ROUTE_LOGITS))
+        return MOE_EXL3_ERR_HIP;
+    if (launch_route_logits((const uint16_t *)x, bf16, T, d.hidden, w.router_w, bias, d.n_experts,
+                            at<float>(ws, p.logits), s) != hipSuccess)
+        return MOE_EXL3_ERR_HIP;
+    if (!mk.mark(MOE_EXL3_STEP_TOPK))
+        return MOE_EXL3_ERR_HIP;
+    if (launch_topk(at<float>(ws, p.logits), T, d.n_experts, d.top_k, at<int32_t>(ws, p.idx),
+                    at<float>(ws, p.w), s) != hipSuccess)
+        return MOE_EXL3_ERR_HIP;
+    if (!mk.mark(MOE_EXL3_STEP_SEGMENTS))
+        return MOE_EXL3_ERR_HIP;
+    if (launch_segments(at<int32_t>(ws, p.idx), T, d.top_k, d.n_experts, p.nblk, gemv_rows_of(d),
+                        kTileM, at<int32_t>(ws, p.bhist), at<int32_t>(ws, p.counts),
+                        at<int32_t>(ws, p.offsets), at<int32_t>(ws, p.sorted),
+                        at<int32_t>(ws, p.pos), at<int32_t>(ws, p.glist), at<int32_t>(ws, p.tiles),
+                        at<WsHeader>(ws, p.hdr), s) != hipSuccess)
+        return MOE_EXL3_ERR_HIP;
+    return MOE_EXL3_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_exl3_version(void) { return MOE_EXL3_ABI_VERSION; }
+
+const char *moe_exl3_strerror(int code)
+{
+    switch (code) {
+    case MOE_EXL3_OK: return "ok";
+    case MOE_EXL3_ERR_INVALID_ARG: return "invalid argument (null pointer, negative size or shape rule)";
+    case MOE_EXL3_ERR_UNSUPPORTED: return "unsupported K, dtype, codebook, flag or size";
+    case MOE_EXL3_ERR_WORKSPACE: return "workspace too small";
+    case MOE_EXL3_ERR_MISALIGNED: return "device pointer not 16-byte aligned (workspace: 256-byte)";
+    case MOE_EXL3_ERR_HIP: return "HIP launch error";
+    default: return "unknown error";
+    }
+}
+
+int moe_exl3_workspace_size(const moe_exl3_desc *desc, int64_t max_tokens, size_t *bytes)
+{
+    const int rc = check_desc(desc);
+    if (rc)
+        return rc;
+    if (!bytes || max_tokens < 0)
+        return MOE_EXL3_ERR_INVALID_ARG;
+    if (max_tokens * desc->top_k >= ((int64_t)1 << 31))
+        return MOE_EXL3_ERR_UNSUPPORTED;
+    *bytes = make_plan(*desc, max_tokens).total;
+    return MOE_EXL3_OK;
+}
+
+int moe_exl3_route(const moe_exl3_desc *desc, const moe_exl3_weights *weights, const void *x,
+                   int64_t T, int32_t *idx, float *w, int32_t *counts, int32_t *offsets,
+                   int32_t *sorted_ids, int32_t *pos, void *workspace, size_t ws_bytes, void *stream)
+{
+    int rc = check_desc(desc);
+    if (rc)
+        return rc;
+    if (T < 0)
+        return MOE_EXL3_ERR_INVALID_ARG;
+    if (T * desc->top_k >= ((int64_t)1 << 31))
+        return MOE_EXL3_ERR_UNSUPPORTED;
+    if (T == 0)
+        return MOE_EXL3_OK;
+    rc = check_weights(*desc, weights, true);
+    if (rc)
+        return rc;
+    if (!x || !idx || !workspace)
+        return MOE_EXL3_ERR_INVALID_ARG;
+    if (!aligned16(x) || ((uintptr_t)workspace % kAlign))
+        return MOE_EXL3_ERR_MISALIGNED;
+    const Plan p = make_plan(*desc, T);
+    if (ws_bytes < p.total)
+        return MOE_EXL3_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    rc = run_route(*desc, *weights, x, T, workspace, p, s);
+    if (rc)
+        return rc;
+    const int64_t n = T * desc->top_k;
+    const int E = desc->n_experts;
+    struct Cp { void *dst; size_t off, bytes; } cps[] = {
+        {idx, p.idx, sizeof(int32_t) * (size_t)n},
+        {w, p.w, sizeof(float) * (size_t)n},
+        {counts, p.counts, sizeof(int32_t) * (size_t)E},
+        {offsets, p.offsets, sizeof(int32_t) * (size_t)(E + 1)},
+        {sorted_ids, p.sorted, sizeof(int32_t) * (size_t)n},
+        {pos, p.pos, sizeof(int32_t) * (size_t)n},
+    };
+    for (const Cp &c : cps)
+        if (c.dst && hipMemcpyAsync(c.dst, at<char>(workspace, c.off), c.bytes, hipMemcpyDeviceToDevice, s) != hipSuccess)
+            return MOE_EXL3_ERR_HIP;
+    return MOE_EXL3_OK;
+}
+
+static int run_layer(const moe_exl3_desc *desc, const moe_exl3_weights *weights, const void *x,
+                     int64_t T, void *out, void *workspace, size_t ws_bytes, void *stream,
+                     void *const *events)
+{
+    int rc = check_desc(desc);
+    if (rc)
+        return rc;
+    if (T < 0)
+        return MOE_EXL3_ERR_INVALID_ARG;
+    if (T * desc->top_k >= ((int64_t)1 << 31))
+        return MOE_EXL3_ERR_UNSUPPORTED;
+    if (T == 0)
+        return MOE_EXL3_OK;
+    rc = check_weights(*desc, weights, false);
+    if (rc)
+        return rc;
+    if (!x || !out || !workspace)
+        return MOE_EXL3_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(out) || ((uintptr_t)workspace % kAlign))
+        return MOE_EXL3_ERR_MISALIGNED;
+    const size_t xbytes = sizeof(uint16_t) * (size_t)T * desc->hidden;
+    if ((const char *)out < (const char *)x + xbytes && (const char *)x < (const char *)out + xbytes)
+        return MOE_EXL3_ERR_INVALID_ARG;
+    const Plan p = make_plan(*desc, T);
+    if (ws_bytes < p.total)
+        return MOE_EXL3_ERR_WORKSPACE;
+    const moe_exl3_desc &d = *desc;
+    const moe_exl3_weights &wt = *weights;
+    hipStream_t s = (hipStream_t)stream;
+    void *ws = workspace;
+
+    Marks mk;
+    mk.ev = events;
+    mk.s = s;
+    rc = run_route(d, wt, x, T, ws, p, s, mk);
+    if (rc)
+        return rc;
+    if (!mk.mark(MOE_EXL3_STEP_CONVERT_X))
+        return MOE_EXL3_ERR_HIP;
+    const bool bf16 = d.act_dtype == MOE_EXL3_DT_BF16;
+    const uint16_t *x16 = (const uint16_t *)x;
+    if (bf16) {
+        if (launch_convert_x((const uint16_t *)x, true, T * d.hidden, at<uint16_t>(ws, p.x16), s) != hipSuccess)
+            return MOE_EXL3_ERR_HIP;
+        x16 = at<uint16_t>(ws, p.x16);
+    }
+    GroupArgs ga{};
+    for (int i = 0; i < 3; ++i) {
+        ga.codes[i] = wt.codes[i];
+        ga.suh[i] = wt.suh[i];
+        ga.svh[i] = wt.svh[i];
+    }
+    ga.H = d.hidden;
+    ga.I = d.inter;
+    ga.E = d.n_experts;
+    ga.k = d.top_k;
+    ga.K = d.K;
+    ga.cb = d.codebook;
+    ga.mcg = d.mcg;
+    ga.counts = at<int32_t>(ws, p.counts);
+    ga.offsets = at<int32_t>(ws, p.offsets);
+    ga.sorted = at<int32_t>(ws, p.sorted);
+    ga.glist = at<int32_t>(ws, p.glist);
+    ga.tiles = at<int32_t>(ws, p.tiles);
+    ga.hdr = at<WsHeader>(ws, p.hdr);
+    ga.w = at<float>(ws, p.w);
+    ga.x16 = x16;
+    ga.hbuf = at<uint16_t>(ws, p.hbuf);
+    ga.ybuf = at<float>(ws, p.ybuf);
+    const int g = gemv_rows_of(d);
+    const int64_t n = T * d.top_k;
+    const int max_list = g > 0 ? (int)std::min<int64_t>(d.n_experts, n) : 0;
+
+    if (!mk.mark(MOE_EXL3_STEP_GEMV_GATEUP) || launch_gemv_gateup(ga, max_list, std::max(1, g), s) != hipSuccess ||
+        !mk.mark(MOE_EXL3_STEP_MFMA_GATEUP) || launch_mfma_gateup(ga, p.max_tiles, s) != hipSuccess ||
+        !mk.mark(MOE_EXL3_STEP_GEMV_DOWN) || launch_gemv_down(ga, max_list, std::max(1, g), s) != hipSuccess ||
+        !mk.mark(MOE_EXL3_STEP_MFMA_DOWN) || launch_mfma_down(ga, p.max_tiles, s) != hipSuccess ||
+        !mk.mark(MOE_EXL3_STEP_SHARED))
+        return MOE_EXL3_ERR_HIP;
+
+    float *sy = nullptr;
+    if (d.flags & MOE_EXL3_HAS_SHARED) {
+        uint16_t *sh = at<uint16_t>(ws, p.sh);
+        sy = at<float>(ws, p.sy);
+        hipError_t e;
+        if (T <= kSharedGemvMaxTokens)
+            e = launch_shared_gemv(x16, (int)T, d.hidden, d.inter, wt.shared_w[0], wt.shared_w[1],
+                                   wt.shared_w[2], sh, sy, s);
+        else {
+            e = launch_shared_gateup(x16, T, d.hidden, d.inter, wt.shared_w[0], wt.shared_w[1], sh, s);
+            if (e == hipSuccess)
+                e = launch_shared_down(sh, T, d.hidden, d.inter, wt.shared_w[2], sy, s);
+        }
+        if (e != hipSuccess)
+            return MOE_EXL3_ERR_HIP;
+    }
+    if (!mk.mark(MOE_EXL3_STEP_COMBINE) ||
+        launch_combine(at<float>(ws, p.ybuf), sy, T, d.hidden, d.top_k, bf16, (uint16_t *)out, s) != hipSuccess ||
+        !mk.mark(MOE_EXL3_STEP_END))
+        return MOE_EXL3_ERR_HIP;
+    return MOE_EXL3_OK;
+}
+
+int moe_exl3_layer(const moe_exl3_desc *desc, const moe_exl3_weights *weights, const void *x,
+                   int64_t T, void *out, void *workspace, size_t ws_bytes, void *stream)
+{
+    return run_layer(desc, weights, x, T, out, workspace, ws_bytes, stream, nullptr);
+}
+
+int moe_exl3_layer_profiled(const moe_exl3_desc *desc, const moe_exl3_weights *weights,
+                            const void *x, int64_t T, void *out, void *workspace, size_t ws_bytes,
+                            void *stream, void *const *events, int n_events)
+{
+    if (!events || n_events != MOE_EXL3_STEP_END + 1)
+        return MOE_EXL3_ERR_INVALID_ARG;
+    for (int i = 0; i < n_events; ++i)
+        if (!events[i])
+            return MOE_EXL3_ERR_INVALID_ARG;
+    return run_layer(desc, weights, x, T, out, workspace, ws_bytes, stream, events);
+}
+
+
+int moe_exl3_decode(const uint16_t *codes, int32_t n_in, int32_t n_out, int32_t K, uint32_t mcg,
+                    int32_t codebook, void *dst, int32_t dst_dtype, void *stream)
+{
+    if (!codes || !dst || n_in <= 0 || n_out <= 0 || n_in % 16 || n_out % 16)
+        return MOE_EXL3_ERR_INVALID_ARG;
+    if (K < 2 || K > 4 || (codebook != MOE_EXL3_CB_MCG && codebook != MOE_EXL3_CB_MCG_E4M3) ||
+        dst_dtype < MOE_EXL3_DT_F32 || dst_dtype > MOE_EXL3_DT_FP8)
+        return MOE_EXL3_ERR_UNSUPPORTED;
+    if (!aligned16(codes) || !aligned16(dst))
+        return MOE_EXL3_ERR_MISALIGNED;
+    if (launch_decode(codes, n_in, n_out, K, mcg, codebook, dst, dst_dtype, (hipStream_t)stream) != hipSuccess)
+        return MOE_EXL3_ERR_HIP;
+    return MOE_EXL3_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,309 @@
+// Routing (fp32 router logits in a fixed order, top-k, softmax) and
+// device-side segment tables (page "GLM-5.3 Flash EXL3 for 2x DGX Sparks",
+// "Cold prefill (E3 grouped MoE)": segment tables built on the device, no
+// per-expert launches, no host sync).
+#include "common.h"
+#include "internal.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------- router logits
+// One wavefront computes an 8-token x 8-expert block of logits.  Lane l owns
+// the hidden indices h = 64i + l and accumulates, for i in order, the exact
+// fp32 products x*w of every (token, expert) pair of the block (a bf16/fp16 by
+// fp16 product has at most 19 significant bits, so fma == add of the product).
+// The 64 lane partials of each logit then go through LDS to one lane, which
+// adds them with the halving tree p[l] += p[l + d], d = 32 .. 1.
+constexpr int kRT = 8, kRE = 8;
+
+template <bool BF16>
+__global__ __launch_bounds__(64) void route_logits_kernel(const uint16_t *__restrict__ x, int64_t T,
+                                                          int H, const uint16_t *__restrict__ Wr,
+                                                          const float *__restrict__ bias, int E,
+                                                          float *__restrict__ logits)
+{
+    __shared__ float part[kRT * kRE][65];
+    const int l = threadIdx.x;
+    const int64_t t0 = (int64_t)blockIdx.x * kRT;
+    const int e0 = blockIdx.y * kRE;
+    float p[kRT][kRE];
+#pragma unroll
+    for (int a = 0; a < kRT; ++a)
+#pragma unroll
+        for (int b = 0; b < kRE; ++b)
+            p[a][b] = 0.0f;
+    const uint16_t *xr[kRT];
+#pragma unroll
+    for (int a = 0; a < kRT; ++a)
+        xr[a] = x + (t0 + a < T ? t0 + a : t0) * (int64_t)H;
+    const int nt = (int)(T - t0 < kRT ? T - t0 : kRT);
+    for (int i = 0; i < H / 64; ++i) {
+        const int hh = 64 * i + l;
+        float xv[kRT], wv[kRE];
+#pragma unroll
+        for (int a = 0; a < kRT; ++a)
+            xv[a] = a < nt ? act_to_f32<BF16>(xr[a][hh]) : 0.0f;
+#pragma unroll
+        for (int b = 0; b < kRE; ++b)
+            wv[b] = f16_to_f32(Wr[(int64_t)(e0 + b) * H + hh]);
+#pragma unroll
+        for (int a = 0; a < kRT; ++a)
+#pragma unroll
+            for (int b = 0; b < kRE; ++b)
+                p[a][b] = __builtin_fmaf(xv[a], wv[b], p[a][b]);
+    }
+#pragma unroll
+    for (int a = 0; a < kRT; ++a)
+#pragma unroll
+        for (int b = 0; b < kRE; ++b)
+            part[a * kRE + b][l] = p[a][b];
+    __syncthreads();
+    // lane q reduces logit q of the block
+    const int q = l;
+    float r[64];
+#pragma unroll
+    for (int j = 0; j < 64; ++j)
+        r[j] = part[q][j];
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1)
+#pragma unroll
+        for (int j = 0; j < d; ++j)
+            r[j] = r[j] + r[j + d];
+    const int a = q / kRE, b = q % kRE;
+    if (a < nt) {
+        const float lg = bias ? r[0] + bias[e0 + b] : r[0];
+        logits[(t0 + a) * E + e0 + b] = lg;
+    }
+}
+
+hipError_t launch_route_logits(const uint16_t *x, bool bf16, int64_t T, int H, const uint16_t *Wr,
+                               const float *bias, int E, float *logits, hipStream_t s)
+{
+    dim3 grid((unsigned)((T + kRT - 1) / kRT), (unsigned)(E / kRE));
+    if (bf16)
+        route_logits_kernel<true><<<grid, 64, 0, s>>>(x, T, H, Wr, bias, E, logits);
+    else
+        route_logits_kernel<false><<<grid, 64, 0, s>>>(x, T, H, Wr, bias, E, logits);
+    return hipGetLastError();
+}
+
+// ----------------------------------------------------------------- top-k, softmax
+// One wavefront per token.  Lane l holds the logits of experts l, l+64, ...;
+// k rounds of a wavefront arg-max by (logit desc, expert asc).
+constexpr int kTopkMaxPerLane = 16;   // E <= 1024
+
+__global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits, int64_t T,
+                                                   int E, int k, int32_t *__restrict__ idx,
+                                                   float *__restrict__ w)
+{
+    const int l = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T)
+        return;
+    float v[kTopkMaxPerLane];
+    int key[kTopkMaxPerLane];
+    const int nper = (E + 63) / 64;
+#pragma unroll
+    for (int i = 0; i < kTopkMaxPerLane; ++i) {
+        const int e = l + 64 * i;
+        const bool ok = i < nper && e < E;
+        v[i] = ok ? logits[t * E + e] : -INFINITY;
+        key[i] = ok ? e : 0x7fffffff;
+    }
+    float selv[16];
+    int seli[16];
+    for (int j = 0; j < k; ++j) {
+        float bv = -INFINITY;
+        int bi = 0x7fffffff;
+#pragma unroll
+        for (int i = 0; i < kTopkMaxPerLane; ++i) {
+            if (key[i] != 0x7fffffff && (v[i] > bv || (v[i] == bv && key[i] < bi))) {
+                bv = v[i];
+                bi = key[i];
+            }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            const float ov = __shfl_xor(bv, off, 64);
+            const int oi = __shfl_xor(bi, off, 64);
+            if (oi != 0x7fffffff && (bi == 0x7fffffff || ov > bv || (ov == bv && oi < bi))) {
+                bv = ov;
+                bi = oi;
+            }
+        }
+        selv[j] = bv;
+        seli[j] = bi;
+        if ((bi & 63) == l) {
+#pragma unroll
+            for (int i = 0; i < kTopkMaxPerLane; ++i)
+                if (key[i] == bi)
+                    key[i] = 0x7fffffff;
+        }
+    }
+    if (l == 0) {
+        float sum = 0.0f;
+        for (int j = 0; j < k; ++j)
+            sum += expf(selv[j] - selv[0]);
+        for (int j = 0; j < k; ++j) {
+            idx[t * k + j] = seli[j];
+            w[t * k + j] = expf(selv[j] - selv[0]) / sum;
+        }
+    }
+}
+
+hipError_t launch_topk(const float *logits, int64_t T, int E, int k, int32_t *idx, float *w,
+                       hipStream_t s)
+{
+    topk_kernel<<<(unsigned)((T + 3) / 4), 256, 0, s>>>(logits, T, E, k, idx, w);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- segment tables
+// Stable counting sort of the slots a = t*k + j by expert, in three launches:
+//  1. per-block expert histograms of kSegChunk consecutive slots;
+//  2. one block: per-expert running sums over blocks, counts, exclusive
+//     offsets, and the work lists (GEMV experts, MFMA row tiles);
+//  3. per block, slots in order: rank inside each 64-slot chunk from ballots,
+//     position = block base + rank.
+
+__global__ __launch_bounds__(256) void seg_hist_kernel(const int32_t *__restrict__ idx, int64_t n,
+                                                       int E, int32_t *__restrict__ bhist)
+{
+    extern __shared__ int32_t hist[];
+    for (int e = threadIdx.x; e < E; e += blockDim.x)
+        hist[e] = 0;
+    __syncthreads();
+    const int64_t a0 = (int64_t)blockIdx.x * kSegChunk;
+    for (int i = threadIdx.x; i < kSegChunk; i += blockDim.x) {
+        const int64_t a = a0 + i;
+        if (a < n)
+            atomicAdd(&hist[idx[a]], 1);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x)
+        bhist[(int64_t)blockIdx.x * E + e] = hist[e];
+}
+
+// Block-wide exclusive scan of one value per thread (blockDim.x == 1024).
+__device__ int block_exclusive_scan(int v, int *total)
+{
+    __shared__ int wsum[16];
+    const int l = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(incl, off, 64);
+        if (l >= off)
+            incl += o;
+    }
+    if (l == 63)
+        wsum[wv] = incl;
+    __syncthreads();
+    int base = 0, tot = 0;
+    for (int i = 0; i < 16; ++i) {
+        if (i < wv)
+            base += wsum[i];
+        tot += wsum[i];
+    }
+    __syncthreads();
+    *total = tot;
+    return base + incl - v;
+}
+
+__global__ __launch_bounds__(1024) void seg_scan_kernel(int32_t *__restrict__ bhist, int nblk, int E,
+                                                        int gemv_rows, int tile_m,
+                                                        int32_t *__restrict__ counts,
+                                                        int32_t *__restrict__ offsets,
+                                                        int32_t *__restrict__ glist,
+                                                        int32_t *__restrict__ tiles,
+                                                        WsHeader *__restrict__ hdr)
+{
+    const int e = threadIdx.x;   // E <= 1024
+    int c = 0;
+    if (e < E) {
+        for (int b = 0; b < nblk; ++b) {
+            const int v = bhist[(int64_t)b * E + e];
+            bhist[(int64_t)b * E + e] = c;
+            c += v;
+        }
+    }
+    int tot;
+    const int off = block_exclusive_scan(e < E ? c : 0, &tot);
+    if (e < E) {
+        counts[e] = c;
+        offsets[e] = off;
+    }
+    if (e == 0)
+        offsets[E] = tot;
+    const bool gemv = e < E && c > 0 && c <= gemv_rows;
+    const int nt = (e < E && c > gemv_rows) ? (c + tile_m - 1) / tile_m : 0;
+    int ng, ntt;
+    const int gpos = block_exclusive_scan(gemv ? 1 : 0, &ng);
+    const int tpos = block_exclusive_scan(nt, &ntt);
+    if (gemv)
+        glist[gpos] = e;
+    for (int m = 0; m < nt; ++m) {
+        tiles[2 * (tpos + m)] = e;
+        tiles[2 * (tpos + m) + 1] = m * tile_m;
+    }
+    if (e == 0) {
+        hdr->n_gemv = ng;
+        hdr->n_tiles = ntt;
+        hdr->status = 0;
+    }
+}
+
+__global__ __launch_bounds__(64) void seg_scatter_kernel(const int32_t *__restrict__ idx, int64_t n,
+                                                         int E, const int32_t *__restrict__ bhist,
+                                                         const int32_t *__restrict__ offsets,
+                                                         int32_t *__restrict__ sorted,
+                                                         int32_t *__restrict__ pos)
+{
+    extern __shared__ int32_t base[];
+    for (int e = threadIdx.x; e < E; e += 64)
+        base[e] = bhist[(int64_t)blockIdx.x * E + e] + offsets[e];
+    __syncthreads();
+    const int l = threadIdx.x;
+    const int64_t a0 = (int64_t)blockIdx.x * kSegChunk;
+    int nbits = 0;
+    while ((1 << nbits) < E)
+        ++nbits;
+    const uint64_t below = (l == 0) ? 0ull : (~0ull >> (64 - l));
+    for (int c0 = 0; c0 < kSegChunk; c0 += 64) {
+        const int64_t a = a0 + c0 + l;
+        const bool valid = a < n;
+        const int e = valid ? idx[a] : 0;
+        uint64_t m = __ballot(valid);
+        for (int b = 0; b < nbits; ++b) {
+            const bool bit = (e >> b) & 1;
+            const uint64_t bb = __ballot(bit);
+            m &= bit ? bb : ~bb;
+        }
+        if (valid) {
+            const int rank = __popcll(m & below);
+            const int p = base[e] + rank;
+            sorted[p] = (int32_t)a;
+            pos[a] = p;
+        }
+        __syncthreads();
+        if (valid && (m >> l) == 1ull)   // last lane of its expert in this chunk
+            base[e] += __popcll(m);
+        __syncthreads();
+    }
+}
+
+hipError_t launch_segments(const int32_t *idx, int64_t T, int k, int E, int nblk, int gemv_rows,
+                           int tile_m, int32_t *bhist, int32_t *counts, int32_t *offsets,
+                           int32_t *sorted, int32_t *pos, int32_t *glist, int32_t *tiles,
+                           WsHeader *hdr, hipStream_t s)
+{
+    const int64_t n = T * k;
+    const size_t lds = sizeof(int32_t) * (size_t)E;
+    seg_hist_kernel<<<nblk, 256, lds, s>>>(idx, n, E, bhist);
+    seg_scan_kernel<<<1, 1024, 0, s>>>(bhist, nblk, E, gemv_rows, tile_m, counts, offsets, glist,
+                                       tiles, hdr);
+    seg_scatter_kernel<<<nblk, 64, lds, s>>>(idx, n, E, bhist, offsets, sorted, pos);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,173 @@
+// Trellis decode on gfx950: K-bit tail-biting streams in 16x16 tiles, mcg
+// codebook (optionally E4M3-rounded).
+//
+// Storage (page "GLM-5.3-Flash EXL3 (~2.1 bpw, SM70 tile order)", header:
+// packed 16-bit words holding 16/K weights each; page "GLM-5.3-Flash EXL3 K2",
+// "What is in the shards": per-tensor `trellis`, `suh`, `svh`, int32 `mcg`):
+//   * a tile is 16*K little-endian 16-bit words = 8*K dwords = 256*K bits;
+//   * the stream reads word 0 first, most significant bit first;
+//   * state j (0..255) is the 16-bit window starting at stream bit j*K, read
+//     circularly inside the tile (tail-biting);
+//   * state j holds the weight at input row j % 16, output column j / 16 of
+//     the tile, so eight consecutive states are eight consecutive input rows of
+//     one output column: exactly the eight k-values one lane feeds to an MFMA
+//     operand or to a dot product;
+//   * value map: h = (mcg * s) mod 2^32, v = sum_{i<4} ((h >> (8i+1)) & 127) - 254,
+//     weight c = v / 64 (E4M3 variant: c rounded to FP8 E4M3, nearest-even;
+//     page "GLM-5.3-Flash . exlr8 (K2/K3/K4)", opening paragraph).
+//
+// A lane "fragment" is (tile column c in 0..15, k-half h in 0..1): states
+// j = 16c + 8h + t for t = 0..7.  Its 7K+16 window bits start at bit K*(16c+8h)
+// and always fit in two consecutive dwords of the tile (the second one wraps to
+// dword 0 at the end of the tile).
+//
+// Instruction budget per weight (gfx950): one shift/alignbit for the window,
+// two 16-bit multiplies for the 32-bit hash, one AND and one SAD for the four
+// field sum, then half an op each to pack and re-centre two fp16 values.
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+template <int K>
+struct Tile {
+    static constexpr int kDwords = 8 * K;
+    static constexpr int kBytes = 32 * K;
+};
+
+// First/second dword of a lane fragment and the bit offset inside the first.
+template <int K>
+MOE_DEV void frag_pos(int c, int h, int &d0, int &d1, int &q)
+{
+    const int b0 = K * (16 * c + 8 * h);
+    d0 = b0 >> 5;
+    q = b0 & 31;
+    d1 = (d0 + 1 == Tile<K>::kDwords) ? 0 : d0 + 1;
+}
+
+// The eight 16-bit states of a fragment from its two raw dwords; state t ends
+// up in the low 16 bits of st[t] (upper bits are not cleared: every consumer
+// reads 16-bit operands).
+template <int K>
+MOE_DEV void frag_states(uint32_t D0, uint32_t D1, int q, uint32_t st[8])
+{
+    // the stream reads the low word of a little-endian dword first
+    const uint32_t S0 = __builtin_amdgcn_alignbit(D0, D0, 16);
+    const uint32_t S1 = __builtin_amdgcn_alignbit(D1, D1, 16);
+    uint32_t A, Bn;
+    if (K == 4) {   // fragment windows start on dword boundaries
+        A = S0;
+        Bn = S1;
+    } else {
+        const uint64_t w = ((uint64_t)S0 << 32) | S1;
+        A = (uint32_t)(w >> (32 - q));   // window bits [0, 32) relative to q
+        Bn = S1 << q;                    // window bits [32, 64 - q)
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const int o = K * t;
+        if (o <= 16)
+            st[t] = A >> (16 - o);
+        else
+            st[t] = __builtin_amdgcn_alignbit(A, Bn, 48 - o);
+    }
+}
+
+// (mcg * s) mod 2^32 for the low 16 bits of s, with mcg split into 16-bit
+// halves: s*lo + ((s*hi) mod 2^16) << 16.  Two full-rate 16-bit multiplies
+// (the SDWA form writes the high half and zeroes the low half) instead of one
+// quarter-rate 32-bit multiply.
+MOE_DEV uint32_t mcg_hash(uint32_t s, uint32_t m_lo, uint32_t m_hi)
+{
+    uint32_t t, h;
+    asm("v_mul_lo_u16_sdwa %0, %1, %2 dst_sel:WORD_1 dst_unused:UNUSED_PAD src0_sel:WORD_0 src1_sel:WORD_0"
+        : "=v"(t) : "v"(s), "v"(m_hi));
+    asm("v_mad_u32_u16 %0, %1, %2, %3" : "=v"(h) : "v"(s), "v"(m_lo), "v"(t));
+    return h;
+}
+
+// base + 2 * sum of the four 7-bit fields (bits 1..7 of every byte of h).
+MOE_DEV uint32_t field_sum2(uint32_t h, uint32_t base)
+{
+    return __builtin_amdgcn_sad_u8(h & 0xFEFEFEFEu, 0u, base);
+}
+
+// 2v as an exact fp32 value.
+MOE_DEV float value2_f32(uint32_t s, uint32_t m_lo, uint32_t m_hi)
+{
+    // bits 0x4B000000 + n are the float 2^23 + n (n < 2^23)
+    const float r = __uint_as_float(field_sum2(mcg_hash(s, m_lo, m_hi), 0x4B000000u));
+    return r - 8389116.0f;   // 2^23 + 508
+}
+
+// E4M3 rounding of c = 2v / 128, returned as 128 * c8 (exact in fp32).
+MOE_DEV float e4m3_value2(float v2)
+{
+    const uint32_t b = __builtin_amdgcn_cvt_pk_fp8_f32(v2 * (1.0f / 128.0f), 0.0f, 0, false);
+    return __builtin_amdgcn_cvt_f32_fp8(b, 0) * 128.0f;
+}
+
+enum { CB_MCG = 0, CB_MCG_E4M3 = 1 };
+
+// Fragment -> eight exact fp16 values of 2v (or 128 * E4M3(v/64)).
+template <int K, int CB>
+MOE_DEV f16x8 frag_decode_f16(uint32_t D0, uint32_t D1, int q, uint32_t m_lo, uint32_t m_hi)
+{
+    uint32_t st[8];
+    frag_states<K>(D0, D1, q, st);
+    f16x8 out;
+    if (CB == CB_MCG) {
+#pragma unroll
+        for (int t = 0; t < 8; t += 2) {
+            // bits 0x6400 + n are the half 1024 + n (n < 1024)
+            const uint32_t ra = field_sum2(mcg_hash(st[t], m_lo, m_hi), 0x6400u);
+            const uint32_t rb = field_sum2(mcg_hash(st[t + 1], m_lo, m_hi), 0x6400u);
+            const f16x2 p = __builtin_bit_cast(f16x2, ra | (rb << 16));
+            const f16x2 v = p - (f16x2){(f16)1532.0f, (f16)1532.0f};   // 1024 + 508
+            out[t] = v[0];
+            out[t + 1] = v[1];
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+            out[t] = (f16)e4m3_value2(value2_f32(st[t], m_lo, m_hi));
+    }
+    return out;
+}
+
+// Fragment -> eight exact bf16 values of 2v (or 128 * E4M3(v/64)).
+template <int K, int CB>
+MOE_DEV bf16x8 frag_decode_bf16(uint32_t D0, uint32_t D1, int q, uint32_t m_lo, uint32_t m_hi)
+{
+    uint32_t st[8];
+    frag_states<K>(D0, D1, q, st);
+    u32x4 pk;
+#pragma unroll
+    for (int t = 0; t < 8; t += 2) {
+        float a = value2_f32(st[t], m_lo, m_hi);
+        float b = value2_f32(st[t + 1], m_lo, m_hi);
+        if (CB == CB_MCG_E4M3) {
+            a = e4m3_value2(a);
+            b = e4m3_value2(b);
+        }
+        // |2v| <= 512 has at most 8 significant bits: truncation is exact
+        pk[t / 2] = __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
+    }
+    return __builtin_bit_cast(bf16x8, pk);
+}
+
+// Fragment -> eight fp32 values of 2v (or 128 * E4M3(v/64)).
+template <int K, int CB>
+MOE_DEV void frag_decode_f32(uint32_t D0, uint32_t D1, int q, uint32_t m_lo, uint32_t m_hi, float out[8])
+{
+    uint32_t st[8];
+    frag_states<K>(D0, D1, q, st);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const float v = value2_f32(st[t], m_lo, m_hi);
+        out[t] = CB == CB_MCG_E4M3 ? e4m3_value2(v) : v;
+    }
+}
+
+}  // namespace moe

@@ -132,8 +132,8 @@ def gen_x(cfg: LayerConfig, tokens: Optional[int] = None) -> np.ndarray:
 
 def gen_router_w(cfg: LayerConfig) -> np.ndarray:
     """Router weights [E][H] fp16 ~ N(0, 0.02)."""
-    v = _rng(cfg.seed, "router_w").normal(0.0, 0.02, (cfg.n_experts, cfg.hidden))
-    return v.astype(np.float16)
+    v = _rng(cfg.seed, "router_w").standard_normal((cfg.n_experts, cfg.hidden), dtype=np.float32)
+    return (v * np.float32(0.02)).astype(np.float16)
 
 
 def gen_router_bias(cfg: LayerConfig) -> Optional[np.ndarray]:
@@ -148,14 +148,14 @@ def gen_codes_expert(cfg: LayerConfig, p: int, e: int) -> np.ndarray:
         0, 1 << 16, size=cfg.words_per_expert(p), dtype=np.uint16)
 
 
-def gen_codes(cfg: LayerConfig, p: int, experts=None) -> np.ndarray:
-    """Codes of projection p for all experts, [E][words] (row e for expert e).
-
-    With `experts` given, only those rows are drawn; the others stay zero.
-    """
+def gen_codes(cfg: LayerConfig, p: int, experts=None):
+    """Codes of projection p: [E][words] for all experts, or, with `experts`
+    given, a dict {expert: words} holding only those experts."""
+    if experts is not None:
+        return {int(e): gen_codes_expert(cfg, p, int(e)) for e in experts}
     n = cfg.words_per_expert(p)
-    out = np.zeros((cfg.n_experts, n), dtype=np.uint16)
-    for e in (range(cfg.n_experts) if experts is None else experts):
+    out = np.empty((cfg.n_experts, n), dtype=np.uint16)
+    for e in range(cfg.n_experts):
         out[e] = gen_codes_expert(cfg, p, e)
     return out
 
@@ -177,8 +177,8 @@ def gen_shared(cfg: LayerConfig):
     H, I = cfg.hidden, cfg.inter
     out = []
     for p, shp in ((0, (I, H)), (1, (I, H)), (2, (H, I))):
-        v = _rng(cfg.seed, "shared", p).normal(0.0, 1.0 / 64.0, shp)
-        out.append(v.astype(np.float16))
+        v = _rng(cfg.seed, "shared", p).standard_normal(shp, dtype=np.float32)
+        out.append((v * np.float32(1.0 / 64.0)).astype(np.float16))
     return out
 
 
@@ -188,7 +188,7 @@ class LayerInputs:
     x: np.ndarray                      # [T][H] uint16 bits of act dtype
     router_w: np.ndarray               # [E][H] fp16
     router_bias: Optional[np.ndarray]  # [E] fp32 or None
-    codes: List[np.ndarray]            # 3 x [E][words] uint16
+    codes: list                        # 3 x ([E][words] uint16, or {expert: words})
     suh: List[np.ndarray]              # 3 x [E][in] fp16
     svh: List[np.ndarray]              # 3 x [E][out] fp16
     shared: Optional[List[np.ndarray]]
