@@ -41,4 +41,5 @@ MOE_DEV float act_to_f32(uint16_t v)
 // Wavefront size on CDNA.
 constexpr int kWave = 64;
 
-MOE_DEV float silu_f(float z) { return z / (1.0f + __expf(-z)); }
+// silu(z) = z / (1 + e^-z) with the hardware reciprocal (about 1 ulp)
+MOE_DEV float silu_f(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }

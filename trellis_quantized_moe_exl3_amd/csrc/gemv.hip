@@ -15,14 +15,95 @@
 
 namespace moe {
 
-constexpr int kGemvU = 8;   // tile rows per prefetch group
+constexpr int kGemvU = 8;      // tile rows per prefetch group
+constexpr int kGemvPass = 2;   // routed rows per pass over the codes
+
+// 1532 * (row sum), the re-centring of the biased decoded values.
+constexpr float kBias2 = 1532.0f;
+
+// Deterministic block sum (256 threads) of one float per thread.
+MOE_DEV float block_sum256(float v, float *part)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        v += __shfl_xor(v, off, 64);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0)
+        part[threadIdx.x >> 6] = v;
+    __syncthreads();
+    return ((part[0] + part[1]) + part[2]) + part[3];
+}
+
+// Each lane decodes a fragment of tile rows and accumulates x * (2v + 1532)
+// into acc[r] with one v_fma_mix_f32 per weight and row (fp16 operands, exact
+// products, fp32 accumulation).  Code words are prefetched kGemvU tile rows
+// ahead.  XS(r, kk) returns the 8 activation values of row r at input rows
+// kk + 8h .. kk + 8h + 7 for the lane.
+template <int K, int CB, int NR, class XS>
+MOE_DEV void gemv_stream(const uint32_t *cb, int64_t rstride, int ntk, int d0, int d1, int q,
+                         uint32_t m_lo, uint32_t m_hi, int nr, XS xs, float acc[NR])
+{
+    uint32_t nx[kGemvU][2];
+#pragma unroll
+    for (int u = 0; u < kGemvU; ++u) {
+        nx[u][0] = cb[u * rstride + d0];
+        nx[u][1] = cb[u * rstride + d1];
+    }
+    for (int g = 0; g < ntk; g += kGemvU) {
+        uint32_t cu[kGemvU][2];
+#pragma unroll
+        for (int u = 0; u < kGemvU; ++u) {
+            cu[u][0] = nx[u][0];
+            cu[u][1] = nx[u][1];
+        }
+        if (g + kGemvU < ntk) {
+            const uint32_t *nb = cb + (int64_t)(g + kGemvU) * rstride;
+#pragma unroll
+            for (int u = 0; u < kGemvU; ++u) {
+                nx[u][0] = nb[u * rstride + d0];
+                nx[u][1] = nb[u * rstride + d1];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kGemvU; ++u) {
+            uint32_t st[8];
+            frag_states<K>(cu[u][0], cu[u][1], q, st);
+            f16 wv[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                if (CB == CB_MCG) {
+                    wv[t] = __builtin_bit_cast(f16, (uint16_t)value2_biased_f16bits(st[t], m_lo, m_hi));
+                } else {
+                    wv[t] = (f16)(e4m3_value2(value2_f32(st[t], m_lo, m_hi)) + kBias2);
+                }
+            }
+            const int kk = 16 * (g + u);
+#pragma unroll
+            for (int r = 0; r < NR; ++r) {
+                if (r < nr) {
+                    float xv[8];
+                    xs(r, kk, xv);
+                    float s = acc[r];
+#pragma unroll
+                    for (int t = 0; t < 8; ++t)
+                        s = __builtin_fmaf((float)wv[t], xv[t], s);
+                    acc[r] = s;
+                }
+            }
+        }
+    }
+}
 
 // gate/up + SwiGLU.  Block = 4 wavefronts = (gate, up) x 2 tile pairs = 64
-// output columns of one expert; grid.x walks the GEMV expert list.
+// output columns of one expert; grid.x walks the GEMV expert list.  Rows are
+// processed kGemvPass at a time (x * suh of the pass in LDS, fp16).
 template <int K, int CB>
-__global__ __launch_bounds__(256) void gemv_gateup_kernel(GroupArgs a, int rows_cap)
+__global__ __launch_bounds__(256) void gemv_gateup_kernel(GroupArgs a)
 {
     extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ float part[4];
+    __shared__ float rsum[2][kGemvPass];
+    __shared__ float gu[2][kGemvPass][64];
     const int li = blockIdx.x;
     if (li >= a.hdr->n_gemv)
         return;
@@ -31,20 +112,7 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(GroupArgs a, int rows_
     const int R = a.counts[e];
     const int p0 = a.offsets[e];
     const int n0 = blockIdx.y * 64;
-    f16 *xs = (f16 *)smem;      // [2][rows_cap][H]
-    float *gu = (float *)smem;  // [2][rows_cap][64], reuses xs after the main loop
-
-    // x * suh for both projections, fp16
-    const int nchunk = H / 8;
-    for (int i = threadIdx.x; i < 2 * R * nchunk; i += 256) {
-        const int pr = i / (R * nchunk), rem = i % (R * nchunk);
-        const int r = rem / nchunk, ch = rem % nchunk;
-        const int t = a.sorted[p0 + r] / a.k;
-        const f16x8 xv = *(const f16x8 *)(a.x16 + (int64_t)t * H + 8 * ch);
-        const f16x8 sv = *(const f16x8 *)(a.suh[pr] + (int64_t)e * H + 8 * ch);
-        *(f16x8 *)(xs + ((size_t)pr * rows_cap + r) * H + 8 * ch) = xv * sv;
-    }
-    __syncthreads();
+    f16 *xs = (f16 *)smem;   // [2][kGemvPass][H]
 
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
     const int pr = w >> 1, tp = w & 1;
@@ -56,84 +124,67 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(GroupArgs a, int rows_
     const uint32_t *cb = (const uint32_t *)a.codes[pr] + e * per_expert + (int64_t)tn * Tile<K>::kDwords;
     const int64_t rstride = (int64_t)(I / 16) * Tile<K>::kDwords;
     const uint32_t m_lo = a.mcg & 0xFFFFu, m_hi = a.mcg >> 16;
-    const f16 *xsp = xs + (size_t)pr * rows_cap * H + 8 * h;
-
-    float acc[kGemvMaxRows];
-#pragma unroll
-    for (int r = 0; r < kGemvMaxRows; ++r)
-        acc[r] = 0.0f;
-
-    const int ntk = H / 16;
-    uint32_t nx[kGemvU][2];
-#pragma unroll
-    for (int u = 0; u < kGemvU; ++u) {
-        nx[u][0] = cb[u * rstride + d0];
-        nx[u][1] = cb[u * rstride + d1];
-    }
-    for (int g = 0; g < ntk; g += kGemvU) {
-        uint32_t cu[kGemvU][2];
-#pragma unroll
-        for (int u = 0; u < kGemvU; ++u) {
-            cu[u][0] = nx[u][0];
-            cu[u][1] = nx[u][1];
-        }
-        if (g + kGemvU < ntk) {
-            const uint32_t *nb = cb + (int64_t)(g + kGemvU) * rstride;
-#pragma unroll
-            for (int u = 0; u < kGemvU; ++u) {
-                nx[u][0] = nb[u * rstride + d0];
-                nx[u][1] = nb[u * rstride + d1];
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < kGemvU; ++u) {
-            const f16x8 v = frag_decode_f16<K, CB>(cu[u][0], cu[u][1], q, m_lo, m_hi);
-            const int kk = 16 * (g + u);
-#pragma unroll
-            for (int r = 0; r < kGemvMaxRows; ++r) {
-                if (r < R && r < rows_cap) {
-                    const f16x8 xv = *(const f16x8 *)(xsp + (size_t)r * H + kk);
-                    float s = acc[r];
-                    s = __builtin_amdgcn_fdot2((f16x2){v[0], v[1]}, (f16x2){xv[0], xv[1]}, s, false);
-                    s = __builtin_amdgcn_fdot2((f16x2){v[2], v[3]}, (f16x2){xv[2], xv[3]}, s, false);
-                    s = __builtin_amdgcn_fdot2((f16x2){v[4], v[5]}, (f16x2){xv[4], xv[5]}, s, false);
-                    s = __builtin_amdgcn_fdot2((f16x2){v[6], v[7]}, (f16x2){xv[6], xv[7]}, s, false);
-                    acc[r] = s;
-                }
-            }
-        }
-    }
-    // the two k-halves of a column sit in lanes l and l ^ 32
     const int col = 16 * (2 * tp + ts) + c;
     const float svh = f16_to_f32(a.svh[pr][(int64_t)e * I + n0 + col]) * (1.0f / 128.0f);
-    float tot[kGemvMaxRows];
+
+    for (int r0 = 0; r0 < R; r0 += kGemvPass) {
+        const int nr = min(kGemvPass, R - r0);
+        // x * suh of the pass's rows for both projections, and their sums
+        for (int pp = 0; pp < 2; ++pp)
+            for (int r = 0; r < nr; ++r) {
+                const int t = a.sorted[p0 + r0 + r] / a.k;
+                float sum = 0.0f;
+                for (int ch = threadIdx.x; ch < H / 8; ch += 256) {
+                    const f16x8 xv = *(const f16x8 *)(a.x16 + (int64_t)t * H + 8 * ch);
+                    const f16x8 sv = *(const f16x8 *)(a.suh[pp] + (int64_t)e * H + 8 * ch);
+                    const f16x8 pv = xv * sv;
+                    *(f16x8 *)(xs + ((size_t)pp * kGemvPass + r) * H + 8 * ch) = pv;
 #pragma unroll
-    for (int r = 0; r < kGemvMaxRows; ++r)
-        tot[r] = acc[r] + __shfl_xor(acc[r], 32, 64);
-    __syncthreads();   // every wavefront is done reading xs
+                    for (int j = 0; j < 8; ++j)
+                        sum += (float)pv[j];
+                }
+                const float tot = block_sum256(sum, part);
+                if (threadIdx.x == 0)
+                    rsum[pp][r] = tot;
+            }
+        __syncthreads();
+
+        float acc[kGemvPass] = {};
+        const f16 *xsp = xs + (size_t)pr * kGemvPass * H + 8 * h;
+        gemv_stream<K, CB, kGemvPass>(cb, rstride, H / 16, d0, d1, q, m_lo, m_hi, nr,
+                                      [&](int r, int kk, float xv[8]) {
+                                          const f16x8 v = *(const f16x8 *)(xsp + (size_t)r * H + kk);
 #pragma unroll
-    for (int r = 0; r < kGemvMaxRows; ++r) {
-        if (r < R && r < rows_cap) {
-            if (h == 0)
-                gu[((size_t)pr * rows_cap + r) * 64 + col] = tot[r] * svh;
+                                          for (int t = 0; t < 8; ++t)
+                                              xv[t] = (float)v[t];
+                                      },
+                                      acc);
+        // the two k-halves of a column sit in lanes l and l ^ 32
+#pragma unroll
+        for (int r = 0; r < kGemvPass; ++r) {
+            const float tot = acc[r] + __shfl_xor(acc[r], 32, 64);
+            if (r < nr && h == 0)
+                gu[pr][r][col] = (tot - kBias2 * rsum[pr][r]) * svh;
         }
-    }
-    __syncthreads();
-    for (int i = threadIdx.x; i < R * 64; i += 256) {
-        const int r = i / 64, cc = i % 64;
-        const float g = gu[(size_t)r * 64 + cc];
-        const float u = gu[((size_t)rows_cap + r) * 64 + cc];
-        const float hv = silu_f(g) * u * f16_to_f32(a.suh[2][(int64_t)e * I + n0 + cc]);
-        a.hbuf[(int64_t)(p0 + r) * I + n0 + cc] = f32_to_bf16_bits(hv);
+        __syncthreads();
+        if (threadIdx.x < nr * 64) {
+            const int r = threadIdx.x >> 6, cc = threadIdx.x & 63;
+            const float g = gu[0][r][cc], u = gu[1][r][cc];
+            const float hv = silu_f(g) * u * f16_to_f32(a.suh[2][(int64_t)e * I + n0 + cc]);
+            a.hbuf[(int64_t)(p0 + r0 + r) * I + n0 + cc] = f32_to_bf16_bits(hv);
+        }
+        __syncthreads();
     }
 }
 
 // down + routing-weighted scatter.  Block = 4 wavefronts x 2 tiles = 128
-// output columns of one expert.
+// output columns of one expert.  h * suh_down rows of the pass in LDS, fp32.
 template <int K, int CB>
-__global__ __launch_bounds__(256) void gemv_down_kernel(GroupArgs a, int rows_cap)
+__global__ __launch_bounds__(256) void gemv_down_kernel(GroupArgs a)
 {
     extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ float part[4];
+    __shared__ float rsum[kGemvPass];
     const int li = blockIdx.x;
     if (li >= a.hdr->n_gemv)
         return;
@@ -142,13 +193,7 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(GroupArgs a, int rows_ca
     const int R = a.counts[e];
     const int p0 = a.offsets[e];
     const int m0 = blockIdx.y * 128;
-    uint16_t *hs = (uint16_t *)smem;   // [rows_cap][I] bf16
-    const int nchunk = I / 8;
-    for (int i = threadIdx.x; i < R * nchunk; i += 256) {
-        const int r = i / nchunk, ch = i % nchunk;
-        *(u32x4 *)(hs + (size_t)r * I + 8 * ch) = *(const u32x4 *)(a.hbuf + (int64_t)(p0 + r) * I + 8 * ch);
-    }
-    __syncthreads();
+    float *hs = (float *)smem;   // [kGemvPass][I]
 
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
     const int c = l & 15, ts = (l >> 4) & 1, h = l >> 5;
@@ -159,93 +204,89 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(GroupArgs a, int rows_ca
     const uint32_t *cb = (const uint32_t *)a.codes[2] + e * per_expert + (int64_t)tn * Tile<K>::kDwords;
     const int64_t rstride = (int64_t)(H / 16) * Tile<K>::kDwords;
     const uint32_t m_lo = a.mcg & 0xFFFFu, m_hi = a.mcg >> 16;
-    const uint16_t *hsp = hs + 8 * h;
-
-    float acc[kGemvMaxRows];
-#pragma unroll
-    for (int r = 0; r < kGemvMaxRows; ++r)
-        acc[r] = 0.0f;
-    const int ntk = I / 16;
-    uint32_t nx[kGemvU][2];
-#pragma unroll
-    for (int u = 0; u < kGemvU; ++u) {
-        nx[u][0] = cb[u * rstride + d0];
-        nx[u][1] = cb[u * rstride + d1];
-    }
-    for (int g = 0; g < ntk; g += kGemvU) {
-        uint32_t cu[kGemvU][2];
-#pragma unroll
-        for (int u = 0; u < kGemvU; ++u) {
-            cu[u][0] = nx[u][0];
-            cu[u][1] = nx[u][1];
-        }
-        if (g + kGemvU < ntk) {
-            const uint32_t *nb = cb + (int64_t)(g + kGemvU) * rstride;
-#pragma unroll
-            for (int u = 0; u < kGemvU; ++u) {
-                nx[u][0] = nb[u * rstride + d0];
-                nx[u][1] = nb[u * rstride + d1];
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < kGemvU; ++u) {
-            const bf16x8 v = frag_decode_bf16<K, CB>(cu[u][0], cu[u][1], q, m_lo, m_hi);
-            const int kk = 16 * (g + u);
-#pragma unroll
-            for (int r = 0; r < kGemvMaxRows; ++r) {
-                if (r < R && r < rows_cap) {
-                    const bf16x8 hv = *(const bf16x8 *)(hsp + (size_t)r * I + kk);
-                    float s = acc[r];
-                    s = __builtin_amdgcn_fdot2_f32_bf16((bf16x2){v[0], v[1]}, (bf16x2){hv[0], hv[1]}, s, false);
-                    s = __builtin_amdgcn_fdot2_f32_bf16((bf16x2){v[2], v[3]}, (bf16x2){hv[2], hv[3]}, s, false);
-                    s = __builtin_amdgcn_fdot2_f32_bf16((bf16x2){v[4], v[5]}, (bf16x2){hv[4], hv[5]}, s, false);
-                    s = __builtin_amdgcn_fdot2_f32_bf16((bf16x2){v[6], v[7]}, (bf16x2){hv[6], hv[7]}, s, false);
-                    acc[r] = s;
-                }
-            }
-        }
-    }
     const int m = m0 + 32 * w + 16 * ts + c;
     const float svh = f16_to_f32(a.svh[2][(int64_t)e * H + m]) * (1.0f / 128.0f);
+
+    for (int r0 = 0; r0 < R; r0 += kGemvPass) {
+        const int nr = min(kGemvPass, R - r0);
+        for (int r = 0; r < nr; ++r) {
+            float sum = 0.0f;
+            for (int ch = threadIdx.x; ch < I / 8; ch += 256) {
+                const u32x4 raw = *(const u32x4 *)(a.hbuf + (int64_t)(p0 + r0 + r) * I + 8 * ch);
+                f32x4 lo, hi;
 #pragma unroll
-    for (int r = 0; r < kGemvMaxRows; ++r) {
-        if (r < R && r < rows_cap) {
+                for (int j = 0; j < 4; ++j) {
+                    const float v0 = __uint_as_float(raw[j] << 16), v1 = __uint_as_float(raw[j] & 0xFFFF0000u);
+                    sum += v0 + v1;
+                    if (j < 2) {
+                        lo[2 * j] = v0;
+                        lo[2 * j + 1] = v1;
+                    } else {
+                        hi[2 * j - 4] = v0;
+                        hi[2 * j - 3] = v1;
+                    }
+                }
+                *(f32x4 *)(hs + (size_t)r * I + 8 * ch) = lo;
+                *(f32x4 *)(hs + (size_t)r * I + 8 * ch + 4) = hi;
+            }
+            const float tot = block_sum256(sum, part);
+            if (threadIdx.x == 0)
+                rsum[r] = tot;
+        }
+        __syncthreads();
+
+        float acc[kGemvPass] = {};
+        const float *hsp = hs + 8 * h;
+        gemv_stream<K, CB, kGemvPass>(cb, rstride, I / 16, d0, d1, q, m_lo, m_hi, nr,
+                                      [&](int r, int kk, float xv[8]) {
+                                          const f32x4 v0 = *(const f32x4 *)(hsp + (size_t)r * I + kk);
+                                          const f32x4 v1 = *(const f32x4 *)(hsp + (size_t)r * I + kk + 4);
+#pragma unroll
+                                          for (int t = 0; t < 4; ++t) {
+                                              xv[t] = v0[t];
+                                              xv[t + 4] = v1[t];
+                                          }
+                                      },
+                                      acc);
+#pragma unroll
+        for (int r = 0; r < kGemvPass; ++r) {
             const float tot = acc[r] + __shfl_xor(acc[r], 32, 64);
-            if (h == 0) {
-                const int slot = a.sorted[p0 + r];
-                a.ybuf[(int64_t)slot * H + m] = tot * svh * a.w[slot];
+            if (r < nr && h == 0) {
+                const int slot = a.sorted[p0 + r0 + r];
+                a.ybuf[(int64_t)slot * H + m] = (tot - kBias2 * rsum[r]) * svh * a.w[slot];
             }
         }
+        __syncthreads();
     }
 }
 
-hipError_t launch_gemv_gateup(const GroupArgs &a, int max_list, int rows_cap, hipStream_t s)
+hipError_t launch_gemv_gateup(const GroupArgs &a, int max_list, hipStream_t s)
 {
     if (max_list <= 0)
         return hipSuccess;
     dim3 grid(max_list, a.I / 64);
-    const size_t lds = sizeof(f16) * 2 * rows_cap * a.H;
-    if (a.K == 2 && a.cb == 0) gemv_gateup_kernel<2, 0><<<grid, 256, lds, s>>>(a, rows_cap);
-    else if (a.K == 3 && a.cb == 0) gemv_gateup_kernel<3, 0><<<grid, 256, lds, s>>>(a, rows_cap);
-    else if (a.K == 4 && a.cb == 0) gemv_gateup_kernel<4, 0><<<grid, 256, lds, s>>>(a, rows_cap);
-    else if (a.K == 2) gemv_gateup_kernel<2, 1><<<grid, 256, lds, s>>>(a, rows_cap);
-    else if (a.K == 3) gemv_gateup_kernel<3, 1><<<grid, 256, lds, s>>>(a, rows_cap);
-    else gemv_gateup_kernel<4, 1><<<grid, 256, lds, s>>>(a, rows_cap);
+    const size_t lds = sizeof(f16) * 2 * kGemvPass * a.H;
+    if (a.K == 2 && a.cb == 0) gemv_gateup_kernel<2, 0><<<grid, 256, lds, s>>>(a);
+    else if (a.K == 3 && a.cb == 0) gemv_gateup_kernel<3, 0><<<grid, 256, lds, s>>>(a);
+    else if (a.K == 4 && a.cb == 0) gemv_gateup_kernel<4, 0><<<grid, 256, lds, s>>>(a);
+    else if (a.K == 2) gemv_gateup_kernel<2, 1><<<grid, 256, lds, s>>>(a);
+    else if (a.K == 3) gemv_gateup_kernel<3, 1><<<grid, 256, lds, s>>>(a);
+    else gemv_gateup_kernel<4, 1><<<grid, 256, lds, s>>>(a);
     return hipGetLastError();
 }
 
-hipError_t launch_gemv_down(const GroupArgs &a, int max_list, int rows_cap, hipStream_t s)
+hipError_t launch_gemv_down(const GroupArgs &a, int max_list, hipStream_t s)
 {
     if (max_list <= 0)
         return hipSuccess;
     dim3 grid(max_list, a.H / 128);
-    const size_t lds = sizeof(uint16_t) * rows_cap * a.I;
-    if (a.K == 2 && a.cb == 0) gemv_down_kernel<2, 0><<<grid, 256, lds, s>>>(a, rows_cap);
-    else if (a.K == 3 && a.cb == 0) gemv_down_kernel<3, 0><<<grid, 256, lds, s>>>(a, rows_cap);
-    else if (a.K == 4 && a.cb == 0) gemv_down_kernel<4, 0><<<grid, 256, lds, s>>>(a, rows_cap);
-    else if (a.K == 2) gemv_down_kernel<2, 1><<<grid, 256, lds, s>>>(a, rows_cap);
-    else if (a.K == 3) gemv_down_kernel<3, 1><<<grid, 256, lds, s>>>(a, rows_cap);
-    else gemv_down_kernel<4, 1><<<grid, 256, lds, s>>>(a, rows_cap);
+    const size_t lds = sizeof(float) * kGemvPass * a.I;
+    if (a.K == 2 && a.cb == 0) gemv_down_kernel<2, 0><<<grid, 256, lds, s>>>(a);
+    else if (a.K == 3 && a.cb == 0) gemv_down_kernel<3, 0><<<grid, 256, lds, s>>>(a);
+    else if (a.K == 4 && a.cb == 0) gemv_down_kernel<4, 0><<<grid, 256, lds, s>>>(a);
+    else if (a.K == 2) gemv_down_kernel<2, 1><<<grid, 256, lds, s>>>(a);
+    else if (a.K == 3) gemv_down_kernel<3, 1><<<grid, 256, lds, s>>>(a);
+    else gemv_down_kernel<4, 1><<<grid, 256, lds, s>>>(a);
     return hipGetLastError();
 }
 

@@ -15,9 +15,13 @@ constexpr int kGateUpN = 128;
 constexpr int kDownN = 256;
 // Entries of the routing table handled by one segment-table block.
 constexpr int kSegChunk = 2048;
-// Largest per-expert row count the GEMV path accepts.
+// Largest per-expert row count the GEMV path accepts (rows beyond two per
+// pass re-stream the expert's codes), and the default threshold.
 constexpr int kGemvMaxRows = 8;
 constexpr int kGemvDefaultRows = 4;
+// The GEMV blocks keep two rows of activations in LDS within 64 KiB.
+constexpr int kGemvMaxHidden = 8192;
+constexpr int kGemvMaxInter = 8192;
 // Tokens up to which the shared expert runs as a GEMV.
 constexpr int kSharedGemvMaxTokens = 16;
 
@@ -54,6 +58,7 @@ struct GroupArgs {
     const uint16_t *suh[3];
     const uint16_t *svh[3];
     int H, I, E, k, K, cb;
+    int64_t T;
     uint32_t mcg;
     const int32_t *counts, *offsets, *sorted, *glist, *tiles;
     const WsHeader *hdr;
@@ -64,8 +69,8 @@ struct GroupArgs {
 };
 
 hipError_t launch_convert_x(const uint16_t *x, bool bf16, int64_t n, uint16_t *x16, hipStream_t s);
-hipError_t launch_gemv_gateup(const GroupArgs &a, int max_list, int rows_cap, hipStream_t s);
-hipError_t launch_gemv_down(const GroupArgs &a, int max_list, int rows_cap, hipStream_t s);
+hipError_t launch_gemv_gateup(const GroupArgs &a, int max_list, hipStream_t s);
+hipError_t launch_gemv_down(const GroupArgs &a, int max_list, hipStream_t s);
 hipError_t launch_mfma_gateup(const GroupArgs &a, int max_tiles, hipStream_t s);
 hipError_t launch_mfma_down(const GroupArgs &a, int max_tiles, hipStream_t s);
 

@@ -2,12 +2,14 @@
 // "GLM-5.3 Flash EXL3 for 2x DGX Sparks", "Cold prefill (E3 grouped MoE)":
 // gather, gate/up + SwiGLU, down + scatter from device segment tables).
 //
-// One work tile = (expert, 256 routed rows, a column slice).  The A operand
-// (activation rows) is staged through LDS, double buffered, 64 input channels
-// per stage.  The B operand never touches LDS: each lane decodes its own MFMA
-// B fragment (8 consecutive input rows of one output column) straight from two
-// code dwords into registers, so a wavefront decodes only the columns it owns
-// and no decoded weight is ever written anywhere.
+// One work tile = (expert, 256 routed rows, a column slice); two blocks share
+// a CU (128 accumulator registers per lane) so one block's decode overlaps the
+// other's MFMAs.  The A operand (activation rows) is staged through LDS,
+// double buffered, 64 input channels per stage.  The B operand never touches
+// LDS: each lane decodes its own MFMA B fragment (8 consecutive input rows of
+// one output column) straight from two code dwords into registers, so a
+// wavefront decodes only the columns it owns and no decoded weight is written
+// anywhere.  32-row blocks past the tile's last routed row skip their MFMAs.
 //
 //   gate/up : A = x (fp16) gathered through the sorted slot list; B = 2v * suh
 //             (fp16, exact 2v times fp16 suh); v_mfma_f32_32x32x16_f16;
@@ -28,8 +30,13 @@ namespace moe {
 
 constexpr int kBM = kTileM;    // rows per work tile
 constexpr int kMB = kBM / 32;  // 32-row MFMA blocks per work tile
-constexpr int kBK = 64;        // input channels per stage
-constexpr int kLdsRow = kBK + 8;   // fp16/bf16 elements per LDS row (16-byte pad)
+constexpr int kBK = 32;        // input channels per pipeline stage
+constexpr int kKT = kBK / 16;  // MFMA k-steps per stage
+constexpr int kRing = 4;       // LDS stages in flight (prefetch distance kRing - 1)
+constexpr int kStageHalves = kBM * kBK;   // one A stage: 256 rows x 32 halves = 16 KiB
+constexpr int kSlotHalves = kStageHalves + 4 * 128;
+
+#define LDS_AS __attribute__((address_space(3)))
 
 enum Mode { GATEUP_TRELLIS = 0, DOWN_TRELLIS = 1, GATEUP_DENSE = 2, DOWN_DENSE = 3 };
 
@@ -38,9 +45,15 @@ struct ModeTraits {
     static constexpr bool kTrellis = MODE == GATEUP_TRELLIS || MODE == DOWN_TRELLIS;
     static constexpr bool kGateUp = MODE == GATEUP_TRELLIS || MODE == GATEUP_DENSE;
     static constexpr bool kBF16 = MODE == DOWN_TRELLIS;   // MFMA input type
-    // columns per wavefront (gate/up: 32 gate + 32 up; down: 64)
-    static constexpr int kWaveN = 64;
-    static constexpr int kBlockN = kGateUp ? 4 * 32 : 4 * 64;   // output columns per block
+    // Each wavefront owns one 32-column MFMA block of one projection: for
+    // gate/up, waves 0,1 hold gate and waves 2,3 up of the same 64 columns;
+    // for down, 32 output columns.  A block is 4 wavefronts.
+    static constexpr int kBlockN = kGateUp ? 64 : 128;
+    // vector-memory instructions every wavefront issues per stage: A rows
+    // (4 LDS-direct loads, plus one for suh in the trellis gate/up mode) and
+    // B (trellis: 2 code dwords per k-step; dense: 16 bytes per k-step)
+    static constexpr int kNA = 4 + (MODE == GATEUP_TRELLIS ? 1 : 0);
+    static constexpr int kNB = kTrellis ? 2 * kKT : kKT;
 };
 
 struct GemmArgs {
@@ -51,6 +64,7 @@ struct GemmArgs {
     uint16_t *dOutH;         // shared gate/up output [T][I] fp16
     float *dOutY;            // shared down output [T][H] fp32
     int64_t T;
+    int nslices;             // column slices per row tile
 };
 
 template <int MODE>
@@ -63,230 +77,391 @@ MOE_DEV f32x16 mfma_step(u32x4 a, u32x4 b, f32x16 c)
                                                    __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
+// Blocks are dealt to the 8 XCDs round-robin (block L runs on XCD L % 8).
+// Map block L so that every column slice of a row tile lands on one XCD and
+// the slices of a tile are consecutive there: the tile's A rows are then
+// fetched into that XCD's L2 once and reused by all its slices.
+MOE_DEV void xcd_map(int L, int nslices, int &tile, int &slice)
+{
+    const int x = L & 7, j = L >> 3;
+    tile = (j / nslices) * 8 + x;
+    slice = j % nslices;
+}
+
+// Raw buffer resource over `bytes` bytes at p (loads past the end return 0).
+MOE_DEV __amdgpu_buffer_rsrc_t buf_rsrc(const void *p, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (int)bytes, 0x00020000);
+}
+
+// s_waitcnt with only the vector-memory counter limited to n (gfx9 encoding:
+// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14).
+template <int N>
+MOE_DEV void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | 0x70 | 0xF00 | ((N >> 4) << 14));
+}
+
+// LDS layout of one A stage: row r is 64 bytes = four 16-byte pieces; the
+// piece holding k-offset 8p is stored in slot p ^ ((r >> 2) & 3), which makes
+// the 16-lane reads of an MFMA A fragment (16 consecutive rows, one piece)
+// hit 16 distinct 4-bank groups.
+MOE_DEV int a_slot(int r, int p) { return p ^ ((r >> 2) & 3); }
+
 template <int MODE, int K, int CB>
-__global__ __launch_bounds__(256, 1) void group_gemm_kernel(GemmArgs args)
+struct GemmTile {
+    using TR = ModeTraits<MODE>;
+    int tid, w, l, c, ts, h, pr;
+    int H, I, Kdim, rows, p0, e, col;
+    int64_t t0;
+    // A rows: LDS-direct buffer loads; lane L of the wavefront's load j moves
+    // 16 bytes of row 64w + 16j + L/4 (rows past the tile's last row repeat
+    // it; their results are never stored)
+    __amdgpu_buffer_rsrc_t arsrc, anull;
+    uint32_t aoff[4];
+    uint32_t aread[kKT];       // LDS byte offset of the lane's A fragment per k-step
+    // suh (gate/up trellis): wave w fetches the 16 values k = 16 (w & 1) + 0..15
+    // of stage s of projection w >> 1 with lanes 0..7 (4 bytes each); the other
+    // lanes point past the end of the buffer, read nothing and fill the rest
+    // of the wave's 256-byte area
+    __amdgpu_buffer_rsrc_t srsrc;
+    uint32_t soff;
+    // B: trellis codes of the lane's column, or dense weight row
+    __amdgpu_buffer_rsrc_t brsrc, bnull;
+    uint32_t boff0, boff1;
+    uint32_t rstride;          // bytes between tile rows (trellis)
+    int q;
+    uint32_t m_lo, m_hi;
+
+    struct BRaw {
+        uint32_t c[kKT][2];
+        u32x4 d[kKT];
+    };
+
+    // Issue the A LDS-direct loads of stage s into one ring slot.  Every
+    // stage issues the same loads, also past the last stage (s >= nst): those
+    // go through a zero-range descriptor (no memory access; the slot they
+    // fill is never read), so the count of loads in flight is the same on
+    // every path through the loop and the compiler's own waits for the B
+    // registers stay tight.
+    MOE_DEV void load_a(int s, int nst, LDS_AS uint16_t *ring)
+    {
+        const __amdgpu_buffer_rsrc_t rs = s < nst ? arsrc : anull;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rs, (LDS_AS void *)(ring + (64 * w + 16 * j) * kBK), 16, aoff[j], s * kBK * 2, 0, 0);
+        if constexpr (MODE == GATEUP_TRELLIS) {
+            const __amdgpu_buffer_rsrc_t ss = s < nst ? srsrc : anull;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                ss, (LDS_AS void *)(ring + kStageHalves + 128 * w), 4, soff, s * kBK * 2, 0, 0);
+        }
+    }
+
+    MOE_DEV void load_b(int s, int nst, BRaw &br)
+    {
+        const __amdgpu_buffer_rsrc_t rs = s < nst ? brsrc : bnull;
+#pragma unroll
+        for (int kt = 0; kt < kKT; ++kt) {
+            if constexpr (TR::kTrellis) {
+                const int so = (kKT * s + kt) * (int)rstride;
+                br.c[kt][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, boff0, so, 0);
+                br.c[kt][1] = __builtin_amdgcn_raw_buffer_load_b32(rs, boff1, so, 0);
+            } else {
+                br.d[kt] = __builtin_amdgcn_raw_buffer_load_b128(rs, boff0, (s * kBK + 16 * kt) * 2, 0);
+            }
+        }
+    }
+
+    // LDS reads of the stage are issued first (suh, then the A fragments in
+    // k-step order, so the k-step 0 MFMAs only wait for their own reads), the
+    // B fragments are decoded while they are in flight, then the MFMAs run.
+    template <int NMB>
+    MOE_DEV void compute(const LDS_AS uint16_t *ring, const BRaw &br, f32x16 acc[kMB])
+    {
+        f16x8 su[kKT];
+        if constexpr (MODE == GATEUP_TRELLIS) {
+            // suh k = 16 kt + 8 h + 0..7 of projection pr: area of wave 2 pr + kt
+#pragma unroll
+            for (int kt = 0; kt < kKT; ++kt)
+                su[kt] = *(const LDS_AS f16x8 *)(ring + kStageHalves + 128 * (2 * pr + kt) + 8 * h);
+        }
+        u32x4 af[kKT][NMB];
+#pragma unroll
+        for (int kt = 0; kt < kKT; ++kt)
+#pragma unroll
+            for (int i = 0; i < NMB; ++i)
+                af[kt][i] = *(const LDS_AS u32x4 *)((const LDS_AS char *)ring + aread[kt] + i * 32 * kBK * 2);
+#pragma unroll
+        for (int kt = 0; kt < kKT; ++kt) {
+            u32x4 bfrag;
+            if constexpr (MODE == GATEUP_TRELLIS) {
+                const f16x8 v = frag_decode_f16<K, CB>(br.c[kt][0], br.c[kt][1], q, m_lo, m_hi);
+                bfrag = __builtin_bit_cast(u32x4, v * su[kt]);
+            } else if constexpr (MODE == DOWN_TRELLIS) {
+                bfrag = __builtin_bit_cast(u32x4, frag_decode_bf16<K, CB>(br.c[kt][0], br.c[kt][1], q, m_lo, m_hi));
+            } else {
+                bfrag = br.d[kt];
+            }
+#pragma unroll
+            for (int i = 0; i < NMB; ++i)
+                acc[i] = mfma_step<MODE>(af[kt][i], bfrag, acc[i]);
+        }
+    }
+
+    // One pipeline stage s (ring slot SLOT = s % 4): wait for this wave's
+    // loads of stage s, barrier (every wave's loads landed, every wave is done
+    // with the slot about to be refilled), prefetch stage s + 3, compute s.
+    // Loads complete in issue order and every stage issues its A and B loads
+    // inside the stage (in either order), so "at most 2 (NA + NB)
+    // outstanding" (the loads of stages s + 1 and s + 2) proves that both the
+    // A and the B loads of stage s are done.
+    template <int NMB, int SLOT>
+    MOE_DEV void stage(int s, int nst, LDS_AS uint16_t *rg, LDS_AS uint16_t *rgp, BRaw &bcur, BRaw &bpf,
+                       f32x16 acc[kMB])
+    {
+        constexpr int NA = TR::kNA, NB = TR::kNB;
+        // nothing but MFMAs crosses a stage boundary: loads stay in their
+        // stage (the wait count relies on it) and decodes are not hoisted
+        // above the wait of the stage whose codes they use
+        __builtin_amdgcn_sched_barrier(0x8);
+        wait_vmcnt<2 * (NA + NB)>();
+        __builtin_amdgcn_s_barrier();
+        load_a(s + 3, nst, rgp);
+        load_b(s + 3, nst, bpf);
+        compute<NMB>(rg, bcur, acc);
+    }
+
+    template <int NMB>
+    MOE_DEV void run(LDS_AS uint16_t *r0, LDS_AS uint16_t *r1, LDS_AS uint16_t *r2, LDS_AS uint16_t *r3,
+                     f32x16 acc[kMB])
+    {
+        const int nst = Kdim / kBK;   // a multiple of 4
+        BRaw b0, b1, b2, b3;
+        load_a(0, nst, r0);
+        load_b(0, nst, b0);
+        load_a(1, nst, r1);
+        load_b(1, nst, b1);
+        load_a(2, nst, r2);
+        load_b(2, nst, b2);
+        for (int s = 0; s < nst; s += 4) {
+            stage<NMB, 0>(s, nst, r0, r3, b0, b3, acc);
+            stage<NMB, 1>(s + 1, nst, r1, r0, b1, b0, acc);
+            stage<NMB, 2>(s + 2, nst, r2, r1, b2, b1, acc);
+            stage<NMB, 3>(s + 3, nst, r3, r2, b3, b2, acc);
+        }
+        wait_vmcnt<0>();   // the trailing zero-range loads still write LDS
+    }
+};
+
+template <int MODE, int K, int CB>
+__global__ __launch_bounds__(256, 2) void group_gemm_kernel(GemmArgs args)
 {
     using TR = ModeTraits<MODE>;
     const GroupArgs &a = args.g;
-    __shared__ __align__(16) uint16_t As[2][kBM * kLdsRow];
+    // four ring slots, each one A stage plus four 256-byte suh areas (used in
+    // the trellis gate/up mode); four distinct LDS objects let the compiler
+    // tell the slots' LDS-direct writes apart
+    __shared__ __align__(16) uint16_t ring0[kSlotHalves];
+    __shared__ __align__(16) uint16_t ring1[kSlotHalves];
+    __shared__ __align__(16) uint16_t ring2[kSlotHalves];
+    __shared__ __align__(16) uint16_t ring3[kSlotHalves];
 
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-    const int H = a.H, I = a.I;
-    const int Kdim = TR::kGateUp ? H : I;
-    const int Nout = TR::kGateUp ? I : H;
+    GemmTile<MODE, K, CB> g;
+    g.tid = threadIdx.x;
+    g.w = __builtin_amdgcn_readfirstlane(g.tid >> 6);   // wave-uniform
+    g.l = g.tid & 63;
+    g.H = a.H;
+    g.I = a.I;
+    g.Kdim = TR::kGateUp ? g.H : g.I;
+    const int Nout = TR::kGateUp ? g.I : g.H;
 
     // ---- work tile
-    int e = 0, rows, p0 = 0;
-    int64_t t0 = 0;
-    if (TR::kTrellis) {
-        const int ti = blockIdx.x;
+    int ti, slice;
+    xcd_map(blockIdx.x, args.nslices, ti, slice);
+    g.e = 0;
+    g.p0 = 0;
+    g.t0 = 0;
+    if constexpr (TR::kTrellis) {
         if (ti >= a.hdr->n_tiles)
             return;
-        e = a.tiles[2 * ti];
+        g.e = a.tiles[2 * ti];
         const int m0 = a.tiles[2 * ti + 1];
-        const int cnt = a.counts[e];
-        rows = min(kBM, cnt - m0);
-        p0 = a.offsets[e] + m0;
+        g.rows = min(kBM, a.counts[g.e] - m0);
+        g.p0 = a.offsets[g.e] + m0;
     } else {
-        t0 = (int64_t)blockIdx.x * kBM;
-        rows = (int)min<int64_t>(kBM, args.T - t0);
+        g.t0 = (int64_t)ti * kBM;
+        if (g.t0 >= args.T)
+            return;
+        g.rows = (int)min<int64_t>(kBM, args.T - g.t0);
     }
-    const int n0 = blockIdx.y * TR::kBlockN;
+    const int n0 = slice * TR::kBlockN;
+    const int mblocks = (g.rows + 31) >> 5;
 
-    // ---- A loader: thread -> 16-byte chunk `ach` of rows arow + 32 i
-    const int ach = tid & 7, arow = tid >> 3;
-    const uint16_t *asrc[kMB];
-#pragma unroll
-    for (int i = 0; i < kMB; ++i) {
-        const int r = arow + 32 * i;
-        const uint16_t *p = nullptr;
-        if (r < rows) {
-            if (MODE == GATEUP_TRELLIS)
-                p = a.x16 + (int64_t)(a.sorted[p0 + r] / a.k) * H;
-            else if (MODE == DOWN_TRELLIS)
-                p = a.hbuf + (int64_t)(p0 + r) * I;
-            else
-                p = args.dA + (t0 + r) * (int64_t)Kdim;
+    // ---- A rows
+    {
+        const uint16_t *abase;
+        uint32_t abytes;
+        if constexpr (MODE == GATEUP_TRELLIS) {
+            abase = a.x16;
+            abytes = (uint32_t)(a.T * (int64_t)g.H * 2);
+        } else if constexpr (MODE == DOWN_TRELLIS) {
+            abase = a.hbuf + (int64_t)g.p0 * g.I;
+            abytes = (uint32_t)((int64_t)g.rows * g.I * 2);
+        } else {
+            abase = args.dA + g.t0 * g.Kdim;
+            abytes = (uint32_t)((int64_t)g.rows * g.Kdim * 2);
         }
-        asrc[i] = p;
+        g.arsrc = buf_rsrc(abase, abytes);
+        g.anull = buf_rsrc(abase, 0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 64 * g.w + 16 * j + (g.l >> 2);
+            const int rc = min(r, g.rows - 1);
+            int64_t row;
+            if constexpr (MODE == GATEUP_TRELLIS)
+                row = a.sorted[g.p0 + rc] / a.k;
+            else
+                row = rc;
+            const int piece = a_slot(r, g.l & 3);   // slot l&3 holds this k piece
+            g.aoff[j] = (uint32_t)((row * g.Kdim + 8 * piece) * 2);
+        }
+        g.h = g.l >> 5;
+#pragma unroll
+        for (int kt = 0; kt < kKT; ++kt) {
+            const int r = g.l & 31;
+            g.aread[kt] = (uint32_t)(r * kBK * 2 + 16 * a_slot(r, 2 * kt + g.h));
+        }
     }
-    u32x4 areg[kMB];
-    auto load_a = [&](int s) {
-#pragma unroll
-        for (int i = 0; i < kMB; ++i)
-            areg[i] = asrc[i] ? *(const u32x4 *)(asrc[i] + s * kBK + 8 * ach) : (u32x4){0, 0, 0, 0};
-    };
-    auto store_a = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < kMB; ++i)
-            *(u32x4 *)(&As[buf][(arow + 32 * i) * kLdsRow + 8 * ach]) = areg[i];
-    };
 
     // ---- B source: lane -> (column c of tile ts, k-half h)
-    const int c = l & 15, ts = (l >> 4) & 1, h = l >> 5;
-    // two B fragments per k-step: gate/up -> (gate, up) of the same 32 columns;
-    // down -> two adjacent 32-column blocks
-    int colb[2];
-    if (TR::kGateUp) {
-        colb[0] = colb[1] = n0 + 32 * w + 16 * ts + c;
-    } else {
-        colb[0] = n0 + 64 * w + 16 * ts + c;
-        colb[1] = colb[0] + 32;
-    }
-    int d0 = 0, d1 = 0, q = 0;
-    const uint32_t *cbase[2] = {nullptr, nullptr};
-    int64_t rstride = 0;
-    const uint16_t *dbase[2] = {nullptr, nullptr};
-    if (TR::kTrellis) {
-        frag_pos<K>(c, h, d0, d1, q);
-        const int64_t per_expert = (int64_t)(Kdim / 16) * (Nout / 16) * Tile<K>::kDwords;
-        rstride = (int64_t)(Nout / 16) * Tile<K>::kDwords;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int pr = TR::kGateUp ? j : 2;
-            const int tn = colb[j] / 16;
-            cbase[j] = (const uint32_t *)a.codes[pr] + e * per_expert + (int64_t)tn * Tile<K>::kDwords;
+    g.c = g.l & 15;
+    g.ts = (g.l >> 4) & 1;
+    // every wavefront owns 32 columns (two 16-column tiles, ts) of one
+    // projection: gate/up -> waves 0,1 gate and waves 2,3 up of the block's 64
+    // intermediate columns; down -> 32 of the block's 128 output columns
+    g.pr = TR::kGateUp ? g.w >> 1 : 2;
+    g.col = TR::kGateUp ? n0 + 32 * (g.w & 1) + 16 * g.ts + g.c : n0 + 32 * g.w + 16 * g.ts + g.c;
+    g.m_lo = a.mcg & 0xFFFFu;
+    g.m_hi = a.mcg >> 16;
+    g.q = 0;
+    if constexpr (TR::kTrellis) {
+        int d0, d1, q;
+        frag_pos<K>(g.c, g.h, d0, d1, q);
+        g.q = q;
+        const int64_t per_expert = (int64_t)(g.Kdim / 16) * (Nout / 16) * Tile<K>::kBytes;
+        g.rstride = (uint32_t)((Nout / 16) * Tile<K>::kBytes);
+        g.brsrc = buf_rsrc((const char *)a.codes[g.pr] + g.e * per_expert, (uint32_t)per_expert);
+        g.bnull = buf_rsrc((const char *)a.codes[g.pr], 0);
+        const uint32_t tile0 = (uint32_t)((g.col / 16) * Tile<K>::kBytes);
+        g.boff0 = tile0 + 4 * d0;
+        g.boff1 = tile0 + 4 * d1;
+        g.srsrc = g.bnull;
+        g.soff = 0;
+        if constexpr (MODE == GATEUP_TRELLIS) {
+            g.srsrc = buf_rsrc(a.suh[g.pr] + (int64_t)g.e * g.H + 16 * (g.w & 1), (uint32_t)(g.H * 2 - 32 * (g.w & 1)));
+            g.soff = g.l < 8 ? 4u * g.l : 0x7FFFFFF0u;
         }
     } else {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const uint16_t *W = TR::kGateUp ? args.dB[j] : args.dB[0];
-            dbase[j] = W + (int64_t)colb[j] * Kdim + 8 * h;
-        }
+        const uint16_t *W = TR::kGateUp ? args.dB[g.pr] : args.dB[0];
+        g.brsrc = buf_rsrc(W, (uint32_t)((int64_t)Nout * g.Kdim * 2));
+        g.bnull = buf_rsrc(W, 0);
+        g.srsrc = g.bnull;
+        g.soff = 0;
+        g.boff0 = (uint32_t)(((int64_t)g.col * g.Kdim + 8 * g.h) * 2);
+        g.boff1 = 0;
+        g.rstride = 0;
     }
-    // raw B words of one stage: trellis 2 dwords per (fragment, k-step);
-    // dense 16 bytes per (fragment, k-step)
-    const uint16_t *suh_e[2] = {nullptr, nullptr};
-    if constexpr (MODE == GATEUP_TRELLIS) {
-        suh_e[0] = a.suh[0] + (int64_t)e * H + 8 * h;
-        suh_e[1] = a.suh[1] + (int64_t)e * H + 8 * h;
-    }
-    // trellis: 2 code dwords per (fragment, k-step) [+ 8 suh values for gate/up];
-    // dense: 16 weight bytes per (fragment, k-step)
-    uint32_t craw[2][4][2];
-    u32x4 draw[2][4];
-    auto load_b = [&](int s) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int kt = 0; kt < 4; ++kt) {
-                if constexpr (TR::kTrellis) {
-                    const uint32_t *tile = cbase[j] + (int64_t)(4 * s + kt) * rstride;
-                    craw[j][kt][0] = tile[d0];
-                    craw[j][kt][1] = tile[d1];
-                    if constexpr (MODE == GATEUP_TRELLIS)
-                        draw[j][kt] = *(const u32x4 *)(suh_e[j] + s * kBK + 16 * kt);
-                } else {
-                    draw[j][kt] = *(const u32x4 *)(dbase[j] + s * kBK + 16 * kt);
-                }
-            }
-    };
-    const uint32_t m_lo = a.mcg & 0xFFFFu, m_hi = a.mcg >> 16;
 
-    f32x16 acc[kMB][2];
+    LDS_AS uint16_t *R0 = (LDS_AS uint16_t *)ring0, *R1 = (LDS_AS uint16_t *)ring1;
+    LDS_AS uint16_t *R2 = (LDS_AS uint16_t *)ring2, *R3 = (LDS_AS uint16_t *)ring3;
+    f32x16 acc[kMB];
 #pragma unroll
     for (int i = 0; i < kMB; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-            acc[i][j] = (f32x16){};
+        acc[i] = (f32x16){};
+    if (mblocks <= 2)
+        g.template run<2>(R0, R1, R2, R3, acc);
+    else if (mblocks <= 4)
+        g.template run<4>(R0, R1, R2, R3, acc);
+    else if (mblocks <= 6)
+        g.template run<6>(R0, R1, R2, R3, acc);
+    else
+        g.template run<8>(R0, R1, R2, R3, acc);
+    __syncthreads();   // every wave is done with the rings (reused below)
 
-    const int nst = Kdim / kBK;
-    load_a(0);
-    load_b(0);
-    store_a(0);
-    __syncthreads();
-    for (int s = 0; s < nst; ++s) {
-        const int buf = s & 1;
-        uint32_t cr[2][4][2];
-        u32x4 dr[2][4];
+    // ---- epilogue; D register r of block i holds row 32i + 8(r/4) + 4h + r%4
+    const int h = g.h, col = g.col, rows = g.rows, e = g.e, p0 = g.p0;
+    const int H = g.H, I = g.I;
+    const int64_t t0 = g.t0;
+    if constexpr (TR::kGateUp) {
+        // up wavefronts hand their scaled results to the gate wavefronts with
+        // the same columns through LDS: block i of column half cb goes to
+        // ring (2 cb + i / 4), 4 KiB per block
+        const int cb = g.w & 1;
+        float *ex_lo = cb ? (float *)ring2 : (float *)ring0;
+        float *ex_hi = cb ? (float *)ring3 : (float *)ring1;
+        if (g.pr == 1) {
+            const float su = MODE == GATEUP_TRELLIS ? f16_to_f32(a.svh[1][(int64_t)e * I + col]) * (1.0f / 128.0f) : 1.0f;
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+            for (int i = 0; i < kMB; ++i)
+                if (i < mblocks)
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt) {
-                cr[j][kt][0] = craw[j][kt][0];
-                cr[j][kt][1] = craw[j][kt][1];
-                dr[j][kt] = draw[j][kt];
-            }
-        if (s + 1 < nst) {
-            load_a(s + 1);
-            load_b(s + 1);
+                    for (int r = 0; r < 16; ++r)
+                        (i < 4 ? ex_lo : ex_hi)[((i & 3) * 16 + r) * 64 + g.l] = acc[i][r] * su;
         }
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-            u32x4 bfrag[2];
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                if constexpr (MODE == GATEUP_TRELLIS) {
-                    const f16x8 v = frag_decode_f16<K, CB>(cr[j][kt][0], cr[j][kt][1], q, m_lo, m_hi);
-                    bfrag[j] = __builtin_bit_cast(u32x4, v * __builtin_bit_cast(f16x8, dr[j][kt]));
-                } else if constexpr (MODE == DOWN_TRELLIS) {
-                    bfrag[j] = __builtin_bit_cast(u32x4, frag_decode_bf16<K, CB>(cr[j][kt][0], cr[j][kt][1], q, m_lo, m_hi));
-                } else {
-                    bfrag[j] = dr[j][kt];
-                }
+        __syncthreads();
+        if (g.pr == 0) {
+            float sg = 1.0f, sd = 1.0f;
+            if constexpr (MODE == GATEUP_TRELLIS) {
+                sg = f16_to_f32(a.svh[0][(int64_t)e * I + col]) * (1.0f / 128.0f);
+                sd = f16_to_f32(a.suh[2][(int64_t)e * I + col]);
             }
 #pragma unroll
             for (int i = 0; i < kMB; ++i) {
-                const u32x4 af = *(const u32x4 *)(&As[buf][(32 * i + (l & 31)) * kLdsRow + 16 * kt + 8 * h]);
-                acc[i][0] = mfma_step<MODE>(af, bfrag[0], acc[i][0]);
-                acc[i][1] = mfma_step<MODE>(af, bfrag[1], acc[i][1]);
-            }
-        }
-        if (s + 1 < nst)
-            store_a(buf ^ 1);
-        __syncthreads();
-    }
-
-    // ---- epilogue
-    if (TR::kGateUp) {
-        const int n = colb[0];
-        float sg = 1.0f, su = 1.0f, sd = 1.0f;
-        if (MODE == GATEUP_TRELLIS) {
-            sg = f16_to_f32(a.svh[0][(int64_t)e * I + n]) * (1.0f / 128.0f);
-            su = f16_to_f32(a.svh[1][(int64_t)e * I + n]) * (1.0f / 128.0f);
-            sd = f16_to_f32(a.suh[2][(int64_t)e * I + n]);
-        }
+                if (i < mblocks) {
 #pragma unroll
-        for (int i = 0; i < kMB; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-                if (row < rows) {
-                    const float g = acc[i][0][r] * sg, u = acc[i][1][r] * su;
-                    const float hv = silu_f(g) * u * sd;
-                    if (MODE == GATEUP_TRELLIS)
-                        a.hbuf[(int64_t)(p0 + row) * I + n] = f32_to_bf16_bits(hv);
-                    else
-                        args.dOutH[(t0 + row) * I + n] = f32_to_f16_bits(hv);
+                    for (int r = 0; r < 16; ++r) {
+                        const int row = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+                        if (row < rows) {
+                            const float u = (i < 4 ? ex_lo : ex_hi)[((i & 3) * 16 + r) * 64 + g.l];
+                            const float hv = silu_f(acc[i][r] * sg) * u * sd;
+                            if constexpr (MODE == GATEUP_TRELLIS)
+                                a.hbuf[(int64_t)(p0 + row) * I + col] = f32_to_bf16_bits(hv);
+                            else
+                                args.dOutH[(t0 + row) * I + col] = f32_to_f16_bits(hv);
+                        }
+                    }
                 }
             }
+        }
     } else {
+        const float sv = MODE == DOWN_TRELLIS ? f16_to_f32(a.svh[2][(int64_t)e * H + col]) * (1.0f / 128.0f) : 1.0f;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int m = colb[j];
-            const float sv = MODE == DOWN_TRELLIS ? f16_to_f32(a.svh[2][(int64_t)e * H + m]) * (1.0f / 128.0f) : 1.0f;
-#pragma unroll
-            for (int i = 0; i < kMB; ++i)
+        for (int i = 0; i < kMB; ++i) {
+            if (i < mblocks) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int row = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
                     if (row < rows) {
-                        if (MODE == DOWN_TRELLIS) {
+                        if constexpr (MODE == DOWN_TRELLIS) {
                             const int slot = a.sorted[p0 + row];
-                            a.ybuf[(int64_t)slot * H + m] = acc[i][j][r] * sv * a.w[slot];
+                            a.ybuf[(int64_t)slot * H + col] = acc[i][r] * sv * a.w[slot];
                         } else {
-                            args.dOutY[(t0 + row) * H + m] = acc[i][j][r];
+                            args.dOutY[(t0 + row) * H + col] = acc[i][r];
                         }
                     }
                 }
+            }
         }
     }
 }
 
 template <int MODE>
-static hipError_t launch_mode(const GemmArgs &ga, dim3 grid, hipStream_t s)
+static hipError_t launch_mode(const GemmArgs &ga, int tiles, hipStream_t s)
 {
     const GroupArgs &a = ga.g;
+    const unsigned grid = (unsigned)(((tiles + 7) / 8) * 8 * ga.nslices);
     if (ModeTraits<MODE>::kTrellis) {
         if (a.K == 2 && a.cb == 0) group_gemm_kernel<MODE, 2, 0><<<grid, 256, 0, s>>>(ga);
         else if (a.K == 3 && a.cb == 0) group_gemm_kernel<MODE, 3, 0><<<grid, 256, 0, s>>>(ga);
@@ -306,7 +481,8 @@ hipError_t launch_mfma_gateup(const GroupArgs &a, int max_tiles, hipStream_t s)
         return hipSuccess;
     GemmArgs ga{};
     ga.g = a;
-    return launch_mode<GATEUP_TRELLIS>(ga, dim3(max_tiles, a.I / ModeTraits<GATEUP_TRELLIS>::kBlockN), s);
+    ga.nslices = a.I / ModeTraits<GATEUP_TRELLIS>::kBlockN;
+    return launch_mode<GATEUP_TRELLIS>(ga, max_tiles, s);
 }
 
 hipError_t launch_mfma_down(const GroupArgs &a, int max_tiles, hipStream_t s)
@@ -315,7 +491,8 @@ hipError_t launch_mfma_down(const GroupArgs &a, int max_tiles, hipStream_t s)
         return hipSuccess;
     GemmArgs ga{};
     ga.g = a;
-    return launch_mode<DOWN_TRELLIS>(ga, dim3(max_tiles, a.H / ModeTraits<DOWN_TRELLIS>::kBlockN), s);
+    ga.nslices = a.H / ModeTraits<DOWN_TRELLIS>::kBlockN;
+    return launch_mode<DOWN_TRELLIS>(ga, max_tiles, s);
 }
 
 hipError_t launch_shared_gateup(const uint16_t *x16, int64_t T, int H, int I, const uint16_t *wg,
@@ -329,8 +506,8 @@ hipError_t launch_shared_gateup(const uint16_t *x16, int64_t T, int H, int I, co
     ga.dB[1] = wu;
     ga.dOutH = sh;
     ga.T = T;
-    const dim3 grid((unsigned)((T + kBM - 1) / kBM), I / ModeTraits<GATEUP_DENSE>::kBlockN);
-    return launch_mode<GATEUP_DENSE>(ga, grid, s);
+    ga.nslices = I / ModeTraits<GATEUP_DENSE>::kBlockN;
+    return launch_mode<GATEUP_DENSE>(ga, (int)((T + kBM - 1) / kBM), s);
 }
 
 hipError_t launch_shared_down(const uint16_t *sh, int64_t T, int H, int I, const uint16_t *wd,
@@ -343,8 +520,8 @@ hipError_t launch_shared_down(const uint16_t *sh, int64_t T, int H, int I, const
     ga.dB[0] = wd;
     ga.dOutY = sy;
     ga.T = T;
-    const dim3 grid((unsigned)((T + kBM - 1) / kBM), H / ModeTraits<DOWN_DENSE>::kBlockN);
-    return launch_mode<DOWN_DENSE>(ga, grid, s);
+    ga.nslices = H / ModeTraits<DOWN_DENSE>::kBlockN;
+    return launch_mode<DOWN_DENSE>(ga, (int)((T + kBM - 1) / kBM), s);
 }
 
 // ---------------------------------------------------------------- small kernels

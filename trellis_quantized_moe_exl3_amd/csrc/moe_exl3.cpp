@@ -20,12 +20,9 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 int gemv_rows_of(const moe_exl3_desc &d)
 {
-    // the GEMV gate/up block keeps x * suh of its rows for both projections
-    // in LDS (2 * rows * hidden fp16 values) and the down block keeps its
-    // rows of h (rows * inter bf16 values), each within 64 KiB
-    const int lds_cap = std::max(1, std::min(16384 / d.hidden, 32768 / d.inter));
-    const int cap = std::min(kGemvMaxRows, lds_cap);
-    if (d.flags & MOE_EXL3_FORCE_MFMA)
+    // the GEMV blocks keep two rows of activations in LDS (64 KiB at most)
+    const int cap = kGemvMaxRows;
+    if ((d.flags & MOE_EXL3_FORCE_MFMA) || d.hidden > kGemvMaxHidden || d.inter > kGemvMaxInter)
         return 0;
     if (d.flags & MOE_EXL3_FORCE_GEMV)
         return cap;
@@ -82,6 +79,15 @@ int check_weights(const moe_exl3_desc &d, const moe_exl3_weights *w, bool routin
         }
     }
     return MOE_EXL3_OK;
+}
+
+// The GEMM kernels read activations, h rows, codes and shared weights through
+// 32-bit buffer offsets: every such buffer must stay below 2 GiB.
+bool buffers_addressable(const moe_exl3_desc &d, int64_t T)
+{
+    const int64_t lim = (int64_t)1 << 31;
+    return T * d.hidden * 2 < lim && T * d.top_k * d.inter * 2 < lim && T * d.inter * 2 < lim &&
+           (int64_t)d.hidden * d.inter * 2 < lim;
 }
 
 Plan make_plan(const moe_exl3_desc &d, int64_t T)
@@ -189,7 +195,7 @@ int moe_exl3_workspace_size(const moe_exl3_desc *desc, int64_t max_tokens, size_
         return rc;
     if (!bytes || max_tokens < 0)
         return MOE_EXL3_ERR_INVALID_ARG;
-    if (max_tokens * desc->top_k >= ((int64_t)1 << 31))
+    if (max_tokens * desc->top_k >= ((int64_t)1 << 31) || !buffers_addressable(*desc, max_tokens))
         return MOE_EXL3_ERR_UNSUPPORTED;
     *bytes = make_plan(*desc, max_tokens).total;
     return MOE_EXL3_OK;
@@ -247,7 +253,7 @@ static int run_layer(const moe_exl3_desc *desc, const moe_exl3_weights *weights,
         return rc;
     if (T < 0)
         return MOE_EXL3_ERR_INVALID_ARG;
-    if (T * desc->top_k >= ((int64_t)1 << 31))
+    if (T * desc->top_k >= ((int64_t)1 << 31) || !buffers_addressable(*desc, T))
         return MOE_EXL3_ERR_UNSUPPORTED;
     if (T == 0)
         return MOE_EXL3_OK;
@@ -294,6 +300,7 @@ static int run_layer(const moe_exl3_desc *desc, const moe_exl3_weights *weights,
     ga.I = d.inter;
     ga.E = d.n_experts;
     ga.k = d.top_k;
+    ga.T = T;
     ga.K = d.K;
     ga.cb = d.codebook;
     ga.mcg = d.mcg;
@@ -311,9 +318,9 @@ static int run_layer(const moe_exl3_desc *desc, const moe_exl3_weights *weights,
     const int64_t n = T * d.top_k;
     const int max_list = g > 0 ? (int)std::min<int64_t>(d.n_experts, n) : 0;
 
-    if (!mk.mark(MOE_EXL3_STEP_GEMV_GATEUP) || launch_gemv_gateup(ga, max_list, std::max(1, g), s) != hipSuccess ||
+    if (!mk.mark(MOE_EXL3_STEP_GEMV_GATEUP) || launch_gemv_gateup(ga, max_list, s) != hipSuccess ||
         !mk.mark(MOE_EXL3_STEP_MFMA_GATEUP) || launch_mfma_gateup(ga, p.max_tiles, s) != hipSuccess ||
-        !mk.mark(MOE_EXL3_STEP_GEMV_DOWN) || launch_gemv_down(ga, max_list, std::max(1, g), s) != hipSuccess ||
+        !mk.mark(MOE_EXL3_STEP_GEMV_DOWN) || launch_gemv_down(ga, max_list, s) != hipSuccess ||
         !mk.mark(MOE_EXL3_STEP_MFMA_DOWN) || launch_mfma_down(ga, p.max_tiles, s) != hipSuccess ||
         !mk.mark(MOE_EXL3_STEP_SHARED))
         return MOE_EXL3_ERR_HIP;

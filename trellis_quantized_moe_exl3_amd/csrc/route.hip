@@ -8,82 +8,156 @@
 namespace moe {
 
 // ---------------------------------------------------------------- router logits
-// One wavefront computes an 8-token x 8-expert block of logits.  Lane l owns
-// the hidden indices h = 64i + l and accumulates, for i in order, the exact
-// fp32 products x*w of every (token, expert) pair of the block (a bf16/fp16 by
-// fp16 product has at most 19 significant bits, so fma == add of the product).
-// The 64 lane partials of each logit then go through LDS to one lane, which
-// adds them with the halving tree p[l] += p[l + d], d = 32 .. 1.
-constexpr int kRT = 8, kRE = 8;
+// Fixed order (64 lane partial sums over h = 64i + l, each accumulated in
+// order of i, then the halving tree p[l] += p[l + d], d = 32 .. 1).  The
+// partial sums are spread over hardware lanes as follows: an 8-lane group
+// holds all 64 of them for its (token, expert) pairs, lane g of the group
+// owning l = 8g + j, j = 0..7, so every load is 16 contiguous bytes of a row.
+// Each lane keeps TPL tokens x EPL experts of partial sums; a wavefront is 8
+// groups = NTQ token quads x (8 / NTQ) expert quads, a block 4 wavefronts that
+// split the experts.  The tree then runs as three DPP row shifts across the
+// group (d = 32, 16, 8: lanes g+4, g+2, g+1) and three in-register steps
+// (d = 4, 2, 1).  Every x*w product is exact in fp32, so fma == add(product).
+template <int TPL, int EPL, int NTQ>
+struct RouteShape {
+    static constexpr int kNEQ = 8 / NTQ;
+    static constexpr int kTokens = NTQ * TPL;          // per block
+    static constexpr int kExpertsWave = kNEQ * EPL;
+    static constexpr int kExperts = 4 * kExpertsWave;  // per block
+};
 
-template <bool BF16>
-__global__ __launch_bounds__(64) void route_logits_kernel(const uint16_t *__restrict__ x, int64_t T,
-                                                          int H, const uint16_t *__restrict__ Wr,
-                                                          const float *__restrict__ bias, int E,
-                                                          float *__restrict__ logits)
+MOE_DEV float dpp_shl(float v, int n)
 {
-    __shared__ float part[kRT * kRE][65];
-    const int l = threadIdx.x;
-    const int64_t t0 = (int64_t)blockIdx.x * kRT;
-    const int e0 = blockIdx.y * kRE;
-    float p[kRT][kRE];
+    // row_shl:n -- lane i of a 16-lane row reads lane i + n
+    const int ctrl = 0x100 + n;
+    int r;
+    switch (ctrl) {
+    case 0x104: r = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x104, 0xF, 0xF, false); break;
+    case 0x102: r = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x102, 0xF, 0xF, false); break;
+    default: r = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x101, 0xF, 0xF, false); break;
+    }
+    return __int_as_float(r);
+}
+
+template <bool BF16, int TPL, int EPL, int NTQ>
+__global__ __launch_bounds__(256) void route_logits_kernel(const uint16_t *__restrict__ x, int64_t T,
+                                                           int H, const uint16_t *__restrict__ Wr,
+                                                           const float *__restrict__ bias, int E,
+                                                           float *__restrict__ logits)
+{
+    using S = RouteShape<TPL, EPL, NTQ>;
+    const int w = threadIdx.x >> 6, L = threadIdx.x & 63;
+    const int g = L & 7, blk = L >> 3;
+    const int tq = blk / S::kNEQ, eq = blk % S::kNEQ;
+    const int64_t tb = (int64_t)blockIdx.x * S::kTokens + tq * TPL;
+    const int eb = blockIdx.y * S::kExperts + w * S::kExpertsWave + eq * EPL;
+    const uint16_t *xr[TPL];
+    bool tok_ok[TPL];
 #pragma unroll
-    for (int a = 0; a < kRT; ++a)
+    for (int a = 0; a < TPL; ++a) {
+        tok_ok[a] = tb + a < T;
+        xr[a] = x + (tok_ok[a] ? tb + a : 0) * (int64_t)H + 8 * g;
+    }
+    const uint16_t *wr[EPL];
+    bool ex_ok[EPL];
 #pragma unroll
-        for (int b = 0; b < kRE; ++b)
-            p[a][b] = 0.0f;
-    const uint16_t *xr[kRT];
+    for (int b = 0; b < EPL; ++b) {
+        ex_ok[b] = eb + b < E;
+        wr[b] = Wr + (int64_t)(ex_ok[b] ? eb + b : 0) * H + 8 * g;
+    }
+    float p[TPL][EPL][8];
 #pragma unroll
-    for (int a = 0; a < kRT; ++a)
-        xr[a] = x + (t0 + a < T ? t0 + a : t0) * (int64_t)H;
-    const int nt = (int)(T - t0 < kRT ? T - t0 : kRT);
+    for (int a = 0; a < TPL; ++a)
+#pragma unroll
+        for (int b = 0; b < EPL; ++b)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                p[a][b][j] = 0.0f;
+#pragma unroll 4
     for (int i = 0; i < H / 64; ++i) {
-        const int hh = 64 * i + l;
-        float xv[kRT], wv[kRE];
+        float xv[TPL][8];
 #pragma unroll
-        for (int a = 0; a < kRT; ++a)
-            xv[a] = a < nt ? act_to_f32<BF16>(xr[a][hh]) : 0.0f;
+        for (int a = 0; a < TPL; ++a) {
+            const u32x4 raw = tok_ok[a] ? *(const u32x4 *)(xr[a] + 64 * i) : (u32x4){0, 0, 0, 0};
 #pragma unroll
-        for (int b = 0; b < kRE; ++b)
-            wv[b] = f16_to_f32(Wr[(int64_t)(e0 + b) * H + hh]);
+            for (int j = 0; j < 4; ++j) {
+                if (BF16) {
+                    xv[a][2 * j] = __uint_as_float(raw[j] << 16);
+                    xv[a][2 * j + 1] = __uint_as_float(raw[j] & 0xFFFF0000u);
+                } else {
+                    xv[a][2 * j] = f16_to_f32((uint16_t)(raw[j] & 0xFFFFu));
+                    xv[a][2 * j + 1] = f16_to_f32((uint16_t)(raw[j] >> 16));
+                }
+            }
+        }
 #pragma unroll
-        for (int a = 0; a < kRT; ++a)
+        for (int b = 0; b < EPL; ++b) {
+            const f16x8 wv = *(const f16x8 *)(wr[b] + 64 * i);
 #pragma unroll
-            for (int b = 0; b < kRE; ++b)
-                p[a][b] = __builtin_fmaf(xv[a], wv[b], p[a][b]);
+            for (int a = 0; a < TPL; ++a)
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    p[a][b][j] = __builtin_fmaf(xv[a][j], (float)wv[j], p[a][b][j]);
+        }
     }
+    // tree: d = 32, 16, 8 across the group (lane g += lane g + d/8) ...
 #pragma unroll
-    for (int a = 0; a < kRT; ++a)
+    for (int a = 0; a < TPL; ++a)
 #pragma unroll
-        for (int b = 0; b < kRE; ++b)
-            part[a * kRE + b][l] = p[a][b];
-    __syncthreads();
-    // lane q reduces logit q of the block
-    const int q = l;
-    float r[64];
+        for (int b = 0; b < EPL; ++b)
 #pragma unroll
-    for (int j = 0; j < 64; ++j)
-        r[j] = part[q][j];
+            for (int j = 0; j < 8; ++j) {
+                float v = p[a][b][j];
+                v = v + dpp_shl(v, 4);
+                v = v + dpp_shl(v, 2);
+                v = v + dpp_shl(v, 1);
+                p[a][b][j] = v;
+            }
+    // ... then d = 4, 2, 1 inside lane g = 0
+    if (g == 0) {
 #pragma unroll
-    for (int d = 32; d >= 1; d >>= 1)
+        for (int a = 0; a < TPL; ++a)
 #pragma unroll
-        for (int j = 0; j < d; ++j)
-            r[j] = r[j] + r[j + d];
-    const int a = q / kRE, b = q % kRE;
-    if (a < nt) {
-        const float lg = bias ? r[0] + bias[e0 + b] : r[0];
-        logits[(t0 + a) * E + e0 + b] = lg;
+            for (int b = 0; b < EPL; ++b) {
+                float r[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    r[j] = p[a][b][j];
+#pragma unroll
+                for (int d = 4; d >= 1; d >>= 1)
+#pragma unroll
+                    for (int j = 0; j < d; ++j)
+                        r[j] = r[j] + r[j + d];
+                if (tok_ok[a] && ex_ok[b]) {
+                    const int e = eb + b;
+                    logits[(tb + a) * E + e] = bias ? r[0] + bias[e] : r[0];
+                }
+            }
     }
+}
+
+template <bool BF16, int TPL, int EPL, int NTQ>
+static void route_launch(const uint16_t *x, int64_t T, int H, const uint16_t *Wr, const float *bias,
+                         int E, float *logits, hipStream_t s)
+{
+    using S = RouteShape<TPL, EPL, NTQ>;
+    dim3 grid((unsigned)((T + S::kTokens - 1) / S::kTokens), (unsigned)((E + S::kExperts - 1) / S::kExperts));
+    route_logits_kernel<BF16, TPL, EPL, NTQ><<<grid, 256, 0, s>>>(x, T, H, Wr, bias, E, logits);
 }
 
 hipError_t launch_route_logits(const uint16_t *x, bool bf16, int64_t T, int H, const uint16_t *Wr,
                                const float *bias, int E, float *logits, hipStream_t s)
 {
-    dim3 grid((unsigned)((T + kRT - 1) / kRT), (unsigned)(E / kRE));
-    if (bf16)
-        route_logits_kernel<true><<<grid, 64, 0, s>>>(x, T, H, Wr, bias, E, logits);
-    else
-        route_logits_kernel<false><<<grid, 64, 0, s>>>(x, T, H, Wr, bias, E, logits);
+    // many tokens: 4 tokens x 2 experts per lane (8 tokens x 32 experts per
+    // block); few tokens: one (token, expert) pair per lane group so that
+    // enough wavefronts stream the router weights
+    if (T > 64) {
+        if (bf16) route_launch<true, 4, 2, 2>(x, T, H, Wr, bias, E, logits, s);
+        else route_launch<false, 4, 2, 2>(x, T, H, Wr, bias, E, logits, s);
+    } else {
+        if (bf16) route_launch<true, 1, 1, 8>(x, T, H, Wr, bias, E, logits, s);
+        else route_launch<false, 1, 1, 8>(x, T, H, Wr, bias, E, logits, s);
+    }
     return hipGetLastError();
 }
 

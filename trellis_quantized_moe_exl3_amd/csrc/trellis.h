@@ -93,6 +93,15 @@ MOE_DEV uint32_t field_sum2(uint32_t h, uint32_t base)
     return __builtin_amdgcn_sad_u8(h & 0xFEFEFEFEu, 0u, base);
 }
 
+// fp16 bit pattern of 1024 + 2 * (v + 254) = 2v + 1532 in the low 16 bits
+// (upper bits zero): one op after the hash.  Consumers that accumulate
+// x * (2v + 1532) subtract 1532 * sum(x) once per output instead of
+// re-centring every weight.
+MOE_DEV uint32_t value2_biased_f16bits(uint32_t s, uint32_t m_lo, uint32_t m_hi)
+{
+    return field_sum2(mcg_hash(s, m_lo, m_hi), 0x6400u);
+}
+
 // 2v as an exact fp32 value.
 MOE_DEV float value2_f32(uint32_t s, uint32_t m_lo, uint32_t m_hi)
 {
