@@ -9,6 +9,17 @@ as well (code HBM GB/s and us per layer, with rotating copies of the codes so
 the 256 MB last-level cache cannot hold them).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Helpers for rocprofv3 counter passes (each does one thing and exits):
+
+    python bench.py --profile-layer prefill --reps 2   # the layer, N times
+    python bench.py --copy-calibration 1024            # a plain 1 GiB copy, 4 times
+
+The roofline's `traffic` (HBM bytes per launch of the dominant kernel) is read
+from profiles/pmc_traffic_mfma_gateup_prefill.md, which records the FETCH_SIZE /
+WRITE_SIZE readings, the copy-kernel scale factors and a hash of the kernel
+sources they were taken with; when the sources have changed since, `traffic`
+is null.
 """
 from __future__ import annotations
 
@@ -26,6 +37,35 @@ sys.path.insert(0, ROOT)
 
 PEAK_FP16_TFLOPS = 2500.0      # MI355X dense fp16/bf16 MFMA
 PEAK_HBM_GBPS = 8000.0
+GEMV_ROWS = 4                  # default per-expert row count up to which the GEMV path runs
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic_mfma_gateup_prefill.md")
+KERNEL_SOURCES = ["mfma.hip", "trellis.h", "common.h", "internal.h"]
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for n in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "trellis_quantized_moe_exl3_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the gate/up MFMA kernel from the committed counter
+    summary, or None when it is missing or was taken with other kernel sources."""
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if ":" in line and line.startswith("- "):
+                    k, v = line[2:].split(":", 1)
+                    kv[k.strip()] = v.strip().strip("`")
+        if kv.get("kernel_sources_sha256") != kernel_source_hash():
+            return None
+        return float(kv["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def _dev(a):
@@ -136,8 +176,11 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=50)
-    ap.add_argument("--cpu-tokens", type=int, default=16)
+    ap.add_argument("--cpu-tokens", type=int, default=80)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-layer", default=None, help="run this workload's layer --reps times and exit")
+    ap.add_argument("--reps", type=int, default=2)
+    ap.add_argument("--copy-calibration", type=int, default=0, help="copy this many MiB 4 times and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only; multi-GPU scaling is not part of it "
@@ -150,6 +193,27 @@ def main():
     torch.cuda.set_device(0)
     hip = Hip()
 
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        a = torch.ones(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(4):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(f"[bench] copied {n} bytes 4 times", file=sys.stderr, flush=True)
+        return
+    if args.profile_layer:
+        pcfg = W.BY_NAME[args.profile_layer]
+        pinp, pdesc, pweights, pkeep = setup(pcfg)
+        px = _dev(pinp.x)
+        pout = torch.empty_like(px)
+        pws = torch.empty(M.workspace_size(pdesc, px.shape[0]), dtype=torch.uint8, device="cuda")
+        for _ in range(args.reps):
+            M.layer(pdesc, pweights[0], px, pout, pws)
+        torch.cuda.synchronize()
+        print(f"[bench] ran the {args.profile_layer} layer {args.reps} times", file=sys.stderr, flush=True)
+        return
+
     # ---- prefill: the headline workload
     cfg = W.BY_NAME["prefill"]
     inp, desc, weights, keep = setup(cfg)
@@ -157,8 +221,7 @@ def main():
     print(f"[bench] prefill inputs ready (T={cfg.tokens})", file=sys.stderr, flush=True)
     ms, per, total, _, _ = time_layer(desc, weights, x, args.steps, args.warmup, hip)
     counts = routing_counts(desc, weights[0], x, cfg)
-    g = 4
-    mfma_rows = int(counts[counts > g].sum())
+    mfma_rows = int(counts[counts > GEMV_ROWS].sum())
     step_ms = {n: float(per[:, i].mean()) for i, n in enumerate(M.STEPS)}
     gu_ms = step_ms["mfma_gateup"]
     gu_flops = 2.0 * 2 * cfg.hidden * cfg.inter * mfma_rows
@@ -206,7 +269,7 @@ def main():
                    "tokens": cfg.tokens, "parallelism": "single GPU"},
         "roofline": {"kernel": "mfma_gateup (group_gemm_kernel<0,2,0>)", "bound": "mfma",
                      "achieved": achieved, "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_FP16_TFLOPS, "traffic": None,
+                     "frac": achieved / PEAK_FP16_TFLOPS, "traffic": recorded_traffic(),
                      "launch_ms": gu_ms, "flops_per_launch": gu_flops},
         "step_ms": step_ms,
         "decode": {"workload": "decode-8: T=8, same layer, no router bias", "us_per_layer": float(dtotal.mean()) * 1000,

@@ -121,10 +121,11 @@ struct GemmTile {
     __amdgpu_buffer_rsrc_t arsrc, anull;
     uint32_t aoff[4];
     uint32_t aread[kKT];       // LDS byte offset of the lane's A fragment per k-step
-    // suh (gate/up trellis): wave w fetches the 16 values k = 16 (w & 1) + 0..15
-    // of stage s of projection w >> 1 with lanes 0..7 (4 bytes each); the other
-    // lanes point past the end of the buffer, read nothing and fill the rest
-    // of the wave's 256-byte area
+    // suh (gate/up trellis): every wave fetches the 32 values of stage s of
+    // its own projection with lanes 0..15 (4 bytes each) into its own
+    // 256-byte area of the slot; the other lanes point past the end of the
+    // buffer and read nothing.  Only the wave itself reads the area, so its
+    // own vmcnt wait makes the values visible.
     __amdgpu_buffer_rsrc_t srsrc;
     uint32_t soff;
     // B: trellis codes of the lane's column, or dense weight row
@@ -174,63 +175,81 @@ struct GemmTile {
         }
     }
 
-    // LDS reads of the stage are issued first (suh, then the A fragments in
-    // k-step order, so the k-step 0 MFMAs only wait for their own reads), the
-    // B fragments are decoded while they are in flight, then the MFMAs run.
-    template <int NMB>
-    MOE_DEV void compute(const LDS_AS uint16_t *ring, const BRaw &br, f32x16 acc[kMB])
+    // B fragment of k-step kt before the suh scaling: 8 exact values of 2v
+    // (fp16 for gate/up, bf16 for down), or the dense weights as loaded
+    MOE_DEV u32x4 decode(const BRaw &br, int kt) const
     {
+        if constexpr (MODE == GATEUP_TRELLIS)
+            return __builtin_bit_cast(u32x4, frag_decode_f16<K, CB>(br.c[kt][0], br.c[kt][1], q, m_lo, m_hi));
+        else if constexpr (MODE == DOWN_TRELLIS)
+            return __builtin_bit_cast(u32x4, frag_decode_bf16<K, CB>(br.c[kt][0], br.c[kt][1], q, m_lo, m_hi));
+        else
+            return br.d[kt];
+    }
+
+    // Interleave the MFMAs of one k-step with the VALU work scheduled next to
+    // them (the decode of the following k-step): one MFMA occupies the matrix
+    // pipe for 32 cycles, during which the wave can issue ~8 VALU operations.
+    template <int NMB>
+    MOE_DEV static void interleave()
+    {
+        constexpr int kV = (NMB >= 8) ? 7 : 48 / NMB;
+#pragma unroll
+        for (int i = 0; i < NMB; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, kV, 0);
+        }
+    }
+
+    // One pipeline stage s (ring slot SLOT = s % 4):
+    //   wait for this wave's loads of stage s, barrier (every wave's loads
+    //   landed, every wave is done with the slot about to be refilled),
+    //   prefetch stage s + 3, read the stage's A fragments (and this wave's
+    //   suh), then run the k-step 0 MFMAs while decoding k-step 1 and the
+    //   k-step 1 MFMAs while decoding k-step 0 of stage s + 1 (dk0 carries it).
+    // Loads complete in issue order and every stage issues its loads inside
+    // the stage, so "at most 2 (NA + NB) outstanding" (the loads of stages
+    // s + 1 and s + 2) proves that the loads of stage s are done.
+    template <int NMB, int SLOT>
+    MOE_DEV void stage(int s, int nst, LDS_AS uint16_t *rg, LDS_AS uint16_t *rgp, const BRaw &bcur,
+                       const BRaw &bnext, BRaw &bpf, u32x4 &dk0, f32x16 acc[kMB])
+    {
+        constexpr int NA = TR::kNA, NB = TR::kNB;
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<2 * (NA + NB)>();
+        __builtin_amdgcn_s_barrier();
+        load_a(s + 3, nst, rgp);
+        load_b(s + 3, nst, bpf);
         f16x8 su[kKT];
         if constexpr (MODE == GATEUP_TRELLIS) {
-            // suh k = 16 kt + 8 h + 0..7 of projection pr: area of wave 2 pr + kt
 #pragma unroll
             for (int kt = 0; kt < kKT; ++kt)
-                su[kt] = *(const LDS_AS f16x8 *)(ring + kStageHalves + 128 * (2 * pr + kt) + 8 * h);
+                su[kt] = *(const LDS_AS f16x8 *)(rg + kStageHalves + 128 * w + 16 * kt + 8 * h);
         }
         u32x4 af[kKT][NMB];
 #pragma unroll
         for (int kt = 0; kt < kKT; ++kt)
 #pragma unroll
             for (int i = 0; i < NMB; ++i)
-                af[kt][i] = *(const LDS_AS u32x4 *)((const LDS_AS char *)ring + aread[kt] + i * 32 * kBK * 2);
+                af[kt][i] = *(const LDS_AS u32x4 *)((const LDS_AS char *)rg + aread[kt] + i * 32 * kBK * 2);
+        u32x4 b0 = dk0;
+        if constexpr (MODE == GATEUP_TRELLIS)
+            b0 = __builtin_bit_cast(u32x4, __builtin_bit_cast(f16x8, dk0) * su[0]);
+        const u32x4 d1 = decode(bcur, 1);
 #pragma unroll
-        for (int kt = 0; kt < kKT; ++kt) {
-            u32x4 bfrag;
-            if constexpr (MODE == GATEUP_TRELLIS) {
-                const f16x8 v = frag_decode_f16<K, CB>(br.c[kt][0], br.c[kt][1], q, m_lo, m_hi);
-                bfrag = __builtin_bit_cast(u32x4, v * su[kt]);
-            } else if constexpr (MODE == DOWN_TRELLIS) {
-                bfrag = __builtin_bit_cast(u32x4, frag_decode_bf16<K, CB>(br.c[kt][0], br.c[kt][1], q, m_lo, m_hi));
-            } else {
-                bfrag = br.d[kt];
-            }
+        for (int i = 0; i < NMB; ++i)
+            acc[i] = mfma_step<MODE>(af[0][i], b0, acc[i]);
+        if constexpr (TR::kTrellis)
+            interleave<NMB>();
+        u32x4 b1 = d1;
+        if constexpr (MODE == GATEUP_TRELLIS)
+            b1 = __builtin_bit_cast(u32x4, __builtin_bit_cast(f16x8, d1) * su[1]);
+        dk0 = decode(bnext, 0);
 #pragma unroll
-            for (int i = 0; i < NMB; ++i)
-                acc[i] = mfma_step<MODE>(af[kt][i], bfrag, acc[i]);
-        }
-    }
-
-    // One pipeline stage s (ring slot SLOT = s % 4): wait for this wave's
-    // loads of stage s, barrier (every wave's loads landed, every wave is done
-    // with the slot about to be refilled), prefetch stage s + 3, compute s.
-    // Loads complete in issue order and every stage issues its A and B loads
-    // inside the stage (in either order), so "at most 2 (NA + NB)
-    // outstanding" (the loads of stages s + 1 and s + 2) proves that both the
-    // A and the B loads of stage s are done.
-    template <int NMB, int SLOT>
-    MOE_DEV void stage(int s, int nst, LDS_AS uint16_t *rg, LDS_AS uint16_t *rgp, BRaw &bcur, BRaw &bpf,
-                       f32x16 acc[kMB])
-    {
-        constexpr int NA = TR::kNA, NB = TR::kNB;
-        // nothing but MFMAs crosses a stage boundary: loads stay in their
-        // stage (the wait count relies on it) and decodes are not hoisted
-        // above the wait of the stage whose codes they use
-        __builtin_amdgcn_sched_barrier(0x8);
-        wait_vmcnt<2 * (NA + NB)>();
-        __builtin_amdgcn_s_barrier();
-        load_a(s + 3, nst, rgp);
-        load_b(s + 3, nst, bpf);
-        compute<NMB>(rg, bcur, acc);
+        for (int i = 0; i < NMB; ++i)
+            acc[i] = mfma_step<MODE>(af[1][i], b1, acc[i]);
+        if constexpr (TR::kTrellis)
+            interleave<NMB>();
     }
 
     template <int NMB>
@@ -245,11 +264,12 @@ struct GemmTile {
         load_b(1, nst, b1);
         load_a(2, nst, r2);
         load_b(2, nst, b2);
+        u32x4 dk0 = decode(b0, 0);
         for (int s = 0; s < nst; s += 4) {
-            stage<NMB, 0>(s, nst, r0, r3, b0, b3, acc);
-            stage<NMB, 1>(s + 1, nst, r1, r0, b1, b0, acc);
-            stage<NMB, 2>(s + 2, nst, r2, r1, b2, b1, acc);
-            stage<NMB, 3>(s + 3, nst, r3, r2, b3, b2, acc);
+            stage<NMB, 0>(s, nst, r0, r3, b0, b1, b3, dk0, acc);
+            stage<NMB, 1>(s + 1, nst, r1, r0, b1, b2, b0, dk0, acc);
+            stage<NMB, 2>(s + 2, nst, r2, r1, b2, b3, b1, dk0, acc);
+            stage<NMB, 3>(s + 3, nst, r3, r2, b3, b0, b2, dk0, acc);
         }
         wait_vmcnt<0>();   // the trailing zero-range loads still write LDS
     }
@@ -360,8 +380,8 @@ __global__ __launch_bounds__(256, 2) void group_gemm_kernel(GemmArgs args)
         g.srsrc = g.bnull;
         g.soff = 0;
         if constexpr (MODE == GATEUP_TRELLIS) {
-            g.srsrc = buf_rsrc(a.suh[g.pr] + (int64_t)g.e * g.H + 16 * (g.w & 1), (uint32_t)(g.H * 2 - 32 * (g.w & 1)));
-            g.soff = g.l < 8 ? 4u * g.l : 0x7FFFFFF0u;
+            g.srsrc = buf_rsrc(a.suh[g.pr] + (int64_t)g.e * g.H, (uint32_t)(g.H * 2));
+            g.soff = g.l < 16 ? 4u * g.l : 0x7FFFFFF0u;
         }
     } else {
         const uint16_t *W = TR::kGateUp ? args.dB[g.pr] : args.dB[0];
