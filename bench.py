@@ -37,7 +37,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_FP16_TFLOPS = 2500.0      # MI355X dense fp16/bf16 MFMA
 PEAK_HBM_GBPS = 8000.0
-GEMV_ROWS = 4                  # default per-expert row count up to which the GEMV path runs
+GEMV_ROWS = 2                  # default per-expert row count up to which the GEMV path runs
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic_mfma_gateup_prefill.md")
 KERNEL_SOURCES = ["mfma.hip", "trellis.h", "common.h", "internal.h"]
 

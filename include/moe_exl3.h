@@ -103,7 +103,7 @@ typedef struct moe_exl3_desc {
     int32_t act_dtype;      /* dtype of x and out */
     uint32_t flags;         /* MOE_EXL3_* flags */
     int32_t gemv_max_rows;  /* experts with at most this many routed rows use the
-                               GEMV path; 0 selects the default (4) */
+                               GEMV path; 0 selects the default (2) */
 } moe_exl3_desc;
 
 /* Layer weights.  All device pointers, contiguous, row-major. */

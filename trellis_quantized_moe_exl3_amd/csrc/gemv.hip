@@ -253,7 +253,7 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(GroupArgs a)
             const float tot = acc[r] + __shfl_xor(acc[r], 32, 64);
             if (r < nr && h == 0) {
                 const int slot = a.sorted[p0 + r0 + r];
-                a.ybuf[(int64_t)slot * H + m] = (tot - kBias2 * rsum[r]) * svh * a.w[slot];
+                a.ybuf[(int64_t)slot * H + m] = f32_to_bf16_bits((tot - kBias2 * rsum[r]) * svh * a.w[slot]);
             }
         }
         __syncthreads();

@@ -18,7 +18,7 @@ constexpr int kSegChunk = 2048;
 // Largest per-expert row count the GEMV path accepts (rows beyond two per
 // pass re-stream the expert's codes), and the default threshold.
 constexpr int kGemvMaxRows = 8;
-constexpr int kGemvDefaultRows = 4;
+constexpr int kGemvDefaultRows = 2;
 // The GEMV blocks keep two rows of activations in LDS within 64 KiB.
 constexpr int kGemvMaxHidden = 8192;
 constexpr int kGemvMaxInter = 8192;
@@ -65,7 +65,7 @@ struct GroupArgs {
     const float *w;          // routing weights [T*k]
     const uint16_t *x16;     // fp16 activations [T][H]
     uint16_t *hbuf;          // bf16 [T*k][I], sorted order, h * suh_down
-    float *ybuf;             // fp32 [T*k][H], slot order, w * y
+    uint16_t *ybuf;          // bf16 [T*k][H], slot order, w * y
 };
 
 hipError_t launch_convert_x(const uint16_t *x, bool bf16, int64_t n, uint16_t *x16, hipStream_t s);
@@ -81,7 +81,7 @@ hipError_t launch_shared_down(const uint16_t *sh, int64_t T, int H, int I, const
 hipError_t launch_shared_gemv(const uint16_t *x16, int T, int H, int I, const uint16_t *wg,
                               const uint16_t *wu, const uint16_t *wd, uint16_t *sh, float *sy,
                               hipStream_t s);
-hipError_t launch_combine(const float *ybuf, const float *sy, int64_t T, int H, int k, bool bf16,
+hipError_t launch_combine(const uint16_t *ybuf, const float *sy, int64_t T, int H, int k, bool bf16,
                           uint16_t *out, hipStream_t s);
 
 }  // namespace moe

@@ -53,7 +53,7 @@ struct ModeTraits {
     // (4 LDS-direct loads, plus one for suh in the trellis gate/up mode) and
     // B (trellis: 2 code dwords per k-step; dense: 16 bytes per k-step)
     static constexpr int kNA = 4 + (MODE == GATEUP_TRELLIS ? 1 : 0);
-    static constexpr int kNB = kTrellis ? 2 * kKT : kKT;
+    static constexpr int kNB = kTrellis ? 2 * kKT : kKT;   // per column group
 };
 
 struct GemmArgs {
@@ -135,8 +135,11 @@ struct GemmTile {
     int q;
     uint32_t m_lo, m_hi;
 
+    // raw B of one stage: CM column groups of 32 columns (trellis: 2 code
+    // dwords per k-step and group; dense: 16 bytes per k-step)
+    template <int CM>
     struct BRaw {
-        uint32_t c[kKT][2];
+        uint32_t c[kKT][CM][2];
         u32x4 d[kKT];
     };
 
@@ -160,36 +163,43 @@ struct GemmTile {
         }
     }
 
-    MOE_DEV void load_b(int s, int nst, BRaw &br)
+    template <int CM>
+    MOE_DEV void load_b(int s, int nst, BRaw<CM> &br)
     {
         const __amdgpu_buffer_rsrc_t rs = s < nst ? brsrc : bnull;
 #pragma unroll
         for (int kt = 0; kt < kKT; ++kt) {
             if constexpr (TR::kTrellis) {
                 const int so = (kKT * s + kt) * (int)rstride;
-                br.c[kt][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, boff0, so, 0);
-                br.c[kt][1] = __builtin_amdgcn_raw_buffer_load_b32(rs, boff1, so, 0);
+#pragma unroll
+                for (int cm = 0; cm < CM; ++cm) {
+                    // group cm starts two 16-column tiles further on
+                    const uint32_t go = (uint32_t)(cm * 2 * Tile<K>::kBytes);
+                    br.c[kt][cm][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, boff0 + go, so, 0);
+                    br.c[kt][cm][1] = __builtin_amdgcn_raw_buffer_load_b32(rs, boff1 + go, so, 0);
+                }
             } else {
                 br.d[kt] = __builtin_amdgcn_raw_buffer_load_b128(rs, boff0, (s * kBK + 16 * kt) * 2, 0);
             }
         }
     }
 
-    // B fragment of k-step kt before the suh scaling: 8 exact values of 2v
-    // (fp16 for gate/up, bf16 for down), or the dense weights as loaded
-    MOE_DEV u32x4 decode(const BRaw &br, int kt) const
+    // B fragment (k-step kt, column group cm) before the suh scaling: 8 exact
+    // values of 2v (fp16 for gate/up, bf16 for down), or dense weights
+    template <int CM>
+    MOE_DEV u32x4 decode(const BRaw<CM> &br, int kt, int cm) const
     {
         if constexpr (MODE == GATEUP_TRELLIS)
-            return __builtin_bit_cast(u32x4, frag_decode_f16<K, CB>(br.c[kt][0], br.c[kt][1], q, m_lo, m_hi));
+            return __builtin_bit_cast(u32x4, frag_decode_f16<K, CB>(br.c[kt][cm][0], br.c[kt][cm][1], q, m_lo, m_hi));
         else if constexpr (MODE == DOWN_TRELLIS)
-            return __builtin_bit_cast(u32x4, frag_decode_bf16<K, CB>(br.c[kt][0], br.c[kt][1], q, m_lo, m_hi));
+            return __builtin_bit_cast(u32x4, frag_decode_bf16<K, CB>(br.c[kt][cm][0], br.c[kt][cm][1], q, m_lo, m_hi));
         else
             return br.d[kt];
     }
 
-    // Interleave the MFMAs of one k-step with the VALU work scheduled next to
-    // them (the decode of the following k-step): one MFMA occupies the matrix
-    // pipe for 32 cycles, during which the wave can issue ~8 VALU operations.
+    // Interleave the MFMAs of one fragment with the VALU work scheduled next
+    // to them (the decode of the following fragment): one MFMA occupies the
+    // matrix pipe for 32 cycles, in which the wave can issue ~8 VALU ops.
     template <int NMB>
     MOE_DEV static void interleave()
     {
@@ -205,21 +215,22 @@ struct GemmTile {
     //   wait for this wave's loads of stage s, barrier (every wave's loads
     //   landed, every wave is done with the slot about to be refilled),
     //   prefetch stage s + 3, read the stage's A fragments (and this wave's
-    //   suh), then run the k-step 0 MFMAs while decoding k-step 1 and the
-    //   k-step 1 MFMAs while decoding k-step 0 of stage s + 1 (dk0 carries it).
+    //   suh), then walk the 2 CM fragments f = (k-step, column group): the
+    //   MFMAs of f (one per 32-row block) run while fragment f + 1 is decoded;
+    //   the last one decodes fragment 0 of stage s + 1 (carried in dk0).
     // Loads complete in issue order and every stage issues its loads inside
     // the stage, so "at most 2 (NA + NB) outstanding" (the loads of stages
     // s + 1 and s + 2) proves that the loads of stage s are done.
-    template <int NMB, int SLOT>
-    MOE_DEV void stage(int s, int nst, LDS_AS uint16_t *rg, LDS_AS uint16_t *rgp, const BRaw &bcur,
-                       const BRaw &bnext, BRaw &bpf, u32x4 &dk0, f32x16 acc[kMB])
+    template <int NMB, int CM, int SLOT>
+    MOE_DEV void stage(int s, int nst, LDS_AS uint16_t *rg, LDS_AS uint16_t *rgp, const BRaw<CM> &bcur,
+                       const BRaw<CM> &bnext, BRaw<CM> &bpf, u32x4 &dk0, f32x16 acc[kMB])
     {
-        constexpr int NA = TR::kNA, NB = TR::kNB;
+        constexpr int NA = TR::kNA, NB = TR::kNB * CM;
         __builtin_amdgcn_sched_barrier(0);
         wait_vmcnt<2 * (NA + NB)>();
         __builtin_amdgcn_s_barrier();
         load_a(s + 3, nst, rgp);
-        load_b(s + 3, nst, bpf);
+        load_b<CM>(s + 3, nst, bpf);
         f16x8 su[kKT];
         if constexpr (MODE == GATEUP_TRELLIS) {
 #pragma unroll
@@ -232,48 +243,193 @@ struct GemmTile {
 #pragma unroll
             for (int i = 0; i < NMB; ++i)
                 af[kt][i] = *(const LDS_AS u32x4 *)((const LDS_AS char *)rg + aread[kt] + i * 32 * kBK * 2);
-        u32x4 b0 = dk0;
-        if constexpr (MODE == GATEUP_TRELLIS)
-            b0 = __builtin_bit_cast(u32x4, __builtin_bit_cast(f16x8, dk0) * su[0]);
-        const u32x4 d1 = decode(bcur, 1);
+        u32x4 dcur = dk0;
 #pragma unroll
-        for (int i = 0; i < NMB; ++i)
-            acc[i] = mfma_step<MODE>(af[0][i], b0, acc[i]);
-        if constexpr (TR::kTrellis)
-            interleave<NMB>();
-        u32x4 b1 = d1;
-        if constexpr (MODE == GATEUP_TRELLIS)
-            b1 = __builtin_bit_cast(u32x4, __builtin_bit_cast(f16x8, d1) * su[1]);
-        dk0 = decode(bnext, 0);
+        for (int f = 0; f < kKT * CM; ++f) {
+            const int kt = f / CM, cm = f % CM;
+            u32x4 b = dcur;
+            if constexpr (MODE == GATEUP_TRELLIS)
+                b = __builtin_bit_cast(u32x4, __builtin_bit_cast(f16x8, dcur) * su[kt]);
+            if (f + 1 < kKT * CM)
+                dcur = decode<CM>(bcur, (f + 1) / CM, (f + 1) % CM);
+            else
+                dcur = decode<CM>(bnext, 0, 0);
 #pragma unroll
-        for (int i = 0; i < NMB; ++i)
-            acc[i] = mfma_step<MODE>(af[1][i], b1, acc[i]);
-        if constexpr (TR::kTrellis)
-            interleave<NMB>();
+            for (int i = 0; i < NMB; ++i)
+                acc[cm * NMB + i] = mfma_step<MODE>(af[kt][i], b, acc[cm * NMB + i]);
+            if constexpr (TR::kTrellis)
+                interleave<NMB>();
+        }
+        dk0 = dcur;
     }
 
-    template <int NMB>
+    template <int NMB, int CM>
     MOE_DEV void run(LDS_AS uint16_t *r0, LDS_AS uint16_t *r1, LDS_AS uint16_t *r2, LDS_AS uint16_t *r3,
                      f32x16 acc[kMB])
     {
         const int nst = Kdim / kBK;   // a multiple of 4
-        BRaw b0, b1, b2, b3;
+        BRaw<CM> b0, b1, b2, b3;
         load_a(0, nst, r0);
-        load_b(0, nst, b0);
+        load_b<CM>(0, nst, b0);
         load_a(1, nst, r1);
-        load_b(1, nst, b1);
+        load_b<CM>(1, nst, b1);
         load_a(2, nst, r2);
-        load_b(2, nst, b2);
-        u32x4 dk0 = decode(b0, 0);
+        load_b<CM>(2, nst, b2);
+        u32x4 dk0 = decode<CM>(b0, 0, 0);
         for (int s = 0; s < nst; s += 4) {
-            stage<NMB, 0>(s, nst, r0, r3, b0, b1, b3, dk0, acc);
-            stage<NMB, 1>(s + 1, nst, r1, r0, b1, b2, b0, dk0, acc);
-            stage<NMB, 2>(s + 2, nst, r2, r1, b2, b3, b1, dk0, acc);
-            stage<NMB, 3>(s + 3, nst, r3, r2, b3, b0, b2, dk0, acc);
+            stage<NMB, CM, 0>(s, nst, r0, r3, b0, b1, b3, dk0, acc);
+            stage<NMB, CM, 1>(s + 1, nst, r1, r0, b1, b2, b0, dk0, acc);
+            stage<NMB, CM, 2>(s + 2, nst, r2, r1, b2, b3, b1, dk0, acc);
+            stage<NMB, CM, 3>(s + 3, nst, r3, r2, b3, b0, b2, dk0, acc);
         }
         wait_vmcnt<0>();   // the trailing zero-range loads still write LDS
     }
 };
+
+// Column groups per wavefront for a tile of NMB 32-row blocks: small tiles
+// take more columns so that every stage issues (close to) 16 MFMAs per
+// wavefront, reuses each A fragment CM times and amortises its barrier and
+// loads.
+template <int MODE, int NMB>
+struct Groups {
+    static constexpr int kMax = !ModeTraits<MODE>::kTrellis ? 1 : (NMB <= 2 ? 4 : (NMB <= 4 ? 2 : 1));
+};
+
+template <int MODE, int K, int CB, int NMB, int CM>
+MOE_DEV void tile_body(GemmTile<MODE, K, CB> &g, const GemmArgs &args, int n0,
+                       uint16_t *ring0, uint16_t *ring1, uint16_t *ring2, uint16_t *ring3)
+{
+    using TR = ModeTraits<MODE>;
+    const GroupArgs &a = args.g;
+    // ---- B source: lane -> (column c of tile ts, k-half h); the wavefront
+    // owns CM groups of 32 columns of one projection: gate/up -> waves 0,1
+    // gate and waves 2,3 up of the block's 64 CM intermediate columns; down ->
+    // 32 CM of the block's 128 CM output columns
+    const int Nout = TR::kGateUp ? g.I : g.H;
+    g.col = (TR::kGateUp ? n0 + 32 * CM * (g.w & 1) : n0 + 32 * CM * g.w) + 16 * g.ts + g.c;
+    if constexpr (TR::kTrellis) {
+        int d0, d1, q;
+        frag_pos<K>(g.c, g.h, d0, d1, q);
+        g.q = q;
+        const int64_t per_expert = (int64_t)(g.Kdim / 16) * (Nout / 16) * Tile<K>::kBytes;
+        g.rstride = (uint32_t)((Nout / 16) * Tile<K>::kBytes);
+        g.brsrc = buf_rsrc((const char *)a.codes[g.pr] + g.e * per_expert, (uint32_t)per_expert);
+        g.bnull = buf_rsrc((const char *)a.codes[g.pr], 0);
+        const uint32_t tile0 = (uint32_t)((g.col / 16) * Tile<K>::kBytes);
+        g.boff0 = tile0 + 4 * d0;
+        g.boff1 = tile0 + 4 * d1;
+        g.srsrc = g.bnull;
+        g.soff = 0;
+        if constexpr (MODE == GATEUP_TRELLIS) {
+            g.srsrc = buf_rsrc(a.suh[g.pr] + (int64_t)g.e * g.H, (uint32_t)(g.H * 2));
+            g.soff = g.l < 16 ? 4u * g.l : 0x7FFFFFF0u;
+        }
+    } else {
+        const uint16_t *W = TR::kGateUp ? args.dB[g.pr] : args.dB[0];
+        g.brsrc = buf_rsrc(W, (uint32_t)((int64_t)Nout * g.Kdim * 2));
+        g.bnull = buf_rsrc(W, 0);
+        g.srsrc = g.bnull;
+        g.soff = 0;
+        g.boff0 = (uint32_t)(((int64_t)g.col * g.Kdim + 8 * g.h) * 2);
+        g.boff1 = 0;
+        g.rstride = 0;
+    }
+
+    LDS_AS uint16_t *R0 = (LDS_AS uint16_t *)ring0, *R1 = (LDS_AS uint16_t *)ring1;
+    LDS_AS uint16_t *R2 = (LDS_AS uint16_t *)ring2, *R3 = (LDS_AS uint16_t *)ring3;
+    f32x16 acc[kMB];
+#pragma unroll
+    for (int i = 0; i < kMB; ++i)
+        acc[i] = (f32x16){};
+    g.template run<NMB, CM>(R0, R1, R2, R3, acc);
+    __syncthreads();   // every wave is done with the rings (reused below)
+
+    // ---- epilogue.  Accumulator block b = cm * NMB + i covers rows 32 i + ..
+    // of column group cm; its D register r holds row 32i + 8(r/4) + 4h + r%4.
+    constexpr int NB = NMB * CM;
+    const int h = g.h, rows = g.rows, e = g.e, p0 = g.p0;
+    const int H = g.H, I = g.I;
+    const int64_t t0 = g.t0;
+    const int mblocks = (rows + 31) >> 5;
+    if constexpr (TR::kGateUp) {
+        // up wavefronts hand their scaled results to the gate wavefronts with
+        // the same columns through LDS: block b of column half cb goes to
+        // ring (2 cb + b / 4), 4 KiB per block
+        const int cb = g.w & 1;
+        float *ex_lo = cb ? (float *)ring2 : (float *)ring0;
+        float *ex_hi = cb ? (float *)ring3 : (float *)ring1;
+        if (g.pr == 1) {
+#pragma unroll
+            for (int cm = 0; cm < CM; ++cm) {
+                const int col = g.col + 32 * cm;
+                const float su = MODE == GATEUP_TRELLIS ? f16_to_f32(a.svh[1][(int64_t)e * I + col]) * (1.0f / 128.0f) : 1.0f;
+#pragma unroll
+                for (int i = 0; i < NMB; ++i) {
+                    const int b = cm * NMB + i;
+                    if (i < mblocks)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            (b < 4 ? ex_lo : ex_hi)[((b & 3) * 16 + r) * 64 + g.l] = acc[b][r] * su;
+                }
+            }
+        }
+        __syncthreads();
+        if (g.pr == 0) {
+#pragma unroll
+            for (int cm = 0; cm < CM; ++cm) {
+                const int col = g.col + 32 * cm;
+                float sg = 1.0f, sd = 1.0f;
+                if constexpr (MODE == GATEUP_TRELLIS) {
+                    sg = f16_to_f32(a.svh[0][(int64_t)e * I + col]) * (1.0f / 128.0f);
+                    sd = f16_to_f32(a.suh[2][(int64_t)e * I + col]);
+                }
+#pragma unroll
+                for (int i = 0; i < NMB; ++i) {
+                    const int b = cm * NMB + i;
+                    if (i < mblocks) {
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int row = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+                            if (row < rows) {
+                                const float u = (b < 4 ? ex_lo : ex_hi)[((b & 3) * 16 + r) * 64 + g.l];
+                                const float hv = silu_f(acc[b][r] * sg) * u * sd;
+                                if constexpr (MODE == GATEUP_TRELLIS)
+                                    a.hbuf[(int64_t)(p0 + row) * I + col] = f32_to_bf16_bits(hv);
+                                else
+                                    args.dOutH[(t0 + row) * I + col] = f32_to_f16_bits(hv);
+                            }
+                        }
+                    }
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int cm = 0; cm < CM; ++cm) {
+            const int col = g.col + 32 * cm;
+            const float sv = MODE == DOWN_TRELLIS ? f16_to_f32(a.svh[2][(int64_t)e * H + col]) * (1.0f / 128.0f) : 1.0f;
+#pragma unroll
+            for (int i = 0; i < NMB; ++i) {
+                const int b = cm * NMB + i;
+                if (i < mblocks) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int row = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+                        if (row < rows) {
+                            if constexpr (MODE == DOWN_TRELLIS) {
+                                const int slot = a.sorted[p0 + row];
+                                a.ybuf[(int64_t)slot * H + col] = f32_to_bf16_bits(acc[b][r] * sv * a.w[slot]);
+                            } else {
+                                args.dOutY[(t0 + row) * H + col] = acc[b][r];
+                            }
+                        }
+                    }
+                }
+            }
+        }
+    }
+    static_assert(NB <= kMB, "accumulator blocks");
+}
 
 template <int MODE, int K, int CB>
 __global__ __launch_bounds__(256, 2) void group_gemm_kernel(GemmArgs args)
@@ -295,9 +451,8 @@ __global__ __launch_bounds__(256, 2) void group_gemm_kernel(GemmArgs args)
     g.H = a.H;
     g.I = a.I;
     g.Kdim = TR::kGateUp ? g.H : g.I;
-    const int Nout = TR::kGateUp ? g.I : g.H;
 
-    // ---- work tile
+    // ---- work tile; `nslices` counts column slices at one group per wave
     int ti, slice;
     xcd_map(blockIdx.x, args.nslices, ti, slice);
     g.e = 0;
@@ -316,8 +471,17 @@ __global__ __launch_bounds__(256, 2) void group_gemm_kernel(GemmArgs args)
             return;
         g.rows = (int)min<int64_t>(kBM, args.T - g.t0);
     }
-    const int n0 = slice * TR::kBlockN;
     const int mblocks = (g.rows + 31) >> 5;
+    // column groups per wavefront for this tile (a slice beyond the tile's
+    // share has no work: the whole block leaves before any barrier)
+    int cm = 1;
+    if (TR::kTrellis && mblocks <= 2)
+        cm = (args.nslices % 4 == 0) ? 4 : 2;
+    else if (TR::kTrellis && mblocks <= 4)
+        cm = 2;
+    if (slice >= args.nslices / cm)
+        return;
+    const int n0 = slice * TR::kBlockN * cm;
 
     // ---- A rows
     {
@@ -354,126 +518,24 @@ __global__ __launch_bounds__(256, 2) void group_gemm_kernel(GemmArgs args)
             g.aread[kt] = (uint32_t)(r * kBK * 2 + 16 * a_slot(r, 2 * kt + g.h));
         }
     }
-
-    // ---- B source: lane -> (column c of tile ts, k-half h)
     g.c = g.l & 15;
     g.ts = (g.l >> 4) & 1;
-    // every wavefront owns 32 columns (two 16-column tiles, ts) of one
-    // projection: gate/up -> waves 0,1 gate and waves 2,3 up of the block's 64
-    // intermediate columns; down -> 32 of the block's 128 output columns
     g.pr = TR::kGateUp ? g.w >> 1 : 2;
-    g.col = TR::kGateUp ? n0 + 32 * (g.w & 1) + 16 * g.ts + g.c : n0 + 32 * g.w + 16 * g.ts + g.c;
     g.m_lo = a.mcg & 0xFFFFu;
     g.m_hi = a.mcg >> 16;
     g.q = 0;
-    if constexpr (TR::kTrellis) {
-        int d0, d1, q;
-        frag_pos<K>(g.c, g.h, d0, d1, q);
-        g.q = q;
-        const int64_t per_expert = (int64_t)(g.Kdim / 16) * (Nout / 16) * Tile<K>::kBytes;
-        g.rstride = (uint32_t)((Nout / 16) * Tile<K>::kBytes);
-        g.brsrc = buf_rsrc((const char *)a.codes[g.pr] + g.e * per_expert, (uint32_t)per_expert);
-        g.bnull = buf_rsrc((const char *)a.codes[g.pr], 0);
-        const uint32_t tile0 = (uint32_t)((g.col / 16) * Tile<K>::kBytes);
-        g.boff0 = tile0 + 4 * d0;
-        g.boff1 = tile0 + 4 * d1;
-        g.srsrc = g.bnull;
-        g.soff = 0;
-        if constexpr (MODE == GATEUP_TRELLIS) {
-            g.srsrc = buf_rsrc(a.suh[g.pr] + (int64_t)g.e * g.H, (uint32_t)(g.H * 2));
-            g.soff = g.l < 16 ? 4u * g.l : 0x7FFFFFF0u;
-        }
-    } else {
-        const uint16_t *W = TR::kGateUp ? args.dB[g.pr] : args.dB[0];
-        g.brsrc = buf_rsrc(W, (uint32_t)((int64_t)Nout * g.Kdim * 2));
-        g.bnull = buf_rsrc(W, 0);
-        g.srsrc = g.bnull;
-        g.soff = 0;
-        g.boff0 = (uint32_t)(((int64_t)g.col * g.Kdim + 8 * g.h) * 2);
-        g.boff1 = 0;
-        g.rstride = 0;
-    }
 
-    LDS_AS uint16_t *R0 = (LDS_AS uint16_t *)ring0, *R1 = (LDS_AS uint16_t *)ring1;
-    LDS_AS uint16_t *R2 = (LDS_AS uint16_t *)ring2, *R3 = (LDS_AS uint16_t *)ring3;
-    f32x16 acc[kMB];
-#pragma unroll
-    for (int i = 0; i < kMB; ++i)
-        acc[i] = (f32x16){};
-    if (mblocks <= 2)
-        g.template run<2>(R0, R1, R2, R3, acc);
-    else if (mblocks <= 4)
-        g.template run<4>(R0, R1, R2, R3, acc);
-    else if (mblocks <= 6)
-        g.template run<6>(R0, R1, R2, R3, acc);
-    else
-        g.template run<8>(R0, R1, R2, R3, acc);
-    __syncthreads();   // every wave is done with the rings (reused below)
-
-    // ---- epilogue; D register r of block i holds row 32i + 8(r/4) + 4h + r%4
-    const int h = g.h, col = g.col, rows = g.rows, e = g.e, p0 = g.p0;
-    const int H = g.H, I = g.I;
-    const int64_t t0 = g.t0;
-    if constexpr (TR::kGateUp) {
-        // up wavefronts hand their scaled results to the gate wavefronts with
-        // the same columns through LDS: block i of column half cb goes to
-        // ring (2 cb + i / 4), 4 KiB per block
-        const int cb = g.w & 1;
-        float *ex_lo = cb ? (float *)ring2 : (float *)ring0;
-        float *ex_hi = cb ? (float *)ring3 : (float *)ring1;
-        if (g.pr == 1) {
-            const float su = MODE == GATEUP_TRELLIS ? f16_to_f32(a.svh[1][(int64_t)e * I + col]) * (1.0f / 128.0f) : 1.0f;
-#pragma unroll
-            for (int i = 0; i < kMB; ++i)
-                if (i < mblocks)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        (i < 4 ? ex_lo : ex_hi)[((i & 3) * 16 + r) * 64 + g.l] = acc[i][r] * su;
-        }
-        __syncthreads();
-        if (g.pr == 0) {
-            float sg = 1.0f, sd = 1.0f;
-            if constexpr (MODE == GATEUP_TRELLIS) {
-                sg = f16_to_f32(a.svh[0][(int64_t)e * I + col]) * (1.0f / 128.0f);
-                sd = f16_to_f32(a.suh[2][(int64_t)e * I + col]);
-            }
-#pragma unroll
-            for (int i = 0; i < kMB; ++i) {
-                if (i < mblocks) {
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int row = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-                        if (row < rows) {
-                            const float u = (i < 4 ? ex_lo : ex_hi)[((i & 3) * 16 + r) * 64 + g.l];
-                            const float hv = silu_f(acc[i][r] * sg) * u * sd;
-                            if constexpr (MODE == GATEUP_TRELLIS)
-                                a.hbuf[(int64_t)(p0 + row) * I + col] = f32_to_bf16_bits(hv);
-                            else
-                                args.dOutH[(t0 + row) * I + col] = f32_to_f16_bits(hv);
-                        }
-                    }
-                }
-            }
-        }
+    if (mblocks <= 2) {
+        if (cm == 4)
+            tile_body<MODE, K, CB, 2, Groups<MODE, 2>::kMax>(g, args, n0, ring0, ring1, ring2, ring3);
+        else
+            tile_body<MODE, K, CB, 2, (Groups<MODE, 2>::kMax > 2 ? 2 : Groups<MODE, 2>::kMax)>(g, args, n0, ring0, ring1, ring2, ring3);
+    } else if (mblocks <= 4) {
+        tile_body<MODE, K, CB, 4, Groups<MODE, 4>::kMax>(g, args, n0, ring0, ring1, ring2, ring3);
+    } else if (mblocks <= 6) {
+        tile_body<MODE, K, CB, 6, 1>(g, args, n0, ring0, ring1, ring2, ring3);
     } else {
-        const float sv = MODE == DOWN_TRELLIS ? f16_to_f32(a.svh[2][(int64_t)e * H + col]) * (1.0f / 128.0f) : 1.0f;
-#pragma unroll
-        for (int i = 0; i < kMB; ++i) {
-            if (i < mblocks) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-                    if (row < rows) {
-                        if constexpr (MODE == DOWN_TRELLIS) {
-                            const int slot = a.sorted[p0 + row];
-                            a.ybuf[(int64_t)slot * H + col] = acc[i][r] * sv * a.w[slot];
-                        } else {
-                            args.dOutY[(t0 + row) * H + col] = acc[i][r];
-                        }
-                    }
-                }
-            }
-        }
+        tile_body<MODE, K, CB, 8, 1>(g, args, n0, ring0, ring1, ring2, ring3);
     }
 }
 
@@ -570,36 +632,53 @@ hipError_t launch_convert_x(const uint16_t *x, bool bf16, int64_t n, uint16_t *x
     return hipGetLastError();
 }
 
-// out[t] = shared[t] + sum_j ybuf[t*k + j], cast to the activation dtype.
+// out[t] = shared[t] + sum_j ybuf[t*k + j] (bf16 slot rows, summed in fp32 in
+// slot order: deterministic), cast to the activation dtype.  8 outputs per
+// thread.
 template <bool BF16>
-__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ ybuf,
+__global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict__ ybuf,
                                                       const float *__restrict__ sy, int64_t T, int H,
                                                       int k, uint16_t *__restrict__ out)
 {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;   // 4 outputs per thread
-    const int64_t n4 = T * H / 4;
-    if (i >= n4)
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t n8 = T * H / 8;
+    if (i >= n8)
         return;
-    const int64_t t = (4 * i) / H, m = (4 * i) % H;
-    f32x4 s = sy ? *(const f32x4 *)(sy + t * H + m) : (f32x4){0, 0, 0, 0};
-    for (int j = 0; j < k; ++j)
-        s += *(const f32x4 *)(ybuf + (t * k + j) * H + m);
-    uint32_t o0, o1;
-    if (BF16) {
-        o0 = (uint32_t)f32_to_bf16_bits(s[0]) | ((uint32_t)f32_to_bf16_bits(s[1]) << 16);
-        o1 = (uint32_t)f32_to_bf16_bits(s[2]) | ((uint32_t)f32_to_bf16_bits(s[3]) << 16);
+    const int64_t t = (8 * i) / H, m = (8 * i) % H;
+    float s[8];
+    if (sy) {
+        const f32x4 a = *(const f32x4 *)(sy + t * H + m), b = *(const f32x4 *)(sy + t * H + m + 4);
+        s[0] = a[0]; s[1] = a[1]; s[2] = a[2]; s[3] = a[3];
+        s[4] = b[0]; s[5] = b[1]; s[6] = b[2]; s[7] = b[3];
     } else {
-        o0 = (uint32_t)f32_to_f16_bits(s[0]) | ((uint32_t)f32_to_f16_bits(s[1]) << 16);
-        o1 = (uint32_t)f32_to_f16_bits(s[2]) | ((uint32_t)f32_to_f16_bits(s[3]) << 16);
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            s[q] = 0.0f;
     }
-    *(u32x2 *)(out + t * H + m) = (u32x2){o0, o1};
+    for (int j = 0; j < k; ++j) {
+        const u32x4 v = *(const u32x4 *)(ybuf + (t * k + j) * H + m);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            s[2 * q] += __uint_as_float(v[q] << 16);
+            s[2 * q + 1] += __uint_as_float(v[q] & 0xFFFF0000u);
+        }
+    }
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        if (BF16)
+            o[q] = (uint32_t)f32_to_bf16_bits(s[2 * q]) | ((uint32_t)f32_to_bf16_bits(s[2 * q + 1]) << 16);
+        else
+            o[q] = (uint32_t)f32_to_f16_bits(s[2 * q]) | ((uint32_t)f32_to_f16_bits(s[2 * q + 1]) << 16);
+    }
+    *(u32x4 *)(out + t * H + m) = o;
 }
 
-hipError_t launch_combine(const float *ybuf, const float *sy, int64_t T, int H, int k, bool bf16,
+hipError_t launch_combine(const uint16_t *ybuf, const float *sy, int64_t T, int H, int k, bool bf16,
                           uint16_t *out, hipStream_t s)
 {
-    const int64_t n4 = T * H / 4;
-    const unsigned grid = (unsigned)((n4 + 255) / 256);
+    const int64_t n8 = T * H / 8;
+    const unsigned grid = (unsigned)((n8 + 255) / 256);
     if (bf16)
         combine_kernel<true><<<grid, 256, 0, s>>>(ybuf, sy, T, H, k, out);
     else

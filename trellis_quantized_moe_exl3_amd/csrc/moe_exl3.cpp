@@ -119,7 +119,7 @@ Plan make_plan(const moe_exl3_desc &d, int64_t T)
     p.tiles = take(sizeof(int32_t) * 2 * (size_t)std::max(1, p.max_tiles));
     p.x16 = take(d.act_dtype == MOE_EXL3_DT_BF16 ? sizeof(uint16_t) * (size_t)T * d.hidden : 0);
     p.hbuf = take(sizeof(uint16_t) * (size_t)n * d.inter);
-    p.ybuf = take(sizeof(float) * (size_t)n * d.hidden);
+    p.ybuf = take(sizeof(uint16_t) * (size_t)n * d.hidden);
     const bool sh = d.flags & MOE_EXL3_HAS_SHARED;
     p.sh = take(sh ? sizeof(uint16_t) * (size_t)T * d.inter : 0);
     p.sy = take(sh ? sizeof(float) * (size_t)T * d.hidden : 0);
@@ -313,7 +313,7 @@ static int run_layer(const moe_exl3_desc *desc, const moe_exl3_weights *weights,
     ga.w = at<float>(ws, p.w);
     ga.x16 = x16;
     ga.hbuf = at<uint16_t>(ws, p.hbuf);
-    ga.ybuf = at<float>(ws, p.ybuf);
+    ga.ybuf = at<uint16_t>(ws, p.ybuf);
     const int g = gemv_rows_of(d);
     const int64_t n = T * d.top_k;
     const int max_list = g > 0 ? (int)std::min<int64_t>(d.n_experts, n) : 0;
@@ -342,7 +342,7 @@ static int run_layer(const moe_exl3_desc *desc, const moe_exl3_weights *weights,
             return MOE_EXL3_ERR_HIP;
     }
     if (!mk.mark(MOE_EXL3_STEP_COMBINE) ||
-        launch_combine(at<float>(ws, p.ybuf), sy, T, d.hidden, d.top_k, bf16, (uint16_t *)out, s) != hipSuccess ||
+        launch_combine(at<uint16_t>(ws, p.ybuf), sy, T, d.hidden, d.top_k, bf16, (uint16_t *)out, s) != hipSuccess ||
         !mk.mark(MOE_EXL3_STEP_END))
         return MOE_EXL3_ERR_HIP;
     return MOE_EXL3_OK;

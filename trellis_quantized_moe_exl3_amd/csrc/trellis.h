@@ -23,7 +23,8 @@
 //
 // Instruction budget per weight (gfx950): one shift/alignbit for the window,
 // two 16-bit multiplies for the 32-bit hash, one AND and one SAD for the four
-// field sum, then half an op each to pack and re-centre two fp16 values.
+// field sum (the SAD of the second state of a pair writes the high half, so
+// packing is free), then half an op to re-centre two fp16 values.
 #pragma once
 
 #include "common.h"
@@ -129,10 +130,13 @@ MOE_DEV f16x8 frag_decode_f16(uint32_t D0, uint32_t D1, int q, uint32_t m_lo, ui
     if (CB == CB_MCG) {
 #pragma unroll
         for (int t = 0; t < 8; t += 2) {
-            // bits 0x6400 + n are the half 1024 + n (n < 1024)
-            const uint32_t ra = field_sum2(mcg_hash(st[t], m_lo, m_hi), 0x6400u);
-            const uint32_t rb = field_sum2(mcg_hash(st[t + 1], m_lo, m_hi), 0x6400u);
-            const f16x2 p = __builtin_bit_cast(f16x2, ra | (rb << 16));
+            // bits 0x6400 + n are the half 1024 + n (n < 1024): the low half
+            // gets 0x6400 + 2 (field sum of state t) from v_sad_u8, the high
+            // half 0x6400 + 2 (field sum of state t+1) from v_sad_hi_u8, which
+            // adds its sum shifted left by 16 (no carry: 0x6400 + 508 < 2^16)
+            const uint32_t ra = field_sum2(mcg_hash(st[t], m_lo, m_hi), 0x64006400u);
+            const uint32_t rb = __builtin_amdgcn_sad_hi_u8(mcg_hash(st[t + 1], m_lo, m_hi) & 0xFEFEFEFEu, 0u, ra);
+            const f16x2 p = __builtin_bit_cast(f16x2, rb);
             const f16x2 v = p - (f16x2){(f16)1532.0f, (f16)1532.0f};   // 1024 + 508
             out[t] = v[0];
             out[t + 1] = v[1];
