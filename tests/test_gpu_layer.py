@@ -107,3 +107,18 @@ def test_mixed_width_sampled(name):
 
 def test_e4m3_codebook_sampled():
     _sampled("fp8", [0, 8191, 16383])
+
+
+def test_shared_expert_ragged_row_tile():
+    # 300 tokens at the real shapes: the shared expert runs on the MFMA path
+    # (more than 16 tokens) with a last row tile of 44 rows, so one of its two
+    # row halves is empty; the full output is dominated by the shared expert
+    cfg = W.BY_NAME["decode"].replace(tokens=300)
+    inp = W.gen_layer(cfg)
+    sample = [0, 127, 128, 255, 256, 299]
+    out = DevLayer(inp).run()
+    _, _, ref = oracle.layer(inp, sample)
+    err = rel_err(out[sample], ref)
+    print(f"shared ragged err={err:.3e}")
+    assert err <= TOL
+    assert np.isfinite(out).all()

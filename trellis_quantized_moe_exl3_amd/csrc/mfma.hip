@@ -140,7 +140,7 @@ struct GemmTile {
     template <int CM>
     struct BRaw {
         uint32_t c[kKT][CM][2];
-        u32x4 d[kKT];
+        u32x4 d[kKT][CM];
     };
 
     // Issue the A LDS-direct loads of stage s into one ring slot.  Every
@@ -179,7 +179,11 @@ struct GemmTile {
                     br.c[kt][cm][1] = __builtin_amdgcn_raw_buffer_load_b32(rs, boff1 + go, so, 0);
                 }
             } else {
-                br.d[kt] = __builtin_amdgcn_raw_buffer_load_b128(rs, boff0, (s * kBK + 16 * kt) * 2, 0);
+                // group cm: 32 weight rows (output columns) further on
+#pragma unroll
+                for (int cm = 0; cm < CM; ++cm)
+                    br.d[kt][cm] = __builtin_amdgcn_raw_buffer_load_b128(rs, boff0 + (uint32_t)(cm * 32 * Kdim * 2),
+                                                                         (s * kBK + 16 * kt) * 2, 0);
             }
         }
     }
@@ -194,7 +198,7 @@ struct GemmTile {
         else if constexpr (MODE == DOWN_TRELLIS)
             return __builtin_bit_cast(u32x4, frag_decode_bf16<K, CB>(br.c[kt][cm][0], br.c[kt][cm][1], q, m_lo, m_hi));
         else
-            return br.d[kt];
+            return br.d[kt][cm];
     }
 
     // Interleave the MFMAs of one fragment with the VALU work scheduled next
@@ -302,9 +306,9 @@ MOE_DEV void tile_body(GemmTile<MODE, K, CB> &g, const GemmArgs &args, int n0,
     using TR = ModeTraits<MODE>;
     const GroupArgs &a = args.g;
     // ---- B source: lane -> (column c of tile ts, k-half h); the wavefront
-    // owns CM groups of 32 columns of one projection: gate/up -> waves 0,1
-    // gate and waves 2,3 up of the block's 64 CM intermediate columns; down ->
-    // 32 CM of the block's 128 CM output columns
+    // owns CM groups of 32 columns of one projection over all 256 rows:
+    // gate/up -> waves 0,1 gate and waves 2,3 up of the block's 64 CM
+    // intermediate columns; down -> 32 CM of the block's 128 CM output columns
     const int Nout = TR::kGateUp ? g.I : g.H;
     g.col = (TR::kGateUp ? n0 + 32 * CM * (g.w & 1) : n0 + 32 * CM * g.w) + 16 * g.ts + g.c;
     if constexpr (TR::kTrellis) {
@@ -544,7 +548,7 @@ static hipError_t launch_mode(const GemmArgs &ga, int tiles, hipStream_t s)
 {
     const GroupArgs &a = ga.g;
     const unsigned grid = (unsigned)(((tiles + 7) / 8) * 8 * ga.nslices);
-    if (ModeTraits<MODE>::kTrellis) {
+    if constexpr (ModeTraits<MODE>::kTrellis) {
         if (a.K == 2 && a.cb == 0) group_gemm_kernel<MODE, 2, 0><<<grid, 256, 0, s>>>(ga);
         else if (a.K == 3 && a.cb == 0) group_gemm_kernel<MODE, 3, 0><<<grid, 256, 0, s>>>(ga);
         else if (a.K == 4 && a.cb == 0) group_gemm_kernel<MODE, 4, 0><<<grid, 256, 0, s>>>(ga);

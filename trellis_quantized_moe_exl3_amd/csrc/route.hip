@@ -73,12 +73,17 @@ __global__ __launch_bounds__(256) void route_logits_kernel(const uint16_t *__res
 #pragma unroll
             for (int j = 0; j < 8; ++j)
                 p[a][b][j] = 0.0f;
-#pragma unroll 4
+    // rows past the last token or expert read row 0 (in bounds); their sums
+    // are never stored.  With few pairs per lane (few tokens) the loads stay
+    // predicated, which lets the compiler keep more iterations in flight.
+    constexpr bool kWide = TPL * EPL >= 8;
+    constexpr int kUnroll = kWide ? 2 : 4;
+#pragma unroll kUnroll
     for (int i = 0; i < H / 64; ++i) {
         float xv[TPL][8];
 #pragma unroll
         for (int a = 0; a < TPL; ++a) {
-            const u32x4 raw = tok_ok[a] ? *(const u32x4 *)(xr[a] + 64 * i) : (u32x4){0, 0, 0, 0};
+            const u32x4 raw = (kWide || tok_ok[a]) ? *(const u32x4 *)(xr[a] + 64 * i) : (u32x4){0, 0, 0, 0};
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 if (BF16) {
@@ -148,12 +153,13 @@ static void route_launch(const uint16_t *x, int64_t T, int H, const uint16_t *Wr
 hipError_t launch_route_logits(const uint16_t *x, bool bf16, int64_t T, int H, const uint16_t *Wr,
                                const float *bias, int E, float *logits, hipStream_t s)
 {
-    // many tokens: 4 tokens x 2 experts per lane (8 tokens x 32 experts per
-    // block); few tokens: one (token, expert) pair per lane group so that
-    // enough wavefronts stream the router weights
+    // many tokens: 2 tokens x 4 experts per lane (8 tokens x 32 experts per
+    // block; each converted activation feeds 4 fma_mix); few tokens: one
+    // (token, expert) pair per lane group so that enough wavefronts stream the
+    // router weights
     if (T > 64) {
-        if (bf16) route_launch<true, 4, 2, 2>(x, T, H, Wr, bias, E, logits, s);
-        else route_launch<false, 4, 2, 2>(x, T, H, Wr, bias, E, logits, s);
+        if (bf16) route_launch<true, 2, 4, 4>(x, T, H, Wr, bias, E, logits, s);
+        else route_launch<false, 2, 4, 4>(x, T, H, Wr, bias, E, logits, s);
     } else {
         if (bf16) route_launch<true, 1, 1, 8>(x, T, H, Wr, bias, E, logits, s);
         else route_launch<false, 1, 1, 8>(x, T, H, Wr, bias, E, logits, s);
