@@ -15,8 +15,9 @@
 
 namespace moe {
 
-constexpr int kGemvU = 8;      // tile rows per prefetch group
+constexpr int kGemvU = 4;      // tile rows per prefetch group
 constexpr int kGemvPass = 2;   // routed rows per pass over the codes
+constexpr int kGemvCols = 32;  // output columns (two 16-column tiles) per block
 
 // 1532 * (row sum), the re-centring of the biased decoded values.
 constexpr float kBias2 = 1532.0f;
@@ -34,29 +35,51 @@ MOE_DEV float block_sum256(float v, float *part)
     return ((part[0] + part[1]) + part[2]) + part[3];
 }
 
-// Each lane decodes a fragment of tile rows and accumulates x * (2v + 1532)
-// into acc[r] with one v_fma_mix_f32 per weight and row (fp16 operands, exact
-// products, fp32 accumulation).  Code words are prefetched kGemvU tile rows
-// ahead.  XS(r, kk) returns the 8 activation values of row r at input rows
-// kk + 8h .. kk + 8h + 7 for the lane.
-template <int K, int CB, int NR, class XS>
-MOE_DEV void gemv_stream(const uint32_t *cb, int64_t rstride, int ntk, int d0, int d1, int q,
-                         uint32_t m_lo, uint32_t m_hi, int nr, XS xs, float acc[NR])
+// The fragment's eight decoded values as fp16 pairs of 2v + 1532 (exact:
+// integers in [1020, 2044]).  mcg: the low half from v_sad_u8 on base
+// 0x64006400, the high half from v_sad_hi_u8; E4M3: 128 * c8 + 1532.
+template <int K, int CB>
+MOE_DEV void frag_biased_pairs(uint32_t D0, uint32_t D1, int q, uint32_t m_lo, uint32_t m_hi, f16x2 wp[4])
+{
+    uint32_t st[8];
+    frag_states<K>(D0, D1, q, st);
+#pragma unroll
+    for (int t = 0; t < 8; t += 2) {
+        if (CB == CB_MCG) {
+            const uint32_t ra = field_sum2(mcg_hash(st[t], m_lo, m_hi), 0x64006400u);
+            const uint32_t rb = __builtin_amdgcn_sad_hi_u8(mcg_hash(st[t + 1], m_lo, m_hi) & 0xFEFEFEFEu, 0u, ra);
+            wp[t / 2] = __builtin_bit_cast(f16x2, rb);
+        } else {
+            const float a = e4m3_value2(value2_f32(st[t], m_lo, m_hi)) + kBias2;
+            const float b = e4m3_value2(value2_f32(st[t + 1], m_lo, m_hi)) + kBias2;
+            wp[t / 2] = (f16x2){(f16)a, (f16)b};
+        }
+    }
+}
+
+// Stream tile rows [tk0, tk1) of the lane's fragment (two code dwords per
+// tile row, prefetched kGemvU rows ahead) and accumulate x . (2v + 1532) for
+// NR routed rows.  DOT(r, kk, wp, acc) adds the lane's 8 products of row r
+// at input rows kk + 8h .. kk + 8h + 7.
+template <int K, int CB, int NR, class DOT>
+MOE_DEV void gemv_stream(const uint32_t *cb, int64_t rstride, int tk0, int tk1, int d0, int d1, int q,
+                         uint32_t m_lo, uint32_t m_hi, DOT dot, float acc[NR])
 {
     uint32_t nx[kGemvU][2];
+    const uint32_t *base = cb + (int64_t)tk0 * rstride;
 #pragma unroll
     for (int u = 0; u < kGemvU; ++u) {
-        nx[u][0] = cb[u * rstride + d0];
-        nx[u][1] = cb[u * rstride + d1];
+        nx[u][0] = base[u * rstride + d0];
+        nx[u][1] = base[u * rstride + d1];
     }
-    for (int g = 0; g < ntk; g += kGemvU) {
+    for (int g = tk0; g < tk1; g += kGemvU) {
         uint32_t cu[kGemvU][2];
 #pragma unroll
         for (int u = 0; u < kGemvU; ++u) {
             cu[u][0] = nx[u][0];
             cu[u][1] = nx[u][1];
         }
-        if (g + kGemvU < ntk) {
+        if (g + kGemvU < tk1) {
             const uint32_t *nb = cb + (int64_t)(g + kGemvU) * rstride;
 #pragma unroll
             for (int u = 0; u < kGemvU; ++u) {
@@ -66,44 +89,29 @@ MOE_DEV void gemv_stream(const uint32_t *cb, int64_t rstride, int ntk, int d0, i
         }
 #pragma unroll
         for (int u = 0; u < kGemvU; ++u) {
-            uint32_t st[8];
-            frag_states<K>(cu[u][0], cu[u][1], q, st);
-            f16 wv[8];
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                if (CB == CB_MCG) {
-                    wv[t] = __builtin_bit_cast(f16, (uint16_t)value2_biased_f16bits(st[t], m_lo, m_hi));
-                } else {
-                    wv[t] = (f16)(e4m3_value2(value2_f32(st[t], m_lo, m_hi)) + kBias2);
-                }
-            }
+            f16x2 wp[4];
+            frag_biased_pairs<K, CB>(cu[u][0], cu[u][1], q, m_lo, m_hi, wp);
             const int kk = 16 * (g + u);
 #pragma unroll
-            for (int r = 0; r < NR; ++r) {
-                if (r < nr) {
-                    float xv[8];
-                    xs(r, kk, xv);
-                    float s = acc[r];
-#pragma unroll
-                    for (int t = 0; t < 8; ++t)
-                        s = __builtin_fmaf((float)wv[t], xv[t], s);
-                    acc[r] = s;
-                }
-            }
+            for (int r = 0; r < NR; ++r)
+                acc[r] = dot(r, kk, wp, acc[r]);
         }
     }
 }
 
-// gate/up + SwiGLU.  Block = 4 wavefronts = (gate, up) x 2 tile pairs = 64
-// output columns of one expert; grid.x walks the GEMV expert list.  Rows are
-// processed kGemvPass at a time (x * suh of the pass in LDS, fp16).
+// gate/up + SwiGLU.  Block = 32 output columns (two tiles) of one expert for
+// both projections; wavefront w = 2p + kh streams projection p over input
+// half kh, so a launch has 4 wavefronts per 32 columns.  Rows are processed
+// kGemvPass at a time: x * suh of the pass's rows in LDS (fp16, both
+// projections), one v_dot2_f32_f16 per pair of weights and row.  The partial
+// sums of the two halves meet in LDS and are added in a fixed order.
 template <int K, int CB>
-__global__ __launch_bounds__(256) void gemv_gateup_kernel(GroupArgs a)
+__global__ __launch_bounds__(256, 4) void gemv_gateup_kernel(GroupArgs a)
 {
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ float part[4];
     __shared__ float rsum[2][kGemvPass];
-    __shared__ float gu[2][kGemvPass][64];
+    __shared__ float psum[2][2][kGemvPass][kGemvCols];   // [projection][half][row][column]
     const int li = blockIdx.x;
     if (li >= a.hdr->n_gemv)
         return;
@@ -111,21 +119,20 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(GroupArgs a)
     const int e = a.glist[li];
     const int R = a.counts[e];
     const int p0 = a.offsets[e];
-    const int n0 = blockIdx.y * 64;
+    const int n0 = blockIdx.y * kGemvCols;
     f16 *xs = (f16 *)smem;   // [2][kGemvPass][H]
 
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-    const int pr = w >> 1, tp = w & 1;
+    const int pr = w >> 1, kh = w & 1;
     const int c = l & 15, ts = (l >> 4) & 1, h = l >> 5;
-    const int tn = n0 / 16 + 2 * tp + ts;
+    const int tn = n0 / 16 + ts;
     int d0, d1, q;
     frag_pos<K>(c, h, d0, d1, q);
     const int64_t per_expert = (int64_t)(H / 16) * (I / 16) * Tile<K>::kDwords;
     const uint32_t *cb = (const uint32_t *)a.codes[pr] + e * per_expert + (int64_t)tn * Tile<K>::kDwords;
     const int64_t rstride = (int64_t)(I / 16) * Tile<K>::kDwords;
     const uint32_t m_lo = a.mcg & 0xFFFFu, m_hi = a.mcg >> 16;
-    const int col = 16 * (2 * tp + ts) + c;
-    const float svh = f16_to_f32(a.svh[pr][(int64_t)e * I + n0 + col]) * (1.0f / 128.0f);
+    const int ntk = H / 16, tk0 = kh * (ntk / 2), tk1 = tk0 + ntk / 2;
 
     for (int r0 = 0; r0 < R; r0 += kGemvPass) {
         const int nr = min(kGemvPass, R - r0);
@@ -151,40 +158,53 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(GroupArgs a)
 
         float acc[kGemvPass] = {};
         const f16 *xsp = xs + (size_t)pr * kGemvPass * H + 8 * h;
-        gemv_stream<K, CB, kGemvPass>(cb, rstride, H / 16, d0, d1, q, m_lo, m_hi, nr,
-                                      [&](int r, int kk, float xv[8]) {
-                                          const f16x8 v = *(const f16x8 *)(xsp + (size_t)r * H + kk);
+        auto dot = [&](int r, int kk, const f16x2 wp[4], float s) {
+            const f16x8 v = *(const f16x8 *)(xsp + (size_t)r * H + kk);
 #pragma unroll
-                                          for (int t = 0; t < 8; ++t)
-                                              xv[t] = (float)v[t];
-                                      },
-                                      acc);
-        // the two k-halves of a column sit in lanes l and l ^ 32
+            for (int j = 0; j < 4; ++j)
+                s = __builtin_amdgcn_fdot2(wp[j], (f16x2){v[2 * j], v[2 * j + 1]}, s, false);
+            return s;
+        };
+        // nr is the same for the whole block: branch once, not per fragment
+        if (__builtin_amdgcn_readfirstlane(nr) == 2)
+            gemv_stream<K, CB, 2>(cb, rstride, tk0, tk1, d0, d1, q, m_lo, m_hi, dot, acc);
+        else
+            gemv_stream<K, CB, 1>(cb, rstride, tk0, tk1, d0, d1, q, m_lo, m_hi, dot, acc);
+        // the two k-halves of a tile row sit in lanes l and l ^ 32
 #pragma unroll
         for (int r = 0; r < kGemvPass; ++r) {
             const float tot = acc[r] + __shfl_xor(acc[r], 32, 64);
             if (r < nr && h == 0)
-                gu[pr][r][col] = (tot - kBias2 * rsum[pr][r]) * svh;
+                psum[pr][kh][r][16 * ts + c] = tot;
         }
         __syncthreads();
-        if (threadIdx.x < nr * 64) {
-            const int r = threadIdx.x >> 6, cc = threadIdx.x & 63;
-            const float g = gu[0][r][cc], u = gu[1][r][cc];
-            const float hv = silu_f(g) * u * f16_to_f32(a.suh[2][(int64_t)e * I + n0 + cc]);
-            a.hbuf[(int64_t)(p0 + r0 + r) * I + n0 + cc] = f32_to_bf16_bits(hv);
+        if (threadIdx.x < nr * kGemvCols) {
+            const int r = threadIdx.x / kGemvCols, cc = threadIdx.x % kGemvCols;
+            const int col = n0 + cc;
+            const float g = (psum[0][0][r][cc] + psum[0][1][r][cc] - kBias2 * rsum[0][r]) *
+                            (f16_to_f32(a.svh[0][(int64_t)e * I + col]) * (1.0f / 128.0f));
+            const float u = (psum[1][0][r][cc] + psum[1][1][r][cc] - kBias2 * rsum[1][r]) *
+                            (f16_to_f32(a.svh[1][(int64_t)e * I + col]) * (1.0f / 128.0f));
+            const float hv = silu_f(g) * u * f16_to_f32(a.suh[2][(int64_t)e * I + col]);
+            a.hbuf[(int64_t)(p0 + r0 + r) * I + col] = f32_to_bf16_bits(hv);
         }
         __syncthreads();
     }
 }
 
-// down + routing-weighted scatter.  Block = 4 wavefronts x 2 tiles = 128
-// output columns of one expert.  h * suh_down rows of the pass in LDS, fp32.
+// down + routing weight.  Block = 32 output columns (two tiles) of one
+// expert; the input rows are split into S = 4 (or 2, or 1 for small inter
+// sizes) ranges of a multiple of kGemvU tile rows, wavefront w < S streams
+// range w.  h rows of the pass in LDS
+// (fp32); one v_fma_mix_f32 per weight and row (h has fp32 range, so it stays
+// fp32); quarter sums meet in LDS and are added in a fixed order.
 template <int K, int CB>
-__global__ __launch_bounds__(256) void gemv_down_kernel(GroupArgs a)
+__global__ __launch_bounds__(256, 4) void gemv_down_kernel(GroupArgs a)
 {
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ float part[4];
     __shared__ float rsum[kGemvPass];
+    __shared__ float psum[4][kGemvPass][kGemvCols];   // [quarter][row][column]
     const int li = blockIdx.x;
     if (li >= a.hdr->n_gemv)
         return;
@@ -192,20 +212,22 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(GroupArgs a)
     const int e = a.glist[li];
     const int R = a.counts[e];
     const int p0 = a.offsets[e];
-    const int m0 = blockIdx.y * 128;
+    const int m0 = blockIdx.y * kGemvCols;
     float *hs = (float *)smem;   // [kGemvPass][I]
 
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
     const int c = l & 15, ts = (l >> 4) & 1, h = l >> 5;
-    const int tn = m0 / 16 + 2 * w + ts;
+    const int tn = m0 / 16 + ts;
     int d0, d1, q;
     frag_pos<K>(c, h, d0, d1, q);
     const int64_t per_expert = (int64_t)(I / 16) * (H / 16) * Tile<K>::kDwords;
     const uint32_t *cb = (const uint32_t *)a.codes[2] + e * per_expert + (int64_t)tn * Tile<K>::kDwords;
     const int64_t rstride = (int64_t)(H / 16) * Tile<K>::kDwords;
     const uint32_t m_lo = a.mcg & 0xFFFFu, m_hi = a.mcg >> 16;
-    const int m = m0 + 32 * w + 16 * ts + c;
-    const float svh = f16_to_f32(a.svh[2][(int64_t)e * H + m]) * (1.0f / 128.0f);
+    // I % 128 == 0, so ntk is a multiple of kGemvU and S = 1 always fits
+    const int ntk = I / 16;
+    const int S = (ntk % (4 * kGemvU) == 0) ? 4 : (ntk % (2 * kGemvU) == 0) ? 2 : 1;
+    const int tk0 = w * (ntk / S), tk1 = tk0 + ntk / S;
 
     for (int r0 = 0; r0 < R; r0 += kGemvPass) {
         const int nr = min(kGemvPass, R - r0);
@@ -237,24 +259,43 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(GroupArgs a)
 
         float acc[kGemvPass] = {};
         const float *hsp = hs + 8 * h;
-        gemv_stream<K, CB, kGemvPass>(cb, rstride, I / 16, d0, d1, q, m_lo, m_hi, nr,
-                                      [&](int r, int kk, float xv[8]) {
-                                          const f32x4 v0 = *(const f32x4 *)(hsp + (size_t)r * I + kk);
-                                          const f32x4 v1 = *(const f32x4 *)(hsp + (size_t)r * I + kk + 4);
+        auto dot = [&](int r, int kk, const f16x2 wp[4], float s) {
+            const f32x4 v0 = *(const f32x4 *)(hsp + (size_t)r * I + kk);
+            const f32x4 v1 = *(const f32x4 *)(hsp + (size_t)r * I + kk + 4);
 #pragma unroll
-                                          for (int t = 0; t < 4; ++t) {
-                                              xv[t] = v0[t];
-                                              xv[t + 4] = v1[t];
-                                          }
-                                      },
-                                      acc);
+            for (int j = 0; j < 2; ++j) {
+                s = __builtin_fmaf((float)wp[j][0], v0[2 * j], s);
+                s = __builtin_fmaf((float)wp[j][1], v0[2 * j + 1], s);
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                s = __builtin_fmaf((float)wp[2 + j][0], v1[2 * j], s);
+                s = __builtin_fmaf((float)wp[2 + j][1], v1[2 * j + 1], s);
+            }
+            return s;
+        };
+        if (w < S) {
+            // nr is the same for the whole block: branch once, not per fragment
+            if (__builtin_amdgcn_readfirstlane(nr) == 2)
+                gemv_stream<K, CB, 2>(cb, rstride, tk0, tk1, d0, d1, q, m_lo, m_hi, dot, acc);
+            else
+                gemv_stream<K, CB, 1>(cb, rstride, tk0, tk1, d0, d1, q, m_lo, m_hi, dot, acc);
+        }
 #pragma unroll
         for (int r = 0; r < kGemvPass; ++r) {
             const float tot = acc[r] + __shfl_xor(acc[r], 32, 64);
-            if (r < nr && h == 0) {
-                const int slot = a.sorted[p0 + r0 + r];
-                a.ybuf[(int64_t)slot * H + m] = f32_to_bf16_bits((tot - kBias2 * rsum[r]) * svh * a.w[slot]);
-            }
+            if (r < nr && h == 0)
+                psum[w][r][16 * ts + c] = tot;
+        }
+        __syncthreads();
+        if (threadIdx.x < nr * kGemvCols) {
+            const int r = threadIdx.x / kGemvCols, cc = threadIdx.x % kGemvCols;
+            const int m = m0 + cc;
+            const float tot = ((psum[0][r][cc] + psum[1][r][cc]) + (psum[2][r][cc] + psum[3][r][cc])) -
+                              kBias2 * rsum[r];
+            const int slot = a.sorted[p0 + r0 + r];
+            const float svh = f16_to_f32(a.svh[2][(int64_t)e * H + m]) * (1.0f / 128.0f);
+            a.ybuf[(int64_t)slot * H + m] = f32_to_bf16_bits(tot * svh * a.w[slot]);
         }
         __syncthreads();
     }
@@ -264,7 +305,7 @@ hipError_t launch_gemv_gateup(const GroupArgs &a, int max_list, hipStream_t s)
 {
     if (max_list <= 0)
         return hipSuccess;
-    dim3 grid(max_list, a.I / 64);
+    dim3 grid(max_list, a.I / kGemvCols);
     const size_t lds = sizeof(f16) * 2 * kGemvPass * a.H;
     if (a.K == 2 && a.cb == 0) gemv_gateup_kernel<2, 0><<<grid, 256, lds, s>>>(a);
     else if (a.K == 3 && a.cb == 0) gemv_gateup_kernel<3, 0><<<grid, 256, lds, s>>>(a);
@@ -279,7 +320,7 @@ hipError_t launch_gemv_down(const GroupArgs &a, int max_list, hipStream_t s)
 {
     if (max_list <= 0)
         return hipSuccess;
-    dim3 grid(max_list, a.H / 128);
+    dim3 grid(max_list, a.H / kGemvCols);
     const size_t lds = sizeof(float) * kGemvPass * a.I;
     if (a.K == 2 && a.cb == 0) gemv_down_kernel<2, 0><<<grid, 256, lds, s>>>(a);
     else if (a.K == 3 && a.cb == 0) gemv_down_kernel<3, 0><<<grid, 256, lds, s>>>(a);
@@ -293,7 +334,7 @@ hipError_t launch_gemv_down(const GroupArgs &a, int max_list, hipStream_t s)
 // ------------------------------------------------------------ shared expert GEMV
 // Dense fp16 weights in nn.Linear layout [out][in]; one wavefront streams
 // whole weight rows in 16-byte chunks and reduces across lanes at the end.
-constexpr int kShRows = 4;   // weight rows (gate+up pairs, or down rows) per wavefront
+constexpr int kShRows = 1;   // weight rows (gate+up pairs, or down rows) per wavefront
 
 __global__ __launch_bounds__(256) void shared_gemv_gateup_kernel(const uint16_t *__restrict__ x16,
                                                                  int T, int H, int I,
