@@ -34,7 +34,9 @@ constexpr int kBK = 32;        // input channels per pipeline stage
 constexpr int kKT = kBK / 16;  // MFMA k-steps per stage
 constexpr int kRing = 4;       // LDS stages in flight (prefetch distance kRing - 1)
 constexpr int kStageHalves = kBM * kBK;   // one A stage: 256 rows x 32 halves = 16 KiB
-constexpr int kSlotHalves = kStageHalves + 4 * 128;
+constexpr int kWaves = 8;                 // wavefronts per block (two per SIMD)
+constexpr int kThreads = 64 * kWaves;
+constexpr int kSlotHalves = kStageHalves + kWaves * 128;   // + one 256-byte suh area per wave
 
 #define LDS_AS __attribute__((address_space(3)))
 
@@ -48,11 +50,11 @@ struct ModeTraits {
     // Each wavefront owns one 32-column MFMA block of one projection: for
     // gate/up, waves 0,1 hold gate and waves 2,3 up of the same 64 columns;
     // for down, 32 output columns.  A block is 4 wavefronts.
-    static constexpr int kBlockN = kGateUp ? 64 : 128;
+    static constexpr int kBlockN = kGateUp ? 128 : 256;
     // vector-memory instructions every wavefront issues per stage: A rows
     // (4 LDS-direct loads, plus one for suh in the trellis gate/up mode) and
     // B (trellis: 2 code dwords per k-step; dense: 16 bytes per k-step)
-    static constexpr int kNA = 4 + (MODE == GATEUP_TRELLIS ? 1 : 0);
+    static constexpr int kNA = 2 + (MODE == GATEUP_TRELLIS ? 1 : 0);
     static constexpr int kNB = kTrellis ? 2 * kKT : kKT;   // per column group
 };
 
@@ -119,7 +121,7 @@ struct GemmTile {
     // 16 bytes of row 64w + 16j + L/4 (rows past the tile's last row repeat
     // it; their results are never stored)
     __amdgpu_buffer_rsrc_t arsrc, anull;
-    uint32_t aoff[4];
+    uint32_t aoff[2];
     uint32_t aread[kKT];       // LDS byte offset of the lane's A fragment per k-step
     // suh (gate/up trellis): every wave fetches the 32 values of stage s of
     // its own projection with lanes 0..15 (4 bytes each) into its own
@@ -153,9 +155,9 @@ struct GemmTile {
     {
         const __amdgpu_buffer_rsrc_t rs = s < nst ? arsrc : anull;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rs, (LDS_AS void *)(ring + (64 * w + 16 * j) * kBK), 16, aoff[j], s * kBK * 2, 0, 0);
+                rs, (LDS_AS void *)(ring + (32 * w + 16 * j) * kBK), 16, aoff[j], s * kBK * 2, 0, 0);
         if constexpr (MODE == GATEUP_TRELLIS) {
             const __amdgpu_buffer_rsrc_t ss = s < nst ? srsrc : anull;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -239,7 +241,7 @@ struct GemmTile {
         if constexpr (MODE == GATEUP_TRELLIS) {
 #pragma unroll
             for (int kt = 0; kt < kKT; ++kt)
-                su[kt] = *(const LDS_AS f16x8 *)(rg + kStageHalves + 128 * w + 16 * kt + 8 * h);
+                su[kt] = *(const LDS_AS f16x8 *)(rg + kStageHalves + 128 * (4 * pr + 2 * kt + h));
         }
         u32x4 af[kKT][NMB];
 #pragma unroll
@@ -310,7 +312,7 @@ MOE_DEV void tile_body(GemmTile<MODE, K, CB> &g, const GemmArgs &args, int n0,
     // gate/up -> waves 0,1 gate and waves 2,3 up of the block's 64 CM
     // intermediate columns; down -> 32 CM of the block's 128 CM output columns
     const int Nout = TR::kGateUp ? g.I : g.H;
-    g.col = (TR::kGateUp ? n0 + 32 * CM * (g.w & 1) : n0 + 32 * CM * g.w) + 16 * g.ts + g.c;
+    g.col = (TR::kGateUp ? n0 + 32 * CM * (g.w & 3) : n0 + 32 * CM * g.w) + 16 * g.ts + g.c;
     if constexpr (TR::kTrellis) {
         int d0, d1, q;
         frag_pos<K>(g.c, g.h, d0, d1, q);
@@ -325,8 +327,10 @@ MOE_DEV void tile_body(GemmTile<MODE, K, CB> &g, const GemmArgs &args, int n0,
         g.srsrc = g.bnull;
         g.soff = 0;
         if constexpr (MODE == GATEUP_TRELLIS) {
-            g.srsrc = buf_rsrc(a.suh[g.pr] + (int64_t)g.e * g.H, (uint32_t)(g.H * 2));
-            g.soff = g.l < 16 ? 4u * g.l : 0x7FFFFFF0u;
+            // piece w & 3 (k = 8 (w & 3) .. + 7 of the stage) of projection w >> 2
+            g.srsrc = buf_rsrc(a.suh[g.pr] + (int64_t)g.e * g.H + 8 * (g.w & 3),
+                               (uint32_t)(g.H * 2 - 16 * (g.w & 3)));
+            g.soff = g.l < 4 ? 4u * g.l : 0x7FFFFFF0u;
         }
     } else {
         const uint16_t *W = TR::kGateUp ? args.dB[g.pr] : args.dB[0];
@@ -356,46 +360,42 @@ MOE_DEV void tile_body(GemmTile<MODE, K, CB> &g, const GemmArgs &args, int n0,
     const int64_t t0 = g.t0;
     const int mblocks = (rows + 31) >> 5;
     if constexpr (TR::kGateUp) {
-        // up wavefronts hand their scaled results to the gate wavefronts with
-        // the same columns through LDS: block b of column half cb goes to
-        // ring (2 cb + b / 4), 4 KiB per block
-        const int cb = g.w & 1;
-        float *ex_lo = cb ? (float *)ring2 : (float *)ring0;
-        float *ex_hi = cb ? (float *)ring3 : (float *)ring1;
-        if (g.pr == 1) {
+        // up wavefront w + 4 hands its scaled results to gate wavefront w (the
+        // same columns) through LDS, in rounds of four accumulator blocks:
+        // block b of column group cg = w & 3 goes to ring cg at 4 KiB per block
+        const int cg = g.w & 3;
+        float *ex = cg == 0 ? (float *)ring0 : cg == 1 ? (float *)ring1 : cg == 2 ? (float *)ring2 : (float *)ring3;
 #pragma unroll
-            for (int cm = 0; cm < CM; ++cm) {
-                const int col = g.col + 32 * cm;
-                const float su = MODE == GATEUP_TRELLIS ? f16_to_f32(a.svh[1][(int64_t)e * I + col]) * (1.0f / 128.0f) : 1.0f;
+        for (int round = 0; round < (NB + 3) / 4; ++round) {
+            if (g.pr == 1) {
 #pragma unroll
-                for (int i = 0; i < NMB; ++i) {
-                    const int b = cm * NMB + i;
+                for (int b = 4 * round; b < 4 * round + 4 && b < NB; ++b) {
+                    const int cm = b / NMB, i = b % NMB;
+                    const int col = g.col + 32 * cm;
+                    const float su = MODE == GATEUP_TRELLIS ? f16_to_f32(a.svh[1][(int64_t)e * I + col]) * (1.0f / 128.0f) : 1.0f;
                     if (i < mblocks)
 #pragma unroll
                         for (int r = 0; r < 16; ++r)
-                            (b < 4 ? ex_lo : ex_hi)[((b & 3) * 16 + r) * 64 + g.l] = acc[b][r] * su;
+                            ex[((b & 3) * 16 + r) * 64 + g.l] = acc[b][r] * su;
                 }
             }
-        }
-        __syncthreads();
-        if (g.pr == 0) {
+            __syncthreads();
+            if (g.pr == 0) {
 #pragma unroll
-            for (int cm = 0; cm < CM; ++cm) {
-                const int col = g.col + 32 * cm;
-                float sg = 1.0f, sd = 1.0f;
-                if constexpr (MODE == GATEUP_TRELLIS) {
-                    sg = f16_to_f32(a.svh[0][(int64_t)e * I + col]) * (1.0f / 128.0f);
-                    sd = f16_to_f32(a.suh[2][(int64_t)e * I + col]);
-                }
-#pragma unroll
-                for (int i = 0; i < NMB; ++i) {
-                    const int b = cm * NMB + i;
+                for (int b = 4 * round; b < 4 * round + 4 && b < NB; ++b) {
+                    const int cm = b / NMB, i = b % NMB;
+                    const int col = g.col + 32 * cm;
+                    float sg = 1.0f, sd = 1.0f;
+                    if constexpr (MODE == GATEUP_TRELLIS) {
+                        sg = f16_to_f32(a.svh[0][(int64_t)e * I + col]) * (1.0f / 128.0f);
+                        sd = f16_to_f32(a.suh[2][(int64_t)e * I + col]);
+                    }
                     if (i < mblocks) {
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
                             const int row = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
                             if (row < rows) {
-                                const float u = (b < 4 ? ex_lo : ex_hi)[((b & 3) * 16 + r) * 64 + g.l];
+                                const float u = ex[((b & 3) * 16 + r) * 64 + g.l];
                                 const float hv = silu_f(acc[b][r] * sg) * u * sd;
                                 if constexpr (MODE == GATEUP_TRELLIS)
                                     a.hbuf[(int64_t)(p0 + row) * I + col] = f32_to_bf16_bits(hv);
@@ -406,6 +406,7 @@ MOE_DEV void tile_body(GemmTile<MODE, K, CB> &g, const GemmArgs &args, int n0,
                     }
                 }
             }
+            __syncthreads();
         }
     } else {
 #pragma unroll
@@ -436,7 +437,7 @@ MOE_DEV void tile_body(GemmTile<MODE, K, CB> &g, const GemmArgs &args, int n0,
 }
 
 template <int MODE, int K, int CB>
-__global__ __launch_bounds__(256, 2) void group_gemm_kernel(GemmArgs args)
+__global__ __launch_bounds__(kThreads, 1) void group_gemm_kernel(GemmArgs args)
 {
     using TR = ModeTraits<MODE>;
     const GroupArgs &a = args.g;
@@ -480,9 +481,9 @@ __global__ __launch_bounds__(256, 2) void group_gemm_kernel(GemmArgs args)
     // share has no work: the whole block leaves before any barrier)
     int cm = 1;
     if (TR::kTrellis && mblocks <= 2)
-        cm = (args.nslices % 4 == 0) ? 4 : 2;
+        cm = (args.nslices % 4 == 0) ? 4 : (args.nslices % 2 == 0) ? 2 : 1;
     else if (TR::kTrellis && mblocks <= 4)
-        cm = 2;
+        cm = (args.nslices % 2 == 0) ? 2 : 1;
     if (slice >= args.nslices / cm)
         return;
     const int n0 = slice * TR::kBlockN * cm;
@@ -504,8 +505,8 @@ __global__ __launch_bounds__(256, 2) void group_gemm_kernel(GemmArgs args)
         g.arsrc = buf_rsrc(abase, abytes);
         g.anull = buf_rsrc(abase, 0);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = 64 * g.w + 16 * j + (g.l >> 2);
+        for (int j = 0; j < 2; ++j) {
+            const int r = 32 * g.w + 16 * j + (g.l >> 2);
             const int rc = min(r, g.rows - 1);
             int64_t row;
             if constexpr (MODE == GATEUP_TRELLIS)
@@ -524,7 +525,7 @@ __global__ __launch_bounds__(256, 2) void group_gemm_kernel(GemmArgs args)
     }
     g.c = g.l & 15;
     g.ts = (g.l >> 4) & 1;
-    g.pr = TR::kGateUp ? g.w >> 1 : 2;
+    g.pr = TR::kGateUp ? g.w >> 2 : 2;
     g.m_lo = a.mcg & 0xFFFFu;
     g.m_hi = a.mcg >> 16;
     g.q = 0;
@@ -532,10 +533,15 @@ __global__ __launch_bounds__(256, 2) void group_gemm_kernel(GemmArgs args)
     if (mblocks <= 2) {
         if (cm == 4)
             tile_body<MODE, K, CB, 2, Groups<MODE, 2>::kMax>(g, args, n0, ring0, ring1, ring2, ring3);
-        else
+        else if (cm == 2)
             tile_body<MODE, K, CB, 2, (Groups<MODE, 2>::kMax > 2 ? 2 : Groups<MODE, 2>::kMax)>(g, args, n0, ring0, ring1, ring2, ring3);
+        else
+            tile_body<MODE, K, CB, 2, 1>(g, args, n0, ring0, ring1, ring2, ring3);
     } else if (mblocks <= 4) {
-        tile_body<MODE, K, CB, 4, Groups<MODE, 4>::kMax>(g, args, n0, ring0, ring1, ring2, ring3);
+        if (cm == 2)
+            tile_body<MODE, K, CB, 4, Groups<MODE, 4>::kMax>(g, args, n0, ring0, ring1, ring2, ring3);
+        else
+            tile_body<MODE, K, CB, 4, 1>(g, args, n0, ring0, ring1, ring2, ring3);
     } else if (mblocks <= 6) {
         tile_body<MODE, K, CB, 6, 1>(g, args, n0, ring0, ring1, ring2, ring3);
     } else {
@@ -549,14 +555,14 @@ static hipError_t launch_mode(const GemmArgs &ga, int tiles, hipStream_t s)
     const GroupArgs &a = ga.g;
     const unsigned grid = (unsigned)(((tiles + 7) / 8) * 8 * ga.nslices);
     if constexpr (ModeTraits<MODE>::kTrellis) {
-        if (a.K == 2 && a.cb == 0) group_gemm_kernel<MODE, 2, 0><<<grid, 256, 0, s>>>(ga);
-        else if (a.K == 3 && a.cb == 0) group_gemm_kernel<MODE, 3, 0><<<grid, 256, 0, s>>>(ga);
-        else if (a.K == 4 && a.cb == 0) group_gemm_kernel<MODE, 4, 0><<<grid, 256, 0, s>>>(ga);
-        else if (a.K == 2) group_gemm_kernel<MODE, 2, 1><<<grid, 256, 0, s>>>(ga);
-        else if (a.K == 3) group_gemm_kernel<MODE, 3, 1><<<grid, 256, 0, s>>>(ga);
-        else group_gemm_kernel<MODE, 4, 1><<<grid, 256, 0, s>>>(ga);
+        if (a.K == 2 && a.cb == 0) group_gemm_kernel<MODE, 2, 0><<<grid, kThreads, 0, s>>>(ga);
+        else if (a.K == 3 && a.cb == 0) group_gemm_kernel<MODE, 3, 0><<<grid, kThreads, 0, s>>>(ga);
+        else if (a.K == 4 && a.cb == 0) group_gemm_kernel<MODE, 4, 0><<<grid, kThreads, 0, s>>>(ga);
+        else if (a.K == 2) group_gemm_kernel<MODE, 2, 1><<<grid, kThreads, 0, s>>>(ga);
+        else if (a.K == 3) group_gemm_kernel<MODE, 3, 1><<<grid, kThreads, 0, s>>>(ga);
+        else group_gemm_kernel<MODE, 4, 1><<<grid, kThreads, 0, s>>>(ga);
     } else {
-        group_gemm_kernel<MODE, 2, 0><<<grid, 256, 0, s>>>(ga);
+        group_gemm_kernel<MODE, 2, 0><<<grid, kThreads, 0, s>>>(ga);
     }
     return hipGetLastError();
 }
