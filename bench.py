@@ -99,7 +99,7 @@ class Hip:
         self.l.hipEventDestroy(e)
 
 
-def setup(cfg, copies=1, shared=True):
+def setup(cfg, copies=1, shared=True, extra_flags=0):
     import trellis_quantized_moe_exl3_amd as M
     import workloads as W
     inp = W.gen_layer(cfg)
@@ -110,6 +110,7 @@ def setup(cfg, copies=1, shared=True):
     bias = _dev(inp.router_bias) if inp.router_bias is not None else None
     sh = [_dev(s) for s in inp.shared] if (shared and inp.shared is not None) else None
     flags = (M.HAS_SHARED if sh is not None else 0) | (M.HAS_ROUTER_BIAS if bias is not None else 0)
+    flags |= extra_flags
     desc = M.make_desc(cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k, cfg.K, cfg.codebook,
                        cfg.mcg, cfg.act_dtype, flags, 0)
     weights = [M.make_weights(c, suh, svh, rw, bias, sh) for c in codes]
@@ -178,6 +179,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=50)
     ap.add_argument("--cpu-tokens", type=int, default=80)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the 16384-token E4M3 workload")
     ap.add_argument("--profile-layer", default=None, help="run this workload's layer --reps times and exit")
     ap.add_argument("--reps", type=int, default=2)
     ap.add_argument("--copy-calibration", type=int, default=0, help="copy this many MiB 4 times and exit")
@@ -247,6 +249,22 @@ def main():
     del dkeep, dweights
     torch.cuda.empty_cache()
 
+    # ---- 16384-token prefill with the E4M3 codebook: fp16 and fp8 MFMA
+    fp8 = None
+    if not args.no_fp8:
+        fcfg = W.BY_NAME["fp8"]
+        fp8 = {"workload": "prefill-16384: T=16384, K=4, E4M3-rounded mcg codebook, bf16 activations"}
+        for name, fl in (("fp16_mfma", 0), ("fp8_mfma", M.FP8_MFMA)):
+            finp, fdesc, fweights, fkeep = setup(fcfg, extra_flags=fl)
+            fx = _dev(finp.x)
+            fms, fper, _, _, _ = time_layer(fdesc, fweights, fx, min(args.steps, 10), 2, hip)
+            fstep = {n: float(fper[:, i].mean()) for i, n in enumerate(M.STEPS)}
+            fp8[name] = {"ms_per_step": fms, "tokens_per_s": fcfg.tokens / (fms * 1e-3), "step_ms": fstep}
+            print(f"[bench] fp8 workload {name} {fms:.3f} ms/step; steps "
+                  f"{json.dumps({k: round(v, 4) for k, v in fstep.items()})}", file=sys.stderr, flush=True)
+            del fkeep, fweights, fx
+            torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, args.cpu_tokens)
@@ -277,6 +295,7 @@ def main():
                    "routed_kernels_us": routed_ms * 1000, "code_GBps": code_gbps,
                    "code_hbm_frac": code_gbps / PEAK_HBM_GBPS,
                    "step_us": {k: v * 1000 for k, v in dstep.items()}},
+        "e4m3_prefill": fp8,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec))

@@ -84,7 +84,7 @@ extern "C" {
 #define MOE_EXL3_HAS_ROUTER_BIAS (1u << 1)  /* add router_bias to the logits */
 #define MOE_EXL3_FORCE_GEMV (1u << 2)       /* every routed expert on the decode-fused GEMV path */
 #define MOE_EXL3_FORCE_MFMA (1u << 3)       /* every routed expert on the MFMA path */
-#define MOE_EXL3_FP8_MFMA (1u << 4)         /* routed MFMA GEMMs in fp8 (needs CB_MCG_E4M3) */
+#define MOE_EXL3_FP8_MFMA (1u << 4)         /* routed MFMA GEMMs in fp8 (needs CB_MCG_E4M3 and hidden, inter % 256 == 0) */
 
 /*
  * Layer description.  Shape rules: hidden is a multiple of 256, inter a

@@ -1,5 +1,7 @@
 """Layer parity of the HIP path (moe_exl3_layer through the C ABI) with the
-fp64 oracle, max |out - ref| / max |ref| <= 2e-2.
+fp64 oracle, max |out - ref| / max |ref| <= 2e-2 (fp16/bf16 arithmetic) or
+<= 6e-2 with the routed GEMMs in fp8 (the activations are then rounded to
+E4M3 with a per-row scale, which the oracle does not do).
 
 With the synthetic side vectors (~1/64 on both sides) the routed experts add
 about 1e-5 of what the shared expert adds, so a whole-output comparison would
@@ -18,6 +20,7 @@ from gpu_util import DevLayer, dev, rel_err
 pytestmark = pytest.mark.gpu
 
 TOL = 2e-2
+TOL_FP8 = 6e-2
 
 
 def _routed_only(inp):
@@ -81,7 +84,7 @@ def test_decode_step():
     assert err_r <= TOL and err <= TOL
 
 
-def _sampled(name, sample, flags=0):
+def _sampled(name, sample, flags=0, tol=TOL):
     cfg = W.BY_NAME[name]
     inp = W.gen_layer(cfg)
     routed = _routed_only(inp)
@@ -91,8 +94,8 @@ def _sampled(name, sample, flags=0):
     out = DevLayer(inp, flags=flags).run()
     _, _, ref = oracle.layer(inp, sample)
     err = rel_err(out[sample], ref)
-    print(f"{name} sampled routed err={err_r:.3e} full err={err:.3e}")
-    assert err_r <= TOL and err <= TOL
+    print(f"{name} flags={flags} sampled routed err={err_r:.3e} full err={err:.3e}")
+    assert err_r <= tol and err <= tol
     assert np.isfinite(out).all() and np.isfinite(out_r).all()
 
 
@@ -107,6 +110,41 @@ def test_mixed_width_sampled(name):
 
 def test_e4m3_codebook_sampled():
     _sampled("fp8", [0, 8191, 16383])
+
+
+def test_e4m3_fp8_mfma_sampled():
+    _sampled("fp8", [0, 1, 8191, 16383], flags=M.FP8_MFMA, tol=TOL_FP8)
+
+
+def _tiny_e4m3(T):
+    # the fp8 GEMMs need hidden and inter in whole 256-channel rounds
+    return W.BY_NAME["tiny"].replace(tokens=T, inter=256, codebook=W.CB_MCG_E4M3)
+
+
+@pytest.mark.parametrize("T", [1, 37, 300])
+def test_tiny_fp8_mfma(T):
+    inp = W.gen_layer(_tiny_e4m3(T))
+    for part in (_routed_only(inp), inp):
+        out = DevLayer(part, flags=M.FORCE_MFMA | M.FP8_MFMA).run()
+        _, _, ref = oracle.layer(part)
+        err = rel_err(out, ref)
+        print(f"tiny fp8 T={T} shared={part.shared is not None} err={err:.3e}")
+        assert err <= TOL_FP8 and np.isfinite(out).all()
+
+
+def test_tiny_fp8_one_expert_takes_every_token():
+    # 600 slots on expert 3: the fp8 GEMMs run three row tiles, the last one
+    # ragged (88 rows), for the same expert
+    cfg = _tiny_e4m3(600).replace(router_bias=True)
+    inp = W.gen_layer(cfg)
+    inp.router_bias = np.zeros(cfg.n_experts, dtype=np.float32)
+    inp.router_bias[3] = 100.0
+    routed = _routed_only(inp)
+    out = DevLayer(routed, flags=M.FP8_MFMA).run()
+    _, _, ref = oracle.layer(routed)
+    err = rel_err(out, ref)
+    print(f"tiny fp8 one expert err={err:.3e}")
+    assert err <= TOL_FP8
 
 
 def test_shared_expert_ragged_row_tile():

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmoe_exl3.so")
-SOURCES = ["route.hip", "decode.hip", "gemv.hip", "mfma.hip", "moe_exl3.cpp"]
+SOURCES = ["route.hip", "decode.hip", "gemv.hip", "mfma.hip", "mfma8.hip", "moe_exl3.cpp"]
 ARCH = "gfx950"
 
 

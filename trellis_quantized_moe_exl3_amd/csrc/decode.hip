@@ -25,9 +25,20 @@ __global__ __launch_bounds__(256) void decode_kernel(const uint32_t *__restrict_
     frag_pos<K>(c, h, d0, d1, q);
     const uint32_t *tile = codes + ti * Tile<K>::kDwords;
     const uint32_t D0 = tile[d0], D1 = tile[d1];
+    const int col = 16 * tn + c;
+    if (DT == DT_FP8) {
+        // the same fragment decoder as the fp8 MFMA path (either codebook:
+        // the bytes are the E4M3 rounding of c)
+        const u32x2 b8 = frag_decode_fp8<K>(D0, D1, q, m_lo, m_hi);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int64_t o = (int64_t)(16 * tk + 8 * h + t) * n_out + col;
+            ((uint8_t *)dst)[o] = (uint8_t)(b8[t >> 2] >> (8 * (t & 3)));
+        }
+        return;
+    }
     float v2[8];
     frag_decode_f32<K, CB>(D0, D1, q, m_lo, m_hi, v2);
-    const int col = 16 * tn + c;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
         const int64_t o = (int64_t)(16 * tk + 8 * h + t) * n_out + col;
@@ -38,8 +49,6 @@ __global__ __launch_bounds__(256) void decode_kernel(const uint32_t *__restrict_
             ((uint16_t *)dst)[o] = f32_to_f16_bits(cval);
         else if (DT == DT_BF16)
             ((uint16_t *)dst)[o] = f32_to_bf16_bits(cval);
-        else
-            ((uint8_t *)dst)[o] = (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(cval, 0.0f, 0, false) & 0xFF);
     }
 }
 

@@ -38,7 +38,7 @@ struct Plan {
     int nblk;        // segment-table blocks
     int max_tiles;   // upper bound on MFMA work tiles
     size_t hdr, logits, idx, w, counts, offsets, bhist, sorted, pos, glist, tiles, x16, hbuf,
-        ybuf, sh, sy, total;
+        ybuf, sh, sy, a8g, a8u, h8, sg8, su8, sh8, total;
 };
 
 hipError_t launch_route_logits(const uint16_t *x, bool bf16, int64_t T, int H, const uint16_t *Wr,
@@ -66,6 +66,10 @@ struct GroupArgs {
     const uint16_t *x16;     // fp16 activations [T][H]
     uint16_t *hbuf;          // bf16 [T*k][I], sorted order, h * suh_down
     uint16_t *ybuf;          // bf16 [T*k][H], slot order, w * y
+    // fp8 MFMA path (E4M3 codebook): per routed row in sorted order
+    uint8_t *a8g, *a8u;      // E4M3 [T*k][H]: x * suh_gate / sg8, x * suh_up / su8
+    uint8_t *h8;             // E4M3 [T*k][I]: h / sh8
+    float *sg8, *su8, *sh8;  // row scales (least power of two >= row amax / 448)
 };
 
 hipError_t launch_convert_x(const uint16_t *x, bool bf16, int64_t n, uint16_t *x16, hipStream_t s);
@@ -73,6 +77,10 @@ hipError_t launch_gemv_gateup(const GroupArgs &a, int max_list, hipStream_t s);
 hipError_t launch_gemv_down(const GroupArgs &a, int max_list, hipStream_t s);
 hipError_t launch_mfma_gateup(const GroupArgs &a, int max_tiles, hipStream_t s);
 hipError_t launch_mfma_down(const GroupArgs &a, int max_tiles, hipStream_t s);
+hipError_t launch_quant_gateup(const GroupArgs &a, int64_t n, hipStream_t s);
+hipError_t launch_quant_h(const GroupArgs &a, int64_t n, hipStream_t s);
+hipError_t launch_mfma8_gateup(const GroupArgs &a, int max_tiles, hipStream_t s);
+hipError_t launch_mfma8_down(const GroupArgs &a, int max_tiles, hipStream_t s);
 
 hipError_t launch_shared_gateup(const uint16_t *x16, int64_t T, int H, int I, const uint16_t *wg,
                                 const uint16_t *wu, uint16_t *sh, hipStream_t s);

@@ -49,7 +49,10 @@ int check_desc(const moe_exl3_desc *d)
         return MOE_EXL3_ERR_UNSUPPORTED;
     if (d->gemv_max_rows < 0)
         return MOE_EXL3_ERR_INVALID_ARG;
-    if (d->flags & MOE_EXL3_FP8_MFMA)
+    // fp8 MFMA: only the E4M3 codebook (its values are exact in E4M3), and
+    // whole 4-stage pipeline rounds of 64 input channels
+    if ((d->flags & MOE_EXL3_FP8_MFMA) &&
+        (d->codebook != MOE_EXL3_CB_MCG_E4M3 || d->hidden % 256 || d->inter % 256))
         return MOE_EXL3_ERR_UNSUPPORTED;
     if ((d->flags & MOE_EXL3_FORCE_GEMV) && (d->flags & MOE_EXL3_FORCE_MFMA))
         return MOE_EXL3_ERR_INVALID_ARG;
@@ -123,6 +126,13 @@ Plan make_plan(const moe_exl3_desc &d, int64_t T)
     const bool sh = d.flags & MOE_EXL3_HAS_SHARED;
     p.sh = take(sh ? sizeof(uint16_t) * (size_t)T * d.inter : 0);
     p.sy = take(sh ? sizeof(float) * (size_t)T * d.hidden : 0);
+    const bool f8 = d.flags & MOE_EXL3_FP8_MFMA;
+    p.a8g = take(f8 ? (size_t)n * d.hidden : 0);
+    p.a8u = take(f8 ? (size_t)n * d.hidden : 0);
+    p.h8 = take(f8 ? (size_t)n * d.inter : 0);
+    p.sg8 = take(f8 ? sizeof(float) * (size_t)n : 0);
+    p.su8 = take(f8 ? sizeof(float) * (size_t)n : 0);
+    p.sh8 = take(f8 ? sizeof(float) * (size_t)n : 0);
     p.total = o;
     return p;
 }
@@ -314,14 +324,30 @@ static int run_layer(const moe_exl3_desc *desc, const moe_exl3_weights *weights,
     ga.x16 = x16;
     ga.hbuf = at<uint16_t>(ws, p.hbuf);
     ga.ybuf = at<uint16_t>(ws, p.ybuf);
+    const bool f8 = d.flags & MOE_EXL3_FP8_MFMA;
+    if (f8) {
+        ga.a8g = at<uint8_t>(ws, p.a8g);
+        ga.a8u = at<uint8_t>(ws, p.a8u);
+        ga.h8 = at<uint8_t>(ws, p.h8);
+        ga.sg8 = at<float>(ws, p.sg8);
+        ga.su8 = at<float>(ws, p.su8);
+        ga.sh8 = at<float>(ws, p.sh8);
+    }
     const int g = gemv_rows_of(d);
     const int64_t n = T * d.top_k;
     const int max_list = g > 0 ? (int)std::min<int64_t>(d.n_experts, n) : 0;
 
+    // fp8: the activation rows are quantized at the end of the convert step,
+    // the h rows at the start of the GEMV down step
+    if (f8 && launch_quant_gateup(ga, n, s) != hipSuccess)
+        return MOE_EXL3_ERR_HIP;
     if (!mk.mark(MOE_EXL3_STEP_GEMV_GATEUP) || launch_gemv_gateup(ga, max_list, s) != hipSuccess ||
-        !mk.mark(MOE_EXL3_STEP_MFMA_GATEUP) || launch_mfma_gateup(ga, p.max_tiles, s) != hipSuccess ||
-        !mk.mark(MOE_EXL3_STEP_GEMV_DOWN) || launch_gemv_down(ga, max_list, s) != hipSuccess ||
-        !mk.mark(MOE_EXL3_STEP_MFMA_DOWN) || launch_mfma_down(ga, p.max_tiles, s) != hipSuccess ||
+        !mk.mark(MOE_EXL3_STEP_MFMA_GATEUP) ||
+        (f8 ? launch_mfma8_gateup(ga, p.max_tiles, s) : launch_mfma_gateup(ga, p.max_tiles, s)) != hipSuccess ||
+        !mk.mark(MOE_EXL3_STEP_GEMV_DOWN) || (f8 && launch_quant_h(ga, n, s) != hipSuccess) ||
+        launch_gemv_down(ga, max_list, s) != hipSuccess ||
+        !mk.mark(MOE_EXL3_STEP_MFMA_DOWN) ||
+        (f8 ? launch_mfma8_down(ga, p.max_tiles, s) : launch_mfma_down(ga, p.max_tiles, s)) != hipSuccess ||
         !mk.mark(MOE_EXL3_STEP_SHARED))
         return MOE_EXL3_ERR_HIP;
 

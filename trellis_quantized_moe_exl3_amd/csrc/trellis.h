@@ -170,6 +170,27 @@ MOE_DEV bf16x8 frag_decode_bf16(uint32_t D0, uint32_t D1, int q, uint32_t m_lo, 
     return __builtin_bit_cast(bf16x8, pk);
 }
 
+// Fragment -> eight FP8 E4M3 bytes of c = v / 64 (nearest-even, saturating;
+// the E4M3 codebook value itself), state t in byte t % 4 of dword t / 4.
+// v_cvt_scalef32_pk_fp8_f32 divides by its scale: E4M3(2v / 128).
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+template <int K>
+MOE_DEV u32x2 frag_decode_fp8(uint32_t D0, uint32_t D1, int q, uint32_t m_lo, uint32_t m_hi)
+{
+    uint32_t st[8];
+    frag_states<K>(D0, D1, q, st);
+    u32x2 out;
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+        s16x2 w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32((s16x2){0, 0}, value2_f32(st[4 * d], m_lo, m_hi),
+                                                            value2_f32(st[4 * d + 1], m_lo, m_hi), 128.0f, false);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, value2_f32(st[4 * d + 2], m_lo, m_hi),
+                                                      value2_f32(st[4 * d + 3], m_lo, m_hi), 128.0f, true);
+        out[d] = __builtin_bit_cast(uint32_t, w);
+    }
+    return out;
+}
+
 // Fragment -> eight fp32 values of 2v (or 128 * E4M3(v/64)).
 template <int K, int CB>
 MOE_DEV void frag_decode_f32(uint32_t D0, uint32_t D1, int q, uint32_t m_lo, uint32_t m_hi, float out[8])
