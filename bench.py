@@ -39,7 +39,7 @@ PEAK_FP16_TFLOPS = 2500.0      # MI355X dense fp16/bf16 MFMA
 PEAK_HBM_GBPS = 8000.0
 GEMV_ROWS = 2                  # default per-expert row count up to which the GEMV path runs
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic_mfma_gateup_prefill.md")
-KERNEL_SOURCES = ["mfma.hip", "trellis.h", "common.h", "internal.h"]
+KERNEL_SOURCES = ["mfma.hip", "gemm.h", "trellis.h", "common.h", "internal.h"]
 
 
 def kernel_source_hash() -> str:
