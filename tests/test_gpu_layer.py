@@ -147,6 +147,19 @@ def test_tiny_fp8_one_expert_takes_every_token():
     assert err <= TOL_FP8
 
 
+@pytest.mark.parametrize("T", [1, 3, 16])
+def test_shared_expert_gemv_token_counts(T):
+    # up to 16 tokens the shared expert runs on its GEMV kernels, which work
+    # on a power-of-two token count (3 -> 4 with one padding token); the full
+    # output is dominated by the shared expert
+    inp = W.gen_layer(W.BY_NAME["decode"].replace(tokens=T))
+    out = DevLayer(inp).run()
+    _, _, ref = oracle.layer(inp)
+    err = rel_err(out, ref)
+    print(f"shared gemv T={T} err={err:.3e}")
+    assert err <= TOL and np.isfinite(out).all()
+
+
 def test_shared_expert_ragged_row_tile():
     # 300 tokens at the real shapes: the shared expert runs on the MFMA path
     # (more than 16 tokens) with a last row tile of 44 rows, so one of its two

@@ -332,10 +332,34 @@ hipError_t launch_gemv_down(const GroupArgs &a, int max_list, hipStream_t s)
 }
 
 // ------------------------------------------------------------ shared expert GEMV
-// Dense fp16 weights in nn.Linear layout [out][in]; one wavefront streams
-// whole weight rows in 16-byte chunks and reduces across lanes at the end.
-constexpr int kShRows = 1;   // weight rows (gate+up pairs, or down rows) per wavefront
+// Dense fp16 weights in nn.Linear layout [out][in]; one wavefront per weight
+// row (gate/up: the gate and the up row of one channel).  Lane l owns the
+// 16-byte chunks k = 8l + 512c; a pass issues the loads of kShChunks chunks
+// (all of a 4096-wide row) before the first dot product, so every wavefront
+// keeps its whole row in flight.  The code is branch-free so that the
+// activation loads of a token issue together: TT (a power of two >= T)
+// tokens are processed, tokens past T re-read the last one and are not
+// stored, and chunks past the row end read chunk 0 with a zero weight.
+constexpr int kShChunks = 8;
 
+// Sum over the wavefront (all lanes active), the result in every lane.
+MOE_DEV float wave_sum(float v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+MOE_DEV float dot8(const f16x8 &a, const f16x8 &b, float s)
+{
+#pragma unroll
+    for (int j = 0; j < 8; j += 2)
+        s = __builtin_amdgcn_fdot2((f16x2){a[j], a[j + 1]}, (f16x2){b[j], b[j + 1]}, s, false);
+    return s;
+}
+
+template <int TT>
 __global__ __launch_bounds__(256) void shared_gemv_gateup_kernel(const uint16_t *__restrict__ x16,
                                                                  int T, int H, int I,
                                                                  const uint16_t *__restrict__ wg,
@@ -343,119 +367,118 @@ __global__ __launch_bounds__(256) void shared_gemv_gateup_kernel(const uint16_t 
                                                                  uint16_t *__restrict__ sh)
 {
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-    const int n0 = (blockIdx.x * 4 + w) * kShRows;
-    if (n0 >= I)
+    const int n = blockIdx.x * 4 + w;
+    if (n >= I)   // whole wavefronts leave
         return;
-    float acc[2][kShRows][kSharedGemvMaxTokens];
+    float acc[2][TT];
 #pragma unroll
-    for (int p = 0; p < 2; ++p)
+    for (int t = 0; t < TT; ++t)
+        acc[0][t] = acc[1][t] = 0.0f;
+    const uint16_t *gr = wg + (int64_t)n * H, *ur = wu + (int64_t)n * H;
+    for (int kb = 0; kb < H; kb += 512 * kShChunks) {
+        int kc[kShChunks];
+        f16x8 vg[kShChunks], vu[kShChunks];
 #pragma unroll
-        for (int r = 0; r < kShRows; ++r)
-#pragma unroll
-            for (int t = 0; t < kSharedGemvMaxTokens; ++t)
-                acc[p][r][t] = 0.0f;
-    for (int k0 = 8 * l; k0 < H; k0 += 512) {
-        f16x8 wv[2][kShRows];
-#pragma unroll
-        for (int r = 0; r < kShRows; ++r) {
-            wv[0][r] = *(const f16x8 *)(wg + (int64_t)(n0 + r) * H + k0);
-            wv[1][r] = *(const f16x8 *)(wu + (int64_t)(n0 + r) * H + k0);
+        for (int c = 0; c < kShChunks; ++c) {
+            const int k0 = kb + 512 * c + 8 * l;
+            const bool ok = k0 < H;   // H % 256 == 0: whole chunks
+            kc[c] = ok ? k0 : 0;
+            const f16x8 a = *(const f16x8 *)(gr + kc[c]), b = *(const f16x8 *)(ur + kc[c]);
+            vg[c] = ok ? a : (f16x8){};
+            vu[c] = ok ? b : (f16x8){};
         }
 #pragma unroll
-        for (int t = 0; t < kSharedGemvMaxTokens; ++t) {
-            if (t < T) {
-                const f16x8 xv = *(const f16x8 *)(x16 + (int64_t)t * H + k0);
+        for (int t = 0; t < TT; ++t) {
+            const uint16_t *xr = x16 + (int64_t)(t < T ? t : T - 1) * H;
+            f16x8 xv[kShChunks];
 #pragma unroll
-                for (int p = 0; p < 2; ++p)
+            for (int c = 0; c < kShChunks; ++c)
+                xv[c] = *(const f16x8 *)(xr + kc[c]);
+            float g = acc[0][t], u = acc[1][t];
 #pragma unroll
-                    for (int r = 0; r < kShRows; ++r) {
-                        float s = acc[p][r][t];
-#pragma unroll
-                        for (int j = 0; j < 8; j += 2)
-                            s = __builtin_amdgcn_fdot2((f16x2){wv[p][r][j], wv[p][r][j + 1]},
-                                                       (f16x2){xv[j], xv[j + 1]}, s, false);
-                        acc[p][r][t] = s;
-                    }
+            for (int c = 0; c < kShChunks; ++c) {
+                g = dot8(vg[c], xv[c], g);
+                u = dot8(vu[c], xv[c], u);
             }
+            acc[0][t] = g;
+            acc[1][t] = u;
         }
     }
 #pragma unroll
-    for (int t = 0; t < kSharedGemvMaxTokens; ++t) {
-        if (t < T) {
-#pragma unroll
-            for (int r = 0; r < kShRows; ++r) {
-                float g = acc[0][r][t], u = acc[1][r][t];
-#pragma unroll
-                for (int off = 32; off >= 1; off >>= 1) {
-                    g += __shfl_xor(g, off, 64);
-                    u += __shfl_xor(u, off, 64);
-                }
-                if (l == 0)
-                    sh[(int64_t)t * I + n0 + r] = f32_to_f16_bits(silu_f(g) * u);
-            }
-        }
+    for (int t = 0; t < TT; ++t) {
+        const float g = wave_sum(acc[0][t]), u = wave_sum(acc[1][t]);
+        if (l == 0 && t < T)
+            sh[(int64_t)t * I + n] = f32_to_f16_bits(silu_f(g) * u);
     }
 }
 
+template <int TT>
 __global__ __launch_bounds__(256) void shared_gemv_down_kernel(const uint16_t *__restrict__ sh, int T,
                                                                int H, int I,
                                                                const uint16_t *__restrict__ wd,
                                                                float *__restrict__ sy)
 {
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-    const int m0 = (blockIdx.x * 4 + w) * kShRows;
-    if (m0 >= H)
+    const int m = blockIdx.x * 4 + w;
+    if (m >= H)   // whole wavefronts leave
         return;
-    float acc[kShRows][kSharedGemvMaxTokens];
+    float acc[TT];
 #pragma unroll
-    for (int r = 0; r < kShRows; ++r)
+    for (int t = 0; t < TT; ++t)
+        acc[t] = 0.0f;
+    const uint16_t *dr = wd + (int64_t)m * I;
+    for (int kb = 0; kb < I; kb += 512 * kShChunks) {
+        int kc[kShChunks];
+        f16x8 vd[kShChunks];
 #pragma unroll
-        for (int t = 0; t < kSharedGemvMaxTokens; ++t)
-            acc[r][t] = 0.0f;
-    for (int k0 = 8 * l; k0 < I; k0 += 512) {
-        f16x8 wv[kShRows];
+        for (int c = 0; c < kShChunks; ++c) {
+            const int k0 = kb + 512 * c + 8 * l;
+            const bool ok = k0 < I;
+            kc[c] = ok ? k0 : 0;
+            const f16x8 a = *(const f16x8 *)(dr + kc[c]);
+            vd[c] = ok ? a : (f16x8){};
+        }
 #pragma unroll
-        for (int r = 0; r < kShRows; ++r)
-            wv[r] = *(const f16x8 *)(wd + (int64_t)(m0 + r) * I + k0);
+        for (int t = 0; t < TT; ++t) {
+            const uint16_t *hr = sh + (int64_t)(t < T ? t : T - 1) * I;
+            f16x8 hv[kShChunks];
 #pragma unroll
-        for (int t = 0; t < kSharedGemvMaxTokens; ++t) {
-            if (t < T) {
-                const f16x8 hv = *(const f16x8 *)(sh + (int64_t)t * I + k0);
+            for (int c = 0; c < kShChunks; ++c)
+                hv[c] = *(const f16x8 *)(hr + kc[c]);
+            float v = acc[t];
 #pragma unroll
-                for (int r = 0; r < kShRows; ++r) {
-                    float s = acc[r][t];
-#pragma unroll
-                    for (int j = 0; j < 8; j += 2)
-                        s = __builtin_amdgcn_fdot2((f16x2){wv[r][j], wv[r][j + 1]},
-                                                   (f16x2){hv[j], hv[j + 1]}, s, false);
-                    acc[r][t] = s;
-                }
-            }
+            for (int c = 0; c < kShChunks; ++c)
+                v = dot8(vd[c], hv[c], v);
+            acc[t] = v;
         }
     }
 #pragma unroll
-    for (int t = 0; t < kSharedGemvMaxTokens; ++t) {
-        if (t < T) {
-#pragma unroll
-            for (int r = 0; r < kShRows; ++r) {
-                float v = acc[r][t];
-#pragma unroll
-                for (int off = 32; off >= 1; off >>= 1)
-                    v += __shfl_xor(v, off, 64);
-                if (l == 0)
-                    sy[(int64_t)t * H + m0 + r] = v;
-            }
-        }
+    for (int t = 0; t < TT; ++t) {
+        const float v = wave_sum(acc[t]);
+        if (l == 0 && t < T)
+            sy[(int64_t)t * H + m] = v;
     }
+}
+
+template <int TT>
+static void shared_gemv_launch(const uint16_t *x16, int T, int H, int I, const uint16_t *wg,
+                               const uint16_t *wu, const uint16_t *wd, uint16_t *sh, float *sy,
+                               hipStream_t s)
+{
+    shared_gemv_gateup_kernel<TT><<<(I + 3) / 4, 256, 0, s>>>(x16, T, H, I, wg, wu, sh);
+    shared_gemv_down_kernel<TT><<<(H + 3) / 4, 256, 0, s>>>(sh, T, H, I, wd, sy);
 }
 
 hipError_t launch_shared_gemv(const uint16_t *x16, int T, int H, int I, const uint16_t *wg,
                               const uint16_t *wu, const uint16_t *wd, uint16_t *sh, float *sy,
                               hipStream_t s)
 {
-    const int rows_per_block = 4 * kShRows;
-    shared_gemv_gateup_kernel<<<(I + rows_per_block - 1) / rows_per_block, 256, 0, s>>>(x16, T, H, I, wg, wu, sh);
-    shared_gemv_down_kernel<<<(H + rows_per_block - 1) / rows_per_block, 256, 0, s>>>(sh, T, H, I, wd, sy);
+    // 1 <= T <= kSharedGemvMaxTokens (16)
+    if (T <= 1) shared_gemv_launch<1>(x16, T, H, I, wg, wu, wd, sh, sy, s);
+    else if (T <= 2) shared_gemv_launch<2>(x16, T, H, I, wg, wu, wd, sh, sy, s);
+    else if (T <= 4) shared_gemv_launch<4>(x16, T, H, I, wg, wu, wd, sh, sy, s);
+    else if (T <= 8) shared_gemv_launch<8>(x16, T, H, I, wg, wu, wd, sh, sy, s);
+    else shared_gemv_launch<16>(x16, T, H, I, wg, wu, wd, sh, sy, s);
     return hipGetLastError();
 }
 

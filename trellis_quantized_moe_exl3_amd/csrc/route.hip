@@ -168,56 +168,98 @@ hipError_t launch_route_logits(const uint16_t *x, bool bf16, int64_t T, int H, c
 }
 
 // ----------------------------------------------------------------- top-k, softmax
-// One wavefront per token.  Lane l holds the logits of experts l, l+64, ...;
-// k rounds of a wavefront arg-max by (logit desc, expert asc).
-constexpr int kTopkMaxPerLane = 16;   // E <= 1024
+// One wavefront per token.  Lane l holds the logits of experts l, l + 64, ...
+// (NPER slots, enough for E).  k rounds: each lane offers its best remaining
+// (logit, expert), a DPP reduction finds the wave maximum, and a ballot of the
+// lanes holding it names the winner (the lowest expert among ties, which needs
+// a second reduction only when several lanes tie).
 
+// v <- op(v, v of the lane the DPP control names); rows outside row_mask
+// keep their own value (op(v, v) = v).
+template <int CTRL, int ROW_MASK>
+MOE_DEV float dpp_fmax(float v)
+{
+    const int o = __builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, ROW_MASK, 0xF, false);
+    return fmaxf(v, __int_as_float(o));
+}
+template <int CTRL, int ROW_MASK>
+MOE_DEV int dpp_imin(int v)
+{
+    return min(v, __builtin_amdgcn_update_dpp(v, v, CTRL, ROW_MASK, 0xF, false));
+}
+
+// Wave-wide maximum / minimum (all 64 lanes active), read from lane 63:
+// xor 1 and xor 2 inside quads, mirrored halves of 8 and 16 lanes, then the
+// last lane of rows 0 and 2 into rows 1 and 3, and of row 1 into rows 2, 3.
+MOE_DEV float wave_max(float v)
+{
+    v = dpp_fmax<0xB1, 0xF>(v);    // quad_perm [1, 0, 3, 2]
+    v = dpp_fmax<0x4E, 0xF>(v);    // quad_perm [2, 3, 0, 1]
+    v = dpp_fmax<0x141, 0xF>(v);   // row_half_mirror
+    v = dpp_fmax<0x140, 0xF>(v);   // row_mirror
+    v = dpp_fmax<0x142, 0xA>(v);   // row_bcast15
+    v = dpp_fmax<0x143, 0xC>(v);   // row_bcast31
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+MOE_DEV int wave_min(int v)
+{
+    v = dpp_imin<0xB1, 0xF>(v);
+    v = dpp_imin<0x4E, 0xF>(v);
+    v = dpp_imin<0x141, 0xF>(v);
+    v = dpp_imin<0x140, 0xF>(v);
+    v = dpp_imin<0x142, 0xA>(v);
+    v = dpp_imin<0x143, 0xC>(v);
+    return __builtin_amdgcn_readlane(v, 63);
+}
+
+constexpr int kNoExpert = 0x7fffffff;
+
+template <int NPER>
 __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits, int64_t T,
                                                    int E, int k, int32_t *__restrict__ idx,
                                                    float *__restrict__ w)
 {
     const int l = threadIdx.x & 63;
     const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= T)
+    if (t >= T)   // whole wavefronts leave
         return;
-    float v[kTopkMaxPerLane];
-    int key[kTopkMaxPerLane];
-    const int nper = (E + 63) / 64;
+    float v[NPER];
+    int key[NPER];
 #pragma unroll
-    for (int i = 0; i < kTopkMaxPerLane; ++i) {
+    for (int i = 0; i < NPER; ++i) {
         const int e = l + 64 * i;
-        const bool ok = i < nper && e < E;
+        const bool ok = e < E;
         v[i] = ok ? logits[t * E + e] : -INFINITY;
-        key[i] = ok ? e : 0x7fffffff;
+        key[i] = ok ? e : kNoExpert;
     }
     float selv[16];
     int seli[16];
     for (int j = 0; j < k; ++j) {
+        // the lane's best remaining: slots are in ascending expert order, so
+        // the strict compare keeps the lowest expert among equal logits
         float bv = -INFINITY;
-        int bi = 0x7fffffff;
+        int bi = kNoExpert;
 #pragma unroll
-        for (int i = 0; i < kTopkMaxPerLane; ++i) {
-            if (key[i] != 0x7fffffff && (v[i] > bv || (v[i] == bv && key[i] < bi))) {
+        for (int i = 0; i < NPER; ++i) {
+            if (key[i] != kNoExpert && (bi == kNoExpert || v[i] > bv)) {
                 bv = v[i];
                 bi = key[i];
             }
         }
+        const float m = wave_max(bi == kNoExpert ? -INFINITY : bv);
+        const uint64_t tie = __ballot(bi != kNoExpert && bv == m);
+        int win;
+        if (__popcll(tie) == 1)
+            win = __builtin_amdgcn_readlane(bi, __builtin_ctzll(tie));
+        else
+            win = wave_min(((tie >> l) & 1) ? bi : kNoExpert);
+        selv[j] = m;
+        seli[j] = win;
+        if ((win & 63) == l) {
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            const float ov = __shfl_xor(bv, off, 64);
-            const int oi = __shfl_xor(bi, off, 64);
-            if (oi != 0x7fffffff && (bi == 0x7fffffff || ov > bv || (ov == bv && oi < bi))) {
-                bv = ov;
-                bi = oi;
-            }
-        }
-        selv[j] = bv;
-        seli[j] = bi;
-        if ((bi & 63) == l) {
-#pragma unroll
-            for (int i = 0; i < kTopkMaxPerLane; ++i)
-                if (key[i] == bi)
-                    key[i] = 0x7fffffff;
+            for (int i = 0; i < NPER; ++i)
+                if (key[i] == win)
+                    key[i] = kNoExpert;
         }
     }
     if (l == 0) {
@@ -234,7 +276,18 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
 hipError_t launch_topk(const float *logits, int64_t T, int E, int k, int32_t *idx, float *w,
                        hipStream_t s)
 {
-    topk_kernel<<<(unsigned)((T + 3) / 4), 256, 0, s>>>(logits, T, E, k, idx, w);
+    const unsigned grid = (unsigned)((T + 3) / 4);
+    const int nper = (E + 63) / 64;   // E <= 1024
+    if (nper <= 1)
+        topk_kernel<1><<<grid, 256, 0, s>>>(logits, T, E, k, idx, w);
+    else if (nper <= 2)
+        topk_kernel<2><<<grid, 256, 0, s>>>(logits, T, E, k, idx, w);
+    else if (nper <= 5)
+        topk_kernel<5><<<grid, 256, 0, s>>>(logits, T, E, k, idx, w);
+    else if (nper <= 8)
+        topk_kernel<8><<<grid, 256, 0, s>>>(logits, T, E, k, idx, w);
+    else
+        topk_kernel<16><<<grid, 256, 0, s>>>(logits, T, E, k, idx, w);
     return hipGetLastError();
 }
 
@@ -349,7 +402,8 @@ __global__ __launch_bounds__(64) void seg_scatter_kernel(const int32_t *__restri
     while ((1 << nbits) < E)
         ++nbits;
     const uint64_t below = (l == 0) ? 0ull : (~0ull >> (64 - l));
-    for (int c0 = 0; c0 < kSegChunk; c0 += 64) {
+    const int64_t span = n - a0 < kSegChunk ? n - a0 : kSegChunk;   // slots of this block
+    for (int c0 = 0; c0 < span; c0 += 64) {
         const int64_t a = a0 + c0 + l;
         const bool valid = a < n;
         const int e = valid ? idx[a] : 0;
