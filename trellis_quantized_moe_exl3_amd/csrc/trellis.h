@@ -21,10 +21,11 @@
 // and always fit in two consecutive dwords of the tile (the second one wraps to
 // dword 0 at the end of the tile).
 //
-// Instruction budget per weight (gfx950): one shift/alignbit for the window,
-// two 16-bit multiplies for the 32-bit hash, one AND and one SAD for the four
-// field sum (the SAD of the second state of a pair writes the high half, so
-// packing is free), then half an op to re-centre two fp16 values.
+// Instruction budget per weight (gfx950): one bit-field extract for the
+// window (plus a byte permute per fragment), one 32-bit multiply for the
+// hash, one AND and one SAD for the four-field sum (the SAD of the second
+// state of a pair writes the high half, so packing is free), then half an op
+// to re-centre two fp16 values.
 #pragma once
 
 #include "common.h"
@@ -47,45 +48,40 @@ MOE_DEV void frag_pos(int c, int h, int &d0, int &d1, int &q)
     d1 = (d0 + 1 == Tile<K>::kDwords) ? 0 : d0 + 1;
 }
 
-// The eight 16-bit states of a fragment from its two raw dwords; state t ends
-// up in the low 16 bits of st[t] (upper bits are not cleared: every consumer
-// reads 16-bit operands).
+// v_perm_b32 selector (src0 = D0, src1 = D1) that assembles the 32 stream
+// bits starting at stream byte b (0..4) of the dword pair, first stream bit
+// most significant.  Stream byte j of the pair (word 0 first, high byte
+// first) is v_perm byte 5, 4, 7, 6, 1, 0, 3, 2.
+MOE_DEV uint32_t frag_sel(int b)
+{
+    return __builtin_bswap32((uint32_t)(0x0203000106070405ull >> (8 * b)));
+}
+
+// The eight 16-bit states of a fragment from its two raw dwords, each in the
+// low 16 bits of st[t] with the upper bits clear.  A fragment starts at a
+// multiple of 8 stream bits (K * 8 * (2c + h)), so one byte permute yields
+// the 32 bits from its first state on and one bit-field extract per state
+// picks a window; states past bit 16 come from a second permute that starts
+// one (K = 3) or two (K = 4) bytes further.  The selectors depend on q only.
 template <int K>
 MOE_DEV void frag_states(uint32_t D0, uint32_t D1, int q, uint32_t st[8])
 {
-    // the stream reads the low word of a little-endian dword first
-    const uint32_t S0 = __builtin_amdgcn_alignbit(D0, D0, 16);
-    const uint32_t S1 = __builtin_amdgcn_alignbit(D1, D1, 16);
-    uint32_t A, Bn;
-    if (K == 4) {   // fragment windows start on dword boundaries
-        A = S0;
-        Bn = S1;
-    } else {
-        const uint64_t w = ((uint64_t)S0 << 32) | S1;
-        A = (uint32_t)(w >> (32 - q));   // window bits [0, 32) relative to q
-        Bn = S1 << q;                    // window bits [32, 64 - q)
-    }
+    constexpr int kC = K == 4 ? 2 : 1;   // byte offset of the second permute
+    const int b = q >> 3;
+    const uint32_t A = __builtin_amdgcn_perm(D0, D1, frag_sel(b));
+    const uint32_t C = K == 2 ? 0u : __builtin_amdgcn_perm(D0, D1, frag_sel(b + kC));
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-        const int o = K * t;
-        if (o <= 16)
-            st[t] = A >> (16 - o);
-        else
-            st[t] = __builtin_amdgcn_alignbit(A, Bn, 48 - o);
+        const int o = K * t;   // window start relative to the fragment
+        st[t] = o <= 16 ? __builtin_amdgcn_ubfe(A, 16 - o, 16) : __builtin_amdgcn_ubfe(C, 16 + 8 * kC - o, 16);
     }
 }
 
-// (mcg * s) mod 2^32 for the low 16 bits of s, with mcg split into 16-bit
-// halves: s*lo + ((s*hi) mod 2^16) << 16.  Two full-rate 16-bit multiplies
-// (the SDWA form writes the high half and zeroes the low half) instead of one
-// quarter-rate 32-bit multiply.
+// (mcg * s) mod 2^32 for a 16-bit state s (upper bits clear): one full-rate
+// 32-bit multiply on gfx950.
 MOE_DEV uint32_t mcg_hash(uint32_t s, uint32_t m_lo, uint32_t m_hi)
 {
-    uint32_t t, h;
-    asm("v_mul_lo_u16_sdwa %0, %1, %2 dst_sel:WORD_1 dst_unused:UNUSED_PAD src0_sel:WORD_0 src1_sel:WORD_0"
-        : "=v"(t) : "v"(s), "v"(m_hi));
-    asm("v_mad_u32_u16 %0, %1, %2, %3" : "=v"(h) : "v"(s), "v"(m_lo), "v"(t));
-    return h;
+    return s * (m_lo | (m_hi << 16));
 }
 
 // base + 2 * sum of the four 7-bit fields (bits 1..7 of every byte of h).
