@@ -473,6 +473,10 @@ __global__ __launch_bounds__(kThreads, 1) void group_gemm_kernel(GemmArgs args)
         }
         g.arsrc = buf_rsrc(abase, abytes);
         g.anull = buf_rsrc(abase, 0);
+        // rows past the tile's last 32-row block feed no stored result: the
+        // waves that would load them go through the zero-range descriptor
+        if (g.w >= mblocks)
+            g.arsrc = g.anull;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int r = 32 * g.w + 16 * j + (g.l >> 2);
@@ -499,7 +503,14 @@ __global__ __launch_bounds__(kThreads, 1) void group_gemm_kernel(GemmArgs args)
     g.m_hi = a.mcg >> 16;
     g.q = 0;
 
-    if (mblocks <= 2) {
+    if (mblocks <= 1) {
+        if (cm == 4)
+            tile_body<MODE, K, CB, 1, Groups<MODE, 1>::kMax>(g, args, n0, ring0, ring1, ring2, ring3);
+        else if (cm == 2)
+            tile_body<MODE, K, CB, 1, (Groups<MODE, 1>::kMax > 2 ? 2 : Groups<MODE, 1>::kMax)>(g, args, n0, ring0, ring1, ring2, ring3);
+        else
+            tile_body<MODE, K, CB, 1, 1>(g, args, n0, ring0, ring1, ring2, ring3);
+    } else if (mblocks <= 2) {
         if (cm == 4)
             tile_body<MODE, K, CB, 2, Groups<MODE, 2>::kMax>(g, args, n0, ring0, ring1, ring2, ring3);
         else if (cm == 2)
