@@ -119,27 +119,43 @@ def setup(cfg, copies=1, shared=True, extra_flags=0):
 
 
 def time_layer(desc, weights_list, x, steps, warmup, hip):
-    """Returns (ms per step from host clocks, per-step-kind event ms arrays)."""
+    """Times `steps` layers through moe_exl3_layer (no timing hooks inside the
+    timed region) between two device synchronisations, then runs the same
+    number of layers through moe_exl3_layer_profiled for the per-step split.
+    Returns (ms per step from host clocks, per-step event ms [steps][STEP_END],
+    device ms per step from two events around the plain run, out, workspace).
+    Each event recorded between steps adds a few microseconds of its own, so
+    only the plain run gives the layer time."""
     import torch
     import trellis_quantized_moe_exl3_amd as M
     out = torch.empty_like(x)
     ws = torch.empty(M.workspace_size(desc, x.shape[0]), dtype=torch.uint8, device="cuda")
     nw = len(weights_list)
+    stream = torch.cuda.current_stream().cuda_stream
+    hip.l.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
     for i in range(warmup):
         M.layer(desc, weights_list[i % nw], x, out, ws)
-    evs = [[hip.event() for _ in range(M.STEP_END + 1)] for _ in range(steps)]
+    a, b = hip.event(), hip.event()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    assert hip.l.hipEventRecord(a, stream) == 0
+    for i in range(steps):
+        M.layer(desc, weights_list[i % nw], x, out, ws)
+    assert hip.l.hipEventRecord(b, stream) == 0
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    dev_ms = hip.ms(a, b) / steps
+    hip.destroy(a)
+    hip.destroy(b)
+    evs = [[hip.event() for _ in range(M.STEP_END + 1)] for _ in range(steps)]
     for i in range(steps):
         M.layer_profiled(desc, weights_list[i % nw], x, out, ws, evs[i])
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
     per = np.array([[hip.ms(e[j], e[j + 1]) for j in range(M.STEP_END)] for e in evs])
-    total = np.array([hip.ms(e[0], e[M.STEP_END]) for e in evs])
     for e in evs:
         for x_ in e:
             hip.destroy(x_)
-    return (t1 - t0) * 1000.0 / steps, per, total, out, ws
+    return (t1 - t0) * 1000.0 / steps, per, dev_ms, out, ws
 
 
 def routing_counts(desc, weights, x, cfg):
@@ -237,14 +253,14 @@ def main():
     dcfg = W.BY_NAME["decode"]
     dinp, ddesc, dweights, dkeep = setup(dcfg, copies=4)
     dx = _dev(dinp.x)
-    dms, dper, dtotal, _, _ = time_layer(ddesc, dweights, dx, args.decode_steps, 5, hip)
+    dms, dper, ddev, _, _ = time_layer(ddesc, dweights, dx, args.decode_steps, 5, hip)
     dcounts = routing_counts(ddesc, dweights[0], dx, dcfg)
     touched = int((dcounts > 0).sum())
     code_bytes = touched * 3 * (dcfg.hidden * dcfg.inter * dcfg.K // 8)
     dstep = {n: float(dper[:, i].mean()) for i, n in enumerate(M.STEPS)}
     routed_ms = dstep["gemv_gateup"] + dstep["mfma_gateup"] + dstep["gemv_down"] + dstep["mfma_down"]
     code_gbps = code_bytes / (routed_ms * 1e-3) / 1e9
-    print(f"[bench] decode {float(dtotal.mean()) * 1000:.1f} us/layer (events), code {code_gbps:.0f} GB/s; "
+    print(f"[bench] decode {ddev * 1000:.1f} us/layer, code {code_gbps:.0f} GB/s; "
           f"steps {json.dumps({k: round(v * 1000, 1) for k, v in dstep.items()})}", file=sys.stderr, flush=True)
     del dkeep, dweights
     torch.cuda.empty_cache()
@@ -290,7 +306,7 @@ def main():
                      "frac": achieved / PEAK_FP16_TFLOPS, "traffic": recorded_traffic(),
                      "launch_ms": gu_ms, "flops_per_launch": gu_flops},
         "step_ms": step_ms,
-        "decode": {"workload": "decode-8: T=8, same layer, no router bias", "us_per_layer": float(dtotal.mean()) * 1000,
+        "decode": {"workload": "decode-8: T=8, same layer, no router bias", "us_per_layer": ddev * 1000,
                    "host_ms_per_step": dms, "touched_experts": touched, "code_bytes": code_bytes,
                    "routed_kernels_us": routed_ms * 1000, "code_GBps": code_gbps,
                    "code_hbm_frac": code_gbps / PEAK_HBM_GBPS,

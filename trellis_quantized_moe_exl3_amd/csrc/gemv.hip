@@ -333,14 +333,15 @@ hipError_t launch_gemv_down(const GroupArgs &a, int max_list, hipStream_t s)
 
 // ------------------------------------------------------------ shared expert GEMV
 // Dense fp16 weights in nn.Linear layout [out][in]; one wavefront per weight
-// row (gate/up: the gate and the up row of one channel).  Lane l owns the
-// 16-byte chunks k = 8l + 512c; a pass issues the loads of kShChunks chunks
-// (all of a 4096-wide row) before the first dot product, so every wavefront
-// keeps its whole row in flight.  The code is branch-free so that the
-// activation loads of a token issue together: TT (a power of two >= T)
-// tokens are processed, tokens past T re-read the last one and are not
-// stored, and chunks past the row end read chunk 0 with a zero weight.
-constexpr int kShChunks = 8;
+// row (gate/up: the gate and the up row of one channel), four per block.  The
+// input dimension is walked in slabs of kShSlab channels: the block stages
+// the slab of all TT token rows (a power of two >= T; rows past T and
+// channels past the end are zero) in LDS once, so every token row is read
+// from L2 once per block instead of once per wavefront, while each lane
+// streams its 16-byte weight chunks k = 8l + 512c of the slab (the next
+// slab's chunks are loaded before the current one is used).
+constexpr int kShSlab = 2048;
+constexpr int kShChunks = kShSlab / 512;
 
 // Sum over the wavefront (all lanes active), the result in every lane.
 MOE_DEV float wave_sum(float v)
@@ -359,6 +360,31 @@ MOE_DEV float dot8(const f16x8 &a, const f16x8 &b, float s)
     return s;
 }
 
+// Rows [0, TT) of the slab [kb, kb + kShSlab) of a [T][n] fp16 matrix into LDS
+// (zeros past T or n), by all 256 threads of the block.
+template <int TT>
+MOE_DEV void stage_slab(const uint16_t *__restrict__ src, int T, int n, int kb, f16 *xs)
+{
+    for (int i = threadIdx.x; i < TT * kShSlab / 8; i += 256) {
+        const int t = i / (kShSlab / 8), k = kb + 8 * (i % (kShSlab / 8));
+        f16x8 v = {};
+        if (t < T && k < n)
+            v = *(const f16x8 *)(src + (int64_t)t * n + k);
+        *(f16x8 *)(xs + 8 * i) = v;
+    }
+}
+
+// The lane's weight chunks of one slab of row r (zeros past the row end).
+MOE_DEV void load_chunks(const uint16_t *__restrict__ r, int n, int kb, int l, f16x8 v[kShChunks])
+{
+#pragma unroll
+    for (int c = 0; c < kShChunks; ++c) {
+        const int k0 = kb + 512 * c + 8 * l;
+        const f16x8 a = *(const f16x8 *)(r + (k0 < n ? k0 : 0));
+        v[c] = k0 < n ? a : (f16x8){};
+    }
+}
+
 template <int TT>
 __global__ __launch_bounds__(256) void shared_gemv_gateup_kernel(const uint16_t *__restrict__ x16,
                                                                  int T, int H, int I,
@@ -366,48 +392,49 @@ __global__ __launch_bounds__(256) void shared_gemv_gateup_kernel(const uint16_t 
                                                                  const uint16_t *__restrict__ wu,
                                                                  uint16_t *__restrict__ sh)
 {
+    __shared__ __align__(16) f16 xs[TT * kShSlab];
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-    const int n = blockIdx.x * 4 + w;
-    if (n >= I)   // whole wavefronts leave
-        return;
+    const int n = min(blockIdx.x * 4 + w, I - 1);   // spare wavefronts repeat the last row
     float acc[2][TT];
 #pragma unroll
     for (int t = 0; t < TT; ++t)
         acc[0][t] = acc[1][t] = 0.0f;
     const uint16_t *gr = wg + (int64_t)n * H, *ur = wu + (int64_t)n * H;
-    for (int kb = 0; kb < H; kb += 512 * kShChunks) {
-        int kc[kShChunks];
-        f16x8 vg[kShChunks], vu[kShChunks];
+    f16x8 vg[kShChunks], vu[kShChunks];
+    load_chunks(gr, H, 0, l, vg);
+    load_chunks(ur, H, 0, l, vu);
+    for (int kb = 0; kb < H; kb += kShSlab) {
+        __syncthreads();   // the previous slab's LDS reads are done
+        stage_slab<TT>(x16, T, H, kb, xs);
+        __syncthreads();
+        f16x8 cg[kShChunks], cu[kShChunks];
 #pragma unroll
         for (int c = 0; c < kShChunks; ++c) {
-            const int k0 = kb + 512 * c + 8 * l;
-            const bool ok = k0 < H;   // H % 256 == 0: whole chunks
-            kc[c] = ok ? k0 : 0;
-            const f16x8 a = *(const f16x8 *)(gr + kc[c]), b = *(const f16x8 *)(ur + kc[c]);
-            vg[c] = ok ? a : (f16x8){};
-            vu[c] = ok ? b : (f16x8){};
+            cg[c] = vg[c];
+            cu[c] = vu[c];
+        }
+        if (kb + kShSlab < H) {
+            load_chunks(gr, H, kb + kShSlab, l, vg);
+            load_chunks(ur, H, kb + kShSlab, l, vu);
         }
 #pragma unroll
         for (int t = 0; t < TT; ++t) {
-            const uint16_t *xr = x16 + (int64_t)(t < T ? t : T - 1) * H;
-            f16x8 xv[kShChunks];
-#pragma unroll
-            for (int c = 0; c < kShChunks; ++c)
-                xv[c] = *(const f16x8 *)(xr + kc[c]);
             float g = acc[0][t], u = acc[1][t];
 #pragma unroll
             for (int c = 0; c < kShChunks; ++c) {
-                g = dot8(vg[c], xv[c], g);
-                u = dot8(vu[c], xv[c], u);
+                const f16x8 xv = *(const f16x8 *)(xs + t * kShSlab + 512 * c + 8 * l);
+                g = dot8(cg[c], xv, g);
+                u = dot8(cu[c], xv, u);
             }
             acc[0][t] = g;
             acc[1][t] = u;
         }
     }
+    const bool own = blockIdx.x * 4 + w < I;
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
         const float g = wave_sum(acc[0][t]), u = wave_sum(acc[1][t]);
-        if (l == 0 && t < T)
+        if (own && l == 0 && t < T)
             sh[(int64_t)t * I + n] = f32_to_f16_bits(silu_f(g) * u);
     }
 }
@@ -418,44 +445,40 @@ __global__ __launch_bounds__(256) void shared_gemv_down_kernel(const uint16_t *_
                                                                const uint16_t *__restrict__ wd,
                                                                float *__restrict__ sy)
 {
+    __shared__ __align__(16) f16 hs[TT * kShSlab];
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-    const int m = blockIdx.x * 4 + w;
-    if (m >= H)   // whole wavefronts leave
-        return;
+    const int m = min(blockIdx.x * 4 + w, H - 1);
     float acc[TT];
 #pragma unroll
     for (int t = 0; t < TT; ++t)
         acc[t] = 0.0f;
     const uint16_t *dr = wd + (int64_t)m * I;
-    for (int kb = 0; kb < I; kb += 512 * kShChunks) {
-        int kc[kShChunks];
-        f16x8 vd[kShChunks];
+    f16x8 vd[kShChunks];
+    load_chunks(dr, I, 0, l, vd);
+    for (int kb = 0; kb < I; kb += kShSlab) {
+        __syncthreads();
+        stage_slab<TT>(sh, T, I, kb, hs);
+        __syncthreads();
+        f16x8 cd[kShChunks];
 #pragma unroll
-        for (int c = 0; c < kShChunks; ++c) {
-            const int k0 = kb + 512 * c + 8 * l;
-            const bool ok = k0 < I;
-            kc[c] = ok ? k0 : 0;
-            const f16x8 a = *(const f16x8 *)(dr + kc[c]);
-            vd[c] = ok ? a : (f16x8){};
-        }
+        for (int c = 0; c < kShChunks; ++c)
+            cd[c] = vd[c];
+        if (kb + kShSlab < I)
+            load_chunks(dr, I, kb + kShSlab, l, vd);
 #pragma unroll
         for (int t = 0; t < TT; ++t) {
-            const uint16_t *hr = sh + (int64_t)(t < T ? t : T - 1) * I;
-            f16x8 hv[kShChunks];
-#pragma unroll
-            for (int c = 0; c < kShChunks; ++c)
-                hv[c] = *(const f16x8 *)(hr + kc[c]);
             float v = acc[t];
 #pragma unroll
             for (int c = 0; c < kShChunks; ++c)
-                v = dot8(vd[c], hv[c], v);
+                v = dot8(cd[c], *(const f16x8 *)(hs + t * kShSlab + 512 * c + 8 * l), v);
             acc[t] = v;
         }
     }
+    const bool own = blockIdx.x * 4 + w < H;
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
         const float v = wave_sum(acc[t]);
-        if (l == 0 && t < T)
+        if (own && l == 0 && t < T)
             sy[(int64_t)t * H + m] = v;
     }
 }

@@ -22,6 +22,9 @@ constexpr int kGemvDefaultRows = 2;
 // The GEMV blocks keep two rows of activations in LDS within 64 KiB.
 constexpr int kGemvMaxHidden = 8192;
 constexpr int kGemvMaxInter = 8192;
+// Tokens up to which one block runs the whole routing tail (top-k, segment
+// tables, activation copy) in a single launch.
+constexpr int kSmallRouteTokens = 64;
 // Tokens up to which the shared expert runs as a GEMV.
 constexpr int kSharedGemvMaxTokens = 16;
 
@@ -49,6 +52,11 @@ hipError_t launch_segments(const int32_t *idx, int64_t T, int k, int E, int nblk
                            int tile_m, int32_t *bhist, int32_t *counts, int32_t *offsets,
                            int32_t *sorted, int32_t *pos, int32_t *glist, int32_t *tiles,
                            WsHeader *hdr, hipStream_t s);
+
+hipError_t launch_route_small(const float *logits, int64_t T, int E, int k, int gemv_rows, int tile_m,
+                              int32_t *idx, float *w, int32_t *counts, int32_t *offsets, int32_t *sorted,
+                              int32_t *pos, int32_t *glist, int32_t *tiles, WsHeader *hdr,
+                              const uint16_t *x, int H, uint16_t *x16, hipStream_t s);
 
 hipError_t launch_decode(const uint16_t *codes, int n_in, int n_out, int K, uint32_t mcg, int cb,
                          void *dst, int dst_dtype, hipStream_t s);

@@ -153,8 +153,13 @@ struct Marks {
     }
 };
 
+// Routing steps a1-a3.  Decode-sized calls (T <= kSmallRouteTokens, one
+// segment chunk) run everything after the logits in one single-block launch,
+// which also writes the fp16 copy of bf16 activations when x16 is given (then
+// *converted is set).
 int run_route(const moe_exl3_desc &d, const moe_exl3_weights &w, const void *x, int64_t T,
-              void *ws, const Plan &p, hipStream_t s, const Marks &mk = Marks())
+              void *ws, const Plan &p, hipStream_t s, const Marks &mk = Marks(),
+              uint16_t *x16 = nullptr, bool *converted = nullptr)
 {
     const bool bf16 = d.act_dtype == MOE_EXL3_DT_BF16;
     const float *bias = (d.flags & MOE_EXL3_HAS_ROUTER_BIAS) ? w.router_bias : nullptr;
@@ -165,6 +170,18 @@ int run_route(const moe_exl3_desc &d, const moe_exl3_weights &w, const void *x, 
         return MOE_EXL3_ERR_HIP;
     if (!mk.mark(MOE_EXL3_STEP_TOPK))
         return MOE_EXL3_ERR_HIP;
+    if (T <= kSmallRouteTokens && p.nblk == 1) {
+        if (launch_route_small(at<float>(ws, p.logits), T, d.n_experts, d.top_k, gemv_rows_of(d), kTileM,
+                               at<int32_t>(ws, p.idx), at<float>(ws, p.w), at<int32_t>(ws, p.counts),
+                               at<int32_t>(ws, p.offsets), at<int32_t>(ws, p.sorted), at<int32_t>(ws, p.pos),
+                               at<int32_t>(ws, p.glist), at<int32_t>(ws, p.tiles), at<WsHeader>(ws, p.hdr),
+                               (const uint16_t *)x, d.hidden, x16, s) != hipSuccess ||
+            !mk.mark(MOE_EXL3_STEP_SEGMENTS))
+            return MOE_EXL3_ERR_HIP;
+        if (converted)
+            *converted = x16 != nullptr;
+        return MOE_EXL3_OK;
+    }
     if (launch_topk(at<float>(ws, p.logits), T, d.n_experts, d.top_k, at<int32_t>(ws, p.idx),
                     at<float>(ws, p.w), s) != hipSuccess)
         return MOE_EXL3_ERR_HIP;
@@ -288,15 +305,17 @@ static int run_layer(const moe_exl3_desc *desc, const moe_exl3_weights *weights,
     Marks mk;
     mk.ev = events;
     mk.s = s;
-    rc = run_route(d, wt, x, T, ws, p, s, mk);
+    const bool bf16 = d.act_dtype == MOE_EXL3_DT_BF16;
+    bool converted = false;
+    rc = run_route(d, wt, x, T, ws, p, s, mk, bf16 ? at<uint16_t>(ws, p.x16) : nullptr, &converted);
     if (rc)
         return rc;
     if (!mk.mark(MOE_EXL3_STEP_CONVERT_X))
         return MOE_EXL3_ERR_HIP;
-    const bool bf16 = d.act_dtype == MOE_EXL3_DT_BF16;
     const uint16_t *x16 = (const uint16_t *)x;
     if (bf16) {
-        if (launch_convert_x((const uint16_t *)x, true, T * d.hidden, at<uint16_t>(ws, p.x16), s) != hipSuccess)
+        if (!converted &&
+            launch_convert_x((const uint16_t *)x, true, T * d.hidden, at<uint16_t>(ws, p.x16), s) != hipSuccess)
             return MOE_EXL3_ERR_HIP;
         x16 = at<uint16_t>(ws, p.x16);
     }

@@ -214,15 +214,12 @@ MOE_DEV int wave_min(int v)
 
 constexpr int kNoExpert = 0x7fffffff;
 
+// Top-k and softmax of token t by the calling wavefront (all 64 lanes).
 template <int NPER>
-__global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits, int64_t T,
-                                                   int E, int k, int32_t *__restrict__ idx,
-                                                   float *__restrict__ w)
+MOE_DEV void topk_token(const float *__restrict__ logits, int64_t t, int E, int k, int32_t *__restrict__ idx,
+                        float *__restrict__ w, int32_t *sidx = nullptr)
 {
     const int l = threadIdx.x & 63;
-    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= T)   // whole wavefronts leave
-        return;
     float v[NPER];
     int key[NPER];
 #pragma unroll
@@ -269,8 +266,21 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
         for (int j = 0; j < k; ++j) {
             idx[t * k + j] = seli[j];
             w[t * k + j] = expf(selv[j] - selv[0]) / sum;
+            if (sidx)
+                sidx[t * k + j] = seli[j];
         }
     }
+}
+
+template <int NPER>
+__global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits, int64_t T,
+                                                   int E, int k, int32_t *__restrict__ idx,
+                                                   float *__restrict__ w)
+{
+    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T)   // whole wavefronts leave
+        return;
+    topk_token<NPER>(logits, t, E, k, idx, w);
 }
 
 hipError_t launch_topk(const float *logits, int64_t T, int E, int k, int32_t *idx, float *w,
@@ -437,6 +447,122 @@ hipError_t launch_segments(const int32_t *idx, int64_t T, int k, int E, int nblk
     seg_scan_kernel<<<1, 1024, 0, s>>>(bhist, nblk, E, gemv_rows, tile_m, counts, offsets, glist,
                                        tiles, hdr);
     seg_scatter_kernel<<<nblk, 64, lds, s>>>(idx, n, E, bhist, offsets, sorted, pos);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- decode-sized calls
+// One block of 1024 threads runs the whole routing tail of a decode-sized call
+// (T <= kSmallRouteTokens, T * k <= kSegChunk) in one launch: top-k and
+// softmax (one wavefront per token), the expert histogram, counts, offsets
+// and work lists (as seg_scan_kernel with a single chunk), the stable scatter
+// (as seg_scatter_kernel, by wavefront 0 alone), and, when x16 is given, the
+// bf16 -> fp16 copy of the activations.
+template <int NPER>
+__global__ __launch_bounds__(1024) void route_small_kernel(
+    const float *__restrict__ logits, int64_t T, int E, int k, int gemv_rows, int tile_m,
+    int32_t *__restrict__ idx, float *__restrict__ w, int32_t *__restrict__ counts,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ sorted, int32_t *__restrict__ pos,
+    int32_t *__restrict__ glist, int32_t *__restrict__ tiles, WsHeader *__restrict__ hdr,
+    const uint16_t *__restrict__ x, int H, uint16_t *__restrict__ x16)
+{
+    __shared__ int32_t sidx[kSegChunk];
+    __shared__ int32_t hist[1024];
+    const int wv = threadIdx.x >> 6, l = threadIdx.x & 63;
+    for (int64_t t = wv; t < T; t += 16)
+        topk_token<NPER>(logits, t, E, k, idx, w, sidx);
+    if (x16) {
+        const int64_t n8 = T * H / 8;
+        for (int64_t i = threadIdx.x; i < n8; i += 1024) {
+            const u32x4 v = ((const u32x4 *)x)[i];
+            u32x4 o;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float lo = __uint_as_float(v[j] << 16), hi = __uint_as_float(v[j] & 0xFFFF0000u);
+                o[j] = (uint32_t)f32_to_f16_bits(lo) | ((uint32_t)f32_to_f16_bits(hi) << 16);
+            }
+            ((u32x4 *)x16)[i] = o;
+        }
+    }
+    hist[threadIdx.x] = 0;
+    __syncthreads();
+    const int n = (int)(T * k);
+    for (int a = threadIdx.x; a < n; a += 1024)
+        atomicAdd(&hist[sidx[a]], 1);
+    __syncthreads();
+    const int e = threadIdx.x;   // E <= 1024
+    const int c = e < E ? hist[e] : 0;
+    int tot;
+    const int off = block_exclusive_scan(c, &tot);
+    if (e < E) {
+        counts[e] = c;
+        offsets[e] = off;
+    }
+    if (e == 0)
+        offsets[E] = tot;
+    const bool gemv = e < E && c > 0 && c <= gemv_rows;
+    const int nt = (e < E && c > gemv_rows) ? (c + tile_m - 1) / tile_m : 0;
+    int ng, ntt;
+    const int gpos = block_exclusive_scan(gemv ? 1 : 0, &ng);
+    const int tpos = block_exclusive_scan(nt, &ntt);
+    if (gemv)
+        glist[gpos] = e;
+    for (int m = 0; m < nt; ++m) {
+        tiles[2 * (tpos + m)] = e;
+        tiles[2 * (tpos + m) + 1] = m * tile_m;
+    }
+    if (e == 0) {
+        hdr->n_gemv = ng;
+        hdr->n_tiles = ntt;
+        hdr->status = 0;
+    }
+    __syncthreads();
+    hist[threadIdx.x] = off;   // running base of every expert
+    __syncthreads();
+    if (wv == 0) {
+        int nbits = 0;
+        while ((1 << nbits) < E)
+            ++nbits;
+        const uint64_t below = (l == 0) ? 0ull : (~0ull >> (64 - l));
+        for (int c0 = 0; c0 < n; c0 += 64) {
+            const int a = c0 + l;
+            const bool valid = a < n;
+            const int ea = valid ? sidx[a] : 0;
+            uint64_t m = __ballot(valid);
+            for (int b = 0; b < nbits; ++b) {
+                const bool bit = (ea >> b) & 1;
+                const uint64_t bb = __ballot(bit);
+                m &= bit ? bb : ~bb;
+            }
+            // the wavefront's LDS operations run in order: every lane reads
+            // the base before the last lane of its expert advances it
+            const int p = valid ? hist[ea] + __popcll(m & below) : 0;
+            if (valid) {
+                sorted[p] = a;
+                pos[a] = p;
+            }
+            __builtin_amdgcn_wave_barrier();
+            if (valid && (m >> l) == 1ull)   // last lane of its expert in this chunk
+                hist[ea] += __popcll(m);
+            __builtin_amdgcn_wave_barrier();
+        }
+    }
+}
+
+hipError_t launch_route_small(const float *logits, int64_t T, int E, int k, int gemv_rows, int tile_m,
+                              int32_t *idx, float *w, int32_t *counts, int32_t *offsets, int32_t *sorted,
+                              int32_t *pos, int32_t *glist, int32_t *tiles, WsHeader *hdr,
+                              const uint16_t *x, int H, uint16_t *x16, hipStream_t s)
+{
+    const int nper = (E + 63) / 64;   // E <= 1024
+#define MOE_ROUTE_SMALL(NP) \
+    route_small_kernel<NP><<<1, 1024, 0, s>>>(logits, T, E, k, gemv_rows, tile_m, idx, w, counts, offsets, \
+                                              sorted, pos, glist, tiles, hdr, x, H, x16)
+    if (nper <= 1) MOE_ROUTE_SMALL(1);
+    else if (nper <= 2) MOE_ROUTE_SMALL(2);
+    else if (nper <= 5) MOE_ROUTE_SMALL(5);
+    else if (nper <= 8) MOE_ROUTE_SMALL(8);
+    else MOE_ROUTE_SMALL(16);
+#undef MOE_ROUTE_SMALL
     return hipGetLastError();
 }
 
