@@ -99,6 +99,24 @@ def _sampled(name, sample, flags=0, tol=TOL):
     assert np.isfinite(out).all() and np.isfinite(out_r).all()
 
 
+@pytest.mark.parametrize("T", [64, 65])
+def test_decode_sized_layer_boundary(T):
+    # 64 tokens: the single-block routing tail also writes the fp16 copy of the
+    # bf16 activations; 65 tokens: the multi-launch routing and the separate copy
+    cfg = W.BY_NAME["decode"].replace(tokens=T, router_bias=True)
+    inp = W.gen_layer(cfg)
+    sample = [0, T // 2, T - 1]
+    routed = _routed_only(inp)
+    out_r = DevLayer(routed).run()
+    _, _, ref_r = oracle.layer(routed, sample)
+    out = DevLayer(inp).run()
+    _, _, ref = oracle.layer(inp, sample)
+    err_r, err = rel_err(out_r[sample], ref_r), rel_err(out[sample], ref)
+    print(f"decode-sized T={T} sampled routed err={err_r:.3e} full err={err:.3e}")
+    assert err_r <= TOL and err <= TOL
+    assert np.isfinite(out).all() and np.isfinite(out_r).all()
+
+
 def test_prefill_sampled():
     _sampled("prefill", [0, 1, 2, 1234, 3583, 7167])
 

@@ -33,9 +33,18 @@ def test_route_configs(name):
     _check(dl, inp.x)
 
 
-@pytest.mark.parametrize("T", [1, 13, 300])
+# up to 64 tokens (one segment chunk) one block runs top-k and the segment
+# tables; 65 tokens and more take the multi-launch path
+@pytest.mark.parametrize("T", [1, 13, 64, 65, 300])
 def test_route_ragged_token_counts(T):
     cfg = W.BY_NAME["decode"].replace(tokens=T, router_bias=True)
+    inp = W.gen_layer(cfg, experts=[])
+    _check(DevLayer(inp), inp.x)
+
+
+def test_route_small_path_wide_topk():
+    # 64 tokens x top-16 = 1024 slots in the single-block routing tail
+    cfg = W.BY_NAME["decode"].replace(tokens=64, top_k=16, router_bias=True)
     inp = W.gen_layer(cfg, experts=[])
     _check(DevLayer(inp), inp.x)
 
