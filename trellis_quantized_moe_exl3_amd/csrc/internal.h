@@ -83,8 +83,17 @@ struct GroupArgs {
 hipError_t launch_convert_x(const uint16_t *x, bool bf16, int64_t n, uint16_t *x16, hipStream_t s);
 hipError_t launch_gemv_gateup(const GroupArgs &a, int max_list, hipStream_t s);
 hipError_t launch_gemv_down(const GroupArgs &a, int max_list, hipStream_t s);
-hipError_t launch_mfma_gateup(const GroupArgs &a, int max_tiles, hipStream_t s);
-hipError_t launch_mfma_down(const GroupArgs &a, int max_tiles, hipStream_t s);
+// The dense shared expert, when its tiles ride along in the routed MFMA
+// launches (x16 [T][H] fp16, w = gate, up, down nn.Linear fp16, h [T][I] fp16
+// gate/up output, y [T][H] fp32 down output).
+struct SharedArgs {
+    const uint16_t *x16;
+    const uint16_t *w[3];
+    uint16_t *h;
+    float *y;
+};
+hipError_t launch_mfma_gateup(const GroupArgs &a, int max_tiles, const SharedArgs *sh, hipStream_t s);
+hipError_t launch_mfma_down(const GroupArgs &a, int max_tiles, const SharedArgs *sh, hipStream_t s);
 hipError_t launch_quant_gateup(const GroupArgs &a, int64_t n, hipStream_t s);
 hipError_t launch_quant_h(const GroupArgs &a, int64_t n, hipStream_t s);
 hipError_t launch_mfma8_gateup(const GroupArgs &a, int max_tiles, hipStream_t s);

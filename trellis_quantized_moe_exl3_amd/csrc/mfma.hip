@@ -67,6 +67,10 @@ struct GemmArgs {
     float *dOutY;            // shared down output [T][H] fp32
     int64_t T;
     int nslices;             // column slices per row tile
+    // trellis launches that also carry the dense shared expert: blocks from
+    // routed_grid on run dense tiles with dnslices slices per row tile
+    int routed_grid;
+    int dnslices;
 };
 
 template <int MODE>
@@ -405,19 +409,13 @@ MOE_DEV void tile_body(GemmTile<MODE, K, CB> &g, const GemmArgs &args, int n0,
     static_assert(NB <= kMB, "accumulator blocks");
 }
 
+// One block's work: block L of a grid with `nslices` column slices per row tile.
 template <int MODE, int K, int CB>
-__global__ __launch_bounds__(kThreads, 1) void group_gemm_kernel(GemmArgs args)
+MOE_DEV void block_body(const GemmArgs &args, int L, int nslices, uint16_t *ring0, uint16_t *ring1,
+                        uint16_t *ring2, uint16_t *ring3)
 {
     using TR = ModeTraits<MODE>;
     const GroupArgs &a = args.g;
-    // four ring slots, each one A stage plus four 256-byte suh areas (used in
-    // the trellis gate/up mode); four distinct LDS objects let the compiler
-    // tell the slots' LDS-direct writes apart
-    __shared__ __align__(16) uint16_t ring0[kSlotHalves];
-    __shared__ __align__(16) uint16_t ring1[kSlotHalves];
-    __shared__ __align__(16) uint16_t ring2[kSlotHalves];
-    __shared__ __align__(16) uint16_t ring3[kSlotHalves];
-
     GemmTile<MODE, K, CB> g;
     g.tid = threadIdx.x;
     g.w = __builtin_amdgcn_readfirstlane(g.tid >> 6);   // wave-uniform
@@ -428,7 +426,7 @@ __global__ __launch_bounds__(kThreads, 1) void group_gemm_kernel(GemmArgs args)
 
     // ---- work tile; `nslices` counts column slices at one group per wave
     int ti, slice;
-    xcd_map(blockIdx.x, args.nslices, ti, slice);
+    xcd_map(L, nslices, ti, slice);
     g.e = 0;
     g.p0 = 0;
     g.t0 = 0;
@@ -450,10 +448,10 @@ __global__ __launch_bounds__(kThreads, 1) void group_gemm_kernel(GemmArgs args)
     // share has no work: the whole block leaves before any barrier)
     int cm = 1;
     if (TR::kTrellis && mblocks <= 2)
-        cm = (args.nslices % 4 == 0) ? 4 : (args.nslices % 2 == 0) ? 2 : 1;
+        cm = (nslices % 4 == 0) ? 4 : (nslices % 2 == 0) ? 2 : 1;
     else if (TR::kTrellis && mblocks <= 4)
-        cm = (args.nslices % 2 == 0) ? 2 : 1;
-    if (slice >= args.nslices / cm)
+        cm = (nslices % 2 == 0) ? 2 : 1;
+    if (slice >= nslices / cm)
         return;
     const int n0 = slice * TR::kBlockN * cm;
 
@@ -529,11 +527,35 @@ __global__ __launch_bounds__(kThreads, 1) void group_gemm_kernel(GemmArgs args)
     }
 }
 
+template <int MODE, int K, int CB>
+__global__ __launch_bounds__(kThreads, 1) void group_gemm_kernel(GemmArgs args)
+{
+    // four ring slots, each one A stage plus four 256-byte suh areas (used in
+    // the trellis gate/up mode); four distinct LDS objects let the compiler
+    // tell the slots' LDS-direct writes apart
+    __shared__ __align__(16) uint16_t ring0[kSlotHalves];
+    __shared__ __align__(16) uint16_t ring1[kSlotHalves];
+    __shared__ __align__(16) uint16_t ring2[kSlotHalves];
+    __shared__ __align__(16) uint16_t ring3[kSlotHalves];
+    if constexpr (ModeTraits<MODE>::kTrellis) {
+        // blocks past the routed experts' grid run tiles of the dense shared
+        // expert, so its work fills the CUs the routed tiles leave idle at the
+        // end of the launch (routed_grid is a multiple of 8: XCD order holds)
+        if ((int)blockIdx.x >= args.routed_grid) {
+            constexpr int DM = MODE == GATEUP_TRELLIS ? GATEUP_DENSE : DOWN_DENSE;
+            block_body<DM, K, CB>(args, (int)blockIdx.x - args.routed_grid, args.dnslices, ring0, ring1, ring2, ring3);
+            return;
+        }
+    }
+    block_body<MODE, K, CB>(args, (int)blockIdx.x, args.nslices, ring0, ring1, ring2, ring3);
+}
+
 template <int MODE>
-static hipError_t launch_mode(const GemmArgs &ga, int tiles, hipStream_t s)
+static hipError_t launch_grid(const GemmArgs &ga, unsigned grid, hipStream_t s)
 {
     const GroupArgs &a = ga.g;
-    const unsigned grid = (unsigned)(((tiles + 7) / 8) * 8 * ga.nslices);
+    if (grid == 0)
+        return hipSuccess;
     if constexpr (ModeTraits<MODE>::kTrellis) {
         if (a.K == 2 && a.cb == 0) group_gemm_kernel<MODE, 2, 0><<<grid, kThreads, 0, s>>>(ga);
         else if (a.K == 3 && a.cb == 0) group_gemm_kernel<MODE, 3, 0><<<grid, kThreads, 0, s>>>(ga);
@@ -547,24 +569,49 @@ static hipError_t launch_mode(const GemmArgs &ga, int tiles, hipStream_t s)
     return hipGetLastError();
 }
 
-hipError_t launch_mfma_gateup(const GroupArgs &a, int max_tiles, hipStream_t s)
+// Blocks for `tiles` row tiles at `nslices` slices each, in whole XCD rounds.
+static unsigned grid_of(int tiles, int nslices)
 {
-    if (max_tiles <= 0)
-        return hipSuccess;
+    return tiles > 0 ? (unsigned)(((tiles + 7) / 8) * 8 * nslices) : 0u;
+}
+
+static int dense_tiles(int64_t T) { return (int)((T + kBM - 1) / kBM); }
+
+hipError_t launch_mfma_gateup(const GroupArgs &a, int max_tiles, const SharedArgs *sh, hipStream_t s)
+{
     GemmArgs ga{};
     ga.g = a;
     ga.nslices = a.I / ModeTraits<GATEUP_TRELLIS>::kBlockN;
-    return launch_mode<GATEUP_TRELLIS>(ga, max_tiles, s);
+    ga.routed_grid = (int)grid_of(max_tiles, ga.nslices);
+    unsigned grid = (unsigned)ga.routed_grid;
+    if (sh) {
+        ga.dA = sh->x16;
+        ga.dB[0] = sh->w[0];
+        ga.dB[1] = sh->w[1];
+        ga.dOutH = sh->h;
+        ga.T = a.T;
+        ga.dnslices = a.I / ModeTraits<GATEUP_DENSE>::kBlockN;
+        grid += grid_of(dense_tiles(a.T), ga.dnslices);
+    }
+    return launch_grid<GATEUP_TRELLIS>(ga, grid, s);
 }
 
-hipError_t launch_mfma_down(const GroupArgs &a, int max_tiles, hipStream_t s)
+hipError_t launch_mfma_down(const GroupArgs &a, int max_tiles, const SharedArgs *sh, hipStream_t s)
 {
-    if (max_tiles <= 0)
-        return hipSuccess;
     GemmArgs ga{};
     ga.g = a;
     ga.nslices = a.H / ModeTraits<DOWN_TRELLIS>::kBlockN;
-    return launch_mode<DOWN_TRELLIS>(ga, max_tiles, s);
+    ga.routed_grid = (int)grid_of(max_tiles, ga.nslices);
+    unsigned grid = (unsigned)ga.routed_grid;
+    if (sh) {
+        ga.dA = sh->h;
+        ga.dB[0] = sh->w[2];
+        ga.dOutY = sh->y;
+        ga.T = a.T;
+        ga.dnslices = a.H / ModeTraits<DOWN_DENSE>::kBlockN;
+        grid += grid_of(dense_tiles(a.T), ga.dnslices);
+    }
+    return launch_grid<DOWN_TRELLIS>(ga, grid, s);
 }
 
 hipError_t launch_shared_gateup(const uint16_t *x16, int64_t T, int H, int I, const uint16_t *wg,
@@ -579,7 +626,7 @@ hipError_t launch_shared_gateup(const uint16_t *x16, int64_t T, int H, int I, co
     ga.dOutH = sh;
     ga.T = T;
     ga.nslices = I / ModeTraits<GATEUP_DENSE>::kBlockN;
-    return launch_mode<GATEUP_DENSE>(ga, (int)((T + kBM - 1) / kBM), s);
+    return launch_grid<GATEUP_DENSE>(ga, grid_of(dense_tiles(T), ga.nslices), s);
 }
 
 hipError_t launch_shared_down(const uint16_t *sh, int64_t T, int H, int I, const uint16_t *wd,
@@ -593,7 +640,7 @@ hipError_t launch_shared_down(const uint16_t *sh, int64_t T, int H, int I, const
     ga.dOutY = sy;
     ga.T = T;
     ga.nslices = H / ModeTraits<DOWN_DENSE>::kBlockN;
-    return launch_mode<DOWN_DENSE>(ga, (int)((T + kBM - 1) / kBM), s);
+    return launch_grid<DOWN_DENSE>(ga, grid_of(dense_tiles(T), ga.nslices), s);
 }
 
 // ---------------------------------------------------------------- small kernels

@@ -356,24 +356,39 @@ static int run_layer(const moe_exl3_desc *desc, const moe_exl3_weights *weights,
     const int64_t n = T * d.top_k;
     const int max_list = g > 0 ? (int)std::min<int64_t>(d.n_experts, n) : 0;
 
+    // The shared expert: a dot-product GEMV for up to kSharedGemvMaxTokens
+    // tokens; otherwise its dense tiles ride along in the routed 16-bit MFMA
+    // launches (filling the CUs their last routed tiles leave idle), or, on the
+    // fp8 path, run in launches of their own.
+    const bool shared = d.flags & MOE_EXL3_HAS_SHARED;
+    uint16_t *sh = shared ? at<uint16_t>(ws, p.sh) : nullptr;
+    float *sy = shared ? at<float>(ws, p.sy) : nullptr;
+    SharedArgs sa{};
+    const bool merged = shared && !f8 && T > kSharedGemvMaxTokens;
+    if (merged) {
+        sa.x16 = x16;
+        for (int i = 0; i < 3; ++i)
+            sa.w[i] = wt.shared_w[i];
+        sa.h = sh;
+        sa.y = sy;
+    }
+    const SharedArgs *sap = merged ? &sa : nullptr;
+
     // fp8: the activation rows are quantized at the end of the convert step,
     // the h rows at the start of the GEMV down step
     if (f8 && launch_quant_gateup(ga, n, s) != hipSuccess)
         return MOE_EXL3_ERR_HIP;
     if (!mk.mark(MOE_EXL3_STEP_GEMV_GATEUP) || launch_gemv_gateup(ga, max_list, s) != hipSuccess ||
         !mk.mark(MOE_EXL3_STEP_MFMA_GATEUP) ||
-        (f8 ? launch_mfma8_gateup(ga, p.max_tiles, s) : launch_mfma_gateup(ga, p.max_tiles, s)) != hipSuccess ||
+        (f8 ? launch_mfma8_gateup(ga, p.max_tiles, s) : launch_mfma_gateup(ga, p.max_tiles, sap, s)) != hipSuccess ||
         !mk.mark(MOE_EXL3_STEP_GEMV_DOWN) || (f8 && launch_quant_h(ga, n, s) != hipSuccess) ||
         launch_gemv_down(ga, max_list, s) != hipSuccess ||
         !mk.mark(MOE_EXL3_STEP_MFMA_DOWN) ||
-        (f8 ? launch_mfma8_down(ga, p.max_tiles, s) : launch_mfma_down(ga, p.max_tiles, s)) != hipSuccess ||
+        (f8 ? launch_mfma8_down(ga, p.max_tiles, s) : launch_mfma_down(ga, p.max_tiles, sap, s)) != hipSuccess ||
         !mk.mark(MOE_EXL3_STEP_SHARED))
         return MOE_EXL3_ERR_HIP;
 
-    float *sy = nullptr;
-    if (d.flags & MOE_EXL3_HAS_SHARED) {
-        uint16_t *sh = at<uint16_t>(ws, p.sh);
-        sy = at<float>(ws, p.sy);
+    if (shared && !merged) {
         hipError_t e;
         if (T <= kSharedGemvMaxTokens)
             e = launch_shared_gemv(x16, (int)T, d.hidden, d.inter, wt.shared_w[0], wt.shared_w[1],
