@@ -38,6 +38,8 @@ sys.path.insert(0, ROOT)
 PEAK_FP16_TFLOPS = 2500.0      # MI355X dense fp16/bf16 MFMA
 PEAK_HBM_GBPS = 8000.0
 GEMV_ROWS = 2                  # default per-expert row count up to which the GEMV path runs
+SHARED_GEMV_TOKENS = 16        # above this many tokens the shared expert's 16-bit MFMA tiles run inside
+                               # the routed gate/up and down launches
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic_mfma_gateup_prefill.md")
 KERNEL_SOURCES = ["mfma.hip", "gemm.h", "trellis.h", "common.h", "internal.h"]
 
@@ -242,7 +244,9 @@ def main():
     mfma_rows = int(counts[counts > GEMV_ROWS].sum())
     step_ms = {n: float(per[:, i].mean()) for i, n in enumerate(M.STEPS)}
     gu_ms = step_ms["mfma_gateup"]
-    gu_flops = 2.0 * 2 * cfg.hidden * cfg.inter * mfma_rows
+    # the gate/up launch also carries the shared expert's T rows (same H x 2I shape)
+    shared_rows = cfg.tokens if (cfg.shared and cfg.tokens > SHARED_GEMV_TOKENS) else 0
+    gu_flops = 2.0 * 2 * cfg.hidden * cfg.inter * (mfma_rows + shared_rows)
     achieved = gu_flops / (gu_ms * 1e-3) / 1e12
     print(f"[bench] prefill {ms:.3f} ms/step; steps {json.dumps({k: round(v, 4) for k, v in step_ms.items()})}",
           file=sys.stderr, flush=True)
