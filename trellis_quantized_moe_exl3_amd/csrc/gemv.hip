@@ -10,6 +10,7 @@
 // code stream is read exactly once per expert; it is the only large HBM
 // traffic of a decode-sized step.
 #include "common.h"
+#include "gemm.h"
 #include "internal.h"
 #include "trellis.h"
 
@@ -17,22 +18,34 @@ namespace moe {
 
 constexpr int kGemvU = 4;      // tile rows per prefetch group
 constexpr int kGemvPass = 2;   // routed rows per pass over the codes
-constexpr int kGemvCols = 32;  // output columns (two 16-column tiles) per block
 
 // 1532 * (row sum), the re-centring of the biased decoded values.
 constexpr float kBias2 = 1532.0f;
 
-// Deterministic block sum (256 threads) of one float per thread.
-MOE_DEV float block_sum256(float v, float *part)
+// Deterministic block reduction (256 threads) of N floats per thread, all
+// in one pair of barriers: entry i is summed, or maximised where bit i of
+// MAXMASK is set.  Every lane of the butterfly ends with the same value; the
+// four wavefront results are combined as ((w0 + w1) + w2) + w3.
+template <int N, unsigned MAXMASK = 0u>
+MOE_DEV void block_reduce256(float v[N], float (*part)[4])
 {
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
-        v += __shfl_xor(v, off, 64);
+    for (int i = 0; i < N; ++i)
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            const float o = __shfl_xor(v[i], off, 64);
+            v[i] = ((MAXMASK >> i) & 1u) ? fmaxf(v[i], o) : v[i] + o;
+        }
     __syncthreads();
     if ((threadIdx.x & 63) == 0)
-        part[threadIdx.x >> 6] = v;
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            part[i][threadIdx.x >> 6] = v[i];
     __syncthreads();
-    return ((part[0] + part[1]) + part[2]) + part[3];
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        v[i] = ((MAXMASK >> i) & 1u) ? fmaxf(fmaxf(part[i][0], part[i][1]), fmaxf(part[i][2], part[i][3]))
+                                     : ((part[i][0] + part[i][1]) + part[i][2]) + part[i][3];
 }
 
 // The fragment's eight decoded values as fp16 pairs of 2v + 1532 (exact:
@@ -57,61 +70,76 @@ MOE_DEV void frag_biased_pairs(uint32_t D0, uint32_t D1, int q, uint32_t m_lo, u
     }
 }
 
-// Stream tile rows [tk0, tk1) of the lane's fragment (two code dwords per
-// tile row, prefetched kGemvU rows ahead) and accumulate x . (2v + 1532) for
-// NR routed rows.  DOT(r, kk, wp, acc) adds the lane's 8 products of row r
-// at input rows kk + 8h .. kk + 8h + 7.
+// Stream tile rows [tk0, tk1) of the lane's fragment and accumulate
+// x . (2v + 1532) for NR routed rows.  The codes come in through a buffer
+// resource over the wavefront's 16-column tile pair: the lane's two dwords
+// sit at fixed byte offsets v0, v1 inside a tile row and the tile row at a
+// scalar offset, so a load costs no vector address arithmetic.  Two register
+// sets of kGemvU tile rows alternate, one decoding while the other fills.
+// DOT(r, kk, wp, acc) adds the lane's 8 products of row r at input rows
+// kk + 8h .. kk + 8h + 7.
 template <int K, int CB, int NR, class DOT>
-MOE_DEV void gemv_stream(const uint32_t *cb, int64_t rstride, int tk0, int tk1, int d0, int d1, int q,
-                         uint32_t m_lo, uint32_t m_hi, DOT dot, float acc[NR])
+MOE_DEV void gemv_stream(__amdgpu_buffer_rsrc_t rs, uint32_t v0, uint32_t v1, uint32_t rowb, int tk0, int tk1,
+                         int q, uint32_t m_lo, uint32_t m_hi, DOT dot, float acc[NR])
 {
-    uint32_t nx[kGemvU][2];
-    const uint32_t *base = cb + (int64_t)tk0 * rstride;
-#pragma unroll
-    for (int u = 0; u < kGemvU; ++u) {
-        nx[u][0] = base[u * rstride + d0];
-        nx[u][1] = base[u * rstride + d1];
-    }
-    for (int g = tk0; g < tk1; g += kGemvU) {
-        uint32_t cu[kGemvU][2];
+    uint32_t A[kGemvU][2], B[kGemvU][2];
+    auto load = [&](uint32_t(&buf)[kGemvU][2], int g) {
 #pragma unroll
         for (int u = 0; u < kGemvU; ++u) {
-            cu[u][0] = nx[u][0];
-            cu[u][1] = nx[u][1];
+            const int so = (g + u) * (int)rowb;
+            buf[u][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, v0, so, 0);
+            buf[u][1] = __builtin_amdgcn_raw_buffer_load_b32(rs, v1, so, 0);
         }
-        if (g + kGemvU < tk1) {
-            const uint32_t *nb = cb + (int64_t)(g + kGemvU) * rstride;
-#pragma unroll
-            for (int u = 0; u < kGemvU; ++u) {
-                nx[u][0] = nb[u * rstride + d0];
-                nx[u][1] = nb[u * rstride + d1];
-            }
-        }
+    };
+    auto run = [&](const uint32_t(&buf)[kGemvU][2], int g) {
 #pragma unroll
         for (int u = 0; u < kGemvU; ++u) {
             f16x2 wp[4];
-            frag_biased_pairs<K, CB>(cu[u][0], cu[u][1], q, m_lo, m_hi, wp);
+            frag_biased_pairs<K, CB>(buf[u][0], buf[u][1], q, m_lo, m_hi, wp);
             const int kk = 16 * (g + u);
 #pragma unroll
             for (int r = 0; r < NR; ++r)
                 acc[r] = dot(r, kk, wp, acc[r]);
         }
+    };
+    // tk0, tk1 are wavefront-uniform: every branch below is scalar
+    int g = tk0;
+    load(A, g);
+    if (g + kGemvU < tk1)
+        load(B, g + kGemvU);
+    for (; g + 2 * kGemvU <= tk1; g += 2 * kGemvU) {
+        run(A, g);
+        if (g + 2 * kGemvU < tk1)
+            load(A, g + 2 * kGemvU);
+        run(B, g + kGemvU);
+        if (g + 3 * kGemvU < tk1)
+            load(B, g + 3 * kGemvU);
     }
+    if (g < tk1)
+        run(A, g);
 }
 
-// gate/up + SwiGLU.  Block = 32 output columns (two tiles) of one expert for
-// both projections; wavefront w = 2p + kh streams projection p over input
-// half kh, so a launch has 4 wavefronts per 32 columns.  Rows are processed
-// kGemvPass at a time: x * suh of the pass's rows in LDS (fp16, both
-// projections), one v_dot2_f32_f16 per pair of weights and row.  The partial
-// sums of the two halves meet in LDS and are added in a fixed order.
+// gate/up + SwiGLU.  Block = kGuCP pairs of 16-column tiles of one expert
+// for both projections; wavefront w = 2p + j streams projection p, over
+// input half j (one tile pair) or over all inputs for tile pair j (two).
+// Rows are processed kGemvPass at a time: x * suh of the pass's rows in LDS
+// (fp16, both projections), one v_dot2_f32_f16 per pair of weights and row.
+// The partial sums of the two halves meet in LDS and are added in a fixed
+// order.
+// Two tile pairs per block measured faster than one (longer streams per
+// wavefront amortise the staging of x * suh).
+constexpr int kGuCP = 2;
+constexpr int kGuCols = 32 * kGuCP;
+constexpr int kGuKH = 2 / kGuCP;
+static_assert(kGuCP == 1 || kGuCP == 2, "gate/up tile pairs per block");
+
 template <int K, int CB>
 __global__ __launch_bounds__(256, 4) void gemv_gateup_kernel(GroupArgs a)
 {
     extern __shared__ __align__(16) unsigned char smem[];
-    __shared__ float part[4];
+    __shared__ float part[2 * kGemvPass][4];
     __shared__ float rsum[2][kGemvPass];
-    __shared__ float psum[2][2][kGemvPass][kGemvCols];   // [projection][half][row][column]
+    __shared__ float psum[2][kGuKH][kGemvPass][kGuCols];   // [projection][half][row][column]
     const int li = blockIdx.x;
     if (li >= a.hdr->n_gemv)
         return;
@@ -119,28 +147,36 @@ __global__ __launch_bounds__(256, 4) void gemv_gateup_kernel(GroupArgs a)
     const int e = a.glist[li];
     const int R = a.counts[e];
     const int p0 = a.offsets[e];
-    const int n0 = blockIdx.y * kGemvCols;
+    const int n0 = blockIdx.y * kGuCols;
     f16 *xs = (f16 *)smem;   // [2][kGemvPass][H]
 
-    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-    const int pr = w >> 1, kh = w & 1;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
+    const int pr = w >> 1, kh = kGuKH == 2 ? (w & 1) : 0, cp = kGuCP == 2 ? (w & 1) : 0;
     const int c = l & 15, ts = (l >> 4) & 1, h = l >> 5;
-    const int tn = n0 / 16 + ts;
     int d0, d1, q;
     frag_pos<K>(c, h, d0, d1, q);
+    // the block's tile pair in every tile row of expert e's projection pr
     const int64_t per_expert = (int64_t)(H / 16) * (I / 16) * Tile<K>::kDwords;
-    const uint32_t *cb = (const uint32_t *)a.codes[pr] + e * per_expert + (int64_t)tn * Tile<K>::kDwords;
-    const int64_t rstride = (int64_t)(I / 16) * Tile<K>::kDwords;
+    const uint32_t rowb = (uint32_t)(I / 16) * Tile<K>::kBytes;
+    const __amdgpu_buffer_rsrc_t rs =
+        buf_rsrc((const uint32_t *)a.codes[pr] + e * per_expert + (int64_t)(n0 / 16) * Tile<K>::kDwords,
+                 (uint32_t)(H / 16) * rowb);
+    const uint32_t tb = (uint32_t)(2 * cp + ts) * Tile<K>::kDwords;
+    const uint32_t v0 = 4u * (tb + d0), v1 = 4u * (tb + d1);
     const uint32_t m_lo = a.mcg & 0xFFFFu, m_hi = a.mcg >> 16;
-    const int ntk = H / 16, tk0 = kh * (ntk / 2), tk1 = tk0 + ntk / 2;
+    const int ntk = H / 16, tk0 = kh * (ntk / kGuKH), tk1 = tk0 + ntk / kGuKH;
 
     for (int r0 = 0; r0 < R; r0 += kGemvPass) {
         const int nr = min(kGemvPass, R - r0);
         // x * suh of the pass's rows for both projections, and their sums
+        float sums[2 * kGemvPass] = {};
+#pragma unroll
         for (int pp = 0; pp < 2; ++pp)
-            for (int r = 0; r < nr; ++r) {
+#pragma unroll
+            for (int r = 0; r < kGemvPass; ++r) {
+                if (r >= nr)
+                    continue;
                 const int t = a.sorted[p0 + r0 + r] / a.k;
-                float sum = 0.0f;
                 for (int ch = threadIdx.x; ch < H / 8; ch += 256) {
                     const f16x8 xv = *(const f16x8 *)(a.x16 + (int64_t)t * H + 8 * ch);
                     const f16x8 sv = *(const f16x8 *)(a.suh[pp] + (int64_t)e * H + 8 * ch);
@@ -148,12 +184,14 @@ __global__ __launch_bounds__(256, 4) void gemv_gateup_kernel(GroupArgs a)
                     *(f16x8 *)(xs + ((size_t)pp * kGemvPass + r) * H + 8 * ch) = pv;
 #pragma unroll
                     for (int j = 0; j < 8; ++j)
-                        sum += (float)pv[j];
+                        sums[pp * kGemvPass + r] += (float)pv[j];
                 }
-                const float tot = block_sum256(sum, part);
-                if (threadIdx.x == 0)
-                    rsum[pp][r] = tot;
             }
+        block_reduce256<2 * kGemvPass>(sums, part);
+        if (threadIdx.x == 0)
+#pragma unroll
+            for (int i = 0; i < 2 * kGemvPass; ++i)
+                rsum[i / kGemvPass][i % kGemvPass] = sums[i];
         __syncthreads();
 
         float acc[kGemvPass] = {};
@@ -167,24 +205,24 @@ __global__ __launch_bounds__(256, 4) void gemv_gateup_kernel(GroupArgs a)
         };
         // nr is the same for the whole block: branch once, not per fragment
         if (__builtin_amdgcn_readfirstlane(nr) == 2)
-            gemv_stream<K, CB, 2>(cb, rstride, tk0, tk1, d0, d1, q, m_lo, m_hi, dot, acc);
+            gemv_stream<K, CB, 2>(rs, v0, v1, rowb, tk0, tk1, q, m_lo, m_hi, dot, acc);
         else
-            gemv_stream<K, CB, 1>(cb, rstride, tk0, tk1, d0, d1, q, m_lo, m_hi, dot, acc);
+            gemv_stream<K, CB, 1>(rs, v0, v1, rowb, tk0, tk1, q, m_lo, m_hi, dot, acc);
         // the two k-halves of a tile row sit in lanes l and l ^ 32
 #pragma unroll
         for (int r = 0; r < kGemvPass; ++r) {
             const float tot = acc[r] + __shfl_xor(acc[r], 32, 64);
             if (r < nr && h == 0)
-                psum[pr][kh][r][16 * ts + c] = tot;
+                psum[pr][kh][r][32 * cp + 16 * ts + c] = tot;
         }
         __syncthreads();
-        if (threadIdx.x < nr * kGemvCols) {
-            const int r = threadIdx.x / kGemvCols, cc = threadIdx.x % kGemvCols;
+        if (threadIdx.x < nr * kGuCols) {
+            const int r = threadIdx.x / kGuCols, cc = threadIdx.x % kGuCols;
             const int col = n0 + cc;
-            const float g = (psum[0][0][r][cc] + psum[0][1][r][cc] - kBias2 * rsum[0][r]) *
-                            (f16_to_f32(a.svh[0][(int64_t)e * I + col]) * (1.0f / 128.0f));
-            const float u = (psum[1][0][r][cc] + psum[1][1][r][cc] - kBias2 * rsum[1][r]) *
-                            (f16_to_f32(a.svh[1][(int64_t)e * I + col]) * (1.0f / 128.0f));
+            const float sg = kGuKH == 2 ? psum[0][0][r][cc] + psum[0][kGuKH - 1][r][cc] : psum[0][0][r][cc];
+            const float su = kGuKH == 2 ? psum[1][0][r][cc] + psum[1][kGuKH - 1][r][cc] : psum[1][0][r][cc];
+            const float g = (sg - kBias2 * rsum[0][r]) * (f16_to_f32(a.svh[0][(int64_t)e * I + col]) * (1.0f / 128.0f));
+            const float u = (su - kBias2 * rsum[1][r]) * (f16_to_f32(a.svh[1][(int64_t)e * I + col]) * (1.0f / 128.0f));
             const float hv = silu_f(g) * u * f16_to_f32(a.suh[2][(int64_t)e * I + col]);
             a.hbuf[(int64_t)(p0 + r0 + r) * I + col] = f32_to_bf16_bits(hv);
         }
@@ -192,19 +230,29 @@ __global__ __launch_bounds__(256, 4) void gemv_gateup_kernel(GroupArgs a)
     }
 }
 
-// down + routing weight.  Block = 32 output columns (two tiles) of one
-// expert; the input rows are split into S = 4 (or 2, or 1 for small inter
-// sizes) ranges of a multiple of kGemvU tile rows, wavefront w < S streams
-// range w.  h rows of the pass in LDS
-// (fp32); one v_fma_mix_f32 per weight and row (h has fp32 range, so it stays
-// fp32); quarter sums meet in LDS and are added in a fixed order.
+// down + routing weight.  Block = kDownCP pairs of 16-column tiles of one
+// expert; the input rows are split into S = 4 / kDownCP (fewer for small
+// inter sizes) ranges of a multiple of kGemvU tile rows, and wavefront w
+// streams range w / kDownCP of tile pair w % kDownCP.  The pass's h rows sit
+// in LDS as fp16, each scaled by a power of two that brings its largest
+// magnitude into [2^14, 2^15): every bf16 value within 2^28 of the row
+// maximum converts exactly, so one v_dot2_f32_f16 per pair of weights and
+// row serves here as in gate/up, and the scale comes off the finished sum.
+// Range sums meet in LDS and are added in a fixed order.
+// Four tile pairs per block (each wavefront streams every input row of its
+// pair) measured faster than one or two.
+constexpr int kDownCP = 4;
+constexpr int kDownCols = 32 * kDownCP;
+constexpr int kDownS = 4 / kDownCP;
+
 template <int K, int CB>
 __global__ __launch_bounds__(256, 4) void gemv_down_kernel(GroupArgs a)
 {
     extern __shared__ __align__(16) unsigned char smem[];
-    __shared__ float part[4];
+    __shared__ float part[2 * kGemvPass][4];
     __shared__ float rsum[kGemvPass];
-    __shared__ float psum[4][kGemvPass][kGemvCols];   // [quarter][row][column]
+    __shared__ int rexp[kGemvPass];
+    __shared__ float psum[kDownS][kGemvPass][kDownCols];   // [range][row][column]
     const int li = blockIdx.x;
     if (li >= a.hdr->n_gemv)
         return;
@@ -212,87 +260,110 @@ __global__ __launch_bounds__(256, 4) void gemv_down_kernel(GroupArgs a)
     const int e = a.glist[li];
     const int R = a.counts[e];
     const int p0 = a.offsets[e];
-    const int m0 = blockIdx.y * kGemvCols;
-    float *hs = (float *)smem;   // [kGemvPass][I]
+    const int m0 = blockIdx.y * kDownCols;
+    f16 *hs = (f16 *)smem;   // [kGemvPass][I]
 
-    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
+    const int cp = w % kDownCP, kr = w / kDownCP;
     const int c = l & 15, ts = (l >> 4) & 1, h = l >> 5;
-    const int tn = m0 / 16 + ts;
     int d0, d1, q;
     frag_pos<K>(c, h, d0, d1, q);
     const int64_t per_expert = (int64_t)(I / 16) * (H / 16) * Tile<K>::kDwords;
-    const uint32_t *cb = (const uint32_t *)a.codes[2] + e * per_expert + (int64_t)tn * Tile<K>::kDwords;
-    const int64_t rstride = (int64_t)(H / 16) * Tile<K>::kDwords;
+    const uint32_t rowb = (uint32_t)(H / 16) * Tile<K>::kBytes;
+    const __amdgpu_buffer_rsrc_t rs =
+        buf_rsrc((const uint32_t *)a.codes[2] + e * per_expert + (int64_t)(m0 / 16) * Tile<K>::kDwords,
+                 (uint32_t)(I / 16) * rowb);
+    const uint32_t tb = (uint32_t)(2 * cp + ts) * Tile<K>::kDwords;
+    const uint32_t v0 = 4u * (tb + d0), v1 = 4u * (tb + d1);
     const uint32_t m_lo = a.mcg & 0xFFFFu, m_hi = a.mcg >> 16;
     // I % 128 == 0, so ntk is a multiple of kGemvU and S = 1 always fits
     const int ntk = I / 16;
-    const int S = (ntk % (4 * kGemvU) == 0) ? 4 : (ntk % (2 * kGemvU) == 0) ? 2 : 1;
-    const int tk0 = w * (ntk / S), tk1 = tk0 + ntk / S;
+    const int S = (kDownS >= 4 && ntk % (4 * kGemvU) == 0) ? 4 : (kDownS >= 2 && ntk % (2 * kGemvU) == 0) ? 2 : 1;
+    const int tk0 = kr * (ntk / S), tk1 = tk0 + ntk / S;
 
     for (int r0 = 0; r0 < R; r0 += kGemvPass) {
         const int nr = min(kGemvPass, R - r0);
-        for (int r = 0; r < nr; ++r) {
-            float sum = 0.0f;
+        // per row: the largest magnitude and the sum, in one reduction
+        float red[2 * kGemvPass] = {};   // [2r] max |h|, [2r + 1] sum h
+#pragma unroll
+        for (int r = 0; r < kGemvPass; ++r) {
+            if (r >= nr)
+                continue;
+            const uint16_t *hrow = a.hbuf + (int64_t)(p0 + r0 + r) * I;
             for (int ch = threadIdx.x; ch < I / 8; ch += 256) {
-                const u32x4 raw = *(const u32x4 *)(a.hbuf + (int64_t)(p0 + r0 + r) * I + 8 * ch);
-                f32x4 lo, hi;
+                const u32x4 raw = *(const u32x4 *)(hrow + 8 * ch);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const float v0 = __uint_as_float(raw[j] << 16), v1 = __uint_as_float(raw[j] & 0xFFFF0000u);
-                    sum += v0 + v1;
-                    if (j < 2) {
-                        lo[2 * j] = v0;
-                        lo[2 * j + 1] = v1;
-                    } else {
-                        hi[2 * j - 4] = v0;
-                        hi[2 * j - 3] = v1;
-                    }
+                    const float lo = __uint_as_float(raw[j] << 16), hi = __uint_as_float(raw[j] & 0xFFFF0000u);
+                    red[2 * r] = fmaxf(red[2 * r], fmaxf(fabsf(lo), fabsf(hi)));
+                    red[2 * r + 1] += lo + hi;
                 }
-                *(f32x4 *)(hs + (size_t)r * I + 8 * ch) = lo;
-                *(f32x4 *)(hs + (size_t)r * I + 8 * ch + 4) = hi;
             }
-            const float tot = block_sum256(sum, part);
-            if (threadIdx.x == 0)
-                rsum[r] = tot;
         }
+        block_reduce256<2 * kGemvPass, 0x5u>(red, part);
+        int ex[kGemvPass];
+#pragma unroll
+        for (int r = 0; r < kGemvPass; ++r) {
+            // red * 2^ex in [2^14, 2^15); zero, inf and NaN rows keep scale 1
+            const float mx = red[2 * r];
+            ex[r] = (mx > 0.0f && mx < __builtin_inff()) ? 15 - __builtin_amdgcn_frexp_expf(mx) : 0;
+        }
+#pragma unroll
+        for (int r = 0; r < kGemvPass; ++r) {
+            if (r >= nr)
+                continue;
+            const uint16_t *hrow = a.hbuf + (int64_t)(p0 + r0 + r) * I;
+            for (int ch = threadIdx.x; ch < I / 8; ch += 256) {
+                const u32x4 raw = *(const u32x4 *)(hrow + 8 * ch);
+                f16x8 hv;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    hv[2 * j] = (f16)__builtin_ldexpf(__uint_as_float(raw[j] << 16), ex[r]);
+                    hv[2 * j + 1] = (f16)__builtin_ldexpf(__uint_as_float(raw[j] & 0xFFFF0000u), ex[r]);
+                }
+                *(f16x8 *)(hs + (size_t)r * I + 8 * ch) = hv;
+            }
+        }
+        if (threadIdx.x == 0)
+#pragma unroll
+            for (int r = 0; r < kGemvPass; ++r) {
+                rsum[r] = __builtin_ldexpf(red[2 * r + 1], ex[r]);
+                rexp[r] = ex[r];
+            }
         __syncthreads();
 
         float acc[kGemvPass] = {};
-        const float *hsp = hs + 8 * h;
+        const f16 *hsp = hs + 8 * h;
         auto dot = [&](int r, int kk, const f16x2 wp[4], float s) {
-            const f32x4 v0 = *(const f32x4 *)(hsp + (size_t)r * I + kk);
-            const f32x4 v1 = *(const f32x4 *)(hsp + (size_t)r * I + kk + 4);
+            const f16x8 v = *(const f16x8 *)(hsp + (size_t)r * I + kk);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                s = __builtin_fmaf((float)wp[j][0], v0[2 * j], s);
-                s = __builtin_fmaf((float)wp[j][1], v0[2 * j + 1], s);
-            }
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                s = __builtin_fmaf((float)wp[2 + j][0], v1[2 * j], s);
-                s = __builtin_fmaf((float)wp[2 + j][1], v1[2 * j + 1], s);
-            }
+            for (int j = 0; j < 4; ++j)
+                s = __builtin_amdgcn_fdot2(wp[j], (f16x2){v[2 * j], v[2 * j + 1]}, s, false);
             return s;
         };
-        if (w < S) {
+        if (kr < S) {
             // nr is the same for the whole block: branch once, not per fragment
             if (__builtin_amdgcn_readfirstlane(nr) == 2)
-                gemv_stream<K, CB, 2>(cb, rstride, tk0, tk1, d0, d1, q, m_lo, m_hi, dot, acc);
+                gemv_stream<K, CB, 2>(rs, v0, v1, rowb, tk0, tk1, q, m_lo, m_hi, dot, acc);
             else
-                gemv_stream<K, CB, 1>(cb, rstride, tk0, tk1, d0, d1, q, m_lo, m_hi, dot, acc);
+                gemv_stream<K, CB, 1>(rs, v0, v1, rowb, tk0, tk1, q, m_lo, m_hi, dot, acc);
         }
 #pragma unroll
         for (int r = 0; r < kGemvPass; ++r) {
             const float tot = acc[r] + __shfl_xor(acc[r], 32, 64);
-            if (r < nr && h == 0)
-                psum[w][r][16 * ts + c] = tot;
+            if (kr < S && r < nr && h == 0)
+                psum[kr][r][32 * cp + 16 * ts + c] = tot;
         }
         __syncthreads();
-        if (threadIdx.x < nr * kGemvCols) {
-            const int r = threadIdx.x / kGemvCols, cc = threadIdx.x % kGemvCols;
+        if (threadIdx.x < nr * kDownCols) {
+            const int r = threadIdx.x / kDownCols, cc = threadIdx.x % kDownCols;
             const int m = m0 + cc;
-            const float tot = ((psum[0][r][cc] + psum[1][r][cc]) + (psum[2][r][cc] + psum[3][r][cc])) -
-                              kBias2 * rsum[r];
+            float raw = psum[0][r][cc];
+            if (S == 2)
+                raw += psum[1][r][cc];
+            else if (S == 4)
+                raw = (psum[0][r][cc] + psum[1][r][cc]) + (psum[2 % kDownS][r][cc] + psum[3 % kDownS][r][cc]);
+            const float tot = __builtin_ldexpf(raw - kBias2 * rsum[r], -rexp[r]);
             const int slot = a.sorted[p0 + r0 + r];
             const float svh = f16_to_f32(a.svh[2][(int64_t)e * H + m]) * (1.0f / 128.0f);
             a.ybuf[(int64_t)slot * H + m] = f32_to_bf16_bits(tot * svh * a.w[slot]);
@@ -305,7 +376,7 @@ hipError_t launch_gemv_gateup(const GroupArgs &a, int max_list, hipStream_t s)
 {
     if (max_list <= 0)
         return hipSuccess;
-    dim3 grid(max_list, a.I / kGemvCols);
+    dim3 grid(max_list, a.I / kGuCols);
     const size_t lds = sizeof(f16) * 2 * kGemvPass * a.H;
     if (a.K == 2 && a.cb == 0) gemv_gateup_kernel<2, 0><<<grid, 256, lds, s>>>(a);
     else if (a.K == 3 && a.cb == 0) gemv_gateup_kernel<3, 0><<<grid, 256, lds, s>>>(a);
@@ -320,8 +391,8 @@ hipError_t launch_gemv_down(const GroupArgs &a, int max_list, hipStream_t s)
 {
     if (max_list <= 0)
         return hipSuccess;
-    dim3 grid(max_list, a.H / kGemvCols);
-    const size_t lds = sizeof(float) * kGemvPass * a.I;
+    dim3 grid(max_list, a.H / kDownCols);
+    const size_t lds = sizeof(f16) * kGemvPass * a.I;
     if (a.K == 2 && a.cb == 0) gemv_down_kernel<2, 0><<<grid, 256, lds, s>>>(a);
     else if (a.K == 3 && a.cb == 0) gemv_down_kernel<3, 0><<<grid, 256, lds, s>>>(a);
     else if (a.K == 4 && a.cb == 0) gemv_down_kernel<4, 0><<<grid, 256, lds, s>>>(a);
