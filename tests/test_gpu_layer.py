@@ -191,3 +191,38 @@ def test_shared_expert_ragged_row_tile():
     print(f"shared ragged err={err:.3e}")
     assert err <= TOL
     assert np.isfinite(out).all()
+
+
+# The largest hidden and intermediate sizes the descriptor accepts (16384),
+# each with a small other dimension so the oracle stays quick.  H = 16384 puts
+# 128 KiB of activation rows in the gate/up GEMV block's LDS; I = 16384 puts
+# 64 KiB of h rows in the down GEMV block's.  The activations are bf16: the
+# generator's side vectors scale as 1/sqrt(H), which at H = 16384 leaves the
+# layer output near 2e-7, inside fp16's subnormal range (spacing 2^-24), where
+# an fp16 output would keep only two or three significant bits.
+_MAX_SHAPES = [(16384, 128), (256, 16384)]
+
+
+@pytest.mark.parametrize("T,flags", [(5, 0), (300, 0), (300, M.FORCE_GEMV)])
+@pytest.mark.parametrize("H,I", _MAX_SHAPES)
+def test_largest_hidden_and_inter_routed(H, I, T, flags):
+    cfg = W.BY_NAME["tiny"].replace(hidden=H, inter=I, tokens=T, act_dtype=W.DT_BF16)
+    inp = W.gen_layer(cfg)
+    out = DevLayer(inp, flags=flags).run()
+    _, _, ref = oracle.layer(inp)
+    err = rel_err(out, ref)
+    print(f"H={H} I={I} T={T} flags={flags} err={err:.3e}")
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("T", [5, 300])
+@pytest.mark.parametrize("H,I", _MAX_SHAPES)
+def test_largest_hidden_and_inter_shared(H, I, T):
+    # T = 5: shared-expert GEMV; T = 300: its tiles inside the routed launches
+    cfg = W.BY_NAME["tiny"].replace(hidden=H, inter=I, tokens=T, shared=True, act_dtype=W.DT_BF16)
+    inp = W.gen_layer(cfg)
+    out = DevLayer(inp).run()
+    _, _, ref = oracle.layer(inp)
+    err = rel_err(out, ref)
+    print(f"H={H} I={I} T={T} shared err={err:.3e}")
+    assert err <= TOL
