@@ -432,17 +432,25 @@ MOE_DEV float dot8(const f16x8 &a, const f16x8 &b, float s)
 }
 
 // Rows [0, TT) of the slab [kb, kb + kShSlab) of a [T][n] fp16 matrix into LDS
-// (zeros past T or n), by all 256 threads of the block.
+// (zeros past T or n), by all 256 threads of the block: every thread issues
+// all of its loads before its first LDS write, so the slab costs one memory
+// latency rather than one per load.
 template <int TT>
 MOE_DEV void stage_slab(const uint16_t *__restrict__ src, int T, int n, int kb, f16 *xs)
 {
-    for (int i = threadIdx.x; i < TT * kShSlab / 8; i += 256) {
+    constexpr int kPer = TT * kShSlab / 8 / 256;   // 16-byte pieces per thread
+    f16x8 v[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int i = threadIdx.x + 256 * j;
         const int t = i / (kShSlab / 8), k = kb + 8 * (i % (kShSlab / 8));
-        f16x8 v = {};
-        if (t < T && k < n)
-            v = *(const f16x8 *)(src + (int64_t)t * n + k);
-        *(f16x8 *)(xs + 8 * i) = v;
+        const bool in = t < T && k < n;
+        const f16x8 a = *(const f16x8 *)(src + (in ? (int64_t)t * n + k : 0));
+        v[j] = in ? a : (f16x8){};
     }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+        *(f16x8 *)(xs + 8 * (threadIdx.x + 256 * j)) = v[j];
 }
 
 // The lane's weight chunks of one slab of row r (zeros past the row end).
@@ -490,12 +498,15 @@ __global__ __launch_bounds__(256) void shared_gemv_gateup_kernel(const uint16_t 
         }
 #pragma unroll
         for (int t = 0; t < TT; ++t) {
+            f16x8 xv[kShChunks];
+#pragma unroll
+            for (int c = 0; c < kShChunks; ++c)
+                xv[c] = *(const f16x8 *)(xs + t * kShSlab + 512 * c + 8 * l);
             float g = acc[0][t], u = acc[1][t];
 #pragma unroll
             for (int c = 0; c < kShChunks; ++c) {
-                const f16x8 xv = *(const f16x8 *)(xs + t * kShSlab + 512 * c + 8 * l);
-                g = dot8(cg[c], xv, g);
-                u = dot8(cu[c], xv, u);
+                g = dot8(cg[c], xv[c], g);
+                u = dot8(cu[c], xv[c], u);
             }
             acc[0][t] = g;
             acc[1][t] = u;
@@ -538,10 +549,14 @@ __global__ __launch_bounds__(256) void shared_gemv_down_kernel(const uint16_t *_
             load_chunks(dr, I, kb + kShSlab, l, vd);
 #pragma unroll
         for (int t = 0; t < TT; ++t) {
+            f16x8 hv[kShChunks];
+#pragma unroll
+            for (int c = 0; c < kShChunks; ++c)
+                hv[c] = *(const f16x8 *)(hs + t * kShSlab + 512 * c + 8 * l);
             float v = acc[t];
 #pragma unroll
             for (int c = 0; c < kShChunks; ++c)
-                v = dot8(cd[c], *(const f16x8 *)(hs + t * kShSlab + 512 * c + 8 * l), v);
+                v = dot8(cd[c], hv[c], v);
             acc[t] = v;
         }
     }
