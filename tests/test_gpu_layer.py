@@ -165,16 +165,18 @@ def test_tiny_fp8_one_expert_takes_every_token():
     assert err <= TOL_FP8
 
 
-@pytest.mark.parametrize("T", [1, 3, 16])
-def test_shared_expert_gemv_token_counts(T):
-    # up to 16 tokens the shared expert runs on its GEMV kernels, which work
-    # on a power-of-two token count (3 -> 4 with one padding token); the full
-    # output is dominated by the shared expert
+@pytest.mark.parametrize("T,flags", [(1, 0), (3, 0), (8, 0), (9, 0), (16, 0), (3, M.FORCE_MFMA)])
+def test_shared_expert_gemv_token_counts(T, flags):
+    # up to 16 tokens the shared expert runs on its GEMV code, which works on
+    # a power-of-two token count (3 -> 4 with one padding token); up to 8 its
+    # blocks run inside the routed GEMV launches (T = 8 the last such count,
+    # T = 9 the first in launches of its own), unless no expert is on the GEMV
+    # path (forced MFMA).  The full output is dominated by the shared expert.
     inp = W.gen_layer(W.BY_NAME["decode"].replace(tokens=T))
-    out = DevLayer(inp).run()
+    out = DevLayer(inp, flags=flags).run()
     _, _, ref = oracle.layer(inp)
     err = rel_err(out, ref)
-    print(f"shared gemv T={T} err={err:.3e}")
+    print(f"shared gemv T={T} flags={flags} err={err:.3e}")
     assert err <= TOL and np.isfinite(out).all()
 
 
@@ -194,9 +196,10 @@ def test_shared_expert_ragged_row_tile():
 
 
 # The largest hidden and intermediate sizes the descriptor accepts (16384),
-# each with a small other dimension so the oracle stays quick.  H = 16384 puts
-# 128 KiB of activation rows in the gate/up GEMV block's LDS; I = 16384 puts
-# 64 KiB of h rows in the down GEMV block's.  The activations are bf16: the
+# each with a small other dimension so the oracle stays quick.  Past 8192 the
+# routed experts all run on MFMA tiles (the GEMV keeps its activation rows in
+# LDS up to that size), so the forced-GEMV cases check that fallback; the
+# shared expert still takes its GEMV at T = 5.  The activations are bf16: the
 # generator's side vectors scale as 1/sqrt(H), which at H = 16384 leaves the
 # layer output near 2e-7, inside fp16's subnormal range (spacing 2^-24), where
 # an fp16 output would keep only two or three significant bits.

@@ -9,6 +9,8 @@
 // streams two tiles per step and every output column stays in one lane.  The
 // code stream is read exactly once per expert; it is the only large HBM
 // traffic of a decode-sized step.
+#include <algorithm>
+
 #include "common.h"
 #include "gemm.h"
 #include "internal.h"
@@ -119,6 +121,212 @@ MOE_DEV void gemv_stream(__amdgpu_buffer_rsrc_t rs, uint32_t v0, uint32_t v1, ui
         run(A, g);
 }
 
+// ------------------------------------------------------------ shared expert GEMV
+// Dense fp16 weights in nn.Linear layout [out][in]; one wavefront per weight
+// row (gate/up: the gate and the up row of one channel), four per block.  The
+// input dimension is walked in slabs of kShSlab channels: the block stages
+// the slab of all TT token rows (a power of two >= T; rows past T and
+// channels past the end are zero) in LDS once, so every token row is read
+// from L2 once per block instead of once per wavefront, while each lane
+// streams its 16-byte weight chunks k = 8l + 512c of the slab (the next
+// slab's chunks are loaded before the current one is used).
+constexpr int kShSlab = 2048;
+constexpr int kShChunks = kShSlab / 512;
+
+// Sum over the wavefront (all lanes active), the result in every lane.
+MOE_DEV float wave_sum(float v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+MOE_DEV float dot8(const f16x8 &a, const f16x8 &b, float s)
+{
+#pragma unroll
+    for (int j = 0; j < 8; j += 2)
+        s = __builtin_amdgcn_fdot2((f16x2){a[j], a[j + 1]}, (f16x2){b[j], b[j + 1]}, s, false);
+    return s;
+}
+
+// Rows [0, TT) of the slab [kb, kb + kShSlab) of a [T][n] fp16 matrix into LDS
+// (zeros past T or n), by all 256 threads of the block: every thread issues
+// all of its loads before its first LDS write, so the slab costs one memory
+// latency rather than one per load.
+template <int TT>
+MOE_DEV void stage_slab(const uint16_t *__restrict__ src, int T, int n, int kb, f16 *xs)
+{
+    constexpr int kPer = TT * kShSlab / 8 / 256;   // 16-byte pieces per thread
+    f16x8 v[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int i = threadIdx.x + 256 * j;
+        const int t = i / (kShSlab / 8), k = kb + 8 * (i % (kShSlab / 8));
+        const bool in = t < T && k < n;
+        const f16x8 a = *(const f16x8 *)(src + (in ? (int64_t)t * n + k : 0));
+        v[j] = in ? a : (f16x8){};
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+        *(f16x8 *)(xs + 8 * (threadIdx.x + 256 * j)) = v[j];
+}
+
+// The lane's weight chunks of one slab of row r (zeros past the row end).
+MOE_DEV void load_chunks(const uint16_t *__restrict__ r, int n, int kb, int l, f16x8 v[kShChunks])
+{
+#pragma unroll
+    for (int c = 0; c < kShChunks; ++c) {
+        const int k0 = kb + 512 * c + 8 * l;
+        const f16x8 a = *(const f16x8 *)(r + (k0 < n ? k0 : 0));
+        v[c] = k0 < n ? a : (f16x8){};
+    }
+}
+
+// Shared-expert gate/up rows 4 rb .. 4 rb + 3 (xs: TT * kShSlab halves of LDS).
+template <int TT>
+MOE_DEV void shared_gateup_block(const uint16_t *__restrict__ x16, int T, int H, int I,
+                                 const uint16_t *__restrict__ wg, const uint16_t *__restrict__ wu,
+                                 uint16_t *__restrict__ sh, int rb, f16 *xs)
+{
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int n = min(rb * 4 + w, I - 1);   // spare wavefronts repeat the last row
+    float acc[2][TT];
+#pragma unroll
+    for (int t = 0; t < TT; ++t)
+        acc[0][t] = acc[1][t] = 0.0f;
+    const uint16_t *gr = wg + (int64_t)n * H, *ur = wu + (int64_t)n * H;
+    f16x8 vg[kShChunks], vu[kShChunks];
+    load_chunks(gr, H, 0, l, vg);
+    load_chunks(ur, H, 0, l, vu);
+    for (int kb = 0; kb < H; kb += kShSlab) {
+        __syncthreads();   // the previous slab's LDS reads are done
+        stage_slab<TT>(x16, T, H, kb, xs);
+        __syncthreads();
+        f16x8 cg[kShChunks], cu[kShChunks];
+#pragma unroll
+        for (int c = 0; c < kShChunks; ++c) {
+            cg[c] = vg[c];
+            cu[c] = vu[c];
+        }
+        if (kb + kShSlab < H) {
+            load_chunks(gr, H, kb + kShSlab, l, vg);
+            load_chunks(ur, H, kb + kShSlab, l, vu);
+        }
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+            f16x8 xv[kShChunks];
+#pragma unroll
+            for (int c = 0; c < kShChunks; ++c)
+                xv[c] = *(const f16x8 *)(xs + t * kShSlab + 512 * c + 8 * l);
+            float g = acc[0][t], u = acc[1][t];
+#pragma unroll
+            for (int c = 0; c < kShChunks; ++c) {
+                g = dot8(cg[c], xv[c], g);
+                u = dot8(cu[c], xv[c], u);
+            }
+            acc[0][t] = g;
+            acc[1][t] = u;
+        }
+    }
+    const bool own = rb * 4 + w < I;
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+        const float g = wave_sum(acc[0][t]), u = wave_sum(acc[1][t]);
+        if (own && l == 0 && t < T)
+            sh[(int64_t)t * I + n] = f32_to_f16_bits(silu_f(g) * u);
+    }
+}
+
+// Shared-expert down rows 4 rb .. 4 rb + 3 (hs: TT * kShSlab halves of LDS).
+template <int TT>
+MOE_DEV void shared_down_block(const uint16_t *__restrict__ sh, int T, int H, int I,
+                               const uint16_t *__restrict__ wd, float *__restrict__ sy, int rb, f16 *hs)
+{
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int m = min(rb * 4 + w, H - 1);
+    float acc[TT];
+#pragma unroll
+    for (int t = 0; t < TT; ++t)
+        acc[t] = 0.0f;
+    const uint16_t *dr = wd + (int64_t)m * I;
+    f16x8 vd[kShChunks];
+    load_chunks(dr, I, 0, l, vd);
+    for (int kb = 0; kb < I; kb += kShSlab) {
+        __syncthreads();
+        stage_slab<TT>(sh, T, I, kb, hs);
+        __syncthreads();
+        f16x8 cd[kShChunks];
+#pragma unroll
+        for (int c = 0; c < kShChunks; ++c)
+            cd[c] = vd[c];
+        if (kb + kShSlab < I)
+            load_chunks(dr, I, kb + kShSlab, l, vd);
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+            f16x8 hv[kShChunks];
+#pragma unroll
+            for (int c = 0; c < kShChunks; ++c)
+                hv[c] = *(const f16x8 *)(hs + t * kShSlab + 512 * c + 8 * l);
+            float v = acc[t];
+#pragma unroll
+            for (int c = 0; c < kShChunks; ++c)
+                v = dot8(cd[c], hv[c], v);
+            acc[t] = v;
+        }
+    }
+    const bool own = rb * 4 + w < H;
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+        const float v = wave_sum(acc[t]);
+        if (own && l == 0 && t < T)
+            sy[(int64_t)t * H + m] = v;
+    }
+}
+
+template <int TT>
+__global__ __launch_bounds__(256) void shared_gemv_gateup_kernel(const uint16_t *__restrict__ x16, int T, int H,
+                                                                 int I, const uint16_t *__restrict__ wg,
+                                                                 const uint16_t *__restrict__ wu,
+                                                                 uint16_t *__restrict__ sh)
+{
+    __shared__ __align__(16) f16 xs[TT * kShSlab];
+    shared_gateup_block<TT>(x16, T, H, I, wg, wu, sh, (int)blockIdx.x, xs);
+}
+
+template <int TT>
+__global__ __launch_bounds__(256) void shared_gemv_down_kernel(const uint16_t *__restrict__ sh, int T, int H,
+                                                               int I, const uint16_t *__restrict__ wd,
+                                                               float *__restrict__ sy)
+{
+    __shared__ __align__(16) f16 hs[TT * kShSlab];
+    shared_down_block<TT>(sh, T, H, I, wd, sy, (int)blockIdx.x, hs);
+}
+
+// Shared-expert work inside a routed GEMV launch: grid rows past the routed
+// ones carry its blocks of 4 weight rows (T <= 8: TT picked at run time).
+MOE_DEV bool shared_in_gemv(const GroupArgs &a, const SharedArgs &sa, int ny, bool gateup, f16 *smem)
+{
+    if ((int)blockIdx.y < ny)
+        return false;
+    const int rb = ((int)blockIdx.y - ny) * (int)gridDim.x + (int)blockIdx.x;
+    const int T = (int)a.T;
+    if (gateup) {
+        if (rb * 4 < a.I) {
+            if (T <= 1) shared_gateup_block<1>(sa.x16, T, a.H, a.I, sa.w[0], sa.w[1], sa.h, rb, smem);
+            else if (T <= 2) shared_gateup_block<2>(sa.x16, T, a.H, a.I, sa.w[0], sa.w[1], sa.h, rb, smem);
+            else if (T <= 4) shared_gateup_block<4>(sa.x16, T, a.H, a.I, sa.w[0], sa.w[1], sa.h, rb, smem);
+            else shared_gateup_block<8>(sa.x16, T, a.H, a.I, sa.w[0], sa.w[1], sa.h, rb, smem);
+        }
+    } else if (rb * 4 < a.H) {
+        if (T <= 1) shared_down_block<1>(sa.h, T, a.H, a.I, sa.w[2], sa.y, rb, smem);
+        else if (T <= 2) shared_down_block<2>(sa.h, T, a.H, a.I, sa.w[2], sa.y, rb, smem);
+        else if (T <= 4) shared_down_block<4>(sa.h, T, a.H, a.I, sa.w[2], sa.y, rb, smem);
+        else shared_down_block<8>(sa.h, T, a.H, a.I, sa.w[2], sa.y, rb, smem);
+    }
+    return true;
+}
+
 // gate/up + SwiGLU.  Block = kGuCP pairs of 16-column tiles of one expert
 // for both projections; wavefront w = 2p + j streams projection p, over
 // input half j (one tile pair) or over all inputs for tile pair j (two).
@@ -134,12 +342,14 @@ constexpr int kGuKH = 2 / kGuCP;
 static_assert(kGuCP == 1 || kGuCP == 2, "gate/up tile pairs per block");
 
 template <int K, int CB>
-__global__ __launch_bounds__(256, 4) void gemv_gateup_kernel(GroupArgs a)
+__global__ __launch_bounds__(256, 4) void gemv_gateup_kernel(GroupArgs a, SharedArgs sa)
 {
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ float part[2 * kGemvPass][4];
     __shared__ float rsum[2][kGemvPass];
     __shared__ float psum[2][kGuKH][kGemvPass][kGuCols];   // [projection][half][row][column]
+    if (shared_in_gemv(a, sa, a.I / kGuCols, true, (f16 *)smem))
+        return;
     const int li = blockIdx.x;
     if (li >= a.hdr->n_gemv)
         return;
@@ -246,13 +456,15 @@ constexpr int kDownCols = 32 * kDownCP;
 constexpr int kDownS = 4 / kDownCP;
 
 template <int K, int CB>
-__global__ __launch_bounds__(256, 4) void gemv_down_kernel(GroupArgs a)
+__global__ __launch_bounds__(256, 4) void gemv_down_kernel(GroupArgs a, SharedArgs sa)
 {
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ float part[2 * kGemvPass][4];
     __shared__ float rsum[kGemvPass];
     __shared__ int rexp[kGemvPass];
     __shared__ float psum[kDownS][kGemvPass][kDownCols];   // [range][row][column]
+    if (shared_in_gemv(a, sa, a.H / kDownCols, false, (f16 *)smem))
+        return;
     const int li = blockIdx.x;
     if (li >= a.hdr->n_gemv)
         return;
@@ -372,201 +584,51 @@ __global__ __launch_bounds__(256, 4) void gemv_down_kernel(GroupArgs a)
     }
 }
 
-hipError_t launch_gemv_gateup(const GroupArgs &a, int max_list, hipStream_t s)
+// Extra grid rows (of max_list blocks each) for the shared expert's blocks of
+// 4 weight rows out of n, and the LDS they need (TT token rows of a slab).
+static unsigned shared_rows_of(const SharedArgs *sh, int n, int max_list)
+{
+    return sh ? (unsigned)((n / 4 + max_list - 1) / max_list) : 0u;
+}
+
+static size_t shared_lds_of(const SharedArgs *sh, int64_t T)
+{
+    const int tt = T <= 1 ? 1 : T <= 2 ? 2 : T <= 4 ? 4 : 8;
+    return sh ? sizeof(f16) * tt * kShSlab : 0;
+}
+
+hipError_t launch_gemv_gateup(const GroupArgs &a, int max_list, const SharedArgs *sh, hipStream_t s)
 {
     if (max_list <= 0)
         return hipSuccess;
-    dim3 grid(max_list, a.I / kGuCols);
-    const size_t lds = sizeof(f16) * 2 * kGemvPass * a.H;
-    if (a.K == 2 && a.cb == 0) gemv_gateup_kernel<2, 0><<<grid, 256, lds, s>>>(a);
-    else if (a.K == 3 && a.cb == 0) gemv_gateup_kernel<3, 0><<<grid, 256, lds, s>>>(a);
-    else if (a.K == 4 && a.cb == 0) gemv_gateup_kernel<4, 0><<<grid, 256, lds, s>>>(a);
-    else if (a.K == 2) gemv_gateup_kernel<2, 1><<<grid, 256, lds, s>>>(a);
-    else if (a.K == 3) gemv_gateup_kernel<3, 1><<<grid, 256, lds, s>>>(a);
-    else gemv_gateup_kernel<4, 1><<<grid, 256, lds, s>>>(a);
+    // I % 128 == 0: whole blocks of 4 shared rows
+    dim3 grid(max_list, a.I / kGuCols + shared_rows_of(sh, a.I, max_list));
+    const size_t lds = std::max(sizeof(f16) * 2 * kGemvPass * a.H, shared_lds_of(sh, a.T));
+    const SharedArgs sa = sh ? *sh : SharedArgs{};
+    if (a.K == 2 && a.cb == 0) gemv_gateup_kernel<2, 0><<<grid, 256, lds, s>>>(a, sa);
+    else if (a.K == 3 && a.cb == 0) gemv_gateup_kernel<3, 0><<<grid, 256, lds, s>>>(a, sa);
+    else if (a.K == 4 && a.cb == 0) gemv_gateup_kernel<4, 0><<<grid, 256, lds, s>>>(a, sa);
+    else if (a.K == 2) gemv_gateup_kernel<2, 1><<<grid, 256, lds, s>>>(a, sa);
+    else if (a.K == 3) gemv_gateup_kernel<3, 1><<<grid, 256, lds, s>>>(a, sa);
+    else gemv_gateup_kernel<4, 1><<<grid, 256, lds, s>>>(a, sa);
     return hipGetLastError();
 }
 
-hipError_t launch_gemv_down(const GroupArgs &a, int max_list, hipStream_t s)
+hipError_t launch_gemv_down(const GroupArgs &a, int max_list, const SharedArgs *sh, hipStream_t s)
 {
     if (max_list <= 0)
         return hipSuccess;
-    dim3 grid(max_list, a.H / kDownCols);
-    const size_t lds = sizeof(f16) * kGemvPass * a.I;
-    if (a.K == 2 && a.cb == 0) gemv_down_kernel<2, 0><<<grid, 256, lds, s>>>(a);
-    else if (a.K == 3 && a.cb == 0) gemv_down_kernel<3, 0><<<grid, 256, lds, s>>>(a);
-    else if (a.K == 4 && a.cb == 0) gemv_down_kernel<4, 0><<<grid, 256, lds, s>>>(a);
-    else if (a.K == 2) gemv_down_kernel<2, 1><<<grid, 256, lds, s>>>(a);
-    else if (a.K == 3) gemv_down_kernel<3, 1><<<grid, 256, lds, s>>>(a);
-    else gemv_down_kernel<4, 1><<<grid, 256, lds, s>>>(a);
+    // H % 256 == 0: whole blocks of 4 shared rows
+    dim3 grid(max_list, a.H / kDownCols + shared_rows_of(sh, a.H, max_list));
+    const size_t lds = std::max(sizeof(f16) * kGemvPass * a.I, shared_lds_of(sh, a.T));
+    const SharedArgs sa = sh ? *sh : SharedArgs{};
+    if (a.K == 2 && a.cb == 0) gemv_down_kernel<2, 0><<<grid, 256, lds, s>>>(a, sa);
+    else if (a.K == 3 && a.cb == 0) gemv_down_kernel<3, 0><<<grid, 256, lds, s>>>(a, sa);
+    else if (a.K == 4 && a.cb == 0) gemv_down_kernel<4, 0><<<grid, 256, lds, s>>>(a, sa);
+    else if (a.K == 2) gemv_down_kernel<2, 1><<<grid, 256, lds, s>>>(a, sa);
+    else if (a.K == 3) gemv_down_kernel<3, 1><<<grid, 256, lds, s>>>(a, sa);
+    else gemv_down_kernel<4, 1><<<grid, 256, lds, s>>>(a, sa);
     return hipGetLastError();
-}
-
-// ------------------------------------------------------------ shared expert GEMV
-// Dense fp16 weights in nn.Linear layout [out][in]; one wavefront per weight
-// row (gate/up: the gate and the up row of one channel), four per block.  The
-// input dimension is walked in slabs of kShSlab channels: the block stages
-// the slab of all TT token rows (a power of two >= T; rows past T and
-// channels past the end are zero) in LDS once, so every token row is read
-// from L2 once per block instead of once per wavefront, while each lane
-// streams its 16-byte weight chunks k = 8l + 512c of the slab (the next
-// slab's chunks are loaded before the current one is used).
-constexpr int kShSlab = 2048;
-constexpr int kShChunks = kShSlab / 512;
-
-// Sum over the wavefront (all lanes active), the result in every lane.
-MOE_DEV float wave_sum(float v)
-{
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
-        v += __shfl_xor(v, off, 64);
-    return v;
-}
-
-MOE_DEV float dot8(const f16x8 &a, const f16x8 &b, float s)
-{
-#pragma unroll
-    for (int j = 0; j < 8; j += 2)
-        s = __builtin_amdgcn_fdot2((f16x2){a[j], a[j + 1]}, (f16x2){b[j], b[j + 1]}, s, false);
-    return s;
-}
-
-// Rows [0, TT) of the slab [kb, kb + kShSlab) of a [T][n] fp16 matrix into LDS
-// (zeros past T or n), by all 256 threads of the block: every thread issues
-// all of its loads before its first LDS write, so the slab costs one memory
-// latency rather than one per load.
-template <int TT>
-MOE_DEV void stage_slab(const uint16_t *__restrict__ src, int T, int n, int kb, f16 *xs)
-{
-    constexpr int kPer = TT * kShSlab / 8 / 256;   // 16-byte pieces per thread
-    f16x8 v[kPer];
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-        const int i = threadIdx.x + 256 * j;
-        const int t = i / (kShSlab / 8), k = kb + 8 * (i % (kShSlab / 8));
-        const bool in = t < T && k < n;
-        const f16x8 a = *(const f16x8 *)(src + (in ? (int64_t)t * n + k : 0));
-        v[j] = in ? a : (f16x8){};
-    }
-#pragma unroll
-    for (int j = 0; j < kPer; ++j)
-        *(f16x8 *)(xs + 8 * (threadIdx.x + 256 * j)) = v[j];
-}
-
-// The lane's weight chunks of one slab of row r (zeros past the row end).
-MOE_DEV void load_chunks(const uint16_t *__restrict__ r, int n, int kb, int l, f16x8 v[kShChunks])
-{
-#pragma unroll
-    for (int c = 0; c < kShChunks; ++c) {
-        const int k0 = kb + 512 * c + 8 * l;
-        const f16x8 a = *(const f16x8 *)(r + (k0 < n ? k0 : 0));
-        v[c] = k0 < n ? a : (f16x8){};
-    }
-}
-
-template <int TT>
-__global__ __launch_bounds__(256) void shared_gemv_gateup_kernel(const uint16_t *__restrict__ x16,
-                                                                 int T, int H, int I,
-                                                                 const uint16_t *__restrict__ wg,
-                                                                 const uint16_t *__restrict__ wu,
-                                                                 uint16_t *__restrict__ sh)
-{
-    __shared__ __align__(16) f16 xs[TT * kShSlab];
-    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-    const int n = min(blockIdx.x * 4 + w, I - 1);   // spare wavefronts repeat the last row
-    float acc[2][TT];
-#pragma unroll
-    for (int t = 0; t < TT; ++t)
-        acc[0][t] = acc[1][t] = 0.0f;
-    const uint16_t *gr = wg + (int64_t)n * H, *ur = wu + (int64_t)n * H;
-    f16x8 vg[kShChunks], vu[kShChunks];
-    load_chunks(gr, H, 0, l, vg);
-    load_chunks(ur, H, 0, l, vu);
-    for (int kb = 0; kb < H; kb += kShSlab) {
-        __syncthreads();   // the previous slab's LDS reads are done
-        stage_slab<TT>(x16, T, H, kb, xs);
-        __syncthreads();
-        f16x8 cg[kShChunks], cu[kShChunks];
-#pragma unroll
-        for (int c = 0; c < kShChunks; ++c) {
-            cg[c] = vg[c];
-            cu[c] = vu[c];
-        }
-        if (kb + kShSlab < H) {
-            load_chunks(gr, H, kb + kShSlab, l, vg);
-            load_chunks(ur, H, kb + kShSlab, l, vu);
-        }
-#pragma unroll
-        for (int t = 0; t < TT; ++t) {
-            f16x8 xv[kShChunks];
-#pragma unroll
-            for (int c = 0; c < kShChunks; ++c)
-                xv[c] = *(const f16x8 *)(xs + t * kShSlab + 512 * c + 8 * l);
-            float g = acc[0][t], u = acc[1][t];
-#pragma unroll
-            for (int c = 0; c < kShChunks; ++c) {
-                g = dot8(cg[c], xv[c], g);
-                u = dot8(cu[c], xv[c], u);
-            }
-            acc[0][t] = g;
-            acc[1][t] = u;
-        }
-    }
-    const bool own = blockIdx.x * 4 + w < I;
-#pragma unroll
-    for (int t = 0; t < TT; ++t) {
-        const float g = wave_sum(acc[0][t]), u = wave_sum(acc[1][t]);
-        if (own && l == 0 && t < T)
-            sh[(int64_t)t * I + n] = f32_to_f16_bits(silu_f(g) * u);
-    }
-}
-
-template <int TT>
-__global__ __launch_bounds__(256) void shared_gemv_down_kernel(const uint16_t *__restrict__ sh, int T,
-                                                               int H, int I,
-                                                               const uint16_t *__restrict__ wd,
-                                                               float *__restrict__ sy)
-{
-    __shared__ __align__(16) f16 hs[TT * kShSlab];
-    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-    const int m = min(blockIdx.x * 4 + w, H - 1);
-    float acc[TT];
-#pragma unroll
-    for (int t = 0; t < TT; ++t)
-        acc[t] = 0.0f;
-    const uint16_t *dr = wd + (int64_t)m * I;
-    f16x8 vd[kShChunks];
-    load_chunks(dr, I, 0, l, vd);
-    for (int kb = 0; kb < I; kb += kShSlab) {
-        __syncthreads();
-        stage_slab<TT>(sh, T, I, kb, hs);
-        __syncthreads();
-        f16x8 cd[kShChunks];
-#pragma unroll
-        for (int c = 0; c < kShChunks; ++c)
-            cd[c] = vd[c];
-        if (kb + kShSlab < I)
-            load_chunks(dr, I, kb + kShSlab, l, vd);
-#pragma unroll
-        for (int t = 0; t < TT; ++t) {
-            f16x8 hv[kShChunks];
-#pragma unroll
-            for (int c = 0; c < kShChunks; ++c)
-                hv[c] = *(const f16x8 *)(hs + t * kShSlab + 512 * c + 8 * l);
-            float v = acc[t];
-#pragma unroll
-            for (int c = 0; c < kShChunks; ++c)
-                v = dot8(cd[c], hv[c], v);
-            acc[t] = v;
-        }
-    }
-    const bool own = blockIdx.x * 4 + w < H;
-#pragma unroll
-    for (int t = 0; t < TT; ++t) {
-        const float v = wave_sum(acc[t]);
-        if (own && l == 0 && t < T)
-            sy[(int64_t)t * H + m] = v;
-    }
 }
 
 template <int TT>

@@ -27,6 +27,9 @@ constexpr int kGemvMaxInter = 8192;
 constexpr int kSmallRouteTokens = 64;
 // Tokens up to which the shared expert runs as a GEMV.
 constexpr int kSharedGemvMaxTokens = 16;
+// Up to this many tokens the shared-expert GEMV blocks run inside the routed
+// GEMV launches (the bound keeps their registers within those kernels').
+constexpr int kSharedGemvMergeTokens = 8;
 
 // Small header at the start of the workspace, written by the segment kernels.
 struct WsHeader {
@@ -81,17 +84,19 @@ struct GroupArgs {
 };
 
 hipError_t launch_convert_x(const uint16_t *x, bool bf16, int64_t n, uint16_t *x16, hipStream_t s);
-hipError_t launch_gemv_gateup(const GroupArgs &a, int max_list, hipStream_t s);
-hipError_t launch_gemv_down(const GroupArgs &a, int max_list, hipStream_t s);
-// The dense shared expert, when its tiles ride along in the routed MFMA
-// launches (x16 [T][H] fp16, w = gate, up, down nn.Linear fp16, h [T][I] fp16
-// gate/up output, y [T][H] fp32 down output).
+// The dense shared expert, when its work rides along in the routed MFMA or
+// GEMV launches (x16 [T][H] fp16, w = gate, up, down nn.Linear fp16, h [T][I]
+// fp16 gate/up output, y [T][H] fp32 down output).
 struct SharedArgs {
     const uint16_t *x16;
     const uint16_t *w[3];
     uint16_t *h;
     float *y;
 };
+// With sh set (1 <= T <= kSharedGemvMergeTokens), the shared expert's GEMV
+// rows run as extra blocks after the routed ones.
+hipError_t launch_gemv_gateup(const GroupArgs &a, int max_list, const SharedArgs *sh, hipStream_t s);
+hipError_t launch_gemv_down(const GroupArgs &a, int max_list, const SharedArgs *sh, hipStream_t s);
 hipError_t launch_mfma_gateup(const GroupArgs &a, int max_tiles, const SharedArgs *sh, hipStream_t s);
 hipError_t launch_mfma_down(const GroupArgs &a, int max_tiles, const SharedArgs *sh, hipStream_t s);
 hipError_t launch_quant_gateup(const GroupArgs &a, int64_t n, hipStream_t s);

@@ -357,38 +357,43 @@ static int run_layer(const moe_exl3_desc *desc, const moe_exl3_weights *weights,
     const int max_list = g > 0 ? (int)std::min<int64_t>(d.n_experts, n) : 0;
 
     // The shared expert: a dot-product GEMV for up to kSharedGemvMaxTokens
-    // tokens; otherwise its dense tiles ride along in the routed 16-bit MFMA
-    // launches (filling the CUs their last routed tiles leave idle), or, on the
-    // fp8 path, run in launches of their own.
+    // tokens, whose blocks run at the end of the routed GEMV launches for up to
+    // kSharedGemvMergeTokens (the memory-bound shared rows fill the second,
+    // partly empty round of the VALU-bound routed blocks); otherwise its dense
+    // tiles ride along in the routed 16-bit MFMA launches (filling the CUs
+    // their last routed tiles leave idle), or, on the fp8 path, run in
+    // launches of their own.
     const bool shared = d.flags & MOE_EXL3_HAS_SHARED;
     uint16_t *sh = shared ? at<uint16_t>(ws, p.sh) : nullptr;
     float *sy = shared ? at<float>(ws, p.sy) : nullptr;
     SharedArgs sa{};
-    const bool merged = shared && !f8 && T > kSharedGemvMaxTokens;
-    if (merged) {
+    if (shared) {
         sa.x16 = x16;
         for (int i = 0; i < 3; ++i)
             sa.w[i] = wt.shared_w[i];
         sa.h = sh;
         sa.y = sy;
     }
+    const bool merged = shared && !f8 && T > kSharedGemvMaxTokens;
+    const bool gemv_merged = shared && T <= kSharedGemvMergeTokens && max_list > 0;
     const SharedArgs *sap = merged ? &sa : nullptr;
+    const SharedArgs *sgp = gemv_merged ? &sa : nullptr;
 
     // fp8: the activation rows are quantized at the end of the convert step,
     // the h rows at the start of the GEMV down step
     if (f8 && launch_quant_gateup(ga, n, s) != hipSuccess)
         return MOE_EXL3_ERR_HIP;
-    if (!mk.mark(MOE_EXL3_STEP_GEMV_GATEUP) || launch_gemv_gateup(ga, max_list, s) != hipSuccess ||
+    if (!mk.mark(MOE_EXL3_STEP_GEMV_GATEUP) || launch_gemv_gateup(ga, max_list, sgp, s) != hipSuccess ||
         !mk.mark(MOE_EXL3_STEP_MFMA_GATEUP) ||
         (f8 ? launch_mfma8_gateup(ga, p.max_tiles, s) : launch_mfma_gateup(ga, p.max_tiles, sap, s)) != hipSuccess ||
         !mk.mark(MOE_EXL3_STEP_GEMV_DOWN) || (f8 && launch_quant_h(ga, n, s) != hipSuccess) ||
-        launch_gemv_down(ga, max_list, s) != hipSuccess ||
+        launch_gemv_down(ga, max_list, sgp, s) != hipSuccess ||
         !mk.mark(MOE_EXL3_STEP_MFMA_DOWN) ||
         (f8 ? launch_mfma8_down(ga, p.max_tiles, s) : launch_mfma_down(ga, p.max_tiles, sap, s)) != hipSuccess ||
         !mk.mark(MOE_EXL3_STEP_SHARED))
         return MOE_EXL3_ERR_HIP;
 
-    if (shared && !merged) {
+    if (shared && !merged && !gemv_merged) {
         hipError_t e;
         if (T <= kSharedGemvMaxTokens)
             e = launch_shared_gemv(x16, (int)T, d.hidden, d.inter, wt.shared_w[0], wt.shared_w[1],
