@@ -304,12 +304,13 @@ __global__ __launch_bounds__(256) void shared_gemv_down_kernel(const uint16_t *_
 }
 
 // Shared-expert work inside a routed GEMV launch: grid rows past the routed
-// ones carry its blocks of 4 weight rows (T <= 8: TT picked at run time).
-MOE_DEV bool shared_in_gemv(const GroupArgs &a, const SharedArgs &sa, int ny, bool gateup, f16 *smem)
+// experts' (blockIdx.y >= max_list) carry its blocks of 4 weight rows (T <= 8:
+// TT picked at run time).
+MOE_DEV bool shared_in_gemv(const GroupArgs &a, const SharedArgs &sa, int max_list, bool gateup, f16 *smem)
 {
-    if ((int)blockIdx.y < ny)
+    if ((int)blockIdx.y < max_list)
         return false;
-    const int rb = ((int)blockIdx.y - ny) * (int)gridDim.x + (int)blockIdx.x;
+    const int rb = ((int)blockIdx.y - max_list) * (int)gridDim.x + (int)blockIdx.x;
     const int T = (int)a.T;
     if (gateup) {
         if (rb * 4 < a.I) {
@@ -342,22 +343,24 @@ constexpr int kGuKH = 2 / kGuCP;
 static_assert(kGuCP == 1 || kGuCP == 2, "gate/up tile pairs per block");
 
 template <int K, int CB>
-__global__ __launch_bounds__(256, 4) void gemv_gateup_kernel(GroupArgs a, SharedArgs sa)
+__global__ __launch_bounds__(256, 4) void gemv_gateup_kernel(GroupArgs a, int max_list, SharedArgs sa)
 {
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ float part[2 * kGemvPass][4];
     __shared__ float rsum[2][kGemvPass];
     __shared__ float psum[2][kGuKH][kGemvPass][kGuCols];   // [projection][half][row][column]
-    if (shared_in_gemv(a, sa, a.I / kGuCols, true, (f16 *)smem))
+    if (shared_in_gemv(a, sa, max_list, true, (f16 *)smem))
         return;
-    const int li = blockIdx.x;
+    // experts vary slowest: the blocks of the listed experts dispatch before
+    // those past the list's end, which only check the count and leave
+    const int li = blockIdx.y;
     if (li >= a.hdr->n_gemv)
         return;
     const int H = a.H, I = a.I;
     const int e = a.glist[li];
     const int R = a.counts[e];
     const int p0 = a.offsets[e];
-    const int n0 = blockIdx.y * kGuCols;
+    const int n0 = blockIdx.x * kGuCols;
     f16 *xs = (f16 *)smem;   // [2][kGemvPass][H]
 
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
@@ -456,23 +459,23 @@ constexpr int kDownCols = 32 * kDownCP;
 constexpr int kDownS = 4 / kDownCP;
 
 template <int K, int CB>
-__global__ __launch_bounds__(256, 4) void gemv_down_kernel(GroupArgs a, SharedArgs sa)
+__global__ __launch_bounds__(256, 4) void gemv_down_kernel(GroupArgs a, int max_list, SharedArgs sa)
 {
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ float part[2 * kGemvPass][4];
     __shared__ float rsum[kGemvPass];
     __shared__ int rexp[kGemvPass];
     __shared__ float psum[kDownS][kGemvPass][kDownCols];   // [range][row][column]
-    if (shared_in_gemv(a, sa, a.H / kDownCols, false, (f16 *)smem))
+    if (shared_in_gemv(a, sa, max_list, false, (f16 *)smem))
         return;
-    const int li = blockIdx.x;
+    const int li = blockIdx.y;
     if (li >= a.hdr->n_gemv)
         return;
     const int H = a.H, I = a.I;
     const int e = a.glist[li];
     const int R = a.counts[e];
     const int p0 = a.offsets[e];
-    const int m0 = blockIdx.y * kDownCols;
+    const int m0 = blockIdx.x * kDownCols;
     f16 *hs = (f16 *)smem;   // [kGemvPass][I]
 
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
@@ -584,11 +587,11 @@ __global__ __launch_bounds__(256, 4) void gemv_down_kernel(GroupArgs a, SharedAr
     }
 }
 
-// Extra grid rows (of max_list blocks each) for the shared expert's blocks of
-// 4 weight rows out of n, and the LDS they need (TT token rows of a slab).
-static unsigned shared_rows_of(const SharedArgs *sh, int n, int max_list)
+// Extra grid rows (of ncols blocks each) for the shared expert's blocks of 4
+// weight rows out of n, and the LDS they need (TT token rows of a slab).
+static unsigned shared_rows_of(const SharedArgs *sh, int n, int ncols)
 {
-    return sh ? (unsigned)((n / 4 + max_list - 1) / max_list) : 0u;
+    return sh ? (unsigned)((n / 4 + ncols - 1) / ncols) : 0u;
 }
 
 static size_t shared_lds_of(const SharedArgs *sh, int64_t T)
@@ -602,15 +605,15 @@ hipError_t launch_gemv_gateup(const GroupArgs &a, int max_list, const SharedArgs
     if (max_list <= 0)
         return hipSuccess;
     // I % 128 == 0: whole blocks of 4 shared rows
-    dim3 grid(max_list, a.I / kGuCols + shared_rows_of(sh, a.I, max_list));
+    dim3 grid(a.I / kGuCols, max_list + shared_rows_of(sh, a.I, a.I / kGuCols));
     const size_t lds = std::max(sizeof(f16) * 2 * kGemvPass * a.H, shared_lds_of(sh, a.T));
     const SharedArgs sa = sh ? *sh : SharedArgs{};
-    if (a.K == 2 && a.cb == 0) gemv_gateup_kernel<2, 0><<<grid, 256, lds, s>>>(a, sa);
-    else if (a.K == 3 && a.cb == 0) gemv_gateup_kernel<3, 0><<<grid, 256, lds, s>>>(a, sa);
-    else if (a.K == 4 && a.cb == 0) gemv_gateup_kernel<4, 0><<<grid, 256, lds, s>>>(a, sa);
-    else if (a.K == 2) gemv_gateup_kernel<2, 1><<<grid, 256, lds, s>>>(a, sa);
-    else if (a.K == 3) gemv_gateup_kernel<3, 1><<<grid, 256, lds, s>>>(a, sa);
-    else gemv_gateup_kernel<4, 1><<<grid, 256, lds, s>>>(a, sa);
+    if (a.K == 2 && a.cb == 0) gemv_gateup_kernel<2, 0><<<grid, 256, lds, s>>>(a, max_list, sa);
+    else if (a.K == 3 && a.cb == 0) gemv_gateup_kernel<3, 0><<<grid, 256, lds, s>>>(a, max_list, sa);
+    else if (a.K == 4 && a.cb == 0) gemv_gateup_kernel<4, 0><<<grid, 256, lds, s>>>(a, max_list, sa);
+    else if (a.K == 2) gemv_gateup_kernel<2, 1><<<grid, 256, lds, s>>>(a, max_list, sa);
+    else if (a.K == 3) gemv_gateup_kernel<3, 1><<<grid, 256, lds, s>>>(a, max_list, sa);
+    else gemv_gateup_kernel<4, 1><<<grid, 256, lds, s>>>(a, max_list, sa);
     return hipGetLastError();
 }
 
@@ -619,15 +622,15 @@ hipError_t launch_gemv_down(const GroupArgs &a, int max_list, const SharedArgs *
     if (max_list <= 0)
         return hipSuccess;
     // H % 256 == 0: whole blocks of 4 shared rows
-    dim3 grid(max_list, a.H / kDownCols + shared_rows_of(sh, a.H, max_list));
+    dim3 grid(a.H / kDownCols, max_list + shared_rows_of(sh, a.H, a.H / kDownCols));
     const size_t lds = std::max(sizeof(f16) * kGemvPass * a.I, shared_lds_of(sh, a.T));
     const SharedArgs sa = sh ? *sh : SharedArgs{};
-    if (a.K == 2 && a.cb == 0) gemv_down_kernel<2, 0><<<grid, 256, lds, s>>>(a, sa);
-    else if (a.K == 3 && a.cb == 0) gemv_down_kernel<3, 0><<<grid, 256, lds, s>>>(a, sa);
-    else if (a.K == 4 && a.cb == 0) gemv_down_kernel<4, 0><<<grid, 256, lds, s>>>(a, sa);
-    else if (a.K == 2) gemv_down_kernel<2, 1><<<grid, 256, lds, s>>>(a, sa);
-    else if (a.K == 3) gemv_down_kernel<3, 1><<<grid, 256, lds, s>>>(a, sa);
-    else gemv_down_kernel<4, 1><<<grid, 256, lds, s>>>(a, sa);
+    if (a.K == 2 && a.cb == 0) gemv_down_kernel<2, 0><<<grid, 256, lds, s>>>(a, max_list, sa);
+    else if (a.K == 3 && a.cb == 0) gemv_down_kernel<3, 0><<<grid, 256, lds, s>>>(a, max_list, sa);
+    else if (a.K == 4 && a.cb == 0) gemv_down_kernel<4, 0><<<grid, 256, lds, s>>>(a, max_list, sa);
+    else if (a.K == 2) gemv_down_kernel<2, 1><<<grid, 256, lds, s>>>(a, max_list, sa);
+    else if (a.K == 3) gemv_down_kernel<3, 1><<<grid, 256, lds, s>>>(a, max_list, sa);
+    else gemv_down_kernel<4, 1><<<grid, 256, lds, s>>>(a, max_list, sa);
     return hipGetLastError();
 }
 
