@@ -692,14 +692,23 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
         for (int q = 0; q < 8; ++q)
             s[q] = 0.0f;
     }
-    for (int j = 0; j < k; ++j) {
-        const u32x4 v = *(const u32x4 *)(ybuf + (t * k + j) * H + m);
+    // all k slot rows are loaded before the first add (k <= 16), then summed
+    // in slot order
+    constexpr int kMaxK = 16;
+    u32x4 v[kMaxK];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            s[2 * q] += __uint_as_float(v[q] << 16);
-            s[2 * q + 1] += __uint_as_float(v[q] & 0xFFFF0000u);
+    for (int j = 0; j < kMaxK; ++j)
+        if (j < k)
+            v[j] = *(const u32x4 *)(ybuf + (t * k + j) * H + m);
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j)
+        if (j < k) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                s[2 * q] += __uint_as_float(v[j][q] << 16);
+                s[2 * q + 1] += __uint_as_float(v[j][q] & 0xFFFF0000u);
+            }
         }
-    }
     u32x4 o;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
