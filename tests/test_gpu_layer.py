@@ -84,6 +84,26 @@ def test_decode_step():
     assert err_r <= TOL and err <= TOL
 
 
+@pytest.mark.parametrize("K,codebook", [(3, W.CB_MCG), (4, W.CB_MCG), (4, W.CB_MCG_E4M3)])
+def test_decode_step_code_widths(K, codebook):
+    # the 8-token step at 3 and 4 bits per weight and with the E4M3 codebook:
+    # every routed expert on the GEMV path or a small MFMA tile, the shared
+    # expert's GEMV blocks inside the routed GEMV launches
+    # (the full layer, dominated by the shared expert, on two tokens: the
+    # oracle then decodes only the experts those two route to)
+    inp = W.gen_layer(W.BY_NAME["decode"].replace(K=K, codebook=codebook))
+    routed = _routed_only(inp)
+    out_r = DevLayer(routed).run()
+    _, _, ref_r = oracle.layer(routed)
+    sample = [0, 7]
+    out = DevLayer(inp).run()
+    _, _, ref = oracle.layer(inp, sample)
+    err_r, err = rel_err(out_r, ref_r), rel_err(out[sample], ref)
+    print(f"decode K={K} cb={codebook} routed err={err_r:.3e} full err={err:.3e}")
+    assert err_r <= TOL and err <= TOL
+    assert np.isfinite(out).all() and np.isfinite(out_r).all()
+
+
 def _sampled(name, sample, flags=0, tol=TOL):
     cfg = W.BY_NAME[name]
     inp = W.gen_layer(cfg)
