@@ -216,10 +216,11 @@ def test_shared_expert_ragged_row_tile():
 
 
 # The largest hidden and intermediate sizes the descriptor accepts (16384),
-# each with a small other dimension so the oracle stays quick.  Past 8192 the
-# routed experts all run on MFMA tiles (the GEMV keeps its activation rows in
-# LDS up to that size), so the forced-GEMV cases check that fallback; the
-# shared expert still takes its GEMV at T = 5.  The activations are bf16: the
+# each with a small other dimension so the oracle stays quick.  Past hidden
+# 8192 the routed experts all run on MFMA tiles (the gate/up GEMV keeps two
+# projections' activation rows in LDS up to that size), so the forced-GEMV
+# case checks that fallback; at inter 16384 the down GEMV holds 64 KiB of h
+# rows in LDS.  The shared expert takes its GEMV at T = 5.  The activations are bf16: the
 # generator's side vectors scale as 1/sqrt(H), which at H = 16384 leaves the
 # layer output near 2e-7, inside fp16's subnormal range (spacing 2^-24), where
 # an fp16 output would keep only two or three significant bits.

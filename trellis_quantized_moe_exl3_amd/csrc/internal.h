@@ -19,9 +19,11 @@ constexpr int kSegChunk = 2048;
 // pass re-stream the expert's codes), and the default threshold.
 constexpr int kGemvMaxRows = 8;
 constexpr int kGemvDefaultRows = 2;
-// The GEMV blocks keep two rows of activations in LDS within 64 KiB.
+// The GEMV blocks keep two rows of activations in LDS within 64 KiB: fp16
+// x * suh of both projections for gate/up (8 H bytes), fp16 h for down
+// (4 I bytes).
 constexpr int kGemvMaxHidden = 8192;
-constexpr int kGemvMaxInter = 8192;
+constexpr int kGemvMaxInter = 16384;
 // Tokens up to which one block runs the whole routing tail (top-k, segment
 // tables, activation copy) in a single launch.
 constexpr int kSmallRouteTokens = 64;

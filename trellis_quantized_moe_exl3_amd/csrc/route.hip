@@ -75,9 +75,10 @@ __global__ __launch_bounds__(256) void route_logits_kernel(const uint16_t *__res
                 p[a][b][j] = 0.0f;
     // rows past the last token or expert read row 0 (in bounds); their sums
     // are never stored.  With few pairs per lane (few tokens) the loads stay
-    // predicated, which lets the compiler keep more iterations in flight.
+    // predicated and 16 iterations are unrolled, so a wavefront (one of only a
+    // few hundred) keeps 16 chunks of loads in flight.
     constexpr bool kWide = TPL * EPL >= 8;
-    constexpr int kUnroll = kWide ? 2 : 4;
+    constexpr int kUnroll = kWide ? 2 : 16;
 #pragma unroll kUnroll
     for (int i = 0; i < H / 64; ++i) {
         float xv[TPL][8];
