@@ -71,6 +71,9 @@ struct GemmArgs {
     // routed_grid on run dense tiles with dnslices slices per row tile
     int routed_grid;
     int dnslices;
+    // 4 when every routed tile has at most 64 rows (T <= 64): each block then
+    // covers 4 column slices (CM = 4) and only a quarter of the slices launch
+    int sdiv;
 };
 
 template <int MODE>
@@ -409,9 +412,11 @@ MOE_DEV void tile_body(GemmTile<MODE, K, CB> &g, const GemmArgs &args, int n0,
     static_assert(NB <= kMB, "accumulator blocks");
 }
 
-// One block's work: block L of a grid with `nslices` column slices per row tile.
+// One block's work: block L of a grid with `nslices` column slices per row
+// tile, of which nslices / sdiv are launched (sdiv > 1 only where every tile
+// takes sdiv column groups per wavefront).
 template <int MODE, int K, int CB>
-MOE_DEV void block_body(const GemmArgs &args, int L, int nslices, uint16_t *ring0, uint16_t *ring1,
+MOE_DEV void block_body(const GemmArgs &args, int L, int nslices, int sdiv, uint16_t *ring0, uint16_t *ring1,
                         uint16_t *ring2, uint16_t *ring3)
 {
     using TR = ModeTraits<MODE>;
@@ -426,7 +431,7 @@ MOE_DEV void block_body(const GemmArgs &args, int L, int nslices, uint16_t *ring
 
     // ---- work tile; `nslices` counts column slices at one group per wave
     int ti, slice;
-    xcd_map(L, nslices, ti, slice);
+    xcd_map(L, nslices / sdiv, ti, slice);
     g.e = 0;
     g.p0 = 0;
     g.t0 = 0;
@@ -543,11 +548,13 @@ __global__ __launch_bounds__(kThreads, 1) void group_gemm_kernel(GemmArgs args)
         // end of the launch (routed_grid is a multiple of 8: XCD order holds)
         if ((int)blockIdx.x >= args.routed_grid) {
             constexpr int DM = MODE == GATEUP_TRELLIS ? GATEUP_DENSE : DOWN_DENSE;
-            block_body<DM, K, CB>(args, (int)blockIdx.x - args.routed_grid, args.dnslices, ring0, ring1, ring2, ring3);
+            block_body<DM, K, CB>(args, (int)blockIdx.x - args.routed_grid, args.dnslices, 1, ring0, ring1, ring2,
+                                  ring3);
             return;
         }
     }
-    block_body<MODE, K, CB>(args, (int)blockIdx.x, args.nslices, ring0, ring1, ring2, ring3);
+    block_body<MODE, K, CB>(args, (int)blockIdx.x, args.nslices, args.sdiv > 1 ? args.sdiv : 1, ring0, ring1, ring2,
+                            ring3);
 }
 
 template <int MODE>
@@ -582,7 +589,8 @@ hipError_t launch_mfma_gateup(const GroupArgs &a, int max_tiles, const SharedArg
     GemmArgs ga{};
     ga.g = a;
     ga.nslices = a.I / ModeTraits<GATEUP_TRELLIS>::kBlockN;
-    ga.routed_grid = (int)grid_of(max_tiles, ga.nslices);
+    ga.sdiv = (a.T <= 64 && ga.nslices % 4 == 0) ? 4 : 1;
+    ga.routed_grid = (int)grid_of(max_tiles, ga.nslices / ga.sdiv);
     unsigned grid = (unsigned)ga.routed_grid;
     if (sh) {
         ga.dA = sh->x16;
@@ -601,7 +609,8 @@ hipError_t launch_mfma_down(const GroupArgs &a, int max_tiles, const SharedArgs 
     GemmArgs ga{};
     ga.g = a;
     ga.nslices = a.H / ModeTraits<DOWN_TRELLIS>::kBlockN;
-    ga.routed_grid = (int)grid_of(max_tiles, ga.nslices);
+    ga.sdiv = (a.T <= 64 && ga.nslices % 4 == 0) ? 4 : 1;
+    ga.routed_grid = (int)grid_of(max_tiles, ga.nslices / ga.sdiv);
     unsigned grid = (unsigned)ga.routed_grid;
     if (sh) {
         ga.dA = sh->h;
@@ -626,6 +635,7 @@ hipError_t launch_shared_gateup(const uint16_t *x16, int64_t T, int H, int I, co
     ga.dOutH = sh;
     ga.T = T;
     ga.nslices = I / ModeTraits<GATEUP_DENSE>::kBlockN;
+    ga.sdiv = 1;
     return launch_grid<GATEUP_DENSE>(ga, grid_of(dense_tiles(T), ga.nslices), s);
 }
 
@@ -640,6 +650,7 @@ hipError_t launch_shared_down(const uint16_t *sh, int64_t T, int H, int I, const
     ga.dOutY = sy;
     ga.T = T;
     ga.nslices = H / ModeTraits<DOWN_DENSE>::kBlockN;
+    ga.sdiv = 1;
     return launch_grid<DOWN_DENSE>(ga, grid_of(dense_tiles(T), ga.nslices), s);
 }
 
