@@ -5,10 +5,12 @@
 // per-lane window loads with a deep prefetch).
 //
 // Each lane decodes eight consecutive input rows of one output column from
-// two code dwords and feeds them to fp16/bf16 dot products, so a wavefront
-// streams two tiles per step and every output column stays in one lane.  The
-// code stream is read exactly once per expert; it is the only large HBM
-// traffic of a decode-sized step.
+// two code dwords into packed fp16 pairs for v_dot2_f32_f16, so a wavefront
+// streams a pair of 16-column tiles and every output column stays in one
+// lane.  The code stream is read once per pass of up to two routed rows (once
+// per expert at the default split); it is the only large HBM traffic of a
+// decode-sized step.  The dense shared expert's decode-sized GEMV lives here
+// too, as blocks of its own launches or of the routed ones.
 #include <algorithm>
 
 #include "common.h"
