@@ -2,9 +2,9 @@
 // "GLM-5.3 Flash EXL3 for 2x DGX Sparks", "Cold prefill (E3 grouped MoE)":
 // gather, gate/up + SwiGLU, down + scatter from device segment tables).
 //
-// One work tile = (expert, 256 routed rows, a column slice); two blocks share
-// a CU (128 accumulator registers per lane) so one block's decode overlaps the
-// other's MFMAs.  The A operand (activation rows) is staged through LDS,
+// One work tile = (expert, 256 routed rows, a column slice); a block is 8
+// wavefronts, two per SIMD (128 accumulator registers per lane, one block per
+// CU), so one wavefront's decode overlaps the other's MFMAs.  The A operand (activation rows) is staged through LDS,
 // double buffered, 64 input channels per stage.  The B operand never touches
 // LDS: each lane decodes its own MFMA B fragment (8 consecutive input rows of
 // one output column) straight from two code dwords into registers, so a
