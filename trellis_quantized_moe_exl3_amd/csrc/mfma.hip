@@ -385,6 +385,19 @@ MOE_DEV void tile_body(GemmTile<MODE, K, CB> &g, const GemmArgs &args, int n0,
             __syncthreads();
         }
     } else {
+        // down: the tile's slot ids and routing weights come through LDS (one
+        // row per thread, the rings being free now) rather than as two
+        // dependent global loads for every accumulator element
+        LDS_AS int *slots = (LDS_AS int *)R0;
+        LDS_AS float *wts = (LDS_AS float *)(R0 + 2 * kBM);
+        if constexpr (MODE == DOWN_TRELLIS) {
+            if (g.tid < rows) {
+                const int slot = a.sorted[p0 + g.tid];
+                slots[g.tid] = slot;
+                wts[g.tid] = a.w[slot];
+            }
+            __syncthreads();
+        }
 #pragma unroll
         for (int cm = 0; cm < CM; ++cm) {
             const int col = g.col + 32 * cm;
@@ -398,8 +411,8 @@ MOE_DEV void tile_body(GemmTile<MODE, K, CB> &g, const GemmArgs &args, int n0,
                         const int row = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
                         if (row < rows) {
                             if constexpr (MODE == DOWN_TRELLIS) {
-                                const int slot = a.sorted[p0 + row];
-                                a.ybuf[(int64_t)slot * H + col] = f32_to_bf16_bits(acc[b][r] * sv * a.w[slot]);
+                                const int slot = slots[row];
+                                a.ybuf[(int64_t)slot * H + col] = f32_to_bf16_bits(acc[b][r] * sv * wts[row]);
                             } else {
                                 args.dOutY[(t0 + row) * H + col] = acc[b][r];
                             }
