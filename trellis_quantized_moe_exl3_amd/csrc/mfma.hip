@@ -336,48 +336,59 @@ MOE_DEV void tile_body(GemmTile<MODE, K, CB> &g, const GemmArgs &args, int n0,
     const int64_t t0 = g.t0;
     const int mblocks = (rows + 31) >> 5;
     if constexpr (TR::kGateUp) {
-        // up wavefront w + 4 hands its scaled results to gate wavefront w (the
-        // same columns) through LDS, in rounds of four accumulator blocks:
-        // block b of column group cg = w & 3 goes to ring cg at 4 KiB per block
+        // gate wavefront w and up wavefront w + 4 hold the same columns.  In
+        // rounds of four accumulator blocks, the up wavefront hands its scaled
+        // values of the first two blocks to the gate wavefront through LDS and
+        // the gate wavefront its scaled values of the last two to the up
+        // wavefront; each then finishes its two blocks (block b of column group
+        // cg = w & 3 goes to ring cg at 4 KiB per block).
         const int cg = g.w & 3;
         float *ex = cg == 0 ? (float *)ring0 : cg == 1 ? (float *)ring1 : cg == 2 ? (float *)ring2 : (float *)ring3;
 #pragma unroll
         for (int round = 0; round < (NB + 3) / 4; ++round) {
-            if (g.pr == 1) {
 #pragma unroll
-                for (int b = 4 * round; b < 4 * round + 4 && b < NB; ++b) {
-                    const int cm = b / NMB, i = b % NMB;
-                    const int col = g.col + 32 * cm;
-                    const float su = MODE == GATEUP_TRELLIS ? f16_to_f32(a.svh[1][(int64_t)e * I + col]) * (1.0f / 128.0f) : 1.0f;
-                    if (i < mblocks)
+            for (int b = 4 * round; b < 4 * round + 4 && b < NB; ++b) {
+                const int cm = b / NMB, i = b % NMB;
+                const int col = g.col + 32 * cm;
+                // blocks 0, 1 of the round are finished by the gate wavefront
+                const bool mine = (g.pr == 0) == ((b & 3) < 2);
+                if (!mine && i < mblocks) {
+                    const float sc = MODE != GATEUP_TRELLIS ? 1.0f
+                                     : f16_to_f32(a.svh[g.pr][(int64_t)e * I + col]) * (1.0f / 128.0f);
 #pragma unroll
-                        for (int r = 0; r < 16; ++r)
-                            ex[((b & 3) * 16 + r) * 64 + g.l] = acc[b][r] * su;
+                    for (int r = 0; r < 16; ++r)
+                        ex[((b & 3) * 16 + r) * 64 + g.l] = acc[b][r] * sc;
                 }
             }
             __syncthreads();
-            if (g.pr == 0) {
 #pragma unroll
-                for (int b = 4 * round; b < 4 * round + 4 && b < NB; ++b) {
-                    const int cm = b / NMB, i = b % NMB;
-                    const int col = g.col + 32 * cm;
-                    float sg = 1.0f, sd = 1.0f;
+            for (int b = 4 * round; b < 4 * round + 4 && b < NB; ++b) {
+                const int cm = b / NMB, i = b % NMB;
+                const int col = g.col + 32 * cm;
+                const bool mine = (g.pr == 0) == ((b & 3) < 2);
+                if (mine && i < mblocks) {
+                    float sg = 1.0f, su = 1.0f, sd = 1.0f;
                     if constexpr (MODE == GATEUP_TRELLIS) {
                         sg = f16_to_f32(a.svh[0][(int64_t)e * I + col]) * (1.0f / 128.0f);
+                        su = f16_to_f32(a.svh[1][(int64_t)e * I + col]) * (1.0f / 128.0f);
                         sd = f16_to_f32(a.suh[2][(int64_t)e * I + col]);
                     }
-                    if (i < mblocks) {
+                    float hv[16];
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int row = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-                            if (row < rows) {
-                                const float u = ex[((b & 3) * 16 + r) * 64 + g.l];
-                                const float hv = silu_f(acc[b][r] * sg) * u * sd;
-                                if constexpr (MODE == GATEUP_TRELLIS)
-                                    a.hbuf[(int64_t)(p0 + row) * I + col] = f32_to_bf16_bits(hv);
-                                else
-                                    args.dOutH[(t0 + row) * I + col] = f32_to_f16_bits(hv);
-                            }
+                    for (int r = 0; r < 16; ++r) {
+                        const float other = ex[((b & 3) * 16 + r) * 64 + g.l];
+                        const float gv = g.pr == 0 ? acc[b][r] * sg : other;
+                        const float uv = g.pr == 0 ? other : acc[b][r] * su;
+                        hv[r] = silu_f(gv) * uv * sd;
+                    }
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int row = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+                        if (row < rows) {
+                            if constexpr (MODE == GATEUP_TRELLIS)
+                                a.hbuf[(int64_t)(p0 + row) * I + col] = f32_to_bf16_bits(hv[r]);
+                            else
+                                args.dOutH[(t0 + row) * I + col] = f32_to_f16_bits(hv[r]);
                         }
                     }
                 }
