@@ -228,6 +228,15 @@ MOE_DEV void tile8_body(Tile8<GATEUP, K> &g, const GroupArgs &a, int n0, uint8_t
     const int h = g.kh, rows = g.rows, e = g.e, p0 = g.p0;
     const int mblocks = (rows + 31) >> 5;
     if constexpr (GATEUP) {
+        // the tile's row scales through LDS (one row per thread, in the second
+        // half of ring 0, which the exchange below leaves alone)
+        LDS_AS float *sgs = (LDS_AS float *)(R0 + k8Stage);
+        LDS_AS float *sus = sgs + k8BM;
+        if ((int)threadIdx.x < rows) {
+            sgs[threadIdx.x] = a.sg8[p0 + threadIdx.x];
+            sus[threadIdx.x] = a.su8[p0 + threadIdx.x];
+        }
+        __syncthreads();
         // up wavefront w + 4 hands u = acc * s_u(row) * svh_u to gate
         // wavefront w (same columns) through LDS, in rounds of four blocks
         const int cg = g.w & 3;
@@ -243,7 +252,7 @@ MOE_DEV void tile8_body(Tile8<GATEUP, K> &g, const GroupArgs &a, int n0, uint8_t
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
                             const int row = min(32 * i + 8 * (r >> 2) + 4 * h + (r & 3), rows - 1);
-                            ex[((b & 3) * 16 + r) * 64 + g.l] = acc[b][r] * a.su8[p0 + row] * sv;
+                            ex[((b & 3) * 16 + r) * 64 + g.l] = acc[b][r] * sus[row] * sv;
                         }
                 }
             }
@@ -261,7 +270,7 @@ MOE_DEV void tile8_body(Tile8<GATEUP, K> &g, const GroupArgs &a, int n0, uint8_t
                             const int row = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
                             if (row < rows) {
                                 const float u = ex[((b & 3) * 16 + r) * 64 + g.l];
-                                const float gv = acc[b][r] * a.sg8[p0 + row] * sg;
+                                const float gv = acc[b][r] * sgs[row] * sg;
                                 a.hbuf[(int64_t)(p0 + row) * I + col] = f32_to_bf16_bits(silu_f(gv) * u * sd);
                             }
                         }
@@ -271,6 +280,19 @@ MOE_DEV void tile8_body(Tile8<GATEUP, K> &g, const GroupArgs &a, int n0, uint8_t
             __syncthreads();
         }
     } else {
+        // the tile's slot ids, row scales and routing weights through LDS (one
+        // row per thread; the rings are free now) rather than as dependent
+        // global loads for every accumulator element
+        LDS_AS int *slots = (LDS_AS int *)R0;
+        LDS_AS float *rsc = (LDS_AS float *)(R0 + 4 * k8BM);
+        LDS_AS float *wts = (LDS_AS float *)(R0 + 8 * k8BM);
+        if ((int)threadIdx.x < rows) {
+            const int slot = a.sorted[p0 + threadIdx.x];
+            slots[threadIdx.x] = slot;
+            rsc[threadIdx.x] = a.sh8[p0 + threadIdx.x];
+            wts[threadIdx.x] = a.w[slot];
+        }
+        __syncthreads();
 #pragma unroll
         for (int cm = 0; cm < CM; ++cm) {
             const int col = g.col + 32 * cm;
@@ -282,9 +304,9 @@ MOE_DEV void tile8_body(Tile8<GATEUP, K> &g, const GroupArgs &a, int n0, uint8_t
                     for (int r = 0; r < 16; ++r) {
                         const int row = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
                         if (row < rows) {
-                            const int slot = a.sorted[p0 + row];
+                            const int slot = slots[row];
                             a.ybuf[(int64_t)slot * H + col] =
-                                f32_to_bf16_bits(acc[cm * NMB + i][r] * a.sh8[p0 + row] * sv * a.w[slot]);
+                                f32_to_bf16_bits(acc[cm * NMB + i][r] * rsc[row] * sv * wts[row]);
                         }
                     }
                 }
