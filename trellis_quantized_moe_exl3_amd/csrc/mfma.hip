@@ -409,6 +409,10 @@ MOE_DEV void tile_body(GemmTile<MODE, K, CB> &g, const GemmArgs &args, int n0,
             }
             __syncthreads();
         }
+        // each wavefront turns a 32 x 32 accumulator block into bf16 rows in
+        // its own 2 KiB of ring 1, then stores 16 bytes per lane of a row
+        LDS_AS uint16_t *tw = R1 + 1024 * g.w;
+        const int lc = g.l & 31;
 #pragma unroll
         for (int cm = 0; cm < CM; ++cm) {
             const int col = g.col + 32 * cm;
@@ -417,16 +421,25 @@ MOE_DEV void tile_body(GemmTile<MODE, K, CB> &g, const GemmArgs &args, int n0,
             for (int i = 0; i < NMB; ++i) {
                 const int b = cm * NMB + i;
                 if (i < mblocks) {
+                    if constexpr (MODE == DOWN_TRELLIS) {
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int row = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-                        if (row < rows) {
-                            if constexpr (MODE == DOWN_TRELLIS) {
-                                const int slot = slots[row];
-                                a.ybuf[(int64_t)slot * H + col] = f32_to_bf16_bits(acc[b][r] * sv * wts[row]);
-                            } else {
+                        for (int r = 0; r < 16; ++r) {
+                            const int rl = 8 * (r >> 2) + 4 * h + (r & 3);
+                            tw[rl * 32 + lc] = f32_to_bf16_bits(acc[b][r] * sv * wts[32 * i + rl]);
+                        }
+#pragma unroll
+                        for (int q = 0; q < 2; ++q) {
+                            const int rl = (g.l >> 2) + 16 * q, row = 32 * i + rl;
+                            const u32x4 v = *(const LDS_AS u32x4 *)(tw + rl * 32 + 8 * (g.l & 3));
+                            if (row < rows)
+                                *(u32x4 *)(a.ybuf + (int64_t)slots[row] * H + (col - lc) + 8 * (g.l & 3)) = v;
+                        }
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int row = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+                            if (row < rows)
                                 args.dOutY[(t0 + row) * H + col] = acc[b][r];
-                            }
                         }
                     }
                 }
