@@ -237,42 +237,47 @@ MOE_DEV void tile8_body(Tile8<GATEUP, K> &g, const GroupArgs &a, int n0, uint8_t
             sus[threadIdx.x] = a.su8[p0 + threadIdx.x];
         }
         __syncthreads();
-        // up wavefront w + 4 hands u = acc * s_u(row) * svh_u to gate
-        // wavefront w (same columns) through LDS, in rounds of four blocks
+        // gate wavefront w and up wavefront w + 4 hold the same columns.  In
+        // rounds of four accumulator blocks, the up wavefront hands its scaled
+        // values (acc * row scale * svh) of the first two blocks to the gate
+        // wavefront through LDS and the gate wavefront its scaled values of
+        // the last two to the up wavefront; each then finishes its two blocks
         const int cg = g.w & 3;
         float *ex = cg == 0 ? (float *)ring0 : cg == 1 ? (float *)ring1 : cg == 2 ? (float *)ring2 : (float *)ring3;
+        const LDS_AS float *rsm = sgs + (g.pr == 0 ? 0 : k8BM);   // this projection's row scales
 #pragma unroll
         for (int round = 0; round < (NB + 3) / 4; ++round) {
-            if (g.pr == 1) {
 #pragma unroll
-                for (int b = 4 * round; b < 4 * round + 4 && b < NB; ++b) {
-                    const int cm = b / NMB, i = b % NMB;
-                    const float sv = f16_to_f32(a.svh[1][(int64_t)e * I + g.col + 32 * cm]);
-                    if (i < mblocks)
+            for (int b = 4 * round; b < 4 * round + 4 && b < NB; ++b) {
+                const int cm = b / NMB, i = b % NMB;
+                const bool mine = (g.pr == 0) == ((b & 3) < 2);
+                if (!mine && i < mblocks) {
+                    const float sv = f16_to_f32(a.svh[g.pr][(int64_t)e * I + g.col + 32 * cm]);
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int row = min(32 * i + 8 * (r >> 2) + 4 * h + (r & 3), rows - 1);
-                            ex[((b & 3) * 16 + r) * 64 + g.l] = acc[b][r] * sus[row] * sv;
-                        }
+                    for (int r = 0; r < 16; ++r) {
+                        const int row = min(32 * i + 8 * (r >> 2) + 4 * h + (r & 3), rows - 1);
+                        ex[((b & 3) * 16 + r) * 64 + g.l] = acc[b][r] * rsm[row] * sv;
+                    }
                 }
             }
             __syncthreads();
-            if (g.pr == 0) {
 #pragma unroll
-                for (int b = 4 * round; b < 4 * round + 4 && b < NB; ++b) {
-                    const int cm = b / NMB, i = b % NMB;
-                    const int col = g.col + 32 * cm;
-                    const float sg = f16_to_f32(a.svh[0][(int64_t)e * I + col]);
+            for (int b = 4 * round; b < 4 * round + 4 && b < NB; ++b) {
+                const int cm = b / NMB, i = b % NMB;
+                const int col = g.col + 32 * cm;
+                const bool mine = (g.pr == 0) == ((b & 3) < 2);
+                if (mine && i < mblocks) {
+                    const float sv = f16_to_f32(a.svh[g.pr][(int64_t)e * I + col]);
                     const float sd = f16_to_f32(a.suh[2][(int64_t)e * I + col]);
-                    if (i < mblocks) {
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int row = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-                            if (row < rows) {
-                                const float u = ex[((b & 3) * 16 + r) * 64 + g.l];
-                                const float gv = acc[b][r] * sgs[row] * sg;
-                                a.hbuf[(int64_t)(p0 + row) * I + col] = f32_to_bf16_bits(silu_f(gv) * u * sd);
-                            }
+                    for (int r = 0; r < 16; ++r) {
+                        const int row = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+                        if (row < rows) {
+                            const float own = acc[b][r] * rsm[row] * sv;
+                            const float other = ex[((b & 3) * 16 + r) * 64 + g.l];
+                            const float gv = g.pr == 0 ? own : other;
+                            const float uv = g.pr == 0 ? other : own;
+                            a.hbuf[(int64_t)(p0 + row) * I + col] = f32_to_bf16_bits(silu_f(gv) * uv * sd);
                         }
                     }
                 }
@@ -280,19 +285,23 @@ MOE_DEV void tile8_body(Tile8<GATEUP, K> &g, const GroupArgs &a, int n0, uint8_t
             __syncthreads();
         }
     } else {
-        // the tile's slot ids, row scales and routing weights through LDS (one
-        // row per thread; the rings are free now) rather than as dependent
-        // global loads for every accumulator element
+        // the tile's slot ids and per-row factors (row scale times routing
+        // weight) through LDS (one row per thread; the rings are free now)
+        // rather than as dependent global loads for every accumulator element
         LDS_AS int *slots = (LDS_AS int *)R0;
-        LDS_AS float *rsc = (LDS_AS float *)(R0 + 4 * k8BM);
-        LDS_AS float *wts = (LDS_AS float *)(R0 + 8 * k8BM);
+        LDS_AS float *rw = (LDS_AS float *)(R0 + 4 * k8BM);
         if ((int)threadIdx.x < rows) {
             const int slot = a.sorted[p0 + threadIdx.x];
             slots[threadIdx.x] = slot;
-            rsc[threadIdx.x] = a.sh8[p0 + threadIdx.x];
-            wts[threadIdx.x] = a.w[slot];
+            // the row scale is a power of two, so folding it into the routing
+            // weight rounds the same way as applying the two in turn
+            rw[threadIdx.x] = a.sh8[p0 + threadIdx.x] * a.w[slot];
         }
         __syncthreads();
+        // each wavefront turns a 32 x 32 accumulator block into bf16 rows in
+        // its own 2 KiB of ring 1, then stores 16 bytes per lane of a row
+        LDS_AS uint16_t *tw = (LDS_AS uint16_t *)R1 + 1024 * g.w;
+        const int lc = g.l & 31;
 #pragma unroll
         for (int cm = 0; cm < CM; ++cm) {
             const int col = g.col + 32 * cm;
@@ -302,12 +311,15 @@ MOE_DEV void tile8_body(Tile8<GATEUP, K> &g, const GroupArgs &a, int n0, uint8_t
                 if (i < mblocks) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const int row = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-                        if (row < rows) {
-                            const int slot = slots[row];
-                            a.ybuf[(int64_t)slot * H + col] =
-                                f32_to_bf16_bits(acc[cm * NMB + i][r] * rsc[row] * sv * wts[row]);
-                        }
+                        const int rl = 8 * (r >> 2) + 4 * h + (r & 3);
+                        tw[rl * 32 + lc] = f32_to_bf16_bits(acc[cm * NMB + i][r] * sv * rw[32 * i + rl]);
+                    }
+#pragma unroll
+                    for (int q = 0; q < 2; ++q) {
+                        const int rl = (g.l >> 2) + 16 * q, row = 32 * i + rl;
+                        const u32x4 v = *(const LDS_AS u32x4 *)(tw + rl * 32 + 8 * (g.l & 3));
+                        if (row < rows)
+                            *(u32x4 *)(a.ybuf + (int64_t)slots[row] * H + (col - lc) + 8 * (g.l & 3)) = v;
                     }
                 }
             }
