@@ -4,6 +4,7 @@ import pytest
 import torch
 
 import oracle
+import trellis_quantized_moe_exl3_amd as M
 import workloads as W
 from gpu_util import DevLayer, dev
 
@@ -73,3 +74,29 @@ def test_route_deterministic():
     b = dl.route()
     for u, v in zip(a, b):
         np.testing.assert_array_equal(u, v)
+
+
+# The routing entry leaves the fp32 logits in its workspace right after the
+# 256-byte header (an internal layout this test reads on purpose).  They must
+# equal the oracle's fixed-order sums bit for bit: up to 64 tokens on the
+# 32-lanes-per-pair kernel, above that on the register-tiled one; bf16
+# activations at the real shapes, fp16 in the tiny config.
+_LOGITS_AT = 256
+
+
+@pytest.mark.parametrize("T", [1, 8, 13, 64, 65, 300])
+@pytest.mark.parametrize("name", ["decode", "tiny"])
+def test_route_logits_bit_exact(name, T):
+    cfg = W.BY_NAME[name].replace(tokens=T, router_bias=True)
+    inp = W.gen_layer(cfg, experts=[])
+    dl = DevLayer(inp)
+    k, E = cfg.top_k, cfg.n_experts
+    outs = [torch.empty(T * k, dtype=dt, device="cuda")
+            for dt in (torch.int32, torch.float32)]
+    tabs = [torch.empty(n, dtype=torch.int32, device="cuda") for n in (E, E + 1, T * k, T * k)]
+    ws = dl.workspace(T)
+    M.route(dl.desc, dl.weights, dl.x, *outs, *tabs, ws)
+    torch.cuda.synchronize()
+    got = ws[_LOGITS_AT:_LOGITS_AT + 4 * T * E].cpu().numpy().view(np.float32).reshape(T, E)
+    ref = oracle.router_logits(inp.x, cfg.act_dtype, inp.router_w, inp.router_bias)
+    assert got.view(np.uint32).tolist() == ref.view(np.uint32).tolist()

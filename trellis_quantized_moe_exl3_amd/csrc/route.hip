@@ -74,17 +74,13 @@ __global__ __launch_bounds__(256) void route_logits_kernel(const uint16_t *__res
             for (int j = 0; j < 8; ++j)
                 p[a][b][j] = 0.0f;
     // rows past the last token or expert read row 0 (in bounds); their sums
-    // are never stored.  With few pairs per lane (few tokens) the loads stay
-    // predicated and 16 iterations are unrolled, so a wavefront (one of only a
-    // few hundred) keeps 16 chunks of loads in flight.
-    constexpr bool kWide = TPL * EPL >= 8;
-    constexpr int kUnroll = kWide ? 2 : 16;
-#pragma unroll kUnroll
+    // are never stored
+#pragma unroll 2
     for (int i = 0; i < H / 64; ++i) {
         float xv[TPL][8];
 #pragma unroll
         for (int a = 0; a < TPL; ++a) {
-            const u32x4 raw = (kWide || tok_ok[a]) ? *(const u32x4 *)(xr[a] + 64 * i) : (u32x4){0, 0, 0, 0};
+            const u32x4 raw = *(const u32x4 *)(xr[a] + 64 * i);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 if (BF16) {
@@ -142,6 +138,62 @@ __global__ __launch_bounds__(256) void route_logits_kernel(const uint16_t *__res
     }
 }
 
+// Few tokens: 32 lanes per (token, expert) pair, lane m owning the partial
+// sums l = 2m and 2m + 1 (one dword of each row per chunk i), so a call with
+// a few thousand pairs still fills every SIMD and each lane keeps a whole
+// group of kPairChunk chunks of loads in flight.  The tree runs as lane
+// shuffles (d = 32 .. 2: lane m += lane m + d/2) and one in-lane add (d = 1).
+constexpr int kPairChunk = 32;
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void route_logits_pairs_kernel(const uint16_t *__restrict__ x, int64_t T,
+                                                                 int H, const uint16_t *__restrict__ Wr,
+                                                                 const float *__restrict__ bias, int E,
+                                                                 float *__restrict__ logits)
+{
+    const int64_t pair = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
+    const int m = threadIdx.x & 31;
+    const bool ok = pair < T * E;
+    const int64_t t = ok ? pair / E : 0;   // rows past the last pair read row 0
+    const int e = ok ? (int)(pair % E) : 0;
+    const uint32_t *xr = (const uint32_t *)(x + t * H) + m;
+    const uint32_t *wr = (const uint32_t *)(Wr + (int64_t)e * H) + m;
+    const int n = H / 64;
+    float p0 = 0.0f, p1 = 0.0f;
+    for (int i0 = 0; i0 < n; i0 += kPairChunk) {
+        uint32_t xv[kPairChunk], wv[kPairChunk];
+#pragma unroll
+        for (int c = 0; c < kPairChunk; ++c)
+            if (i0 + c < n) {
+                xv[c] = xr[32 * (i0 + c)];
+                wv[c] = wr[32 * (i0 + c)];
+            }
+#pragma unroll
+        for (int c = 0; c < kPairChunk; ++c)
+            if (i0 + c < n) {
+                float x0, x1;
+                if (BF16) {
+                    x0 = __uint_as_float(xv[c] << 16);
+                    x1 = __uint_as_float(xv[c] & 0xFFFF0000u);
+                } else {
+                    x0 = f16_to_f32((uint16_t)(xv[c] & 0xFFFFu));
+                    x1 = f16_to_f32((uint16_t)(xv[c] >> 16));
+                }
+                p0 = __builtin_fmaf(x0, f16_to_f32((uint16_t)(wv[c] & 0xFFFFu)), p0);
+                p1 = __builtin_fmaf(x1, f16_to_f32((uint16_t)(wv[c] >> 16)), p1);
+            }
+    }
+#pragma unroll
+    for (int d = 16; d >= 1; d >>= 1) {
+        p0 = p0 + __shfl_down(p0, d, 32);
+        p1 = p1 + __shfl_down(p1, d, 32);
+    }
+    if (m == 0 && ok) {
+        const float r = p0 + p1;
+        logits[t * E + e] = bias ? r + bias[e] : r;
+    }
+}
+
 template <bool BF16, int TPL, int EPL, int NTQ>
 static void route_launch(const uint16_t *x, int64_t T, int H, const uint16_t *Wr, const float *bias,
                          int E, float *logits, hipStream_t s)
@@ -155,15 +207,15 @@ hipError_t launch_route_logits(const uint16_t *x, bool bf16, int64_t T, int H, c
                                const float *bias, int E, float *logits, hipStream_t s)
 {
     // many tokens: 2 tokens x 4 experts per lane (8 tokens x 32 experts per
-    // block; each converted activation feeds 4 fma_mix); few tokens: one
-    // (token, expert) pair per lane group so that enough wavefronts stream the
-    // router weights
+    // block); few tokens: one (token, expert) pair per 32 lanes so that
+    // enough wavefronts stream the router weights
     if (T > 64) {
         if (bf16) route_launch<true, 2, 4, 4>(x, T, H, Wr, bias, E, logits, s);
         else route_launch<false, 2, 4, 4>(x, T, H, Wr, bias, E, logits, s);
     } else {
-        if (bf16) route_launch<true, 1, 1, 8>(x, T, H, Wr, bias, E, logits, s);
-        else route_launch<false, 1, 1, 8>(x, T, H, Wr, bias, E, logits, s);
+        const unsigned grid = (unsigned)((T * E + 7) / 8);
+        if (bf16) route_logits_pairs_kernel<true><<<grid, 256, 0, s>>>(x, T, H, Wr, bias, E, logits);
+        else route_logits_pairs_kernel<false><<<grid, 256, 0, s>>>(x, T, H, Wr, bias, E, logits);
     }
     return hipGetLastError();
 }
@@ -469,11 +521,16 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
     __shared__ int32_t sidx[kSegChunk];
     __shared__ int32_t hist[1024];
     const int wv = threadIdx.x >> 6, l = threadIdx.x & 63;
-    for (int64_t t = wv; t < T; t += 16)
-        topk_token<NPER>(logits, t, E, k, idx, w, sidx);
-    if (x16) {
+    // up to 8 tokens, wavefronts 8..15 have no token to rank: they copy the
+    // activations while wavefronts 0..T-1 run top-k
+    const bool split = T <= 8;
+    if (!split || wv < 8)
+        for (int64_t t = wv; t < T; t += 16)
+            topk_token<NPER>(logits, t, E, k, idx, w, sidx);
+    if (x16 && (!split || wv >= 8)) {
         const int64_t n8 = T * H / 8;
-        for (int64_t i = threadIdx.x; i < n8; i += 1024) {
+        const int first = split ? (int)threadIdx.x - 512 : (int)threadIdx.x, step = split ? 512 : 1024;
+        for (int64_t i = first; i < n8; i += step) {
             const u32x4 v = ((const u32x4 *)x)[i];
             u32x4 o;
 #pragma unroll
