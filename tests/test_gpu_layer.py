@@ -61,6 +61,25 @@ def test_tiny_one_expert_takes_every_token():
     assert rel_err(out, ref) <= TOL
 
 
+def test_decode_eight_rows_on_one_expert():
+    # a huge bias on expert 3: all 8 tokens route to it.  Up to 8 tokens every
+    # expert runs on the GEMV path (no expert can get more rows than there
+    # are tokens), so expert 3 takes its 8 rows in four passes over its codes
+    cfg = W.BY_NAME["decode"].replace(router_bias=True)
+    inp = W.gen_layer(cfg)
+    inp.router_bias = np.zeros(cfg.n_experts, dtype=np.float32)
+    inp.router_bias[3] = 100.0
+    routed = _routed_only(inp)
+    dl = DevLayer(routed)
+    idx = dl.route()[0]
+    assert (idx[:, 0] == 3).all()
+    out = dl.run()
+    _, _, ref = oracle.layer(routed)
+    err = rel_err(out, ref)
+    print(f"decode eight rows on one expert err={err:.3e}")
+    assert err <= TOL
+
+
 def test_zero_tokens_is_noop():
     inp = W.gen_layer(W.BY_NAME["tiny"])
     dl = DevLayer(inp)

@@ -18,7 +18,12 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-int gemv_rows_of(const moe_exl3_desc &d)
+// The routed-row threshold between the GEMV and MFMA paths for a call of T
+// tokens.  No expert receives more rows than there are tokens (a token's k
+// experts are distinct), so with the default threshold a call of at most
+// kGemvMaxRows tokens puts every expert on the GEMV path and needs no MFMA
+// launch at all.
+int gemv_rows_of(const moe_exl3_desc &d, int64_t T)
 {
     // the GEMV blocks keep two rows of activations in LDS (64 KiB at most)
     const int cap = kGemvMaxRows;
@@ -26,8 +31,9 @@ int gemv_rows_of(const moe_exl3_desc &d)
         return 0;
     if (d.flags & MOE_EXL3_FORCE_GEMV)
         return cap;
-    const int g = d.gemv_max_rows > 0 ? d.gemv_max_rows : kGemvDefaultRows;
-    return std::min(g, cap);
+    if (d.gemv_max_rows > 0)
+        return std::min(d.gemv_max_rows, cap);
+    return T <= cap ? cap : kGemvDefaultRows;
 }
 
 int check_desc(const moe_exl3_desc *d)
@@ -100,9 +106,9 @@ Plan make_plan(const moe_exl3_desc &d, int64_t T)
     const int64_t n = T * d.top_k;
     const int E = d.n_experts;
     p.nblk = (int)std::max<int64_t>(1, (n + kSegChunk - 1) / kSegChunk);
-    const int g = gemv_rows_of(d);
+    const int g = gemv_rows_of(d, T);
     const int64_t heavy = std::min<int64_t>(E, n / (g + 1));
-    p.max_tiles = (int)std::max<int64_t>(0, std::min<int64_t>(n / kTileM + heavy, n));
+    p.max_tiles = T <= g ? 0 : (int)std::max<int64_t>(0, std::min<int64_t>(n / kTileM + heavy, n));
     size_t o = 0;
     auto take = [&](size_t bytes) {
         const size_t at = o;
@@ -171,7 +177,7 @@ int run_route(const moe_exl3_desc &d, const moe_exl3_weights &w, const void *x, 
     if (!mk.mark(MOE_EXL3_STEP_TOPK))
         return MOE_EXL3_ERR_HIP;
     if (T <= kSmallRouteTokens && p.nblk == 1) {
-        if (launch_route_small(at<float>(ws, p.logits), T, d.n_experts, d.top_k, gemv_rows_of(d), kTileM,
+        if (launch_route_small(at<float>(ws, p.logits), T, d.n_experts, d.top_k, gemv_rows_of(d, T), kTileM,
                                at<int32_t>(ws, p.idx), at<float>(ws, p.w), at<int32_t>(ws, p.counts),
                                at<int32_t>(ws, p.offsets), at<int32_t>(ws, p.sorted), at<int32_t>(ws, p.pos),
                                at<int32_t>(ws, p.glist), at<int32_t>(ws, p.tiles), at<WsHeader>(ws, p.hdr),
@@ -187,7 +193,7 @@ int run_route(const moe_exl3_desc &d, const moe_exl3_weights &w, const void *x, 
         return MOE_EXL3_ERR_HIP;
     if (!mk.mark(MOE_EXL3_STEP_SEGMENTS))
         return MOE_EXL3_ERR_HIP;
-    if (launch_segments(at<int32_t>(ws, p.idx), T, d.top_k, d.n_experts, p.nblk, gemv_rows_of(d),
+    if (launch_segments(at<int32_t>(ws, p.idx), T, d.top_k, d.n_experts, p.nblk, gemv_rows_of(d, T),
                         kTileM, at<int32_t>(ws, p.bhist), at<int32_t>(ws, p.counts),
                         at<int32_t>(ws, p.offsets), at<int32_t>(ws, p.sorted),
                         at<int32_t>(ws, p.pos), at<int32_t>(ws, p.glist), at<int32_t>(ws, p.tiles),
@@ -352,7 +358,7 @@ static int run_layer(const moe_exl3_desc *desc, const moe_exl3_weights *weights,
         ga.su8 = at<float>(ws, p.su8);
         ga.sh8 = at<float>(ws, p.sh8);
     }
-    const int g = gemv_rows_of(d);
+    const int g = gemv_rows_of(d, T);
     const int64_t n = T * d.top_k;
     const int max_list = g > 0 ? (int)std::min<int64_t>(d.n_experts, n) : 0;
 
