@@ -417,10 +417,19 @@ __global__ __launch_bounds__(1024) void seg_scan_kernel(int32_t *__restrict__ bh
     const int e = threadIdx.x;   // E <= 1024
     int c = 0;
     if (e < E) {
-        for (int b = 0; b < nblk; ++b) {
-            const int v = bhist[(int64_t)b * E + e];
-            bhist[(int64_t)b * E + e] = c;
-            c += v;
+        // per-chunk counts -> running bases, 16 chunks' loads in flight at a time
+        constexpr int kG = 16;
+        for (int b0 = 0; b0 < nblk; b0 += kG) {
+            int v[kG];
+#pragma unroll
+            for (int j = 0; j < kG; ++j)
+                v[j] = b0 + j < nblk ? bhist[(int64_t)(b0 + j) * E + e] : 0;
+#pragma unroll
+            for (int j = 0; j < kG; ++j)
+                if (b0 + j < nblk) {
+                    bhist[(int64_t)(b0 + j) * E + e] = c;
+                    c += v[j];
+                }
         }
     }
     int tot;
@@ -465,11 +474,23 @@ __global__ __launch_bounds__(64) void seg_scatter_kernel(const int32_t *__restri
     while ((1 << nbits) < E)
         ++nbits;
     const uint64_t below = (l == 0) ? 0ull : (~0ull >> (64 - l));
+    // the chunk's expert ids are loaded up front (one round trip), the ranking
+    // below then runs on registers and LDS only
+    constexpr int kIter = kSegChunk / 64;
+    int ev[kIter];
+#pragma unroll
+    for (int c = 0; c < kIter; ++c) {
+        const int64_t a = a0 + 64 * c + l;
+        ev[c] = a < n ? idx[a] : 0;
+    }
     const int64_t span = n - a0 < kSegChunk ? n - a0 : kSegChunk;   // slots of this block
-    for (int c0 = 0; c0 < span; c0 += 64) {
-        const int64_t a = a0 + c0 + l;
+#pragma unroll
+    for (int c = 0; c < kIter; ++c) {
+        if (64 * c >= span)
+            break;
+        const int64_t a = a0 + 64 * c + l;
         const bool valid = a < n;
-        const int e = valid ? idx[a] : 0;
+        const int e = ev[c];
         uint64_t m = __ballot(valid);
         for (int b = 0; b < nbits; ++b) {
             const bool bit = (e >> b) & 1;
