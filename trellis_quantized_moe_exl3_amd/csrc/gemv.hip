@@ -106,18 +106,20 @@ MOE_DEV void gemv_stream(__amdgpu_buffer_rsrc_t rs, uint32_t v0, uint32_t v1, ui
                 acc[r] = dot(r, kk, wp, acc[r]);
         }
     };
-    // tk0, tk1 are wavefront-uniform: every branch below is scalar
+    // tk0, tk1 are wavefront-uniform: every branch below is scalar.
+    // tk1 - tk0 is a positive multiple of kGemvU.  Every load is issued
+    // unconditionally: a group past the wave's range reloads its last group
+    // (in range, just read, never used), so no load sits behind a branch and
+    // the two register sets need no copies to merge loaded and kept values.
+    const int glast = tk1 - kGemvU;
     int g = tk0;
     load(A, g);
-    if (g + kGemvU < tk1)
-        load(B, g + kGemvU);
+    load(B, min(g + kGemvU, glast));
     for (; g + 2 * kGemvU <= tk1; g += 2 * kGemvU) {
         run(A, g);
-        if (g + 2 * kGemvU < tk1)
-            load(A, g + 2 * kGemvU);
+        load(A, min(g + 2 * kGemvU, glast));
         run(B, g + kGemvU);
-        if (g + 3 * kGemvU < tk1)
-            load(B, g + 3 * kGemvU);
+        load(B, min(g + 3 * kGemvU, glast));
     }
     if (g < tk1)
         run(A, g);
@@ -577,9 +579,9 @@ __global__ __launch_bounds__(256, 4) void gemv_down_kernel(GroupArgs a, int max_
             const int m = m0 + cc;
             float raw = psum[0][r][cc];
             if (S == 2)
-                raw += psum[1][r][cc];
+                raw += psum[1 % kDownS][r][cc];
             else if (S == 4)
-                raw = (psum[0][r][cc] + psum[1][r][cc]) + (psum[2 % kDownS][r][cc] + psum[3 % kDownS][r][cc]);
+                raw = (psum[0][r][cc] + psum[1 % kDownS][r][cc]) + (psum[2 % kDownS][r][cc] + psum[3 % kDownS][r][cc]);
             const float tot = __builtin_ldexpf(raw - kBias2 * rsum[r], -rexp[r]);
             const int slot = a.sorted[p0 + r0 + r];
             const float svh = f16_to_f32(a.svh[2][(int64_t)e * H + m]) * (1.0f / 128.0f);
