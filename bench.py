@@ -120,6 +120,47 @@ def setup(cfg, copies=1, shared=True, extra_flags=0):
     return inp, desc, weights, keep
 
 
+def time_layer_graph(desc, weights_list, x, steps, hip):
+    """Device ms per layer when each layer call is replayed from a HIP graph,
+    as a serving loop would run a decode step: one graph per weight copy
+    (captured after an eager warm-up call on the capture stream), replayed in
+    the same rotation as the eager run, between two events on the replay
+    stream."""
+    import torch
+    import trellis_quantized_moe_exl3_amd as M
+    out = torch.empty_like(x)
+    ws = torch.empty(M.workspace_size(desc, x.shape[0]), dtype=torch.uint8, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for w in weights_list:
+            M.layer(desc, w, x, out, ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for w in weights_list:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            M.layer(desc, w, x, out, ws)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for i in range(len(graphs)):
+        graphs[i].replay()
+    stream = torch.cuda.current_stream().cuda_stream
+    a, b = hip.event(), hip.event()
+    torch.cuda.synchronize()
+    assert hip.l.hipEventRecord(a, stream) == 0
+    for i in range(steps):
+        graphs[i % len(graphs)].replay()
+    assert hip.l.hipEventRecord(b, stream) == 0
+    torch.cuda.synchronize()
+    dev_ms = hip.ms(a, b) / steps
+    hip.destroy(a)
+    hip.destroy(b)
+    del graphs
+    return dev_ms
+
+
 def time_layer(desc, weights_list, x, steps, warmup, hip):
     """Times `steps` layers through moe_exl3_layer (no timing hooks inside the
     timed region) between two device synchronisations, then runs the same
@@ -258,13 +299,14 @@ def main():
     dinp, ddesc, dweights, dkeep = setup(dcfg, copies=4)
     dx = _dev(dinp.x)
     dms, dper, ddev, _, _ = time_layer(ddesc, dweights, dx, args.decode_steps, 5, hip)
+    dgraph = time_layer_graph(ddesc, dweights, dx, args.decode_steps, hip)
     dcounts = routing_counts(ddesc, dweights[0], dx, dcfg)
     touched = int((dcounts > 0).sum())
     code_bytes = touched * 3 * (dcfg.hidden * dcfg.inter * dcfg.K // 8)
     dstep = {n: float(dper[:, i].mean()) for i, n in enumerate(M.STEPS)}
     routed_ms = dstep["gemv_gateup"] + dstep["mfma_gateup"] + dstep["gemv_down"] + dstep["mfma_down"]
     code_gbps = code_bytes / (routed_ms * 1e-3) / 1e9
-    print(f"[bench] decode {ddev * 1000:.1f} us/layer, code {code_gbps:.0f} GB/s; "
+    print(f"[bench] decode {ddev * 1000:.1f} us/layer ({dgraph * 1000:.1f} from graph replays), code {code_gbps:.0f} GB/s; "
           f"steps {json.dumps({k: round(v * 1000, 1) for k, v in dstep.items()})}", file=sys.stderr, flush=True)
     del dkeep, dweights
     torch.cuda.empty_cache()
@@ -311,6 +353,7 @@ def main():
                      "launch_ms": gu_ms, "flops_per_launch": gu_flops},
         "step_ms": step_ms,
         "decode": {"workload": "decode-8: T=8, same layer, no router bias", "us_per_layer": ddev * 1000,
+                   "us_per_layer_graph_replay": dgraph * 1000,
                    "host_ms_per_step": dms, "touched_experts": touched, "code_bytes": code_bytes,
                    "routed_kernels_us": routed_ms * 1000, "code_GBps": code_gbps,
                    "code_hbm_frac": code_gbps / PEAK_HBM_GBPS,
