@@ -107,7 +107,9 @@ MOE_DEV void gemv_stream(__amdgpu_buffer_rsrc_t rs, uint32_t v0, uint32_t v1, ui
         }
     };
     // tk0, tk1 are wavefront-uniform: every branch below is scalar.
-    // tk1 - tk0 is a positive multiple of kGemvU.  Every load is issued
+    // tk1 - tk0 is a positive multiple of kGemvU (an even one for every
+    // shape the library accepts, so the single-group tail below is kept only
+    // for generality).  Every load is issued
     // unconditionally: a group past the wave's range reloads its last group
     // (in range, just read, never used), so no load sits behind a branch and
     // the two register sets need no copies to merge loaded and kept values.
