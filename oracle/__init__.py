@@ -60,7 +60,14 @@ def lib():
             C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, C.c_uint32, C.c_int, C.c_int,
             _u16p, _i64p, C.c_int64, _u16p, C.c_void_p,
             C.POINTER(C.c_void_p), C.POINTER(C.c_void_p), C.POINTER(C.c_void_p),
-            C.c_void_p, _i32p, _f64p, _f64p, C.c_int]
+            C.c_void_p, C.c_void_p, C.c_void_p, C.c_int, _i32p, _f64p, _f64p, C.c_int]
+        l.orc_tile_position.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, C.c_int]
+        l.orc_tile_position.restype = C.c_int64
+        l.orc_decode_matrix_order.argtypes = [_u16p, C.c_int, C.c_int, C.c_int, C.c_uint32, C.c_int,
+                                              C.c_int, _f32p]
+        l.orc_decode_matrix_order.restype = C.c_int
+        l.orc_sylvester.argtypes = [C.c_int, np.ctypeslib.ndpointer(np.int8, flags="C_CONTIGUOUS")]
+        l.orc_rotate.argtypes = [_f64p, C.c_int, C.c_void_p]
         l.orc_layer.restype = C.c_int
         l.orc_f16_to_double.argtypes = [C.c_uint16]
         l.orc_f16_to_double.restype = C.c_double
@@ -117,6 +124,41 @@ def decode_matrix(codes: np.ndarray, n_in: int, n_out: int, K: int, mcg: int,
     return out
 
 
+def tile_position(order: int, n_in: int, n_out: int, tk: int, tn: int) -> int:
+    """Position (in tiles) of tile (tk, tn) in a stored tile order."""
+    return lib().orc_tile_position(order, n_in, n_out, tk, tn)
+
+
+def decode_matrix_order(codes: np.ndarray, n_in: int, n_out: int, K: int, mcg: int,
+                        codebook: int, order: int) -> np.ndarray:
+    """Dense [in][out] fp32 matrix of a projection stored in tile `order`."""
+    c = _u16(codes).reshape(-1)
+    assert c.size == (n_in // 16) * (n_out // 16) * 16 * K
+    out = np.zeros((n_in, n_out), dtype=np.float32)
+    if lib().orc_decode_matrix_order(c, n_in, n_out, K, mcg, codebook, order, out) != 0:
+        raise ValueError("unknown tile order or shape")
+    return out
+
+
+# ------------------------------------------------------------------ rotation
+def sylvester(n: int) -> np.ndarray:
+    """The n x n Hadamard matrix by Sylvester's construction (int8)."""
+    h = np.zeros((n, n), dtype=np.int8)
+    lib().orc_sylvester(n, h)
+    return h
+
+
+def rotate(v: np.ndarray, signs: Optional[np.ndarray] = None) -> np.ndarray:
+    """Block rotation (128-blocks, orthonormal) of each row of v, after an
+    optional elementwise sign vector."""
+    a = np.array(v, dtype=np.float64, order="C", copy=True)
+    rows = a.reshape(-1, a.shape[-1])
+    s = None if signs is None else np.ascontiguousarray(signs, dtype=np.int8)
+    for r in rows:
+        lib().orc_rotate(r, r.size, None if s is None else s.ctypes.data)
+    return a
+
+
 # -------------------------------------------------------------------- routing
 def router_logits(x_bits: np.ndarray, act_dtype: int, router_w: np.ndarray,
                   bias: Optional[np.ndarray]) -> np.ndarray:
@@ -152,26 +194,30 @@ def segments(idx: np.ndarray, E: int):
 
 # ---------------------------------------------------------------------- layer
 def layer(inp, tokens: Optional[Sequence[int]] = None, nthreads: int = 0,
-          codes: Optional[Sequence[np.ndarray]] = None, present=None):
+          codes: Optional[Sequence] = None, present=None):
     """Layer output (fp64) for the given token subset of a `workloads.LayerInputs`.
 
     Returns (idx [n][k] int32, w [n][k] fp64, out [n][H] fp64).  `codes`
-    overrides inp.codes: 3 arrays [E][words] or 3 dicts {expert: words}.
-    Experts missing from a dict, or outside `present`, are passed as NULL and
-    routing a selected token to one of them is an error.
+    overrides inp.codes: 3 sequences indexed by expert ([E][words] arrays or
+    lists of per-expert arrays) or 3 dicts {expert: words}.  Experts missing
+    from a dict, or outside `present`, are passed as NULL and routing a
+    selected token to one of them is an error.  With per-tensor widths
+    (inp.ktab), sign vectors (inp.signs) or a trellis shared expert
+    (cfg.shared_trellis, expert index E) the oracle applies them.
     """
     cfg = inp.cfg
     H, I, E, k = cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k
+    EA = cfg.n_trellis
     T = inp.x.shape[0]
     tok = np.arange(T, dtype=np.int64) if tokens is None else np.asarray(tokens, dtype=np.int64)
     assert tok.size == 0 or (tok.min() >= 0 and tok.max() < T)
     cds = inp.codes if codes is None else codes
-    ptrs = (C.c_void_p * (3 * E))()
+    ptrs = (C.c_void_p * (3 * EA))()
     keep = []
     for p in range(3):
         arr = cds[p]
-        for e in range(E):
-            if present is not None and e not in present:
+        for e in range(EA):
+            if present is not None and e not in present and e < E:
                 continue
             if isinstance(arr, dict):
                 if e not in arr:
@@ -180,11 +226,13 @@ def layer(inp, tokens: Optional[Sequence[int]] = None, nthreads: int = 0,
             else:
                 row = arr[e]
                 assert row.dtype == np.uint16 and row.flags.c_contiguous
-            assert row.size == cfg.words_per_expert(p)
+            assert row.size == cfg.words_of(p, e, inp.ktab)
             keep.append(row)
-            ptrs[p * E + e] = row.ctypes.data
+            ptrs[p * EA + e] = row.ctypes.data
     suh = [np.ascontiguousarray(a) for a in inp.suh]
     svh = [np.ascontiguousarray(a) for a in inp.svh]
+    for p in range(3):
+        assert suh[p].shape[0] == EA and svh[p].shape[0] == EA
     suh_p = (C.c_void_p * 3)(*[a.ctypes.data for a in suh])
     svh_p = (C.c_void_p * 3)(*[a.ctypes.data for a in svh])
     shared_arr = None
@@ -192,6 +240,12 @@ def layer(inp, tokens: Optional[Sequence[int]] = None, nthreads: int = 0,
     if inp.shared is not None:
         shared_arr = [np.ascontiguousarray(a) for a in inp.shared]
         shared_p = (C.c_void_p * 3)(*[a.ctypes.data for a in shared_arr])
+    ktab = None if inp.ktab is None else np.ascontiguousarray(inp.ktab, dtype=np.int32)
+    if ktab is not None:
+        assert ktab.shape == (3, EA)
+    signs = None if inp.signs is None else np.ascontiguousarray(inp.signs, dtype=np.int8)
+    if signs is not None:
+        assert signs.shape == (2, H)
     idx = np.zeros((tok.size, k), dtype=np.int32)
     w = np.zeros((tok.size, k), dtype=np.float64)
     out = np.zeros((tok.size, H), dtype=np.float64)
@@ -202,9 +256,12 @@ def layer(inp, tokens: Optional[Sequence[int]] = None, nthreads: int = 0,
         None if bias is None else bias.ctypes.data,
         ptrs, suh_p, svh_p,
         C.cast(shared_p, C.c_void_p) if shared_p is not None else None,
+        None if ktab is None else ktab.ctypes.data,
+        None if signs is None else signs.ctypes.data,
+        1 if cfg.shared_trellis else 0,
         idx, w, out, nthreads)
     if rc != 0:
-        raise RuntimeError("oracle layer: codes of a routed expert are missing")
+        raise RuntimeError("oracle layer: codes of a needed expert are missing, or a width is invalid")
     return idx, w, out
 
 

@@ -11,14 +11,22 @@
  *        EXL3 tensors are packed 16-bit trellis words holding 16/K weights each.
  *   [p2] "GLM-5.3 Flash EXL3 for 2x DGX Sparks", "Cold prefill (E3 grouped MoE)"
  *        (gather, gate/up + SwiGLU, down + scatter, device segment tables) and
- *        "What runs" (packed trellis + suh + svh + mcg, codebook MCG).
+ *        "What runs" (the routed experts are EXL3 trellis tensors with their
+ *        side vectors, read through the MCG codebook).
  *   [p3] "GLM-5.3-Flash EXL3 K2", "What is in the shards": per expert tensor
  *        `suh`, `svh`, `trellis` and a (1,) int32 `mcg`.
  *   [p4] "GLM-5.3-Flash . exlr8 (K2/K3/K4)": opening paragraph (round every
  *        codebook value to FP8 E4M3, nearest-even, saturating, before the side
  *        vectors) and "Loading" (4096 x 128 gate/up halves, 288 experts top-8,
  *        one shared expert).
- *   [p5] "GLM-5.3-Flash-EXL3-TR3-3.5bpw": shared expert left unquantized.
+ *   [p5] "GLM-5.3-Flash-EXL3-TR3-3.5bpw": shared expert left unquantized; its
+ *        settings table gives every routed-expert tensor its own width (K3 or
+ *        K4), which the tensor's payload shape carries.
+ *   [p4] "Index slices" and "Calibration": per layer, one pair of int8 sign
+ *        vectors over the hidden size (`signs` [2, 4096]) and the 128x128
+ *        Hadamard matrix as a primitive of the format; "Loading": the shared
+ *        expert stored as trellis expert 288 after the routed ones, each
+ *        projection in halves of 128 intermediate channels.
  *
  * Where the pages are silent the readings below are this project's own and
  * are listed with their reasons in the design notes:
@@ -30,12 +38,21 @@
  *   tile order  state j of a tile sits at input row 16*tk + (j % 16) and output
  *               column 16*tn + (j / 16); tile (tk, tn) starts at word
  *               (tk * (out/16) + tn) * 16K of the expert's [in/16][out/16] grid
- *   side vecs   W[k][n] = suh[k] * c[k][n] * svh[n] (no rotation)
+ *   side vecs   W[k][n] = suh[k] * c[k][n] * svh[n]
  *   router      fp32 logits in a fixed order (64 lane partial sums, then a
- *               halving tree), top-k by (logit desc, index asc), softmax over
- *               the k chosen logits
+ *               halving tree), top-k by (logit desc, index asc; a NaN logit
+ *               ranks as -inf), softmax over the k chosen logits
  *   segments    stable counting sort of a = t*k + j by expert
  *   combine     out[t] = sum_j w[t][j] * y[t][j] + shared(x[t])
+ *   rotation    optional: the trellis experts work in a rotated basis of the
+ *               hidden dimension, x' = R(s0 * x) and out = s1 * R(expert sum),
+ *               R the block-diagonal 128x128 Hadamard matrix over 2^(7/2),
+ *               s0, s1 the layer's two sign vectors; the router and the fp16
+ *               shared expert see x itself
+ *   widths      optional: a width K per (projection, expert) tensor
+ *   shared      optional: a trellis-coded shared expert stored as expert E
+ *               after the routed ones, added with weight 1 in the experts'
+ *               basis
  *
  * Precision: routing decides integers, so logits are fp32 in the fixed order
  * (every bf16*fp16 or fp16*fp16 product is exact in fp32).  Everything after
@@ -172,6 +189,49 @@ void orc_decode_matrix(const uint16_t *codes, int in, int out, int K, uint32_t m
     }
 }
 
+/* Tile orders a checkpoint may store a projection's [in/16][out/16] tile grid
+ * in ([p1] header: a column-major tile order recorded in the quantization
+ * config, which the loader reorders to the kernels' own layout; [p4]
+ * "Loading": each projection in halves of 128 intermediate channels).  The
+ * function gives the position, in units of one tile, of tile (tk, tn):
+ *   0  row-major grid:    tk * (out/16) + tn (the layout every kernel reads)
+ *   1  column-major grid: tn * (in/16) + tk
+ *   2  groups of 128 output columns stored one after another, each a
+ *      row-major grid of in/16 x 8 tiles: (tn/8) * (in/16) * 8 + tk * 8 + tn%8
+ *      (a gate or up half of 4096 x 128; a down half, which splits the input
+ *      dimension, is order 0)
+ * Returns -1 for an unknown order. */
+int64_t orc_tile_position(int order, int in, int out, int tk, int tn)
+{
+    int64_t ntk = in / 16, ntn = out / 16;
+    switch (order) {
+    case 0: return (int64_t)tk * ntn + tn;
+    case 1: return (int64_t)tn * ntk + tk;
+    case 2: return (int64_t)(tn / 8) * ntk * 8 + (int64_t)tk * 8 + tn % 8;
+    default: return -1;
+    }
+}
+
+/* Dense decode of a projection whose tiles are stored in `order`. */
+int orc_decode_matrix_order(const uint16_t *codes, int in, int out, int K, uint32_t mcg,
+                            int codebook, int order, float *dst)
+{
+    if (orc_tile_position(order, in, out, 0, 0) < 0 || (order == 2 && out % 128))
+        return -1;
+    int ntn = out / 16, ntk = in / 16;
+#pragma omp parallel for schedule(static)
+    for (int tk = 0; tk < ntk; ++tk) {
+        float vals[256];
+        for (int tn = 0; tn < ntn; ++tn) {
+            const uint16_t *w = codes + orc_tile_position(order, in, out, tk, tn) * 16 * (int64_t)K;
+            orc_decode_tile(w, K, mcg, codebook, vals);
+            for (int j = 0; j < 256; ++j)
+                dst[(size_t)(16 * tk + j % 16) * out + 16 * tn + j / 16] = vals[j];
+        }
+    }
+    return 0;
+}
+
 /* Router logits in fp32 ([p1] "Recipe" and [p4] "Intended use": routers stay
  * in source precision because routing is sensitive).  For each (t, e): 64
  * partial sums p[l] accumulate x[t][64i+l] * Wr[e][64i+l] for i = 0, 1, ...
@@ -212,7 +272,13 @@ void orc_router_logits(const uint16_t *x, int x_dtype, int64_t T, int H, const u
 
 /* Top-k of each token's logits by (logit descending, expert ascending), and
  * softmax weights over the k chosen logits ([p4] "Loading": 288 experts with
- * top-8 routing), computed in fp64 from the fp32 logits. */
+ * top-8 routing), computed in fp64 from the fp32 logits.  The pages do not
+ * say how a NaN logit ranks; here it ranks as -inf (below every number, tied
+ * with -inf and, like any tie, broken by the lower expert index), so every
+ * chosen index is a valid expert.  The softmax takes the ranked values: a NaN
+ * logit enters it as -inf. */
+static double rank_key(float v) { return v != v ? -INFINITY : (double)v; }
+
 void orc_topk_softmax(const float *logits, int64_t T, int E, int k, int32_t *idx, double *w)
 {
     char *chosen = (char *)malloc((size_t)E);
@@ -222,16 +288,16 @@ void orc_topk_softmax(const float *logits, int64_t T, int E, int k, int32_t *idx
         for (int j = 0; j < k; ++j) {
             int best = -1;
             for (int e = 0; e < E; ++e)
-                if (!chosen[e] && (best < 0 || l[e] > l[best]))
+                if (!chosen[e] && (best < 0 || rank_key(l[e]) > rank_key(l[best])))
                     best = e;
             chosen[best] = 1;
             idx[t * k + j] = best;
         }
-        double l0 = l[idx[t * k]], sum = 0.0;
+        double l0 = rank_key(l[idx[t * k]]), sum = 0.0;
         for (int j = 0; j < k; ++j)
-            sum += exp((double)l[idx[t * k + j]] - l0);
+            sum += exp(rank_key(l[idx[t * k + j]]) - l0);
         for (int j = 0; j < k; ++j)
-            w[t * k + j] = exp((double)l[idx[t * k + j]] - l0) / sum;
+            w[t * k + j] = exp(rank_key(l[idx[t * k + j]]) - l0) / sum;
     }
     free(chosen);
 }
@@ -262,32 +328,158 @@ void orc_segments(const int32_t *idx, int64_t T, int k, int E, int32_t *counts,
     free(fill);
 }
 
+/* Hadamard matrix of order n (a power of two) by Sylvester's construction:
+ * H_1 = [1], H_2m = [[H_m, H_m], [H_m, -H_m]] ([p4] "Calibration": the 128x128
+ * Hadamard matrix is one of the format's primitives).  Hm is n x n int8. */
+void orc_sylvester(int n, int8_t *Hm)
+{
+    Hm[0] = 1;
+    for (int m = 1; m < n; m *= 2)
+        for (int i = 0; i < m; ++i)
+            for (int j = 0; j < m; ++j) {
+                int8_t v = Hm[i * n + j];
+                Hm[i * n + j + m] = v;
+                Hm[(i + m) * n + j] = v;
+                Hm[(i + m) * n + j + m] = (int8_t)-v;
+            }
+}
+
+/* Block rotation of a vector of length len (a multiple of 128), optionally
+ * after an elementwise sign vector: u = s * v (s NULL: u = v), then each block
+ * of 128 is replaced by H_128 u_block / sqrt(128), a matrix product with the
+ * Sylvester matrix.  H_128 is symmetric and H_128 H_128 = 128 I, so the
+ * rotation is orthonormal and its own inverse. */
+void orc_rotate(double *v, int len, const int8_t *s)
+{
+    int8_t Hm[128 * 128];
+    orc_sylvester(128, Hm);
+    double u[128];
+    for (int b = 0; b < len; b += 128) {
+        for (int j = 0; j < 128; ++j)
+            u[j] = s ? (double)s[b + j] * v[b + j] : v[b + j];
+        for (int i = 0; i < 128; ++i) {
+            double acc = 0.0;
+            for (int j = 0; j < 128; ++j)
+                acc += (double)Hm[i * 128 + j] * u[j];
+            v[b + i] = acc / sqrt(128.0);
+        }
+    }
+}
+
 static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* Routed rows of one trellis expert: for each listed row r (token row tr[r]
+ * of xin, weight wr[r]) ([p2] "Cold prefill": gate/up + SwiGLU, then down +
+ * scatter):
+ *   g[n] = svh_g[n] * sum_k xin[k] suh_g[k] c_g[k][n]       (u likewise)
+ *   h[n] = silu(g[n]) * u[n]
+ *   y[m] = svh_d[m] * sum_n h[n] suh_d[n] c_d[n][m]
+ *   acc[tr[r]] += wr[r] * y
+ * c_p is the expert's decoded projection p at width Kp[p]. */
+static void expert_rows(int H, int I, const int Kp[3], uint32_t mcg, int codebook,
+                        const uint16_t *const cw[3], const uint16_t *suh_g, const uint16_t *suh_u,
+                        const uint16_t *suh_d, const uint16_t *svh_g, const uint16_t *svh_u,
+                        const uint16_t *svh_d, const double *xin, const int64_t *tr,
+                        const double *wr, int64_t nr, double *acc)
+{
+    float *cg = (float *)malloc(sizeof(float) * (size_t)H * I);
+    float *cu = (float *)malloc(sizeof(float) * (size_t)H * I);
+    float *cd = (float *)malloc(sizeof(float) * (size_t)I * H);
+    double *xs_g = (double *)malloc(sizeof(double) * H);
+    double *xs_u = (double *)malloc(sizeof(double) * H);
+    double *hs = (double *)malloc(sizeof(double) * I);
+    double *y = (double *)malloc(sizeof(double) * H);
+    orc_decode_matrix(cw[0], H, I, Kp[0], mcg, codebook, cg);
+    orc_decode_matrix(cw[1], H, I, Kp[1], mcg, codebook, cu);
+    orc_decode_matrix(cw[2], I, H, Kp[2], mcg, codebook, cd);
+    for (int64_t r = 0; r < nr; ++r) {
+        const double *xt = xin + tr[r] * H;
+        for (int kk = 0; kk < H; ++kk) {
+            xs_g[kk] = xt[kk] * orc_f16_to_double(suh_g[kk]);
+            xs_u[kk] = xt[kk] * orc_f16_to_double(suh_u[kk]);
+        }
+        /* columns in blocks of 64 so that each pass over k reads rows */
+#pragma omp parallel for schedule(static)
+        for (int n0 = 0; n0 < I; n0 += 64) {
+            int nn = I - n0 < 64 ? I - n0 : 64;
+            double sg[64], su[64];
+            for (int c = 0; c < nn; ++c)
+                sg[c] = su[c] = 0.0;
+            for (int kk = 0; kk < H; ++kk) {
+                const float *rg = cg + (size_t)kk * I + n0, *ru = cu + (size_t)kk * I + n0;
+                for (int c = 0; c < nn; ++c) {
+                    sg[c] += xs_g[kk] * (double)rg[c];
+                    su[c] += xs_u[kk] * (double)ru[c];
+                }
+            }
+            for (int c = 0; c < nn; ++c) {
+                int n = n0 + c;
+                double g = sg[c] * orc_f16_to_double(svh_g[n]);
+                double u = su[c] * orc_f16_to_double(svh_u[n]);
+                hs[n] = silu(g) * u * orc_f16_to_double(suh_d[n]);
+            }
+        }
+#pragma omp parallel for schedule(static)
+        for (int m0 = 0; m0 < H; m0 += 64) {
+            int mm = H - m0 < 64 ? H - m0 : 64;
+            double sacc[64];
+            for (int c = 0; c < mm; ++c)
+                sacc[c] = 0.0;
+            for (int n = 0; n < I; ++n) {
+                const float *rd = cd + (size_t)n * H + m0;
+                for (int c = 0; c < mm; ++c)
+                    sacc[c] += hs[n] * (double)rd[c];
+            }
+            for (int c = 0; c < mm; ++c)
+                y[m0 + c] = sacc[c] * orc_f16_to_double(svh_d[m0 + c]);
+        }
+        double *at = acc + tr[r] * H;
+        for (int m = 0; m < H; ++m)
+            at[m] += wr[r] * y[m];
+    }
+    free(cg);
+    free(cu);
+    free(cd);
+    free(xs_g);
+    free(xs_u);
+    free(hs);
+    free(y);
+}
 
 /*
  * The layer for a subset of tokens, in fp64 after routing.
  *
- *   codes[p*E + e]  words of expert e, projection p (0 gate, 1 up, 2 down);
- *                   may be NULL for experts no selected token routes to
- *   suh[p], svh[p]  fp16 [E][in], [E][out]
- *   shared[p]       fp16 nn.Linear weights (gate/up [I][H], down [H][I]) or NULL
+ *   E               routed experts; the trellis tensors hold EA = E experts,
+ *                   or EA = E + 1 with shared_trellis (the shared expert is
+ *                   stored as expert E after the routed ones, [p4] "Loading")
+ *   codes[p*EA + e] words of expert e, projection p (0 gate, 1 up, 2 down);
+ *                   may be NULL for routed experts no selected token routes to
+ *   K, ktab         width of every tensor: ktab[p*EA + e] when ktab is not
+ *                   NULL ([p5] settings table: every tensor its own width),
+ *                   K otherwise
+ *   suh[p], svh[p]  fp16 [EA][in], [EA][out]
+ *   signs           NULL, or int8 [2][H] sign vectors ([p4] "Index slices"):
+ *                   the trellis experts then see x' = R(signs[0] * x) and the
+ *                   layer adds signs[1] * R(their weighted sum), R the
+ *                   orthonormal block rotation of orc_rotate
+ *   shared[p]       fp16 nn.Linear weights (gate/up [I][H], down [H][I]) or
+ *                   NULL: the unquantized shared expert ([p1] "Recipe"; [p5]),
+ *                   added with weight 1 on x itself:
+ *                   out[t] += Wd (silu(Wg x) * (Wu x))
  *
- * For each selected token t and each chosen expert e = idx[t][j]
- * ([p2] "Cold prefill": gate/up + SwiGLU, then down + scatter):
- *   g[n] = svh_g[n] * sum_k x[t][k] suh_g[k] c_g[k][n]       (u likewise)
- *   h[n] = silu(g[n]) * u[n]
- *   y[m] = svh_d[m] * sum_n h[n] suh_d[n] c_d[n][m]
- *   out[t] += w[t][j] * y
- * and the unquantized shared expert ([p1] "Recipe"; [p5]) is added with
- * weight 1: out[t] += Wd (silu(Wg x) * (Wu x)).
+ * Routing (logits, top-k, softmax) always reads x.  Each selected token's k
+ * routed experts are added with their routing weights, the trellis shared
+ * expert with weight 1 (expert_rows).
  *
- * Returns 0, or -1 if a needed expert's codes are NULL.
+ * Returns 0, or -1 if a needed expert's codes are NULL or a width is not 2, 3
+ * or 4.
  */
 int orc_layer(int H, int I, int E, int k, int K, uint32_t mcg, int codebook, int x_dtype,
               const uint16_t *x, const int64_t *tok, int64_t n_tok, const uint16_t *router_w,
               const float *bias, const uint16_t *const *codes, const uint16_t *const *suh,
-              const uint16_t *const *svh, const uint16_t *const *shared, int32_t *idx_out,
-              double *w_out, double *out, int nthreads)
+              const uint16_t *const *svh, const uint16_t *const *shared, const int32_t *ktab,
+              const int8_t *signs, int shared_trellis, int32_t *idx_out, double *w_out,
+              double *out, int nthreads)
 {
 #ifdef _OPENMP
     if (nthreads > 0)
@@ -295,126 +487,103 @@ int orc_layer(int H, int I, int E, int k, int K, uint32_t mcg, int codebook, int
 #else
     (void)nthreads;
 #endif
+    const int EA = E + (shared_trellis ? 1 : 0);
     float *lg = (float *)malloc(sizeof(float) * (size_t)E);
     for (int64_t i = 0; i < n_tok; ++i) {
         orc_router_logits(x + tok[i] * H, x_dtype, 1, H, router_w, bias, E, lg);
         orc_topk_softmax(lg, 1, E, k, idx_out + i * k, w_out + i * k);
     }
     free(lg);
-    memset(out, 0, sizeof(double) * (size_t)n_tok * H);
 
-    float *cg = (float *)malloc(sizeof(float) * (size_t)H * I);
-    float *cu = (float *)malloc(sizeof(float) * (size_t)H * I);
-    float *cd = (float *)malloc(sizeof(float) * (size_t)I * H);
-    double *xs_g = (double *)malloc(sizeof(double) * H);
-    double *xs_u = (double *)malloc(sizeof(double) * H);
-    double *g = (double *)malloc(sizeof(double) * I);
-    double *u = (double *)malloc(sizeof(double) * I);
-    double *hs = (double *)malloc(sizeof(double) * I);
-    double *y = (double *)malloc(sizeof(double) * H);
+    /* the trellis experts' input rows, rotated when sign vectors are given */
+    double *xin = (double *)malloc(sizeof(double) * (size_t)n_tok * H);
+    double *acc = (double *)calloc((size_t)n_tok * H, sizeof(double));
+    for (int64_t ti = 0; ti < n_tok; ++ti) {
+        for (int kk = 0; kk < H; ++kk)
+            xin[ti * H + kk] = act_to_double(x[tok[ti] * H + kk], x_dtype);
+        if (signs)
+            orc_rotate(xin + ti * H, H, signs);
+    }
+    int64_t *tr = (int64_t *)malloc(sizeof(int64_t) * (size_t)(n_tok * k + n_tok + 1));
+    double *wr = (double *)malloc(sizeof(double) * (size_t)(n_tok * k + n_tok + 1));
     int rc = 0;
 
-    for (int e = 0; e < E && rc == 0; ++e) {
-        int used = 0;
-        for (int64_t a = 0; a < n_tok * k; ++a)
-            used |= idx_out[a] == e;
-        if (!used)
+    for (int e = 0; e < EA && rc == 0; ++e) {
+        int64_t nr = 0;
+        if (e < E) {
+            for (int64_t a = 0; a < n_tok * k; ++a)
+                if (idx_out[a] == e) {
+                    tr[nr] = a / k;
+                    wr[nr] = w_out[a];
+                    ++nr;
+                }
+        } else {
+            for (int64_t ti = 0; ti < n_tok; ++ti) {
+                tr[nr] = ti;
+                wr[nr] = 1.0;
+                ++nr;
+            }
+        }
+        if (nr == 0)
             continue;
-        if (!codes[0 * E + e] || !codes[1 * E + e] || !codes[2 * E + e]) {
-            rc = -1;
+        int Kp[3];
+        const uint16_t *cw[3];
+        for (int p = 0; p < 3; ++p) {
+            Kp[p] = ktab ? ktab[p * EA + e] : K;
+            cw[p] = codes[p * EA + e];
+            if (!cw[p] || Kp[p] < 2 || Kp[p] > 4)
+                rc = -1;
+        }
+        if (rc)
             break;
-        }
-        orc_decode_matrix(codes[0 * E + e], H, I, K, mcg, codebook, cg);
-        orc_decode_matrix(codes[1 * E + e], H, I, K, mcg, codebook, cu);
-        orc_decode_matrix(codes[2 * E + e], I, H, K, mcg, codebook, cd);
-        const uint16_t *suh_g = suh[0] + (size_t)e * H, *suh_u = suh[1] + (size_t)e * H;
-        const uint16_t *svh_g = svh[0] + (size_t)e * I, *svh_u = svh[1] + (size_t)e * I;
-        const uint16_t *suh_d = suh[2] + (size_t)e * I, *svh_d = svh[2] + (size_t)e * H;
-        for (int64_t a = 0; a < n_tok * k; ++a) {
-            if (idx_out[a] != e)
-                continue;
-            int64_t ti = a / k;
-            const uint16_t *xt = x + tok[ti] * H;
-            for (int kk = 0; kk < H; ++kk) {
-                double xv = act_to_double(xt[kk], x_dtype);
-                xs_g[kk] = xv * orc_f16_to_double(suh_g[kk]);
-                xs_u[kk] = xv * orc_f16_to_double(suh_u[kk]);
-            }
-            /* columns in blocks of 64 so that each pass over k reads rows */
-#pragma omp parallel for schedule(static)
-            for (int n0 = 0; n0 < I; n0 += 64) {
-                int nn = I - n0 < 64 ? I - n0 : 64;
-                double sg[64], su[64];
-                for (int c = 0; c < nn; ++c)
-                    sg[c] = su[c] = 0.0;
-                for (int kk = 0; kk < H; ++kk) {
-                    const float *rg = cg + (size_t)kk * I + n0, *ru = cu + (size_t)kk * I + n0;
-                    for (int c = 0; c < nn; ++c) {
-                        sg[c] += xs_g[kk] * (double)rg[c];
-                        su[c] += xs_u[kk] * (double)ru[c];
-                    }
-                }
-                for (int c = 0; c < nn; ++c) {
-                    int n = n0 + c;
-                    g[n] = sg[c] * orc_f16_to_double(svh_g[n]);
-                    u[n] = su[c] * orc_f16_to_double(svh_u[n]);
-                    hs[n] = silu(g[n]) * u[n] * orc_f16_to_double(suh_d[n]);
-                }
-            }
-#pragma omp parallel for schedule(static)
-            for (int m0 = 0; m0 < H; m0 += 64) {
-                int mm = H - m0 < 64 ? H - m0 : 64;
-                double s[64];
-                for (int c = 0; c < mm; ++c)
-                    s[c] = 0.0;
-                for (int n = 0; n < I; ++n) {
-                    const float *rd = cd + (size_t)n * H + m0;
-                    for (int c = 0; c < mm; ++c)
-                        s[c] += hs[n] * (double)rd[c];
-                }
-                for (int c = 0; c < mm; ++c)
-                    y[m0 + c] = s[c] * orc_f16_to_double(svh_d[m0 + c]);
-            }
-            double wj = w_out[a];
+        expert_rows(H, I, Kp, mcg, codebook, cw, suh[0] + (size_t)e * H, suh[1] + (size_t)e * H,
+                    suh[2] + (size_t)e * I, svh[0] + (size_t)e * I, svh[1] + (size_t)e * I,
+                    svh[2] + (size_t)e * H, xin, tr, wr, nr, acc);
+    }
+
+    for (int64_t ti = 0; ti < n_tok && rc == 0; ++ti) {
+        double *at = acc + ti * H;
+        if (signs) {
+            orc_rotate(at, H, NULL);
             for (int m = 0; m < H; ++m)
-                out[ti * H + m] += wj * y[m];
+                at[m] *= (double)signs[H + m];
         }
+        memcpy(out + ti * H, at, sizeof(double) * H);
     }
 
     if (rc == 0 && shared && shared[0] && shared[1] && shared[2]) {
+        double *xs = (double *)malloc(sizeof(double) * H);
+        double *hs = (double *)malloc(sizeof(double) * I);
         for (int64_t ti = 0; ti < n_tok; ++ti) {
             const uint16_t *xt = x + tok[ti] * H;
             for (int kk = 0; kk < H; ++kk)
-                xs_g[kk] = act_to_double(xt[kk], x_dtype);
+                xs[kk] = act_to_double(xt[kk], x_dtype);
 #pragma omp parallel for schedule(static)
             for (int n = 0; n < I; ++n) {
                 double sg = 0.0, su = 0.0;
                 const uint16_t *wg = shared[0] + (size_t)n * H, *wu = shared[1] + (size_t)n * H;
                 for (int kk = 0; kk < H; ++kk) {
-                    sg += orc_f16_to_double(wg[kk]) * xs_g[kk];
-                    su += orc_f16_to_double(wu[kk]) * xs_g[kk];
+                    sg += orc_f16_to_double(wg[kk]) * xs[kk];
+                    su += orc_f16_to_double(wu[kk]) * xs[kk];
                 }
                 hs[n] = silu(sg) * su;
             }
 #pragma omp parallel for schedule(static)
             for (int m = 0; m < H; ++m) {
-                double s = 0.0;
+                double sacc = 0.0;
                 const uint16_t *wd = shared[2] + (size_t)m * I;
                 for (int n = 0; n < I; ++n)
-                    s += orc_f16_to_double(wd[n]) * hs[n];
-                out[ti * H + m] += s;
+                    sacc += orc_f16_to_double(wd[n]) * hs[n];
+                out[ti * H + m] += sacc;
             }
         }
+        free(xs);
+        free(hs);
     }
 
-    free(cg);
-    free(cu);
-    free(cd);
-    free(xs_g);
-    free(xs_u);
-    free(g);
-    free(u);
-    free(hs);
-    free(y);
+    free(xin);
+    free(acc);
+    free(tr);
+    free(wr);
     return rc;
 }

@@ -44,7 +44,7 @@ MCG_DEFAULT = 0x9E3779B1
 
 _TAGS = {
     "x": 1, "router_w": 2, "router_bias": 3, "codes": 4, "suh": 5, "svh": 6,
-    "shared": 7,
+    "shared": 7, "ktab": 8, "signs": 9,
 }
 
 
@@ -63,18 +63,33 @@ class LayerConfig:
     router_bias: bool = False
     shared: bool = False
     mcg: int = MCG_DEFAULT
+    # every (projection, expert) tensor at its own width, drawn from {3, 4}
+    mixed_k: bool = False
+    # the layer's two int8 sign vectors over the hidden size (rotated experts)
+    hadamard: bool = False
+    # a trellis-coded shared expert stored after the routed ones (index E)
+    shared_trellis: bool = False
 
     @property
     def side_scale(self) -> float:
         return 1.0 / math.sqrt(self.hidden)
 
+    @property
+    def n_trellis(self) -> int:
+        """Trellis-coded experts stored: the routed ones (+ the shared one)."""
+        return self.n_experts + (1 if self.shared_trellis else 0)
+
     def proj_shape(self, p: int):
         """(in, out) of projection p; gate/up are [H][I], down is [I][H]."""
         return (self.hidden, self.inter) if p != PROJ_DOWN else (self.inter, self.hidden)
 
-    def words_per_expert(self, p: int) -> int:
+    def words_per_expert(self, p: int, K: Optional[int] = None) -> int:
         i, o = self.proj_shape(p)
-        return (i // 16) * (o // 16) * 16 * self.K
+        return (i // 16) * (o // 16) * 16 * (self.K if K is None else K)
+
+    def words_of(self, p: int, e: int, ktab=None) -> int:
+        """Words of tensor (p, e) at its width (ktab[p][e] when given)."""
+        return self.words_per_expert(p, None if ktab is None else int(ktab[p][e]))
 
     def replace(self, **kw) -> "LayerConfig":
         return dataclasses.replace(self, **kw)
@@ -91,7 +106,18 @@ CONFIGS: List[LayerConfig] = [
     LayerConfig("mixed_k4", 3, 2048, 4096, 2048, 288, 8, 4, CB_MCG, DT_BF16, True, True),
     LayerConfig("fp8", 4, 16384, 4096, 2048, 288, 8, 4, CB_MCG_E4M3, DT_BF16, True, True),
 ]
-BY_NAME: Dict[str, LayerConfig] = {c.name: c for c in CONFIGS}
+# Further workloads for the format variants: per-tensor widths K3/K4 at the
+# 2048-token prefill (the K3/K4 split of a 3.5 bpw build), and the decode step
+# and the 2048-token prefill with rotated experts and a trellis-coded shared
+# expert (the exlr8 v2 layout, K4, E4M3-rounded codebook).
+VARIANTS: List[LayerConfig] = [
+    LayerConfig("mixed_k34", 3, 2048, 4096, 2048, 288, 8, 4, CB_MCG, DT_BF16, True, True, mixed_k=True),
+    LayerConfig("exlr8_decode", 5, 8, 4096, 2048, 288, 8, 4, CB_MCG_E4M3, DT_BF16, False, False,
+                hadamard=True, shared_trellis=True),
+    LayerConfig("exlr8_prefill", 6, 2048, 4096, 2048, 288, 8, 4, CB_MCG_E4M3, DT_BF16, True, False,
+                hadamard=True, shared_trellis=True),
+]
+BY_NAME: Dict[str, LayerConfig] = {c.name: c for c in CONFIGS + VARIANTS}
 
 
 def _rng(seed: int, tag: str, *idx: int) -> np.random.Generator:
@@ -142,31 +168,52 @@ def gen_router_bias(cfg: LayerConfig) -> Optional[np.ndarray]:
     return _rng(cfg.seed, "router_bias").standard_normal(cfg.n_experts).astype(np.float32)
 
 
-def gen_codes_expert(cfg: LayerConfig, p: int, e: int) -> np.ndarray:
-    """Uniform random 16-bit trellis words of expert e, projection p (flat)."""
-    return _rng(cfg.seed, "codes", cfg.K, p, e).integers(
-        0, 1 << 16, size=cfg.words_per_expert(p), dtype=np.uint16)
+def gen_ktab(cfg: LayerConfig) -> Optional[np.ndarray]:
+    """Per-tensor widths [3][n_trellis] int32, each K3 or K4 with equal odds,
+    or None for a layer at one width."""
+    if not cfg.mixed_k:
+        return None
+    return _rng(cfg.seed, "ktab").integers(3, 5, size=(3, cfg.n_trellis)).astype(np.int32)
 
 
-def gen_codes(cfg: LayerConfig, p: int, experts=None):
-    """Codes of projection p: [E][words] for all experts, or, with `experts`
-    given, a dict {expert: words} holding only those experts."""
+def gen_signs(cfg: LayerConfig) -> Optional[np.ndarray]:
+    """The layer's two sign vectors [2][H] int8 (+1 or -1 with equal odds)."""
+    if not cfg.hadamard:
+        return None
+    return (_rng(cfg.seed, "signs").integers(0, 2, size=(2, cfg.hidden)) * 2 - 1).astype(np.int8)
+
+
+def gen_codes_expert(cfg: LayerConfig, p: int, e: int, K: Optional[int] = None) -> np.ndarray:
+    """Uniform random 16-bit trellis words of expert e, projection p (flat),
+    at width K (default: the layer's)."""
+    K = cfg.K if K is None else K
+    return _rng(cfg.seed, "codes", K, p, e).integers(
+        0, 1 << 16, size=cfg.words_per_expert(p, K), dtype=np.uint16)
+
+
+def gen_codes(cfg: LayerConfig, p: int, experts=None, ktab=None):
+    """Codes of projection p: [n_trellis][words] for all experts (a list of
+    per-expert arrays when the widths differ), or, with `experts` given, a dict
+    {expert: words} holding only those experts."""
+    kof = (lambda e: None) if ktab is None else (lambda e: int(ktab[p][e]))
     if experts is not None:
-        return {int(e): gen_codes_expert(cfg, p, int(e)) for e in experts}
+        return {int(e): gen_codes_expert(cfg, p, int(e), kof(int(e))) for e in experts}
+    if ktab is not None:
+        return [gen_codes_expert(cfg, p, e, kof(e)) for e in range(cfg.n_trellis)]
     n = cfg.words_per_expert(p)
-    out = np.empty((cfg.n_experts, n), dtype=np.uint16)
-    for e in range(cfg.n_experts):
+    out = np.empty((cfg.n_trellis, n), dtype=np.uint16)
+    for e in range(cfg.n_trellis):
         out[e] = gen_codes_expert(cfg, p, e)
     return out
 
 
 def gen_side(cfg: LayerConfig, p: int):
-    """(suh [E][in], svh [E][out]) fp16 ~ U(0.5, 1.5) * side_scale."""
+    """(suh [n_trellis][in], svh [n_trellis][out]) fp16 ~ U(0.5, 1.5) * side_scale."""
     i, o = cfg.proj_shape(p)
     r = _rng(cfg.seed, "suh", p)
-    suh = (r.uniform(0.5, 1.5, (cfg.n_experts, i)) * cfg.side_scale).astype(np.float16)
+    suh = (r.uniform(0.5, 1.5, (cfg.n_trellis, i)) * cfg.side_scale).astype(np.float16)
     r = _rng(cfg.seed, "svh", p)
-    svh = (r.uniform(0.5, 1.5, (cfg.n_experts, o)) * cfg.side_scale).astype(np.float16)
+    svh = (r.uniform(0.5, 1.5, (cfg.n_trellis, o)) * cfg.side_scale).astype(np.float16)
     return suh, svh
 
 
@@ -188,21 +235,28 @@ class LayerInputs:
     x: np.ndarray                      # [T][H] uint16 bits of act dtype
     router_w: np.ndarray               # [E][H] fp16
     router_bias: Optional[np.ndarray]  # [E] fp32 or None
-    codes: list                        # 3 x ([E][words] uint16, or {expert: words})
-    suh: List[np.ndarray]              # 3 x [E][in] fp16
-    svh: List[np.ndarray]              # 3 x [E][out] fp16
+    codes: list                        # 3 x ([n_trellis][words] uint16, per-expert list, or dict)
+    suh: List[np.ndarray]              # 3 x [n_trellis][in] fp16
+    svh: List[np.ndarray]              # 3 x [n_trellis][out] fp16
     shared: Optional[List[np.ndarray]]
+    ktab: Optional[np.ndarray] = None  # [3][n_trellis] int32 per-tensor widths
+    signs: Optional[np.ndarray] = None # [2][H] int8 sign vectors
 
 
 def gen_layer(cfg: LayerConfig, tokens: Optional[int] = None, experts=None) -> LayerInputs:
     suh, svh = zip(*(gen_side(cfg, p) for p in range(3)))
+    ktab = gen_ktab(cfg)
+    if experts is not None and cfg.shared_trellis:
+        experts = sorted(set(int(e) for e in experts) | {cfg.n_experts})
     return LayerInputs(
         cfg=cfg,
         x=gen_x(cfg, tokens),
         router_w=gen_router_w(cfg),
         router_bias=gen_router_bias(cfg),
-        codes=[gen_codes(cfg, p, experts) for p in range(3)],
+        codes=[gen_codes(cfg, p, experts, ktab) for p in range(3)],
         suh=list(suh),
         svh=list(svh),
         shared=gen_shared(cfg),
+        ktab=ktab,
+        signs=gen_signs(cfg),
     )
