@@ -66,6 +66,8 @@ def lib():
         l.orc_decode_matrix_order.argtypes = [_u16p, C.c_int, C.c_int, C.c_int, C.c_uint32, C.c_int,
                                               C.c_int, _f32p]
         l.orc_decode_matrix_order.restype = C.c_int
+        l.orc_expand_block_scales.argtypes = [_u16p, C.c_int, C.c_int, C.c_int, C.POINTER(C.c_void_p),
+                                              C.POINTER(C.c_void_p)]
         l.orc_sylvester.argtypes = [C.c_int, np.ctypeslib.ndpointer(np.int8, flags="C_CONTIGUOUS")]
         l.orc_rotate.argtypes = [_f64p, C.c_int, C.c_void_p]
         l.orc_layer.restype = C.c_int
@@ -138,6 +140,20 @@ def decode_matrix_order(codes: np.ndarray, n_in: int, n_out: int, K: int, mcg: i
     if lib().orc_decode_matrix_order(c, n_in, n_out, K, mcg, codebook, order, out) != 0:
         raise ValueError("unknown tile order or shape")
     return out
+
+
+def expand_block_scales(block: np.ndarray, H: int, I: int):
+    """(suh[3], svh[3]) fp16 side vectors from an fp16 block table
+    [EA][3][H/128] (exlr8 "Index slices" reading)."""
+    b = np.ascontiguousarray(block, dtype=np.float16)
+    EA = b.shape[0]
+    assert b.shape == (EA, 3, H // 128)
+    suh = [np.zeros((EA, H), np.float16), np.zeros((EA, H), np.float16), np.zeros((EA, I), np.float16)]
+    svh = [np.zeros((EA, I), np.float16), np.zeros((EA, I), np.float16), np.zeros((EA, H), np.float16)]
+    sp = (C.c_void_p * 3)(*[a.ctypes.data for a in suh])
+    vp = (C.c_void_p * 3)(*[a.ctypes.data for a in svh])
+    lib().orc_expand_block_scales(_u16(b), EA, H, I, sp, vp)
+    return suh, svh
 
 
 # ------------------------------------------------------------------ rotation

@@ -232,6 +232,33 @@ int orc_decode_matrix_order(const uint16_t *codes, int in, int out, int K, uint3
     return 0;
 }
 
+/* Side vectors from the exlr8 block table ([p4] "Index slices": F16 block
+ * scales [EA][3][H/128] per layer; "Loading": 32 per projection at hidden
+ * 4096).  This project's reading: a scale covers 128 channels of the hidden
+ * dimension, the input of gate and up and the output of down; the
+ * intermediate side carries no scale (1).
+ *   suh_g[e][k] = block[e][0][k/128]   suh_u[e][k] = block[e][1][k/128]
+ *   svh_d[e][m] = block[e][2][m/128]   svh_g = svh_u = suh_d = 1
+ * suh[p], svh[p] as in orc_layer ([EA][in], [EA][out]). */
+void orc_expand_block_scales(const uint16_t *block, int EA, int H, int I, uint16_t *const *suh,
+                             uint16_t *const *svh)
+{
+    const uint16_t one = 0x3C00; /* fp16 1.0 */
+    int nb = H / 128;
+    for (int e = 0; e < EA; ++e) {
+        for (int k = 0; k < H; ++k) {
+            suh[0][(size_t)e * H + k] = block[((size_t)e * 3 + 0) * nb + k / 128];
+            suh[1][(size_t)e * H + k] = block[((size_t)e * 3 + 1) * nb + k / 128];
+            svh[2][(size_t)e * H + k] = block[((size_t)e * 3 + 2) * nb + k / 128];
+        }
+        for (int n = 0; n < I; ++n) {
+            svh[0][(size_t)e * I + n] = one;
+            svh[1][(size_t)e * I + n] = one;
+            suh[2][(size_t)e * I + n] = one;
+        }
+    }
+}
+
 /* Router logits in fp32 ([p1] "Recipe" and [p4] "Intended use": routers stay
  * in source precision because routing is sensitive).  For each (t, e): 64
  * partial sums p[l] accumulate x[t][64i+l] * Wr[e][64i+l] for i = 0, 1, ...

@@ -235,3 +235,16 @@ def test_exlr8_half_sizes():
     # a 4096 x 128 gate/up half at width K is 65,536 K bytes (exlr8 "Loading")
     for K in (2, 3, 4):
         assert (4096 // 16) * (128 // 16) * 16 * K * 2 == 65536 * K
+
+
+# ---------------------------------------------------------- block scales
+def test_block_scale_expansion_matches_numpy_repeat():
+    rng = np.random.default_rng(5)
+    EA, H, I = 3, 512, 256
+    block = rng.uniform(0.5, 1.5, (EA, 3, H // 128)).astype(np.float16)
+    suh, svh = oracle.expand_block_scales(block, H, I)
+    np.testing.assert_array_equal(suh[0], np.repeat(block[:, 0, :], 128, axis=1))
+    np.testing.assert_array_equal(suh[1], np.repeat(block[:, 1, :], 128, axis=1))
+    np.testing.assert_array_equal(svh[2], np.repeat(block[:, 2, :], 128, axis=1))
+    for a in (svh[0], svh[1], suh[2]):
+        assert a.shape == (EA, I) and (a == np.float16(1.0)).all()
