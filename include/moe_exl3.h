@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define MOE_EXL3_ABI_VERSION 1
+#define MOE_EXL3_ABI_VERSION 2
 
 /* error codes */
 #define MOE_EXL3_OK 0
@@ -74,6 +74,8 @@ extern "C" {
 #define MOE_EXL3_DT_F16 1
 #define MOE_EXL3_DT_BF16 2
 #define MOE_EXL3_DT_FP8 3   /* OCP E4M3FN bit patterns, one byte per value */
+#define MOE_EXL3_DT_GEMV_F16 4   /* moe_exl3_decode only: fp16 128*c + 1532, the
+                                    decode-fused GEMV's dot-product operand */
 
 /* codebooks */
 #define MOE_EXL3_CB_MCG 0
@@ -82,15 +84,78 @@ extern "C" {
 /* desc.flags */
 #define MOE_EXL3_HAS_SHARED (1u << 0)       /* add the fp16 shared expert */
 #define MOE_EXL3_HAS_ROUTER_BIAS (1u << 1)  /* add router_bias to the logits */
-#define MOE_EXL3_FORCE_GEMV (1u << 2)       /* every routed expert on the decode-fused GEMV path */
+#define MOE_EXL3_FORCE_GEMV (1u << 2)       /* raise the GEMV row threshold to its maximum, 8
+                                               rows: experts with more rows still run on MFMA
+                                               tiles, and with hidden > 8192 (the GEMV's LDS
+                                               limit) every expert does */
 #define MOE_EXL3_FORCE_MFMA (1u << 3)       /* every routed expert on the MFMA path */
 #define MOE_EXL3_FP8_MFMA (1u << 4)         /* routed MFMA GEMMs in fp8 (needs CB_MCG_E4M3 and hidden, inter % 256 == 0) */
+#define MOE_EXL3_DEBUG_CHECKS (1u << 5)     /* extra launches that check the routing tables and
+                                               the finiteness of x into the status word */
+#define MOE_EXL3_DETERMINISTIC_COMBINE (1u << 6) /* accepted, always in effect: the k slot rows of
+                                               a token and the shared expert are summed in
+                                               fp32 in a fixed order, so the same inputs give
+                                               the same bits on every call */
+/*
+ * Format variants (page "GLM-5.3-Flash . exlr8 (K2/K3/K4)"; page
+ * "GLM-5.3-Flash-EXL3-TR3-3.5bpw"):
+ *   HADAMARD        the trellis experts work in a rotated basis of the hidden
+ *                   dimension ("Calibration": the 128x128 Hadamard matrix is a
+ *                   format primitive; "Index slices": one pair of int8 sign
+ *                   vectors over the hidden size per layer, weights.signs).
+ *                   The experts read x' = R(s0 * x) and the layer adds
+ *                   s1 * R(their weighted sum), R the block-diagonal matrix of
+ *                   128x128 Sylvester-Hadamard blocks over sqrt(128).  The
+ *                   router and the fp16 shared expert read x itself.  x' is
+ *                   rounded to fp16 once.
+ *   SHARED_TRELLIS  a trellis-coded shared expert stored as expert E after the
+ *                   routed ones ("Loading": the shared expert is expert 288):
+ *                   codes, suh and svh hold E + 1 experts, and expert E is
+ *                   added for every token with weight 1, in the trellis
+ *                   experts' basis.  Needs n_experts <= 1016.
+ *   PER_TENSOR_K    every (projection, expert) tensor has its own width (the
+ *                   TR3-3.5bpw settings table: each routed-expert tensor K3 or
+ *                   K4): weights.k_tab and weights.code_tab replace desc.K and
+ *                   codes[] (see moe_exl3_weights).
+ */
+#define MOE_EXL3_HADAMARD (1u << 7)
+#define MOE_EXL3_SHARED_TRELLIS (1u << 8)
+#define MOE_EXL3_PER_TENSOR_K (1u << 9)
+
+/*
+ * Status word.  Every moe_exl3_layer / moe_exl3_route call clears the int32
+ * at byte MOE_EXL3_STATUS_OFFSET of its workspace in its first launch; later
+ * launches set these bits in it.  It is valid once the call's work on the
+ * stream has finished (the caller synchronises and reads it).  With a bit
+ * other than ACT_RANGE set the outputs are unspecified.
+ */
+#define MOE_EXL3_STATUS_OFFSET 8
+#define MOE_EXL3_STATUS_BAD_INDEX (1u << 0)      /* an expert index outside [0, E) reached the
+                                                    segment tables (left out of them) */
+#define MOE_EXL3_STATUS_TILE_OVERFLOW (1u << 1)  /* more MFMA row tiles than the workspace holds
+                                                    (the list was cut) */
+#define MOE_EXL3_STATUS_ACT_RANGE (1u << 2)      /* a finite bf16 activation beyond the fp16 range
+                                                    (|x| >= 65520) became inf in the fp16 copy the
+                                                    expert GEMMs read */
+#define MOE_EXL3_STATUS_COUNTS (1u << 3)         /* DEBUG_CHECKS: counts do not sum to T*k */
+#define MOE_EXL3_STATUS_TABLES (1u << 4)         /* DEBUG_CHECKS: offsets, sorted_ids or pos are
+                                                    not the stable sort of idx */
+#define MOE_EXL3_STATUS_NONFINITE_X (1u << 5)    /* DEBUG_CHECKS: x holds an inf or NaN */
+#define MOE_EXL3_STATUS_BAD_WIDTH (1u << 6)      /* PER_TENSOR_K: a k_tab entry outside {2, 3, 4} */
 
 /*
  * Layer description.  Shape rules: hidden is a multiple of 256, inter a
  * multiple of 128, both at most 16384; n_experts is a multiple of 8 and at
  * most 1024; 1 <= top_k <= min(n_experts, 16); K in {2, 3, 4}; act_dtype is
  * F16 or BF16; T * top_k < 2^31.
+ *
+ * Activation range: the expert GEMMs and the shared expert read an fp16 copy
+ * of bf16 activations, exact for |x| in [2^-14, 65504]; smaller values round
+ * as fp16 subnormals, and finite values of magnitude 65520 or more become inf
+ * (flagged as MOE_EXL3_STATUS_ACT_RANGE).  The router reads x itself.
+ * NaN logits rank below every number (as -inf, ties to the lower expert), so
+ * the chosen experts are always valid; a token whose chosen logits are all
+ * -inf or NaN gets NaN routing weights.
  */
 typedef struct moe_exl3_desc {
     int32_t hidden;         /* H */
@@ -106,15 +171,28 @@ typedef struct moe_exl3_desc {
                                GEMV path; 0 selects the default (2) */
 } moe_exl3_desc;
 
-/* Layer weights.  All device pointers, contiguous, row-major. */
+/*
+ * Layer weights.  All device pointers, contiguous, row-major.  EA is the
+ * number of trellis-coded experts: E, or E + 1 with SHARED_TRELLIS.
+ */
 typedef struct moe_exl3_weights {
-    const uint16_t *codes[3];   /* gate, up, down: [E][in/16][out/16][16K] */
-    const uint16_t *suh[3];     /* fp16 [E][in]  input-channel side vectors */
-    const uint16_t *svh[3];     /* fp16 [E][out] output-channel side vectors */
+    const uint16_t *codes[3];   /* gate, up, down: [EA][in/16][out/16][16K]; not read
+                                   with PER_TENSOR_K */
+    const uint16_t *suh[3];     /* fp16 [EA][in]  input-channel side vectors */
+    const uint16_t *svh[3];     /* fp16 [EA][out] output-channel side vectors */
     const uint16_t *router_w;   /* fp16 [E][H] */
     const float *router_bias;   /* fp32 [E], read only with HAS_ROUTER_BIAS */
     const uint16_t *shared_w[3];/* fp16 nn.Linear weights: gate/up [I][H], down [H][I];
                                    read only with HAS_SHARED */
+    const int8_t *signs;        /* int8 [2][H] (+1 / -1): s0 = signs[0], s1 = signs[1];
+                                   read only with HADAMARD */
+    const uint64_t *code_tab;   /* PER_TENSOR_K: device array [3][EA] of device addresses,
+                                   the [in/16][out/16][16 K] words of tensor (p, e), each
+                                   16-byte aligned */
+    const int32_t *k_tab;       /* PER_TENSOR_K: device int32 [3][EA], the width of tensor
+                                   (p, e), each 2, 3 or 4 (an entry outside that range
+                                   sets MOE_EXL3_STATUS_BAD_WIDTH and the tensor is read
+                                   as zero) */
 } moe_exl3_weights;
 
 /* ABI version (MOE_EXL3_ABI_VERSION). */
@@ -179,14 +257,65 @@ int moe_exl3_layer_profiled(const moe_exl3_desc *desc, const moe_exl3_weights *w
                             void *stream, void *const *events, int n_events);
 
 /*
- * Dense decode of one trellis-coded [n_in][n_out] matrix (no side vectors):
- * dst[k][n] = c (dst_dtype F32, F16, BF16: exact) or its E4M3FN bit pattern
- * (FP8, exact for the E4M3 codebook; for CB_MCG values are rounded to E4M3).
+ * Dense decode of one trellis-coded [n_in][n_out] matrix (no side vectors),
+ * for the bit-exact check of the decode (page "GLM-5.3-Flash EXL3 (~2.1 bpw,
+ * SM70 tile order)", header: packed 16-bit words, 16/K weights each).  Each
+ * dst_dtype runs the fragment decoder of one kernel of the layer:
+ *   F16       dst = c in fp16, from the gate/up MFMA's decoder (exact)
+ *   BF16      dst = c in bf16, from the down MFMA's decoder (exact)
+ *   FP8       dst = E4M3FN bits of c, from the fp8 MFMA's decoder (exact for
+ *             the E4M3 codebook; CB_MCG values are rounded to E4M3)
+ *   GEMV_F16  dst = 128 c + 1532 in fp16, the decode-fused GEMV's operand (exact)
+ *   F32       dst = c in fp32 (exact)
  * codes: device [n_in/16][n_out/16][16K] uint16; dst: device, row-major.
  * n_in and n_out are positive multiples of 16.
  */
 int moe_exl3_decode(const uint16_t *codes, int32_t n_in, int32_t n_out, int32_t K, uint32_t mcg,
                     int32_t codebook, void *dst, int32_t dst_dtype, void *stream);
+
+/*
+ * Load-time tile reorder of `count` trellis tensors, each an [n_in/16][n_out/16]
+ * grid of 16x16 tiles (16 K words per tile), from a stored tile order into the
+ * row-major grid every kernel reads (page "GLM-5.3-Flash EXL3 (~2.1 bpw, SM70
+ * tile order)", header: the checkpoint's column-major tile order is reordered
+ * by the loader into the kernels' layout; page "GLM-5.3-Flash . exlr8
+ * (K2/K3/K4)", "Loading": each projection in halves of 128 intermediate
+ * channels).  A tile is a self-contained trellis stream, so this is a byte
+ * copy of whole tiles; the tiles' own content is unchanged.  Position, in
+ * tiles, of tile (tk, tn) in src:
+ *   ORDER_ROWMAJOR     tk * (n_out/16) + tn  (the kernels' order: a plain copy)
+ *   ORDER_COLMAJOR     tn * (n_in/16) + tk
+ *   ORDER_COLGROUPS128 (tn/8) * (n_in/16) * 8 + tk * 8 + tn % 8: groups of 128
+ *                      output columns one after another, each row-major (a
+ *                      gate or up projection stored as halves of 4096 x 128;
+ *                      a down projection split by input rows is ROWMAJOR).
+ *                      Needs n_out % 128 == 0.
+ * src, dst: device, count * (n_in/16) * (n_out/16) * 16 K uint16 each,
+ * 16-byte aligned, not overlapping.  count >= 1; n_in, n_out positive
+ * multiples of 16; K in {2, 3, 4}.
+ */
+#define MOE_EXL3_ORDER_ROWMAJOR 0
+#define MOE_EXL3_ORDER_COLMAJOR 1
+#define MOE_EXL3_ORDER_COLGROUPS128 2
+int moe_exl3_repack(const uint16_t *src, uint16_t *dst, int32_t count, int32_t n_in, int32_t n_out, int32_t K,
+                    int32_t src_order, void *stream);
+
+/*
+ * Per-channel side vectors from block scales (page "GLM-5.3-Flash . exlr8
+ * (K2/K3/K4)", "Index slices": an F16 block table [EA][3][hidden/128] per
+ * layer, the shared expert as its last row; "Loading": 32 block scales per
+ * projection at hidden 4096).  A scale covers 128 channels of the hidden
+ * dimension, which is the input of gate and up and the output of down:
+ *   suh[0][e][k] = block[e][0][k/128]   suh[1][e][k] = block[e][1][k/128]
+ *   svh[2][e][m] = block[e][2][m/128]
+ * and the intermediate-side vectors svh[0], svh[1], suh[2] are set to 1.
+ * block: device fp16 [n_trellis][3][hidden/128]; suh, svh: host arrays of 3
+ * device pointers to the fp16 vectors laid out as in moe_exl3_weights
+ * (suh[p] [n_trellis][in], svh[p] [n_trellis][out]).  hidden is a positive
+ * multiple of 128, inter positive, n_trellis >= 1; pointers 16-byte aligned.
+ */
+int moe_exl3_expand_block_scales(const uint16_t *block, int32_t n_trellis, int32_t hidden, int32_t inter,
+                                 uint16_t *const *suh, uint16_t *const *svh, void *stream);
 
 #ifdef __cplusplus
 }

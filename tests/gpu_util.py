@@ -30,7 +30,27 @@ class DevLayer:
         self.inp = inp
         # codes drawn for a subset of experts (a dict) are not needed on the
         # device by routing-only tests
-        self.codes = [None if isinstance(c, dict) else dev(c) for c in inp.codes]
+        self.code_tab = self.k_tab = None
+        if inp.ktab is not None and not isinstance(inp.codes[0], dict):
+            # one pool per projection, each tensor at its own width; the
+            # table holds every tensor's device address
+            self.codes = [dev(np.concatenate([np.asarray(t, dtype=np.uint16) for t in c])) for c in inp.codes]
+            addr = np.zeros((3, cfg.n_trellis), dtype=np.int64)
+            for p in range(3):
+                off = 0
+                for e in range(cfg.n_trellis):
+                    addr[p, e] = self.codes[p].data_ptr() + 2 * off
+                    off += cfg.words_of(p, e, inp.ktab)
+            self.code_tab = dev(addr)
+            self.k_tab = dev(np.ascontiguousarray(inp.ktab, dtype=np.int32))
+            flags |= M.PER_TENSOR_K
+        else:
+            self.codes = [None if isinstance(c, dict) else dev(c) for c in inp.codes]
+        self.signs = dev(inp.signs) if inp.signs is not None else None
+        if self.signs is not None:
+            flags |= M.HADAMARD
+        if cfg.shared_trellis:
+            flags |= M.SHARED_TRELLIS
         self.suh = [dev(s) for s in inp.suh]
         self.svh = [dev(s) for s in inp.svh]
         self.router_w = dev(inp.router_w)
@@ -44,11 +64,11 @@ class DevLayer:
         self.desc = M.make_desc(cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k, cfg.K,
                                 cfg.codebook, cfg.mcg, cfg.act_dtype, f, gemv_max_rows)
         self.weights = M.make_weights(self.codes, self.suh, self.svh, self.router_w, self.bias,
-                                      self.shared)
+                                      self.shared, self.signs, self.code_tab, self.k_tab)
         self.x = dev(inp.x)
 
     def workspace(self, T: int) -> torch.Tensor:
-        return torch.empty(M.workspace_size(self.desc, T), dtype=torch.uint8, device="cuda")
+        return poisoned_workspace(self.desc, T)
 
     def run(self, x: torch.Tensor = None) -> np.ndarray:
         """Layer output as fp32 numpy [T][H]."""
@@ -76,6 +96,12 @@ class DevLayer:
         return (idx.cpu().numpy().reshape(T, k), w.cpu().numpy().reshape(T, k),
                 counts.cpu().numpy(), offsets.cpu().numpy(), sorted_ids.cpu().numpy(),
                 pos.cpu().numpy())
+
+
+def poisoned_workspace(desc, T: int) -> torch.Tensor:
+    """A workspace filled with 0xFF bytes (NaN in every float type, -1 in every
+    int32), so that a read of a slot the call never wrote shows up."""
+    return torch.full((M.workspace_size(desc, T),), 0xFF, dtype=torch.uint8, device="cuda")
 
 
 def rel_err(out: np.ndarray, ref: np.ndarray) -> float:

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert M.version() == 1
+    assert M.version() == 2
     for code in (0, -1, -2, -3, -4, -5, -99):
         assert isinstance(M.strerror(code), str) and M.strerror(code)
 

@@ -1,4 +1,9 @@
-"""Bit-exact parity of the HIP trellis decode (moe_exl3_decode) with the oracle."""
+"""Bit-exact parity of the HIP trellis decode (moe_exl3_decode) with the oracle.
+
+Each output mode runs the fragment decoder of one kernel of the layer, so the
+values checked here are the values those kernels compute with:
+F16 (gate/up MFMA), BF16 (down MFMA), FP8 (fp8 MFMA), GEMV_F16 (the
+decode-fused GEMV's fp16 operand 128 c + 1532) and F32."""
 import numpy as np
 import pytest
 import torch
@@ -10,18 +15,24 @@ from gpu_util import dev
 pytestmark = pytest.mark.gpu
 
 MCG = 0x9E3779B1
+MODES = [M.DT_F32, M.DT_F16, M.DT_BF16, M.DT_FP8, M.DT_GEMV_F16]
 
 
 def _gpu_decode(codes, n_in, n_out, K, cb, dt, mcg=MCG):
     dtype = {M.DT_F32: torch.float32, M.DT_F16: torch.int16, M.DT_BF16: torch.int16,
-             M.DT_FP8: torch.uint8}[dt]
-    dst = torch.empty((n_in, n_out), dtype=dtype, device="cuda")
+             M.DT_FP8: torch.uint8, M.DT_GEMV_F16: torch.int16}[dt]
+    # poisoned: every element must be written
+    dst = torch.full((n_in, n_out), -1, dtype=dtype, device="cuda")
     M.decode(dev(codes), n_in, n_out, K, mcg, cb, dst, dt)
     torch.cuda.synchronize()
     return dst.cpu()
 
 
-def _expect(ref: np.ndarray, dt):
+def _expect(ref: np.ndarray, dt, cb):
+    """The exact value each mode must hold, from the oracle's fp32 c values."""
+    if dt == M.DT_FP8 and cb == 0:
+        # the MCG codebook is rounded to E4M3 by the oracle's own routine
+        ref = np.vectorize(oracle.e4m3_rne)(ref.astype(np.float64)).astype(np.float32)
     t = torch.from_numpy(ref)
     if dt == M.DT_F32:
         return t
@@ -29,42 +40,50 @@ def _expect(ref: np.ndarray, dt):
         return t.to(torch.float16).view(torch.int16)
     if dt == M.DT_BF16:
         return t.to(torch.bfloat16).view(torch.int16)
+    if dt == M.DT_GEMV_F16:
+        biased = ref.astype(np.float64) * 128.0 + 1532.0
+        assert (biased == np.round(biased)).all() and biased.min() >= 1020 and biased.max() <= 2044
+        return torch.from_numpy(biased).to(torch.float16).view(torch.int16)
     return t.to(torch.float8_e4m3fn).view(torch.uint8)
 
 
 @pytest.mark.parametrize("K", [2, 3, 4])
 @pytest.mark.parametrize("cb", [0, 1])
-@pytest.mark.parametrize("dt", [M.DT_F32, M.DT_F16, M.DT_BF16, M.DT_FP8])
+@pytest.mark.parametrize("dt", MODES)
 def test_decode_small_bit_exact(K, cb, dt):
     n_in, n_out = 48, 96
     rng = np.random.default_rng(100 * K + 10 * cb + dt)
     codes = rng.integers(0, 1 << 16, (n_in // 16) * (n_out // 16) * 16 * K, dtype=np.uint16)
     ref = oracle.decode_matrix(codes, n_in, n_out, K, MCG, cb)
-    if dt == M.DT_FP8 and cb == 0:
-        ref = np.vectorize(oracle.e4m3_rne)(ref.astype(np.float64)).astype(np.float32)
     got = _gpu_decode(codes, n_in, n_out, K, cb, dt)
-    exp = _expect(ref, dt)
+    exp = _expect(ref, dt, cb)
     assert torch.equal(got, exp), f"mismatches: {(got != exp).sum().item()}"
 
 
 @pytest.mark.parametrize("K", [2, 3, 4])
-def test_decode_full_projection_bit_exact(K):
-    # one expert's gate projection at the real shape [4096][2048]
+@pytest.mark.parametrize("cb", [0, 1])
+def test_decode_full_projection_bit_exact(K, cb):
+    # one expert's gate projection at the real shape [4096][2048], every mode
     n_in, n_out = 4096, 2048
-    rng = np.random.default_rng(7 + K)
+    rng = np.random.default_rng(7 + K + 10 * cb)
     codes = rng.integers(0, 1 << 16, (n_in // 16) * (n_out // 16) * 16 * K, dtype=np.uint16)
-    ref = oracle.decode_matrix(codes, n_in, n_out, K, MCG, 0)
-    got = _gpu_decode(codes, n_in, n_out, K, 0, M.DT_F32).numpy()
-    np.testing.assert_array_equal(got, ref)
-    again = _gpu_decode(codes, n_in, n_out, K, 0, M.DT_F32).numpy()
-    np.testing.assert_array_equal(again, got)
+    ref = oracle.decode_matrix(codes, n_in, n_out, K, MCG, cb)
+    for dt in MODES:
+        if dt == M.DT_FP8 and cb == 0:
+            continue   # the E4M3 rounding of the plain codebook is covered at the small size
+        got = _gpu_decode(codes, n_in, n_out, K, cb, dt)
+        exp = _expect(ref, dt, cb)
+        assert torch.equal(got, exp), f"dt={dt} mismatches: {(got != exp).sum().item()}"
+    again = _gpu_decode(codes, n_in, n_out, K, cb, M.DT_GEMV_F16)
+    assert torch.equal(again, _expect(ref, M.DT_GEMV_F16, cb))
 
 
 @pytest.mark.parametrize("mcg", [1, 0xFFFFFFFF, 0x12345679])
-def test_decode_other_multipliers(mcg):
+@pytest.mark.parametrize("dt", [M.DT_F32, M.DT_F16, M.DT_GEMV_F16])
+def test_decode_other_multipliers(mcg, dt):
     K, n_in, n_out = 3, 32, 32
     rng = np.random.default_rng(mcg & 0xFFFF)
     codes = rng.integers(0, 1 << 16, 4 * 16 * K, dtype=np.uint16)
     ref = oracle.decode_matrix(codes, n_in, n_out, K, mcg, 0)
-    got = _gpu_decode(codes, n_in, n_out, K, 0, M.DT_F32, mcg=mcg).numpy()
-    np.testing.assert_array_equal(got, ref)
+    got = _gpu_decode(codes, n_in, n_out, K, 0, dt, mcg=mcg)
+    assert torch.equal(got, _expect(ref, dt, 0))

@@ -16,6 +16,7 @@ import oracle
 import trellis_quantized_moe_exl3_amd as M
 import workloads as W
 from gpu_util import DevLayer, dev, rel_err
+from margins import record
 
 pytestmark = pytest.mark.gpu
 
@@ -35,6 +36,7 @@ def test_tiny_full(flags):
     _, _, ref = oracle.layer(inp)
     err = rel_err(out, ref)
     print(f"tiny flags={flags} err={err:.3e}")
+    record(f"tiny flags={flags}", err, TOL)
     assert err <= TOL
 
 
@@ -100,6 +102,8 @@ def test_decode_step():
     _, _, ref = oracle.layer(inp)
     err = rel_err(out, ref)
     print(f"decode routed err={err_r:.3e} full err={err:.3e}")
+    record("decode routed", err_r, TOL)
+    record("decode full", err, TOL)
     assert err_r <= TOL and err <= TOL
 
 
@@ -119,21 +123,71 @@ def test_decode_step_code_widths(K, codebook):
     _, _, ref = oracle.layer(inp, sample)
     err_r, err = rel_err(out_r, ref_r), rel_err(out[sample], ref)
     print(f"decode K={K} cb={codebook} routed err={err_r:.3e} full err={err:.3e}")
+    record(f"decode K={K} cb={codebook} routed", err_r, TOL)
     assert err_r <= TOL and err <= TOL
     assert np.isfinite(out).all() and np.isfinite(out_r).all()
 
 
-def _sampled(name, sample, flags=0, tol=TOL):
+def routing_sample(dl, gemv_rows=2, n_min=64, seed=0):
+    """Tokens chosen from the layer's own segment tables so that the sample
+    reaches every kernel path: the first and last token; in the heaviest
+    expert, rows 0, 255 and 256 (the end of a full 256-row tile and the start
+    of the next) and its last row (the ragged last tile); for every MFMA tile
+    size class (up to 32, 64, 128, 192 and 256 rows: the (NMB, CM) variants of
+    the kernels) the last row of one expert's last tile in that class; one
+    token on an expert at the GEMV threshold; then seeded random tokens up to
+    n_min.  Returns (sorted token list, description)."""
+    cfg = dl.inp.cfg
+    T, k = dl.x.shape[0], cfg.top_k
+    idx, _, counts, offsets, sorted_ids, _ = dl.route()
+    tok = lambda p: int(sorted_ids[p]) // k
+    pick, what = {0, T - 1}, []
+    heavy = int(np.argmax(counts))
+    o, c = int(offsets[heavy]), int(counts[heavy])
+    for r in (0, 255, 256, c - 1):
+        if 0 <= r < c:
+            pick.add(tok(o + r))
+    what.append(f"heaviest expert {heavy} ({c} rows)")
+    classes = [(1, 32), (33, 64), (65, 128), (129, 192), (193, 256)]
+    for lo, hi in classes:
+        for e in np.argsort(-counts, kind="stable"):
+            ce = int(counts[e])
+            if ce <= gemv_rows:
+                continue
+            last = ce - 256 * ((ce - 1) // 256)   # rows in the expert's last tile
+            if lo <= last <= hi:
+                pick.add(tok(int(offsets[e]) + ce - 1))
+                what.append(f"{lo}-{hi} rows: expert {int(e)}")
+                break
+    on_gemv = [int(e) for e in range(cfg.n_experts) if 0 < counts[e] <= gemv_rows]
+    if on_gemv:
+        e = max(on_gemv, key=lambda e: (int(counts[e]), -e))
+        pick.add(tok(int(offsets[e])))
+        what.append(f"GEMV expert {e} ({int(counts[e])} rows)")
+    rng = np.random.default_rng(seed)
+    while len(pick) < n_min:
+        pick.add(int(rng.integers(0, T)))
+    return sorted(pick), "; ".join(what)
+
+
+def _sampled(name, flags=0, tol=TOL, n_min=64, n_full=8):
+    """Routed-only parity on a routing-table sample of >= n_min tokens, and
+    the full layer (shared expert included) on n_full of them."""
     cfg = W.BY_NAME[name]
     inp = W.gen_layer(cfg)
     routed = _routed_only(inp)
-    out_r = DevLayer(routed, flags=flags).run()
+    dlr = DevLayer(routed, flags=flags)
+    sample, what = routing_sample(dlr, n_min=n_min)
+    out_r = dlr.run()
     _, _, ref_r = oracle.layer(routed, sample)
     err_r = rel_err(out_r[sample], ref_r)
+    full = sample[:: max(1, len(sample) // n_full)][:n_full]
     out = DevLayer(inp, flags=flags).run()
-    _, _, ref = oracle.layer(inp, sample)
-    err = rel_err(out[sample], ref)
-    print(f"{name} flags={flags} sampled routed err={err_r:.3e} full err={err:.3e}")
+    _, _, ref = oracle.layer(inp, full)
+    err = rel_err(out[full], ref)
+    print(f"{name} flags={flags} {len(sample)} tokens ({what}) routed err={err_r:.3e} full err={err:.3e}")
+    record(f"{name} flags={flags} routed ({len(sample)} tokens)", err_r, tol)
+    record(f"{name} flags={flags} full ({len(full)} tokens)", err, tol)
     assert err_r <= tol and err <= tol
     assert np.isfinite(out).all() and np.isfinite(out_r).all()
 
@@ -157,20 +211,20 @@ def test_decode_sized_layer_boundary(T):
 
 
 def test_prefill_sampled():
-    _sampled("prefill", [0, 1, 2, 1234, 3583, 7167])
+    _sampled("prefill")
 
 
 @pytest.mark.parametrize("name", ["mixed_k3", "mixed_k4"])
 def test_mixed_width_sampled(name):
-    _sampled(name, [0, 5, 1023, 2047])
+    _sampled(name)
 
 
 def test_e4m3_codebook_sampled():
-    _sampled("fp8", [0, 8191, 16383])
+    _sampled("fp8")
 
 
 def test_e4m3_fp8_mfma_sampled():
-    _sampled("fp8", [0, 1, 8191, 16383], flags=M.FP8_MFMA, tol=TOL_FP8)
+    _sampled("fp8", flags=M.FP8_MFMA, tol=TOL_FP8)
 
 
 def _tiny_e4m3(T):

@@ -38,6 +38,29 @@ MOE_DEV float act_to_f32(uint16_t v)
     return BF16 ? bf16_to_f32(v) : f16_to_f32(v);
 }
 
+// Eight bf16 activations (raw 16-byte piece) -> eight fp16 (round to nearest
+// even; exact in fp16's normal range).  `over` is set when a finite value lies
+// beyond the fp16 range and became infinite.
+MOE_DEV u32x4 bf16x8_to_f16x8(u32x4 v, bool &over)
+{
+    u32x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float lo = __uint_as_float(v[j] << 16), hi = __uint_as_float(v[j] & 0xFFFF0000u);
+        const uint32_t a = f32_to_f16_bits(lo), b = f32_to_f16_bits(hi);
+        // fp16 infinity (0x7C00 after the sign) from a finite bf16 (exponent
+        // field below 0xFF)
+        over |= ((a & 0x7FFFu) == 0x7C00u && (v[j] & 0x7F80u) != 0x7F80u) ||
+                ((b & 0x7FFFu) == 0x7C00u && (v[j] & 0x7F800000u) != 0x7F800000u);
+        o[j] = a | (b << 16);
+    }
+    return o;
+}
+
+// Token of routed-table slot a: a / k for the nr = T * k routed slots, a - nr
+// for the trellis shared expert's slots that follow them.
+MOE_DEV int64_t slot_token(int64_t a, int64_t nr, int k) { return a < nr ? a / k : a - nr; }
+
 // Wavefront size on CDNA.
 constexpr int kWave = 64;
 

@@ -2,6 +2,7 @@
 #pragma once
 
 #include "common.h"
+#include "internal.h"
 
 namespace moe {
 
@@ -38,5 +39,47 @@ MOE_DEV void wait_vmcnt()
 // the 16-lane reads of an MFMA A fragment (16 consecutive rows, one piece)
 // hit 16 distinct 4-bank groups.
 MOE_DEV int a_slot(int r, int p) { return p ^ ((r >> 2) & 3); }
+
+// First/second dword of a lane fragment (column c, k-half h) of a tile at
+// width K, and the bit offset inside the first (the run-time form of
+// frag_pos<K>, for kernels whose width is read per tensor).
+MOE_DEV void frag_pos_rt(int K, int c, int h, int &d0, int &d1, int &q)
+{
+    const int b0 = K * (16 * c + 8 * h);
+    d0 = b0 >> 5;
+    q = b0 & 31;
+    d1 = (d0 + 1 == 8 * K) ? 0 : d0 + 1;
+}
+
+// The code words of tensor (p, e), an [n_in/16][n_out/16] tile grid.  K > 0:
+// every tensor has width K and is slice e of codes[p].  K = 0: the address
+// and width come from the per-tensor tables; a width outside {2, 3, 4} sets
+// the status bit and the tensor is read through an empty range (as zero
+// words, at width 2).
+struct TensorCodes {
+    const uint32_t *base;
+    uint32_t bytes;   // of the tensor (0: nothing may be read)
+    int K;
+};
+
+template <int K>
+MOE_DEV TensorCodes tensor_codes(const GroupArgs &a, int p, int e, int n_in, int n_out)
+{
+    TensorCodes t;
+    if constexpr (K > 0) {
+        t.K = K;
+        t.bytes = (uint32_t)((n_in / 16) * (n_out / 16) * 32 * K);
+        t.base = (const uint32_t *)((const char *)a.codes[p] + (int64_t)e * t.bytes);
+    } else {
+        const int kw = a.k_tab[p * a.E + e];
+        const bool ok = kw >= 2 && kw <= 4;
+        if (!ok)
+            atomicOr((unsigned *)&const_cast<WsHeader *>(a.hdr)->status, MOE_EXL3_STATUS_BAD_WIDTH);
+        t.K = ok ? kw : 2;
+        t.bytes = ok ? (uint32_t)((n_in / 16) * (n_out / 16) * 32 * kw) : 0u;
+        t.base = (const uint32_t *)a.code_tab[p * a.E + e];
+    }
+    return t;
+}
 
 }  // namespace moe

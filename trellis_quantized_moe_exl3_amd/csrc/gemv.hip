@@ -52,28 +52,6 @@ MOE_DEV void block_reduce256(float v[N], float (*part)[4])
                                      : ((part[i][0] + part[i][1]) + part[i][2]) + part[i][3];
 }
 
-// The fragment's eight decoded values as fp16 pairs of 2v + 1532 (exact:
-// integers in [1020, 2044]).  mcg: the low half from v_sad_u8 on base
-// 0x64006400, the high half from v_sad_hi_u8; E4M3: 128 * c8 + 1532.
-template <int K, int CB>
-MOE_DEV void frag_biased_pairs(uint32_t D0, uint32_t D1, int q, uint32_t m_lo, uint32_t m_hi, f16x2 wp[4])
-{
-    uint32_t st[8];
-    frag_states<K>(D0, D1, q, st);
-#pragma unroll
-    for (int t = 0; t < 8; t += 2) {
-        if (CB == CB_MCG) {
-            const uint32_t ra = field_sum2(mcg_hash(st[t], m_lo, m_hi), 0x64006400u);
-            const uint32_t rb = __builtin_amdgcn_sad_hi_u8(mcg_hash(st[t + 1], m_lo, m_hi) & 0xFEFEFEFEu, 0u, ra);
-            wp[t / 2] = __builtin_bit_cast(f16x2, rb);
-        } else {
-            const float a = e4m3_value2(value2_f32(st[t], m_lo, m_hi)) + kBias2;
-            const float b = e4m3_value2(value2_f32(st[t + 1], m_lo, m_hi)) + kBias2;
-            wp[t / 2] = (f16x2){(f16)a, (f16)b};
-        }
-    }
-}
-
 // Stream tile rows [tk0, tk1) of the lane's fragment and accumulate
 // x . (2v + 1532) for NR routed rows.  The codes come in through a buffer
 // resource over the wavefront's 16-column tile pair: the lane's two dwords
@@ -125,6 +103,26 @@ MOE_DEV void gemv_stream(__amdgpu_buffer_rsrc_t rs, uint32_t v0, uint32_t v1, ui
     }
     if (g < tk1)
         run(A, g);
+}
+
+// gemv_stream at the tensor's width: K > 0 fixes it at compile time; K = 0
+// (per-tensor widths) dispatches on the wavefront-uniform run-time width kw.
+// No barrier lies inside, so wavefronts of one block may take different
+// widths.
+template <int K, int CB, int NR, class DOT>
+MOE_DEV void gemv_stream_k(int kw, __amdgpu_buffer_rsrc_t rs, uint32_t v0, uint32_t v1, uint32_t rowb, int tk0,
+                           int tk1, int q, uint32_t m_lo, uint32_t m_hi, DOT dot, float acc[NR])
+{
+    if constexpr (K > 0) {
+        gemv_stream<K, CB, NR>(rs, v0, v1, rowb, tk0, tk1, q, m_lo, m_hi, dot, acc);
+    } else {
+        if (kw == 4)
+            gemv_stream<4, CB, NR>(rs, v0, v1, rowb, tk0, tk1, q, m_lo, m_hi, dot, acc);
+        else if (kw == 3)
+            gemv_stream<3, CB, NR>(rs, v0, v1, rowb, tk0, tk1, q, m_lo, m_hi, dot, acc);
+        else
+            gemv_stream<2, CB, NR>(rs, v0, v1, rowb, tk0, tk1, q, m_lo, m_hi, dot, acc);
+    }
 }
 
 // ------------------------------------------------------------ shared expert GEMV
@@ -372,15 +370,15 @@ __global__ __launch_bounds__(256, 4) void gemv_gateup_kernel(GroupArgs a, int ma
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
     const int pr = w >> 1, kh = kGuKH == 2 ? (w & 1) : 0, cp = kGuCP == 2 ? (w & 1) : 0;
     const int c = l & 15, ts = (l >> 4) & 1, h = l >> 5;
-    int d0, d1, q;
-    frag_pos<K>(c, h, d0, d1, q);
     // the block's tile pair in every tile row of expert e's projection pr
-    const int64_t per_expert = (int64_t)(H / 16) * (I / 16) * Tile<K>::kDwords;
-    const uint32_t rowb = (uint32_t)(I / 16) * Tile<K>::kBytes;
+    const TensorCodes tcs = tensor_codes<K>(a, pr, e, H, I);
+    const int kw = K > 0 ? K : __builtin_amdgcn_readfirstlane(tcs.K);
+    int d0, d1, q;
+    frag_pos_rt(kw, c, h, d0, d1, q);
+    const uint32_t rowb = (uint32_t)(I / 16) * 32u * kw;
     const __amdgpu_buffer_rsrc_t rs =
-        buf_rsrc((const uint32_t *)a.codes[pr] + e * per_expert + (int64_t)(n0 / 16) * Tile<K>::kDwords,
-                 (uint32_t)(H / 16) * rowb);
-    const uint32_t tb = (uint32_t)(2 * cp + ts) * Tile<K>::kDwords;
+        buf_rsrc(tcs.base + (n0 / 16) * 8 * kw, tcs.bytes ? tcs.bytes - (uint32_t)(n0 / 16) * 32u * kw : 0u);
+    const uint32_t tb = (uint32_t)(2 * cp + ts) * 8u * kw;
     const uint32_t v0 = 4u * (tb + d0), v1 = 4u * (tb + d1);
     const uint32_t m_lo = a.mcg & 0xFFFFu, m_hi = a.mcg >> 16;
     const int ntk = H / 16, tk0 = kh * (ntk / kGuKH), tk1 = tk0 + ntk / kGuKH;
@@ -395,7 +393,7 @@ __global__ __launch_bounds__(256, 4) void gemv_gateup_kernel(GroupArgs a, int ma
             for (int r = 0; r < kGemvPass; ++r) {
                 if (r >= nr)
                     continue;
-                const int t = a.sorted[p0 + r0 + r] / a.k;
+                const int64_t t = slot_token(a.sorted[p0 + r0 + r], a.nr, a.k);
                 for (int ch = threadIdx.x; ch < H / 8; ch += 256) {
                     const f16x8 xv = *(const f16x8 *)(a.x16 + (int64_t)t * H + 8 * ch);
                     const f16x8 sv = *(const f16x8 *)(a.suh[pp] + (int64_t)e * H + 8 * ch);
@@ -424,9 +422,9 @@ __global__ __launch_bounds__(256, 4) void gemv_gateup_kernel(GroupArgs a, int ma
         };
         // nr is the same for the whole block: branch once, not per fragment
         if (__builtin_amdgcn_readfirstlane(nr) == 2)
-            gemv_stream<K, CB, 2>(rs, v0, v1, rowb, tk0, tk1, q, m_lo, m_hi, dot, acc);
+            gemv_stream_k<K, CB, 2>(kw, rs, v0, v1, rowb, tk0, tk1, q, m_lo, m_hi, dot, acc);
         else
-            gemv_stream<K, CB, 1>(rs, v0, v1, rowb, tk0, tk1, q, m_lo, m_hi, dot, acc);
+            gemv_stream_k<K, CB, 1>(kw, rs, v0, v1, rowb, tk0, tk1, q, m_lo, m_hi, dot, acc);
         // the two k-halves of a tile row sit in lanes l and l ^ 32
 #pragma unroll
         for (int r = 0; r < kGemvPass; ++r) {
@@ -487,14 +485,14 @@ __global__ __launch_bounds__(256, 4) void gemv_down_kernel(GroupArgs a, int max_
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
     const int cp = w % kDownCP, kr = w / kDownCP;
     const int c = l & 15, ts = (l >> 4) & 1, h = l >> 5;
+    const TensorCodes tcs = tensor_codes<K>(a, 2, e, I, H);
+    const int kw = K > 0 ? K : __builtin_amdgcn_readfirstlane(tcs.K);
     int d0, d1, q;
-    frag_pos<K>(c, h, d0, d1, q);
-    const int64_t per_expert = (int64_t)(I / 16) * (H / 16) * Tile<K>::kDwords;
-    const uint32_t rowb = (uint32_t)(H / 16) * Tile<K>::kBytes;
+    frag_pos_rt(kw, c, h, d0, d1, q);
+    const uint32_t rowb = (uint32_t)(H / 16) * 32u * kw;
     const __amdgpu_buffer_rsrc_t rs =
-        buf_rsrc((const uint32_t *)a.codes[2] + e * per_expert + (int64_t)(m0 / 16) * Tile<K>::kDwords,
-                 (uint32_t)(I / 16) * rowb);
-    const uint32_t tb = (uint32_t)(2 * cp + ts) * Tile<K>::kDwords;
+        buf_rsrc(tcs.base + (m0 / 16) * 8 * kw, tcs.bytes ? tcs.bytes - (uint32_t)(m0 / 16) * 32u * kw : 0u);
+    const uint32_t tb = (uint32_t)(2 * cp + ts) * 8u * kw;
     const uint32_t v0 = 4u * (tb + d0), v1 = 4u * (tb + d1);
     const uint32_t m_lo = a.mcg & 0xFFFFu, m_hi = a.mcg >> 16;
     // I % 128 == 0, so ntk is a multiple of kGemvU and S = 1 always fits
@@ -565,9 +563,9 @@ __global__ __launch_bounds__(256, 4) void gemv_down_kernel(GroupArgs a, int max_
         if (kr < S) {
             // nr is the same for the whole block: branch once, not per fragment
             if (__builtin_amdgcn_readfirstlane(nr) == 2)
-                gemv_stream<K, CB, 2>(rs, v0, v1, rowb, tk0, tk1, q, m_lo, m_hi, dot, acc);
+                gemv_stream_k<K, CB, 2>(kw, rs, v0, v1, rowb, tk0, tk1, q, m_lo, m_hi, dot, acc);
             else
-                gemv_stream<K, CB, 1>(rs, v0, v1, rowb, tk0, tk1, q, m_lo, m_hi, dot, acc);
+                gemv_stream_k<K, CB, 1>(kw, rs, v0, v1, rowb, tk0, tk1, q, m_lo, m_hi, dot, acc);
         }
 #pragma unroll
         for (int r = 0; r < kGemvPass; ++r) {
@@ -614,7 +612,9 @@ hipError_t launch_gemv_gateup(const GroupArgs &a, int max_list, const SharedArgs
     dim3 grid(a.I / kGuCols, max_list + shared_rows_of(sh, a.I, a.I / kGuCols));
     const size_t lds = std::max(sizeof(f16) * 2 * kGemvPass * a.H, shared_lds_of(sh, a.T));
     const SharedArgs sa = sh ? *sh : SharedArgs{};
-    if (a.K == 2 && a.cb == 0) gemv_gateup_kernel<2, 0><<<grid, 256, lds, s>>>(a, max_list, sa);
+    if (a.code_tab && a.cb == 0) gemv_gateup_kernel<0, 0><<<grid, 256, lds, s>>>(a, max_list, sa);
+    else if (a.code_tab) gemv_gateup_kernel<0, 1><<<grid, 256, lds, s>>>(a, max_list, sa);
+    else if (a.K == 2 && a.cb == 0) gemv_gateup_kernel<2, 0><<<grid, 256, lds, s>>>(a, max_list, sa);
     else if (a.K == 3 && a.cb == 0) gemv_gateup_kernel<3, 0><<<grid, 256, lds, s>>>(a, max_list, sa);
     else if (a.K == 4 && a.cb == 0) gemv_gateup_kernel<4, 0><<<grid, 256, lds, s>>>(a, max_list, sa);
     else if (a.K == 2) gemv_gateup_kernel<2, 1><<<grid, 256, lds, s>>>(a, max_list, sa);
@@ -631,7 +631,9 @@ hipError_t launch_gemv_down(const GroupArgs &a, int max_list, const SharedArgs *
     dim3 grid(a.H / kDownCols, max_list + shared_rows_of(sh, a.H, a.H / kDownCols));
     const size_t lds = std::max(sizeof(f16) * kGemvPass * a.I, shared_lds_of(sh, a.T));
     const SharedArgs sa = sh ? *sh : SharedArgs{};
-    if (a.K == 2 && a.cb == 0) gemv_down_kernel<2, 0><<<grid, 256, lds, s>>>(a, max_list, sa);
+    if (a.code_tab && a.cb == 0) gemv_down_kernel<0, 0><<<grid, 256, lds, s>>>(a, max_list, sa);
+    else if (a.code_tab) gemv_down_kernel<0, 1><<<grid, 256, lds, s>>>(a, max_list, sa);
+    else if (a.K == 2 && a.cb == 0) gemv_down_kernel<2, 0><<<grid, 256, lds, s>>>(a, max_list, sa);
     else if (a.K == 3 && a.cb == 0) gemv_down_kernel<3, 0><<<grid, 256, lds, s>>>(a, max_list, sa);
     else if (a.K == 4 && a.cb == 0) gemv_down_kernel<4, 0><<<grid, 256, lds, s>>>(a, max_list, sa);
     else if (a.K == 2) gemv_down_kernel<2, 1><<<grid, 256, lds, s>>>(a, max_list, sa);

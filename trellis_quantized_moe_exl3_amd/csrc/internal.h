@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "moe_exl3.h"
+
 namespace moe {
 
 // Rows of one MFMA work tile (an expert's routed rows are cut into tiles of
@@ -33,45 +35,59 @@ constexpr int kSharedGemvMaxTokens = 16;
 // GEMV launches (the bound keeps their registers within those kernels').
 constexpr int kSharedGemvMergeTokens = 8;
 
-// Small header at the start of the workspace, written by the segment kernels.
+// Small header at the start of the workspace, written by the routing and
+// segment kernels.  status sits at byte MOE_EXL3_STATUS_OFFSET.
 struct WsHeader {
     int32_t n_gemv;    // experts on the GEMV path
     int32_t n_tiles;   // MFMA work tiles
-    int32_t status;
+    int32_t status;    // MOE_EXL3_STATUS_* bits of this call
     int32_t pad[13];
 };
+static_assert(offsetof(WsHeader, status) == MOE_EXL3_STATUS_OFFSET, "status word offset");
 
 struct Plan {
     int64_t T;
     int nblk;        // segment-table blocks
     int max_tiles;   // upper bound on MFMA work tiles
-    size_t hdr, logits, idx, w, counts, offsets, bhist, sorted, pos, glist, tiles, x16, hbuf,
+    size_t hdr, logits, idx, w, counts, offsets, bhist, sorted, pos, glist, tiles, x16, xr16, hbuf,
         ybuf, sh, sy, a8g, a8u, h8, sg8, su8, sh8, total;
 };
 
 hipError_t launch_route_logits(const uint16_t *x, bool bf16, int64_t T, int H, const uint16_t *Wr,
-                               const float *bias, int E, float *logits, hipStream_t s);
+                               const float *bias, int E, float *logits, WsHeader *hdr, hipStream_t s);
 hipError_t launch_topk(const float *logits, int64_t T, int E, int k, int32_t *idx, float *w,
                        hipStream_t s);
-hipError_t launch_segments(const int32_t *idx, int64_t T, int k, int E, int nblk, int gemv_rows,
-                           int tile_m, int32_t *bhist, int32_t *counts, int32_t *offsets,
-                           int32_t *sorted, int32_t *pos, int32_t *glist, int32_t *tiles,
+// With `extra`, expert E (the trellis shared expert) joins the tables with
+// the T slots T*k + t, routing weight 1.
+hipError_t launch_segments(const int32_t *idx, int64_t T, int k, int E, bool extra, int nblk, int gemv_rows,
+                           int tile_m, int max_tiles, int32_t *bhist, int32_t *counts, int32_t *offsets,
+                           int32_t *sorted, int32_t *pos, float *w, int32_t *glist, int32_t *tiles,
                            WsHeader *hdr, hipStream_t s);
 
-hipError_t launch_route_small(const float *logits, int64_t T, int E, int k, int gemv_rows, int tile_m,
-                              int32_t *idx, float *w, int32_t *counts, int32_t *offsets, int32_t *sorted,
+hipError_t launch_route_small(const float *logits, int64_t T, int E, int k, bool extra, int gemv_rows, int tile_m,
+                              int max_tiles, int32_t *idx, float *w, int32_t *counts, int32_t *offsets, int32_t *sorted,
                               int32_t *pos, int32_t *glist, int32_t *tiles, WsHeader *hdr,
                               const uint16_t *x, int H, uint16_t *x16, hipStream_t s);
 
 hipError_t launch_decode(const uint16_t *codes, int n_in, int n_out, int K, uint32_t mcg, int cb,
                          void *dst, int dst_dtype, hipStream_t s);
+hipError_t launch_repack(const uint16_t *src, uint16_t *dst, int count, int n_in, int n_out, int K, int order,
+                         hipStream_t s);
+hipError_t launch_expand_scales(const uint16_t *block, int EA, int H, int I, uint16_t *const suh[3],
+                                uint16_t *const svh[3], hipStream_t s);
 
 struct GroupArgs {
     const uint16_t *codes[3];
     const uint16_t *suh[3];
     const uint16_t *svh[3];
-    int H, I, E, k, K, cb;
+    int H, I, k, K, cb;
+    int E;          // experts in the segment tables: the routed ones (+ the trellis shared expert)
     int64_t T;
+    int64_t nr;     // routed slots T * k; slots nr + t belong to the trellis shared expert
+    // per-tensor widths (PER_TENSOR_K; NULL otherwise): [3][E] device
+    // addresses of each tensor's codes and its width
+    const uint64_t *code_tab;
+    const int32_t *k_tab;
     uint32_t mcg;
     const int32_t *counts, *offsets, *sorted, *glist, *tiles;
     const WsHeader *hdr;
@@ -85,7 +101,12 @@ struct GroupArgs {
     float *sg8, *su8, *sh8;  // row scales (least power of two >= row amax / 448)
 };
 
-hipError_t launch_convert_x(const uint16_t *x, bool bf16, int64_t n, uint16_t *x16, hipStream_t s);
+hipError_t launch_convert_x(const uint16_t *x, int64_t n, uint16_t *x16, WsHeader *hdr, hipStream_t s);
+// DEBUG_CHECKS: consistency of the routing tables and finiteness of x, into
+// the status word.
+hipError_t launch_debug_checks(const uint16_t *x, bool bf16, int64_t T, int H, int k, int E,
+                               const int32_t *idx, const int32_t *counts, const int32_t *offsets,
+                               const int32_t *sorted, const int32_t *pos, WsHeader *hdr, hipStream_t s);
 // The dense shared expert, when its work rides along in the routed MFMA or
 // GEMV launches (x16 [T][H] fp16, w = gate, up, down nn.Linear fp16, h [T][I]
 // fp16 gate/up output, y [T][H] fp32 down output).
@@ -113,7 +134,12 @@ hipError_t launch_shared_down(const uint16_t *sh, int64_t T, int H, int I, const
 hipError_t launch_shared_gemv(const uint16_t *x16, int T, int H, int I, const uint16_t *wg,
                               const uint16_t *wu, const uint16_t *wd, uint16_t *sh, float *sy,
                               hipStream_t s);
-hipError_t launch_combine(const uint16_t *ybuf, const float *sy, int64_t T, int H, int k, bool bf16,
-                          uint16_t *out, hipStream_t s);
+// out = sy + s1 * R(routed slot rows (+ the trellis shared expert's row));
+// without s1 no rotation.
+hipError_t launch_combine(const uint16_t *ybuf, const float *sy, int64_t T, int H, int k, bool extra,
+                          const int8_t *s1, bool bf16, uint16_t *out, hipStream_t s);
+// xr = fp16(R(s0 * x)), the rotated activations of the trellis experts.
+hipError_t launch_rotate_x(const uint16_t *x, bool bf16, int64_t T, int H, const int8_t *s0, uint16_t *xr,
+                           WsHeader *hdr, hipStream_t s);
 
 }  // namespace moe

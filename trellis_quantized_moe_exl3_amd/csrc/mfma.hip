@@ -112,6 +112,12 @@ struct GemmTile {
     uint32_t rstride;          // bytes between tile rows (trellis)
     int q;
     uint32_t m_lo, m_hi;
+    // width of the wavefront's tensor and its tile bytes (K = 0: per-tensor
+    // widths, read from the table; otherwise K)
+    int kw;
+    uint32_t tbytes;
+
+    MOE_DEV uint32_t tile_bytes() const { return K > 0 ? (uint32_t)Tile<K>::kBytes : tbytes; }
 
     // raw B of one stage: CM column groups of 32 columns (trellis: 2 code
     // dwords per k-step and group; dense: 16 bytes per k-step)
@@ -152,7 +158,7 @@ struct GemmTile {
 #pragma unroll
                 for (int cm = 0; cm < CM; ++cm) {
                     // group cm starts two 16-column tiles further on
-                    const uint32_t go = (uint32_t)(cm * 2 * Tile<K>::kBytes);
+                    const uint32_t go = (uint32_t)cm * 2u * tile_bytes();
                     br.c[kt][cm][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, boff0 + go, so, 0);
                     br.c[kt][cm][1] = __builtin_amdgcn_raw_buffer_load_b32(rs, boff1 + go, so, 0);
                 }
@@ -168,15 +174,28 @@ struct GemmTile {
 
     // B fragment (k-step kt, column group cm) before the suh scaling: 8 exact
     // values of 2v (fp16 for gate/up, bf16 for down), or dense weights
+    template <int KK>
+    MOE_DEV u32x4 decode_k(uint32_t D0, uint32_t D1) const
+    {
+        if constexpr (MODE == GATEUP_TRELLIS)
+            return __builtin_bit_cast(u32x4, frag_decode_f16<KK, CB>(D0, D1, q, m_lo, m_hi));
+        else
+            return __builtin_bit_cast(u32x4, frag_decode_bf16<KK, CB>(D0, D1, q, m_lo, m_hi));
+    }
+
+    // K = 0: the wavefront's tensor width kw selects the decoder (a
+    // wavefront-uniform branch with no barrier inside).
     template <int CM>
     MOE_DEV u32x4 decode(const BRaw<CM> &br, int kt, int cm) const
     {
-        if constexpr (MODE == GATEUP_TRELLIS)
-            return __builtin_bit_cast(u32x4, frag_decode_f16<K, CB>(br.c[kt][cm][0], br.c[kt][cm][1], q, m_lo, m_hi));
-        else if constexpr (MODE == DOWN_TRELLIS)
-            return __builtin_bit_cast(u32x4, frag_decode_bf16<K, CB>(br.c[kt][cm][0], br.c[kt][cm][1], q, m_lo, m_hi));
-        else
+        if constexpr (!TR::kTrellis)
             return br.d[kt][cm];
+        else if constexpr (K > 0)
+            return decode_k<K>(br.c[kt][cm][0], br.c[kt][cm][1]);
+        else
+            return kw == 4 ? decode_k<4>(br.c[kt][cm][0], br.c[kt][cm][1])
+                 : kw == 3 ? decode_k<3>(br.c[kt][cm][0], br.c[kt][cm][1])
+                           : decode_k<2>(br.c[kt][cm][0], br.c[kt][cm][1]);
     }
 
     // Interleave the MFMAs of one fragment with the VALU work scheduled next
@@ -290,14 +309,16 @@ MOE_DEV void tile_body(GemmTile<MODE, K, CB> &g, const GemmArgs &args, int n0,
     const int Nout = TR::kGateUp ? g.I : g.H;
     g.col = (TR::kGateUp ? n0 + 32 * CM * (g.w & 3) : n0 + 32 * CM * g.w) + 16 * g.ts + g.c;
     if constexpr (TR::kTrellis) {
+        const TensorCodes tcs = tensor_codes<K>(a, g.pr, g.e, g.Kdim, Nout);
+        g.kw = K > 0 ? K : __builtin_amdgcn_readfirstlane(tcs.K);
+        g.tbytes = 32u * (uint32_t)g.kw;
         int d0, d1, q;
-        frag_pos<K>(g.c, g.h, d0, d1, q);
+        frag_pos_rt(g.kw, g.c, g.h, d0, d1, q);
         g.q = q;
-        const int64_t per_expert = (int64_t)(g.Kdim / 16) * (Nout / 16) * Tile<K>::kBytes;
-        g.rstride = (uint32_t)((Nout / 16) * Tile<K>::kBytes);
-        g.brsrc = buf_rsrc((const char *)a.codes[g.pr] + g.e * per_expert, (uint32_t)per_expert);
-        g.bnull = buf_rsrc((const char *)a.codes[g.pr], 0);
-        const uint32_t tile0 = (uint32_t)((g.col / 16) * Tile<K>::kBytes);
+        g.rstride = (uint32_t)(Nout / 16) * g.tile_bytes();
+        g.brsrc = buf_rsrc(tcs.base, tcs.bytes);
+        g.bnull = buf_rsrc(tcs.base, 0);
+        const uint32_t tile0 = (uint32_t)(g.col / 16) * g.tile_bytes();
         g.boff0 = tile0 + 4 * d0;
         g.boff1 = tile0 + 4 * d1;
         g.srsrc = g.bnull;
@@ -523,7 +544,7 @@ MOE_DEV void block_body(const GemmArgs &args, int L, int nslices, int sdiv, uint
             const int rc = min(r, g.rows - 1);
             int64_t row;
             if constexpr (MODE == GATEUP_TRELLIS)
-                row = a.sorted[g.p0 + rc] / a.k;
+                row = slot_token(a.sorted[g.p0 + rc], a.nr, a.k);
             else
                 row = rc;
             const int piece = a_slot(r, g.l & 3);   // slot l&3 holds this k piece
@@ -601,7 +622,9 @@ static hipError_t launch_grid(const GemmArgs &ga, unsigned grid, hipStream_t s)
     if (grid == 0)
         return hipSuccess;
     if constexpr (ModeTraits<MODE>::kTrellis) {
-        if (a.K == 2 && a.cb == 0) group_gemm_kernel<MODE, 2, 0><<<grid, kThreads, 0, s>>>(ga);
+        if (a.code_tab && a.cb == 0) group_gemm_kernel<MODE, 0, 0><<<grid, kThreads, 0, s>>>(ga);
+        else if (a.code_tab) group_gemm_kernel<MODE, 0, 1><<<grid, kThreads, 0, s>>>(ga);
+        else if (a.K == 2 && a.cb == 0) group_gemm_kernel<MODE, 2, 0><<<grid, kThreads, 0, s>>>(ga);
         else if (a.K == 3 && a.cb == 0) group_gemm_kernel<MODE, 3, 0><<<grid, kThreads, 0, s>>>(ga);
         else if (a.K == 4 && a.cb == 0) group_gemm_kernel<MODE, 4, 0><<<grid, kThreads, 0, s>>>(ga);
         else if (a.K == 2) group_gemm_kernel<MODE, 2, 1><<<grid, kThreads, 0, s>>>(ga);
@@ -692,38 +715,128 @@ hipError_t launch_shared_down(const uint16_t *sh, int64_t T, int H, int I, const
 }
 
 // ---------------------------------------------------------------- small kernels
-// bf16 activations -> fp16 (exact for |x| in the fp16 normal range).
+// bf16 activations -> fp16 (exact for |x| in the fp16 normal range; a finite
+// value past the fp16 range is flagged in the status word).
 __global__ __launch_bounds__(256) void convert_x_kernel(const uint16_t *__restrict__ x, int64_t n8,
-                                                        uint16_t *__restrict__ x16)
+                                                        uint16_t *__restrict__ x16, WsHeader *hdr)
 {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= n8)
         return;
-    const u32x4 v = ((const u32x4 *)x)[i];
-    u32x4 o;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const float lo = __uint_as_float(v[j] << 16), hi = __uint_as_float(v[j] & 0xFFFF0000u);
-        o[j] = (uint32_t)f32_to_f16_bits(lo) | ((uint32_t)f32_to_f16_bits(hi) << 16);
-    }
-    ((u32x4 *)x16)[i] = o;
+    bool over = false;
+    ((u32x4 *)x16)[i] = bf16x8_to_f16x8(((const u32x4 *)x)[i], over);
+    if (over)
+        atomicOr((unsigned *)&hdr->status, MOE_EXL3_STATUS_ACT_RANGE);
 }
 
-hipError_t launch_convert_x(const uint16_t *x, bool bf16, int64_t n, uint16_t *x16, hipStream_t s)
+hipError_t launch_convert_x(const uint16_t *x, int64_t n, uint16_t *x16, WsHeader *hdr, hipStream_t s)
 {
-    (void)bf16;
     const int64_t n8 = n / 8;
-    convert_x_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, s>>>(x, n8, x16);
+    convert_x_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, s>>>(x, n8, x16, hdr);
     return hipGetLastError();
 }
 
-// out[t] = shared[t] + sum_j ybuf[t*k + j] (bf16 slot rows, summed in fp32 in
-// slot order: deterministic), cast to the activation dtype.  8 outputs per
-// thread.
+// ---------------------------------------------------------------- rotation
+// The experts' basis rotation (page "GLM-5.3-Flash . exlr8 (K2/K3/K4)",
+// "Calibration": the 128x128 Hadamard matrix; "Index slices": the layer's two
+// int8 sign vectors over the hidden size).  Sixteen lanes hold one block of
+// 128 consecutive channels, eight per lane: the transform runs as three
+// butterfly stages inside the lane (channel distance 1, 2, 4) and four across
+// the 16 lanes (distance 8, 16, 32, 64: lane l pairs with l ^ m), each
+// (a, b) -> (a + b, a - b) with a the lower channel, in fp32; the result is
+// scaled by 1 / sqrt(128).  The Sylvester matrix is symmetric, so the same
+// transform serves both sides.
+MOE_DEV void fwht128(float v[8], int lane16)
+{
+#pragma unroll
+    for (int d = 1; d < 8; d <<= 1)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (!(i & d)) {
+                const float a = v[i], b = v[i + d];
+                v[i] = a + b;
+                v[i + d] = a - b;
+            }
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) {
+        const bool hi = lane16 & m;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float p = __shfl_xor(v[i], m, 64);
+            v[i] = hi ? p - v[i] : v[i] + p;
+        }
+    }
+    constexpr float kScale = 0.08838834764831845f;   // 1 / sqrt(128)
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        v[i] *= kScale;
+}
+
+// xr[t] = fp16(R(s0 * x[t])): the rotated copy of the activations the trellis
+// experts read.  One thread per 8 channels; 16 consecutive threads = one
+// 128-channel block of one token (hidden is a multiple of 256, so no block
+// straddles a token and every wavefront holds whole blocks).
 template <bool BF16>
+__global__ __launch_bounds__(256) void rotate_x_kernel(const uint16_t *__restrict__ x, int64_t n8, int H,
+                                                       const int8_t *__restrict__ s0, uint16_t *__restrict__ xr,
+                                                       WsHeader *hdr)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n8)   // n8 is a multiple of 16: whole 16-lane groups leave
+        return;
+    const int m = (int)((8 * i) % H);
+    const u32x4 raw = ((const u32x4 *)x)[i];
+    const uint2 sg = *(const uint2 *)(s0 + m);
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        v[2 * j] = act_to_f32<BF16>((uint16_t)(raw[j] & 0xFFFFu));
+        v[2 * j + 1] = act_to_f32<BF16>((uint16_t)(raw[j] >> 16));
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int8_t sj = (int8_t)(((j < 4 ? sg.x : sg.y) >> (8 * (j & 3))) & 0xFF);
+        v[j] = sj < 0 ? -v[j] : v[j];
+    }
+    fwht128(v, (int)(i & 15));
+    u32x4 o;
+    bool over = false;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t a = f32_to_f16_bits(v[2 * j]), b = f32_to_f16_bits(v[2 * j + 1]);
+        over |= (a & 0x7FFFu) == 0x7C00u || (b & 0x7FFFu) == 0x7C00u;
+        o[j] = a | (b << 16);
+    }
+    ((u32x4 *)xr)[i] = o;
+    if (over)
+        atomicOr((unsigned *)&hdr->status, MOE_EXL3_STATUS_ACT_RANGE);
+}
+
+hipError_t launch_rotate_x(const uint16_t *x, bool bf16, int64_t T, int H, const int8_t *s0, uint16_t *xr,
+                           WsHeader *hdr, hipStream_t s)
+{
+    const int64_t n8 = T * H / 8;
+    const unsigned grid = (unsigned)((n8 + 255) / 256);
+    if (bf16)
+        rotate_x_kernel<true><<<grid, 256, 0, s>>>(x, n8, H, s0, xr, hdr);
+    else
+        rotate_x_kernel<false><<<grid, 256, 0, s>>>(x, n8, H, s0, xr, hdr);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- combine
+// out[t] = shared[t] + s1 * R(sum_j ybuf[t*k + j] (+ ybuf[T*k + t]))
+// ybuf holds bf16 slot rows (routing weight applied); the routed rows of a
+// token, then the trellis shared expert's row when there is one (slot T*k + t,
+// weight 1), are summed in fp32 in that fixed order: deterministic.  With
+// sign vectors the sum is rotated back (R, then s1) before the fp16 shared
+// expert's fp32 row is added; then the cast to the activation dtype.  8
+// outputs per thread (16 threads per 128-channel block when rotating).
+template <bool BF16, bool ROT>
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict__ ybuf,
                                                       const float *__restrict__ sy, int64_t T, int H,
-                                                      int k, uint16_t *__restrict__ out)
+                                                      int k, int extra, const int8_t *__restrict__ s1,
+                                                      uint16_t *__restrict__ out)
 {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t n8 = T * H / 8;
@@ -731,32 +844,43 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
         return;
     const int64_t t = (8 * i) / H, m = (8 * i) % H;
     float s[8];
-    if (sy) {
-        const f32x4 a = *(const f32x4 *)(sy + t * H + m), b = *(const f32x4 *)(sy + t * H + m + 4);
-        s[0] = a[0]; s[1] = a[1]; s[2] = a[2]; s[3] = a[3];
-        s[4] = b[0]; s[5] = b[1]; s[6] = b[2]; s[7] = b[3];
-    } else {
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
-            s[q] = 0.0f;
-    }
-    // all k slot rows are loaded before the first add (k <= 16), then summed
-    // in slot order
-    constexpr int kMaxK = 16;
+    for (int q = 0; q < 8; ++q)
+        s[q] = 0.0f;
+    // all slot rows are loaded before the first add (k + 1 <= 17), then
+    // summed in slot order
+    constexpr int kMaxK = 17;
     u32x4 v[kMaxK];
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j)
+    for (int j = 0; j < kMaxK; ++j) {
         if (j < k)
             v[j] = *(const u32x4 *)(ybuf + (t * k + j) * H + m);
+        else if (j == k && extra)
+            v[j] = *(const u32x4 *)(ybuf + (T * k + t) * H + m);
+    }
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j)
-        if (j < k) {
+        if (j < k + extra) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 s[2 * q] += __uint_as_float(v[j][q] << 16);
                 s[2 * q + 1] += __uint_as_float(v[j][q] & 0xFFFF0000u);
             }
         }
+    if constexpr (ROT) {
+        fwht128(s, (int)(i & 15));
+        const uint2 sg = *(const uint2 *)(s1 + m);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int8_t sj = (int8_t)(((j < 4 ? sg.x : sg.y) >> (8 * (j & 3))) & 0xFF);
+            s[j] = sj < 0 ? -s[j] : s[j];
+        }
+    }
+    if (sy) {
+        const f32x4 a = *(const f32x4 *)(sy + t * H + m), b = *(const f32x4 *)(sy + t * H + m + 4);
+        s[0] += a[0]; s[1] += a[1]; s[2] += a[2]; s[3] += a[3];
+        s[4] += b[0]; s[5] += b[1]; s[6] += b[2]; s[7] += b[3];
+    }
     u32x4 o;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -768,15 +892,19 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
     *(u32x4 *)(out + t * H + m) = o;
 }
 
-hipError_t launch_combine(const uint16_t *ybuf, const float *sy, int64_t T, int H, int k, bool bf16,
-                          uint16_t *out, hipStream_t s)
+hipError_t launch_combine(const uint16_t *ybuf, const float *sy, int64_t T, int H, int k, bool extra,
+                          const int8_t *s1, bool bf16, uint16_t *out, hipStream_t s)
 {
     const int64_t n8 = T * H / 8;
     const unsigned grid = (unsigned)((n8 + 255) / 256);
-    if (bf16)
-        combine_kernel<true><<<grid, 256, 0, s>>>(ybuf, sy, T, H, k, out);
-    else
-        combine_kernel<false><<<grid, 256, 0, s>>>(ybuf, sy, T, H, k, out);
+    const int ex = extra ? 1 : 0;
+    if (bf16) {
+        if (s1) combine_kernel<true, true><<<grid, 256, 0, s>>>(ybuf, sy, T, H, k, ex, s1, out);
+        else combine_kernel<true, false><<<grid, 256, 0, s>>>(ybuf, sy, T, H, k, ex, s1, out);
+    } else {
+        if (s1) combine_kernel<false, true><<<grid, 256, 0, s>>>(ybuf, sy, T, H, k, ex, s1, out);
+        else combine_kernel<false, false><<<grid, 256, 0, s>>>(ybuf, sy, T, H, k, ex, s1, out);
+    }
     return hipGetLastError();
 }
 

@@ -469,7 +469,7 @@ __global__ __launch_bounds__(256) void quant_gateup_kernel(GroupArgs a, int64_t 
     if (p >= n)
         return;
     const int H = a.H;
-    const int t = a.sorted[p] / a.k;
+    const int64_t t = slot_token(a.sorted[p], a.nr, a.k);
     // expert of row p: the last e with offsets[e] <= p
     int lo = 0, hi = a.E;
     while (hi - lo > 1) {

@@ -62,7 +62,22 @@ int check_desc(const moe_exl3_desc *d)
         return MOE_EXL3_ERR_UNSUPPORTED;
     if ((d->flags & MOE_EXL3_FORCE_GEMV) && (d->flags & MOE_EXL3_FORCE_MFMA))
         return MOE_EXL3_ERR_INVALID_ARG;
+    // fp8 MFMA kernels read one width per launch
+    if ((d->flags & MOE_EXL3_FP8_MFMA) && (d->flags & MOE_EXL3_PER_TENSOR_K))
+        return MOE_EXL3_ERR_UNSUPPORTED;
+    // the segment kernels keep one thread per table expert (1024)
+    if ((d->flags & MOE_EXL3_SHARED_TRELLIS) && d->n_experts + 1 > 1024)
+        return MOE_EXL3_ERR_UNSUPPORTED;
     return MOE_EXL3_OK;
+}
+
+// Trellis-coded experts in the tensors and the segment tables.
+int trellis_experts(const moe_exl3_desc &d) { return d.n_experts + ((d.flags & MOE_EXL3_SHARED_TRELLIS) ? 1 : 0); }
+
+// Slots of the segment tables: T * k routed, + T of the trellis shared expert.
+int64_t table_slots(const moe_exl3_desc &d, int64_t T)
+{
+    return T * d.top_k + ((d.flags & MOE_EXL3_SHARED_TRELLIS) ? T : 0);
 }
 
 int check_weights(const moe_exl3_desc &d, const moe_exl3_weights *w, bool routing_only)
@@ -75,10 +90,21 @@ int check_weights(const moe_exl3_desc &d, const moe_exl3_weights *w, bool routin
         return MOE_EXL3_ERR_MISALIGNED;
     if (routing_only)
         return MOE_EXL3_OK;
-    for (int p = 0; p < 3; ++p) {
-        if (!w->codes[p] || !w->suh[p] || !w->svh[p])
+    const bool ptk = d.flags & MOE_EXL3_PER_TENSOR_K;
+    if (ptk && (!w->code_tab || !w->k_tab))
+        return MOE_EXL3_ERR_INVALID_ARG;
+    if (ptk && (!aligned16(w->code_tab) || !aligned16(w->k_tab)))
+        return MOE_EXL3_ERR_MISALIGNED;
+    if (d.flags & MOE_EXL3_HADAMARD) {
+        if (!w->signs)
             return MOE_EXL3_ERR_INVALID_ARG;
-        if (!aligned16(w->codes[p]) || !aligned16(w->suh[p]) || !aligned16(w->svh[p]))
+        if (!aligned16(w->signs))
+            return MOE_EXL3_ERR_MISALIGNED;
+    }
+    for (int p = 0; p < 3; ++p) {
+        if ((!ptk && !w->codes[p]) || !w->suh[p] || !w->svh[p])
+            return MOE_EXL3_ERR_INVALID_ARG;
+        if ((!ptk && !aligned16(w->codes[p])) || !aligned16(w->suh[p]) || !aligned16(w->svh[p]))
             return MOE_EXL3_ERR_MISALIGNED;
         if (d.flags & MOE_EXL3_HAS_SHARED) {
             if (!w->shared_w[p])
@@ -95,20 +121,24 @@ int check_weights(const moe_exl3_desc &d, const moe_exl3_weights *w, bool routin
 bool buffers_addressable(const moe_exl3_desc &d, int64_t T)
 {
     const int64_t lim = (int64_t)1 << 31;
-    return T * d.hidden * 2 < lim && T * d.top_k * d.inter * 2 < lim && T * d.inter * 2 < lim &&
-           (int64_t)d.hidden * d.inter * 2 < lim;
+    const int64_t slots = table_slots(d, T);
+    return T * d.hidden * 2 < lim && slots * d.inter * 2 < lim && slots * d.hidden * 2 < lim &&
+           T * d.inter * 2 < lim && (int64_t)d.hidden * d.inter * 2 < lim;
 }
 
 Plan make_plan(const moe_exl3_desc &d, int64_t T)
 {
     Plan p{};
     p.T = T;
-    const int64_t n = T * d.top_k;
-    const int E = d.n_experts;
+    const int64_t n = T * d.top_k;         // routed slots
+    const int64_t ns = table_slots(d, T);  // + the trellis shared expert's
+    const int E = d.n_experts, EA = trellis_experts(d);
     p.nblk = (int)std::max<int64_t>(1, (n + kSegChunk - 1) / kSegChunk);
     const int g = gemv_rows_of(d, T);
-    const int64_t heavy = std::min<int64_t>(E, n / (g + 1));
-    p.max_tiles = T <= g ? 0 : (int)std::max<int64_t>(0, std::min<int64_t>(n / kTileM + heavy, n));
+    // experts with more than g rows (at most ns / (g + 1)) each add one
+    // partial tile to the ns / kTileM full ones
+    const int64_t heavy = std::min<int64_t>(EA, ns / (g + 1));
+    p.max_tiles = T <= g ? 0 : (int)std::max<int64_t>(0, std::min<int64_t>(ns / kTileM + heavy, ns));
     size_t o = 0;
     auto take = [&](size_t bytes) {
         const size_t at = o;
@@ -118,27 +148,28 @@ Plan make_plan(const moe_exl3_desc &d, int64_t T)
     p.hdr = take(sizeof(WsHeader));
     p.logits = take(sizeof(float) * (size_t)T * E);
     p.idx = take(sizeof(int32_t) * (size_t)n);
-    p.w = take(sizeof(float) * (size_t)n);
-    p.counts = take(sizeof(int32_t) * (size_t)E);
-    p.offsets = take(sizeof(int32_t) * (size_t)(E + 1));
+    p.w = take(sizeof(float) * (size_t)ns);
+    p.counts = take(sizeof(int32_t) * (size_t)EA);
+    p.offsets = take(sizeof(int32_t) * (size_t)(EA + 1));
     p.bhist = take(sizeof(int32_t) * (size_t)p.nblk * E);
-    p.sorted = take(sizeof(int32_t) * (size_t)n);
-    p.pos = take(sizeof(int32_t) * (size_t)n);
-    p.glist = take(sizeof(int32_t) * (size_t)E);
+    p.sorted = take(sizeof(int32_t) * (size_t)ns);
+    p.pos = take(sizeof(int32_t) * (size_t)ns);
+    p.glist = take(sizeof(int32_t) * (size_t)EA);
     p.tiles = take(sizeof(int32_t) * 2 * (size_t)std::max(1, p.max_tiles));
     p.x16 = take(d.act_dtype == MOE_EXL3_DT_BF16 ? sizeof(uint16_t) * (size_t)T * d.hidden : 0);
-    p.hbuf = take(sizeof(uint16_t) * (size_t)n * d.inter);
-    p.ybuf = take(sizeof(uint16_t) * (size_t)n * d.hidden);
+    p.xr16 = take((d.flags & MOE_EXL3_HADAMARD) ? sizeof(uint16_t) * (size_t)T * d.hidden : 0);
+    p.hbuf = take(sizeof(uint16_t) * (size_t)ns * d.inter);
+    p.ybuf = take(sizeof(uint16_t) * (size_t)ns * d.hidden);
     const bool sh = d.flags & MOE_EXL3_HAS_SHARED;
     p.sh = take(sh ? sizeof(uint16_t) * (size_t)T * d.inter : 0);
     p.sy = take(sh ? sizeof(float) * (size_t)T * d.hidden : 0);
     const bool f8 = d.flags & MOE_EXL3_FP8_MFMA;
-    p.a8g = take(f8 ? (size_t)n * d.hidden : 0);
-    p.a8u = take(f8 ? (size_t)n * d.hidden : 0);
-    p.h8 = take(f8 ? (size_t)n * d.inter : 0);
-    p.sg8 = take(f8 ? sizeof(float) * (size_t)n : 0);
-    p.su8 = take(f8 ? sizeof(float) * (size_t)n : 0);
-    p.sh8 = take(f8 ? sizeof(float) * (size_t)n : 0);
+    p.a8g = take(f8 ? (size_t)ns * d.hidden : 0);
+    p.a8u = take(f8 ? (size_t)ns * d.hidden : 0);
+    p.h8 = take(f8 ? (size_t)ns * d.inter : 0);
+    p.sg8 = take(f8 ? sizeof(float) * (size_t)ns : 0);
+    p.su8 = take(f8 ? sizeof(float) * (size_t)ns : 0);
+    p.sh8 = take(f8 ? sizeof(float) * (size_t)ns : 0);
     p.total = o;
     return p;
 }
@@ -171,18 +202,27 @@ int run_route(const moe_exl3_desc &d, const moe_exl3_weights &w, const void *x, 
     const float *bias = (d.flags & MOE_EXL3_HAS_ROUTER_BIAS) ? w.router_bias : nullptr;
     if (!mk.mark(MOE_EXL3_STEP_ROUTE_LOGITS))
         return MOE_EXL3_ERR_HIP;
+    WsHeader *hdr = at<WsHeader>(ws, p.hdr);
     if (launch_route_logits((const uint16_t *)x, bf16, T, d.hidden, w.router_w, bias, d.n_experts,
-                            at<float>(ws, p.logits), s) != hipSuccess)
+                            at<float>(ws, p.logits), hdr, s) != hipSuccess)
         return MOE_EXL3_ERR_HIP;
+    const bool debug = d.flags & MOE_EXL3_DEBUG_CHECKS;
+    const bool extra = d.flags & MOE_EXL3_SHARED_TRELLIS;
+    auto checks = [&]() {
+        return !debug || launch_debug_checks((const uint16_t *)x, bf16, T, d.hidden, d.top_k, d.n_experts,
+                                             at<int32_t>(ws, p.idx), at<int32_t>(ws, p.counts),
+                                             at<int32_t>(ws, p.offsets), at<int32_t>(ws, p.sorted),
+                                             at<int32_t>(ws, p.pos), hdr, s) == hipSuccess;
+    };
     if (!mk.mark(MOE_EXL3_STEP_TOPK))
         return MOE_EXL3_ERR_HIP;
     if (T <= kSmallRouteTokens && p.nblk == 1) {
-        if (launch_route_small(at<float>(ws, p.logits), T, d.n_experts, d.top_k, gemv_rows_of(d, T), kTileM,
-                               at<int32_t>(ws, p.idx), at<float>(ws, p.w), at<int32_t>(ws, p.counts),
+        if (launch_route_small(at<float>(ws, p.logits), T, d.n_experts, d.top_k, extra, gemv_rows_of(d, T), kTileM,
+                               p.max_tiles, at<int32_t>(ws, p.idx), at<float>(ws, p.w), at<int32_t>(ws, p.counts),
                                at<int32_t>(ws, p.offsets), at<int32_t>(ws, p.sorted), at<int32_t>(ws, p.pos),
-                               at<int32_t>(ws, p.glist), at<int32_t>(ws, p.tiles), at<WsHeader>(ws, p.hdr),
+                               at<int32_t>(ws, p.glist), at<int32_t>(ws, p.tiles), hdr,
                                (const uint16_t *)x, d.hidden, x16, s) != hipSuccess ||
-            !mk.mark(MOE_EXL3_STEP_SEGMENTS))
+            !checks() || !mk.mark(MOE_EXL3_STEP_SEGMENTS))
             return MOE_EXL3_ERR_HIP;
         if (converted)
             *converted = x16 != nullptr;
@@ -193,11 +233,12 @@ int run_route(const moe_exl3_desc &d, const moe_exl3_weights &w, const void *x, 
         return MOE_EXL3_ERR_HIP;
     if (!mk.mark(MOE_EXL3_STEP_SEGMENTS))
         return MOE_EXL3_ERR_HIP;
-    if (launch_segments(at<int32_t>(ws, p.idx), T, d.top_k, d.n_experts, p.nblk, gemv_rows_of(d, T),
-                        kTileM, at<int32_t>(ws, p.bhist), at<int32_t>(ws, p.counts),
+    if (launch_segments(at<int32_t>(ws, p.idx), T, d.top_k, d.n_experts, extra, p.nblk, gemv_rows_of(d, T),
+                        kTileM, p.max_tiles, at<int32_t>(ws, p.bhist), at<int32_t>(ws, p.counts),
                         at<int32_t>(ws, p.offsets), at<int32_t>(ws, p.sorted),
-                        at<int32_t>(ws, p.pos), at<int32_t>(ws, p.glist), at<int32_t>(ws, p.tiles),
-                        at<WsHeader>(ws, p.hdr), s) != hipSuccess)
+                        at<int32_t>(ws, p.pos), at<float>(ws, p.w), at<int32_t>(ws, p.glist),
+                        at<int32_t>(ws, p.tiles), hdr, s) != hipSuccess ||
+        !checks())
         return MOE_EXL3_ERR_HIP;
     return MOE_EXL3_OK;
 }
@@ -321,9 +362,19 @@ static int run_layer(const moe_exl3_desc *desc, const moe_exl3_weights *weights,
     const uint16_t *x16 = (const uint16_t *)x;
     if (bf16) {
         if (!converted &&
-            launch_convert_x((const uint16_t *)x, true, T * d.hidden, at<uint16_t>(ws, p.x16), s) != hipSuccess)
+            launch_convert_x((const uint16_t *)x, T * d.hidden, at<uint16_t>(ws, p.x16), at<WsHeader>(ws, p.hdr), s) !=
+                hipSuccess)
             return MOE_EXL3_ERR_HIP;
         x16 = at<uint16_t>(ws, p.x16);
+    }
+    // the trellis experts' activations: x in fp16, or its rotation
+    const bool rot = d.flags & MOE_EXL3_HADAMARD;
+    const uint16_t *xe16 = x16;
+    if (rot) {
+        if (launch_rotate_x((const uint16_t *)x, bf16, T, d.hidden, wt.signs, at<uint16_t>(ws, p.xr16),
+                            at<WsHeader>(ws, p.hdr), s) != hipSuccess)
+            return MOE_EXL3_ERR_HIP;
+        xe16 = at<uint16_t>(ws, p.xr16);
     }
     GroupArgs ga{};
     for (int i = 0; i < 3; ++i) {
@@ -333,7 +384,12 @@ static int run_layer(const moe_exl3_desc *desc, const moe_exl3_weights *weights,
     }
     ga.H = d.hidden;
     ga.I = d.inter;
-    ga.E = d.n_experts;
+    ga.E = trellis_experts(d);
+    ga.nr = T * d.top_k;
+    if (d.flags & MOE_EXL3_PER_TENSOR_K) {
+        ga.code_tab = wt.code_tab;
+        ga.k_tab = wt.k_tab;
+    }
     ga.k = d.top_k;
     ga.T = T;
     ga.K = d.K;
@@ -346,7 +402,7 @@ static int run_layer(const moe_exl3_desc *desc, const moe_exl3_weights *weights,
     ga.tiles = at<int32_t>(ws, p.tiles);
     ga.hdr = at<WsHeader>(ws, p.hdr);
     ga.w = at<float>(ws, p.w);
-    ga.x16 = x16;
+    ga.x16 = xe16;
     ga.hbuf = at<uint16_t>(ws, p.hbuf);
     ga.ybuf = at<uint16_t>(ws, p.ybuf);
     const bool f8 = d.flags & MOE_EXL3_FP8_MFMA;
@@ -359,8 +415,8 @@ static int run_layer(const moe_exl3_desc *desc, const moe_exl3_weights *weights,
         ga.sh8 = at<float>(ws, p.sh8);
     }
     const int g = gemv_rows_of(d, T);
-    const int64_t n = T * d.top_k;
-    const int max_list = g > 0 ? (int)std::min<int64_t>(d.n_experts, n) : 0;
+    const int64_t n = table_slots(d, T);
+    const int max_list = g > 0 ? (int)std::min<int64_t>(trellis_experts(d), n) : 0;
 
     // The shared expert: a dot-product GEMV for up to kSharedGemvMaxTokens
     // tokens, whose blocks run at the end of the routed GEMV launches for up to
@@ -413,7 +469,8 @@ static int run_layer(const moe_exl3_desc *desc, const moe_exl3_weights *weights,
             return MOE_EXL3_ERR_HIP;
     }
     if (!mk.mark(MOE_EXL3_STEP_COMBINE) ||
-        launch_combine(at<uint16_t>(ws, p.ybuf), sy, T, d.hidden, d.top_k, bf16, (uint16_t *)out, s) != hipSuccess ||
+        launch_combine(at<uint16_t>(ws, p.ybuf), sy, T, d.hidden, d.top_k, d.flags & MOE_EXL3_SHARED_TRELLIS,
+                       rot ? wt.signs + d.hidden : nullptr, bf16, (uint16_t *)out, s) != hipSuccess ||
         !mk.mark(MOE_EXL3_STEP_END))
         return MOE_EXL3_ERR_HIP;
     return MOE_EXL3_OK;
@@ -444,11 +501,47 @@ int moe_exl3_decode(const uint16_t *codes, int32_t n_in, int32_t n_out, int32_t 
     if (!codes || !dst || n_in <= 0 || n_out <= 0 || n_in % 16 || n_out % 16)
         return MOE_EXL3_ERR_INVALID_ARG;
     if (K < 2 || K > 4 || (codebook != MOE_EXL3_CB_MCG && codebook != MOE_EXL3_CB_MCG_E4M3) ||
-        dst_dtype < MOE_EXL3_DT_F32 || dst_dtype > MOE_EXL3_DT_FP8)
+        dst_dtype < MOE_EXL3_DT_F32 || dst_dtype > MOE_EXL3_DT_GEMV_F16)
         return MOE_EXL3_ERR_UNSUPPORTED;
     if (!aligned16(codes) || !aligned16(dst))
         return MOE_EXL3_ERR_MISALIGNED;
     if (launch_decode(codes, n_in, n_out, K, mcg, codebook, dst, dst_dtype, (hipStream_t)stream) != hipSuccess)
+        return MOE_EXL3_ERR_HIP;
+    return MOE_EXL3_OK;
+}
+
+int moe_exl3_repack(const uint16_t *src, uint16_t *dst, int32_t count, int32_t n_in, int32_t n_out, int32_t K,
+                    int32_t src_order, void *stream)
+{
+    if (!src || !dst || count < 1 || n_in <= 0 || n_out <= 0 || n_in % 16 || n_out % 16)
+        return MOE_EXL3_ERR_INVALID_ARG;
+    if (K < 2 || K > 4 || src_order < MOE_EXL3_ORDER_ROWMAJOR || src_order > MOE_EXL3_ORDER_COLGROUPS128 ||
+        (src_order == MOE_EXL3_ORDER_COLGROUPS128 && n_out % 128))
+        return MOE_EXL3_ERR_UNSUPPORTED;
+    if (!aligned16(src) || !aligned16(dst))
+        return MOE_EXL3_ERR_MISALIGNED;
+    const int64_t bytes = (int64_t)count * (n_in / 16) * (n_out / 16) * 32 * K;
+    if ((const char *)dst < (const char *)src + bytes && (const char *)src < (const char *)dst + bytes)
+        return MOE_EXL3_ERR_INVALID_ARG;
+    if (launch_repack(src, dst, count, n_in, n_out, K, src_order, (hipStream_t)stream) != hipSuccess)
+        return MOE_EXL3_ERR_HIP;
+    return MOE_EXL3_OK;
+}
+
+int moe_exl3_expand_block_scales(const uint16_t *block, int32_t n_trellis, int32_t hidden, int32_t inter,
+                                 uint16_t *const *suh, uint16_t *const *svh, void *stream)
+{
+    if (!block || !suh || !svh || n_trellis < 1 || hidden <= 0 || hidden % 128 || inter <= 0)
+        return MOE_EXL3_ERR_INVALID_ARG;
+    if (!aligned16(block))
+        return MOE_EXL3_ERR_MISALIGNED;
+    for (int p = 0; p < 3; ++p) {
+        if (!suh[p] || !svh[p])
+            return MOE_EXL3_ERR_INVALID_ARG;
+        if (!aligned16(suh[p]) || !aligned16(svh[p]))
+            return MOE_EXL3_ERR_MISALIGNED;
+    }
+    if (launch_expand_scales(block, n_trellis, hidden, inter, suh, svh, (hipStream_t)stream) != hipSuccess)
         return MOE_EXL3_ERR_HIP;
     return MOE_EXL3_OK;
 }

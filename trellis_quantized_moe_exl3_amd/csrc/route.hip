@@ -2,6 +2,8 @@
 // device-side segment tables (page "GLM-5.3 Flash EXL3 for 2x DGX Sparks",
 // "Cold prefill (E3 grouped MoE)": segment tables built on the device, no
 // per-expert launches, no host sync).
+#include <algorithm>
+
 #include "common.h"
 #include "internal.h"
 
@@ -39,12 +41,21 @@ MOE_DEV float dpp_shl(float v, int n)
     return __int_as_float(r);
 }
 
+// The first launch of every call clears the status word of the workspace
+// header; later launches only set bits in it.
+MOE_DEV void clear_status(WsHeader *hdr)
+{
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
+        hdr->status = 0;
+}
+
 template <bool BF16, int TPL, int EPL, int NTQ>
 __global__ __launch_bounds__(256) void route_logits_kernel(const uint16_t *__restrict__ x, int64_t T,
                                                            int H, const uint16_t *__restrict__ Wr,
                                                            const float *__restrict__ bias, int E,
-                                                           float *__restrict__ logits)
+                                                           float *__restrict__ logits, WsHeader *hdr)
 {
+    clear_status(hdr);
     using S = RouteShape<TPL, EPL, NTQ>;
     const int w = threadIdx.x >> 6, L = threadIdx.x & 63;
     const int g = L & 7, blk = L >> 3;
@@ -149,8 +160,9 @@ template <bool BF16>
 __global__ __launch_bounds__(256) void route_logits_pairs_kernel(const uint16_t *__restrict__ x, int64_t T,
                                                                  int H, const uint16_t *__restrict__ Wr,
                                                                  const float *__restrict__ bias, int E,
-                                                                 float *__restrict__ logits)
+                                                                 float *__restrict__ logits, WsHeader *hdr)
 {
+    clear_status(hdr);
     const int64_t pair = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
     const int m = threadIdx.x & 31;
     const bool ok = pair < T * E;
@@ -196,26 +208,26 @@ __global__ __launch_bounds__(256) void route_logits_pairs_kernel(const uint16_t 
 
 template <bool BF16, int TPL, int EPL, int NTQ>
 static void route_launch(const uint16_t *x, int64_t T, int H, const uint16_t *Wr, const float *bias,
-                         int E, float *logits, hipStream_t s)
+                         int E, float *logits, WsHeader *hdr, hipStream_t s)
 {
     using S = RouteShape<TPL, EPL, NTQ>;
     dim3 grid((unsigned)((T + S::kTokens - 1) / S::kTokens), (unsigned)((E + S::kExperts - 1) / S::kExperts));
-    route_logits_kernel<BF16, TPL, EPL, NTQ><<<grid, 256, 0, s>>>(x, T, H, Wr, bias, E, logits);
+    route_logits_kernel<BF16, TPL, EPL, NTQ><<<grid, 256, 0, s>>>(x, T, H, Wr, bias, E, logits, hdr);
 }
 
 hipError_t launch_route_logits(const uint16_t *x, bool bf16, int64_t T, int H, const uint16_t *Wr,
-                               const float *bias, int E, float *logits, hipStream_t s)
+                               const float *bias, int E, float *logits, WsHeader *hdr, hipStream_t s)
 {
     // many tokens: 2 tokens x 4 experts per lane (8 tokens x 32 experts per
     // block); few tokens: one (token, expert) pair per 32 lanes so that
     // enough wavefronts stream the router weights
     if (T > 64) {
-        if (bf16) route_launch<true, 2, 4, 4>(x, T, H, Wr, bias, E, logits, s);
-        else route_launch<false, 2, 4, 4>(x, T, H, Wr, bias, E, logits, s);
+        if (bf16) route_launch<true, 2, 4, 4>(x, T, H, Wr, bias, E, logits, hdr, s);
+        else route_launch<false, 2, 4, 4>(x, T, H, Wr, bias, E, logits, hdr, s);
     } else {
         const unsigned grid = (unsigned)((T * E + 7) / 8);
-        if (bf16) route_logits_pairs_kernel<true><<<grid, 256, 0, s>>>(x, T, H, Wr, bias, E, logits);
-        else route_logits_pairs_kernel<false><<<grid, 256, 0, s>>>(x, T, H, Wr, bias, E, logits);
+        if (bf16) route_logits_pairs_kernel<true><<<grid, 256, 0, s>>>(x, T, H, Wr, bias, E, logits, hdr);
+        else route_logits_pairs_kernel<false><<<grid, 256, 0, s>>>(x, T, H, Wr, bias, E, logits, hdr);
     }
     return hipGetLastError();
 }
@@ -225,7 +237,9 @@ hipError_t launch_route_logits(const uint16_t *x, bool bf16, int64_t T, int H, c
 // (NPER slots, enough for E).  k rounds: each lane offers its best remaining
 // (logit, expert), a DPP reduction finds the wave maximum, and a ballot of the
 // lanes holding it names the winner (the lowest expert among ties, which needs
-// a second reduction only when several lanes tie).
+// a second reduction only when several lanes tie).  A NaN logit ranks as -inf:
+// no NaN reaches the reductions, so while any lane still holds an expert the
+// ballot is never empty and the winner is always a valid expert.
 
 // v <- op(v, v of the lane the DPP control names); rows outside row_mask
 // keep their own value (op(v, v) = v).
@@ -279,7 +293,8 @@ MOE_DEV void topk_token(const float *__restrict__ logits, int64_t t, int E, int 
     for (int i = 0; i < NPER; ++i) {
         const int e = l + 64 * i;
         const bool ok = e < E;
-        v[i] = ok ? logits[t * E + e] : -INFINITY;
+        const float lv = ok ? logits[t * E + e] : -INFINITY;
+        v[i] = lv != lv ? -INFINITY : lv;
         key[i] = ok ? e : kNoExpert;
     }
     float selv[16];
@@ -362,8 +377,14 @@ hipError_t launch_topk(const float *logits, int64_t T, int E, int k, int32_t *id
 //  3. per block, slots in order: rank inside each 64-slot chunk from ballots,
 //     position = block base + rank.
 
+// An expert index outside [0, E) (impossible from topk_token; a guard against
+// a corrupted table) is left out of every table and flagged in the status word.
+MOE_DEV bool valid_expert(int e, int E) { return (unsigned)e < (unsigned)E; }
+
+MOE_DEV void flag_status(WsHeader *hdr, uint32_t bits) { atomicOr((unsigned *)&hdr->status, bits); }
+
 __global__ __launch_bounds__(256) void seg_hist_kernel(const int32_t *__restrict__ idx, int64_t n,
-                                                       int E, int32_t *__restrict__ bhist)
+                                                       int E, int32_t *__restrict__ bhist, WsHeader *hdr)
 {
     extern __shared__ int32_t hist[];
     for (int e = threadIdx.x; e < E; e += blockDim.x)
@@ -372,8 +393,13 @@ __global__ __launch_bounds__(256) void seg_hist_kernel(const int32_t *__restrict
     const int64_t a0 = (int64_t)blockIdx.x * kSegChunk;
     for (int i = threadIdx.x; i < kSegChunk; i += blockDim.x) {
         const int64_t a = a0 + i;
-        if (a < n)
-            atomicAdd(&hist[idx[a]], 1);
+        if (a < n) {
+            const int e = idx[a];
+            if (valid_expert(e, E))
+                atomicAdd(&hist[e], 1);
+            else
+                flag_status(hdr, MOE_EXL3_STATUS_BAD_INDEX);
+        }
     }
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += blockDim.x)
@@ -406,15 +432,55 @@ __device__ int block_exclusive_scan(int v, int *total)
     return base + incl - v;
 }
 
-__global__ __launch_bounds__(1024) void seg_scan_kernel(int32_t *__restrict__ bhist, int nblk, int E,
-                                                        int gemv_rows, int tile_m,
-                                                        int32_t *__restrict__ counts,
+// The GEMV expert list and the MFMA tile list (expert, first row), written by
+// the thread of expert e.  The tile list holds at most max_tiles entries (the
+// host's bound on the tiles a call can produce); a longer one is cut there and
+// flagged.
+MOE_DEV void write_work_lists(int e, bool gemv, int gpos, int ng, int nt, int tpos, int ntt, int tile_m,
+                              int max_tiles, int32_t *__restrict__ glist, int32_t *__restrict__ tiles,
+                              WsHeader *hdr)
+{
+    if (gemv)
+        glist[gpos] = e;
+    for (int m = 0; m < nt; ++m) {
+        if (tpos + m >= max_tiles)
+            break;
+        tiles[2 * (tpos + m)] = e;
+        tiles[2 * (tpos + m) + 1] = m * tile_m;
+    }
+    if (e == 0) {
+        hdr->n_gemv = ng;
+        hdr->n_tiles = min(ntt, max_tiles);
+        if (ntt > max_tiles)
+            flag_status(hdr, MOE_EXL3_STATUS_TILE_OVERFLOW);
+    }
+}
+
+// The slots of the trellis shared expert: slot nr + t is token t's, with
+// routing weight 1, and sits at position nr + t of the sorted list (the
+// expert follows every routed one).
+MOE_DEV void write_extra_slots(int64_t nr, int64_t T, int32_t *__restrict__ sorted, int32_t *__restrict__ pos,
+                               float *__restrict__ w)
+{
+    for (int64_t t = threadIdx.x; t < T; t += blockDim.x) {
+        sorted[nr + t] = (int32_t)(nr + t);
+        pos[nr + t] = (int32_t)(nr + t);
+        w[nr + t] = 1.0f;
+    }
+}
+
+__global__ __launch_bounds__(1024) void seg_scan_kernel(int32_t *__restrict__ bhist, int nblk, int E, int64_t T,
+                                                        int64_t nr, bool extra, int gemv_rows, int tile_m,
+                                                        int max_tiles, int32_t *__restrict__ counts,
                                                         int32_t *__restrict__ offsets,
+                                                        int32_t *__restrict__ sorted, int32_t *__restrict__ pos,
+                                                        float *__restrict__ w,
                                                         int32_t *__restrict__ glist,
                                                         int32_t *__restrict__ tiles,
                                                         WsHeader *__restrict__ hdr)
 {
-    const int e = threadIdx.x;   // E <= 1024
+    const int e = threadIdx.x;   // E + extra <= 1024
+    const int EA = E + (extra ? 1 : 0);
     int c = 0;
     if (e < E) {
         // per-chunk counts -> running bases, 16 chunks' loads in flight at a time
@@ -431,31 +497,25 @@ __global__ __launch_bounds__(1024) void seg_scan_kernel(int32_t *__restrict__ bh
                     c += v[j];
                 }
         }
+    } else if (e < EA) {
+        c = (int)T;
     }
     int tot;
-    const int off = block_exclusive_scan(e < E ? c : 0, &tot);
-    if (e < E) {
+    const int off = block_exclusive_scan(e < EA ? c : 0, &tot);
+    if (e < EA) {
         counts[e] = c;
         offsets[e] = off;
     }
     if (e == 0)
-        offsets[E] = tot;
-    const bool gemv = e < E && c > 0 && c <= gemv_rows;
-    const int nt = (e < E && c > gemv_rows) ? (c + tile_m - 1) / tile_m : 0;
+        offsets[EA] = tot;
+    const bool gemv = e < EA && c > 0 && c <= gemv_rows;
+    const int nt = (e < EA && c > gemv_rows) ? (c + tile_m - 1) / tile_m : 0;
     int ng, ntt;
     const int gpos = block_exclusive_scan(gemv ? 1 : 0, &ng);
     const int tpos = block_exclusive_scan(nt, &ntt);
-    if (gemv)
-        glist[gpos] = e;
-    for (int m = 0; m < nt; ++m) {
-        tiles[2 * (tpos + m)] = e;
-        tiles[2 * (tpos + m) + 1] = m * tile_m;
-    }
-    if (e == 0) {
-        hdr->n_gemv = ng;
-        hdr->n_tiles = ntt;
-        hdr->status = 0;
-    }
+    write_work_lists(e, gemv, gpos, ng, nt, tpos, ntt, tile_m, max_tiles, glist, tiles, hdr);
+    if (extra)
+        write_extra_slots(nr, T, sorted, pos, w);
 }
 
 __global__ __launch_bounds__(64) void seg_scatter_kernel(const int32_t *__restrict__ idx, int64_t n,
@@ -489,8 +549,8 @@ __global__ __launch_bounds__(64) void seg_scatter_kernel(const int32_t *__restri
         if (64 * c >= span)
             break;
         const int64_t a = a0 + 64 * c + l;
-        const bool valid = a < n;
         const int e = ev[c];
+        const bool valid = a < n && valid_expert(e, E);
         uint64_t m = __ballot(valid);
         for (int b = 0; b < nbits; ++b) {
             const bool bit = (e >> b) & 1;
@@ -510,17 +570,81 @@ __global__ __launch_bounds__(64) void seg_scatter_kernel(const int32_t *__restri
     }
 }
 
-hipError_t launch_segments(const int32_t *idx, int64_t T, int k, int E, int nblk, int gemv_rows,
-                           int tile_m, int32_t *bhist, int32_t *counts, int32_t *offsets,
-                           int32_t *sorted, int32_t *pos, int32_t *glist, int32_t *tiles,
+hipError_t launch_segments(const int32_t *idx, int64_t T, int k, int E, bool extra, int nblk, int gemv_rows,
+                           int tile_m, int max_tiles, int32_t *bhist, int32_t *counts, int32_t *offsets,
+                           int32_t *sorted, int32_t *pos, float *w, int32_t *glist, int32_t *tiles,
                            WsHeader *hdr, hipStream_t s)
 {
     const int64_t n = T * k;
     const size_t lds = sizeof(int32_t) * (size_t)E;
-    seg_hist_kernel<<<nblk, 256, lds, s>>>(idx, n, E, bhist);
-    seg_scan_kernel<<<1, 1024, 0, s>>>(bhist, nblk, E, gemv_rows, tile_m, counts, offsets, glist,
-                                       tiles, hdr);
+    seg_hist_kernel<<<nblk, 256, lds, s>>>(idx, n, E, bhist, hdr);
+    seg_scan_kernel<<<1, 1024, 0, s>>>(bhist, nblk, E, T, n, extra, gemv_rows, tile_m, max_tiles, counts,
+                                       offsets, sorted, pos, w, glist, tiles, hdr);
     seg_scatter_kernel<<<nblk, 64, lds, s>>>(idx, n, E, bhist, offsets, sorted, pos);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- debug checks
+// One block: thread e walks expert e's segment and checks that it holds
+// counts[e] slots, in increasing order, each routed to e, with pos its
+// inverse; the counts must sum to n.  Every table value is range-checked
+// before it is used as an index.
+__global__ __launch_bounds__(1024) void debug_tables_kernel(const int32_t *__restrict__ idx, int64_t n, int E,
+                                                            const int32_t *__restrict__ counts,
+                                                            const int32_t *__restrict__ offsets,
+                                                            const int32_t *__restrict__ sorted,
+                                                            const int32_t *__restrict__ pos, WsHeader *hdr)
+{
+    __shared__ long long total;
+    if (threadIdx.x == 0)
+        total = 0;
+    __syncthreads();
+    bool bad = false;
+    long long mine = 0;
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+        const int c = counts[e], o0 = offsets[e], o1 = offsets[e + 1];
+        mine += c;
+        if (o1 - o0 != c || o0 < 0 || o1 > n || o0 > o1) {
+            bad = true;
+            continue;
+        }
+        int prev = -1;
+        for (int p = o0; p < o1; ++p) {
+            const int a = sorted[p];
+            if (a <= prev || a >= n || idx[a] != e || pos[a] != p) {
+                bad = true;
+                break;
+            }
+            prev = a;
+        }
+    }
+    atomicAdd((unsigned long long *)&total, (unsigned long long)mine);
+    if (bad)
+        flag_status(hdr, MOE_EXL3_STATUS_TABLES);
+    __syncthreads();
+    if (threadIdx.x == 0 && (total != n || offsets[0] != 0 || offsets[E] != n))
+        flag_status(hdr, MOE_EXL3_STATUS_COUNTS);
+}
+
+// Grid-stride check that every activation is finite.
+__global__ __launch_bounds__(256) void debug_finite_kernel(const uint16_t *__restrict__ x, int64_t n, uint32_t expo,
+                                                           WsHeader *hdr)
+{
+    bool bad = false;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+        bad |= (x[i] & expo) == expo;
+    if (bad)
+        flag_status(hdr, MOE_EXL3_STATUS_NONFINITE_X);
+}
+
+hipError_t launch_debug_checks(const uint16_t *x, bool bf16, int64_t T, int H, int k, int E,
+                               const int32_t *idx, const int32_t *counts, const int32_t *offsets,
+                               const int32_t *sorted, const int32_t *pos, WsHeader *hdr, hipStream_t s)
+{
+    debug_tables_kernel<<<1, 1024, 0, s>>>(idx, T * k, E, counts, offsets, sorted, pos, hdr);
+    const int64_t n = T * H;
+    const unsigned grid = (unsigned)std::min<int64_t>(2048, (n + 255) / 256);
+    debug_finite_kernel<<<grid, 256, 0, s>>>(x, n, bf16 ? 0x7F80u : 0x7C00u, hdr);
     return hipGetLastError();
 }
 
@@ -533,7 +657,7 @@ hipError_t launch_segments(const int32_t *idx, int64_t T, int k, int E, int nblk
 // bf16 -> fp16 copy of the activations.
 template <int NPER>
 __global__ __launch_bounds__(1024) void route_small_kernel(
-    const float *__restrict__ logits, int64_t T, int E, int k, int gemv_rows, int tile_m,
+    const float *__restrict__ logits, int64_t T, int E, int k, bool extra, int gemv_rows, int tile_m, int max_tiles,
     int32_t *__restrict__ idx, float *__restrict__ w, int32_t *__restrict__ counts,
     int32_t *__restrict__ offsets, int32_t *__restrict__ sorted, int32_t *__restrict__ pos,
     int32_t *__restrict__ glist, int32_t *__restrict__ tiles, WsHeader *__restrict__ hdr,
@@ -551,49 +675,41 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
     if (x16 && (!split || wv >= 8)) {
         const int64_t n8 = T * H / 8;
         const int first = split ? (int)threadIdx.x - 512 : (int)threadIdx.x, step = split ? 512 : 1024;
-        for (int64_t i = first; i < n8; i += step) {
-            const u32x4 v = ((const u32x4 *)x)[i];
-            u32x4 o;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float lo = __uint_as_float(v[j] << 16), hi = __uint_as_float(v[j] & 0xFFFF0000u);
-                o[j] = (uint32_t)f32_to_f16_bits(lo) | ((uint32_t)f32_to_f16_bits(hi) << 16);
-            }
-            ((u32x4 *)x16)[i] = o;
-        }
+        bool over = false;
+        for (int64_t i = first; i < n8; i += step)
+            ((u32x4 *)x16)[i] = bf16x8_to_f16x8(((const u32x4 *)x)[i], over);
+        if (over)
+            flag_status(hdr, MOE_EXL3_STATUS_ACT_RANGE);
     }
     hist[threadIdx.x] = 0;
     __syncthreads();
     const int n = (int)(T * k);
-    for (int a = threadIdx.x; a < n; a += 1024)
-        atomicAdd(&hist[sidx[a]], 1);
+    for (int a = threadIdx.x; a < n; a += 1024) {
+        if (valid_expert(sidx[a], E))
+            atomicAdd(&hist[sidx[a]], 1);
+        else
+            flag_status(hdr, MOE_EXL3_STATUS_BAD_INDEX);
+    }
     __syncthreads();
-    const int e = threadIdx.x;   // E <= 1024
-    const int c = e < E ? hist[e] : 0;
+    const int e = threadIdx.x;   // E + extra <= 1024
+    const int EA = E + (extra ? 1 : 0);
+    const int c = e < E ? hist[e] : e < EA ? (int)T : 0;
     int tot;
     const int off = block_exclusive_scan(c, &tot);
-    if (e < E) {
+    if (e < EA) {
         counts[e] = c;
         offsets[e] = off;
     }
     if (e == 0)
-        offsets[E] = tot;
-    const bool gemv = e < E && c > 0 && c <= gemv_rows;
-    const int nt = (e < E && c > gemv_rows) ? (c + tile_m - 1) / tile_m : 0;
+        offsets[EA] = tot;
+    const bool gemv = e < EA && c > 0 && c <= gemv_rows;
+    const int nt = (e < EA && c > gemv_rows) ? (c + tile_m - 1) / tile_m : 0;
     int ng, ntt;
     const int gpos = block_exclusive_scan(gemv ? 1 : 0, &ng);
     const int tpos = block_exclusive_scan(nt, &ntt);
-    if (gemv)
-        glist[gpos] = e;
-    for (int m = 0; m < nt; ++m) {
-        tiles[2 * (tpos + m)] = e;
-        tiles[2 * (tpos + m) + 1] = m * tile_m;
-    }
-    if (e == 0) {
-        hdr->n_gemv = ng;
-        hdr->n_tiles = ntt;
-        hdr->status = 0;
-    }
+    write_work_lists(e, gemv, gpos, ng, nt, tpos, ntt, tile_m, max_tiles, glist, tiles, hdr);
+    if (extra)
+        write_extra_slots((int64_t)n, T, sorted, pos, w);
     __syncthreads();
     hist[threadIdx.x] = off;   // running base of every expert
     __syncthreads();
@@ -604,8 +720,8 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
         const uint64_t below = (l == 0) ? 0ull : (~0ull >> (64 - l));
         for (int c0 = 0; c0 < n; c0 += 64) {
             const int a = c0 + l;
-            const bool valid = a < n;
-            const int ea = valid ? sidx[a] : 0;
+            const int ea = a < n ? sidx[a] : 0;
+            const bool valid = a < n && valid_expert(ea, E);
             uint64_t m = __ballot(valid);
             for (int b = 0; b < nbits; ++b) {
                 const bool bit = (ea >> b) & 1;
@@ -627,15 +743,15 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
     }
 }
 
-hipError_t launch_route_small(const float *logits, int64_t T, int E, int k, int gemv_rows, int tile_m,
-                              int32_t *idx, float *w, int32_t *counts, int32_t *offsets, int32_t *sorted,
-                              int32_t *pos, int32_t *glist, int32_t *tiles, WsHeader *hdr,
+hipError_t launch_route_small(const float *logits, int64_t T, int E, int k, bool extra, int gemv_rows, int tile_m,
+                              int max_tiles, int32_t *idx, float *w, int32_t *counts, int32_t *offsets,
+                              int32_t *sorted, int32_t *pos, int32_t *glist, int32_t *tiles, WsHeader *hdr,
                               const uint16_t *x, int H, uint16_t *x16, hipStream_t s)
 {
     const int nper = (E + 63) / 64;   // E <= 1024
 #define MOE_ROUTE_SMALL(NP) \
-    route_small_kernel<NP><<<1, 1024, 0, s>>>(logits, T, E, k, gemv_rows, tile_m, idx, w, counts, offsets, \
-                                              sorted, pos, glist, tiles, hdr, x, H, x16)
+    route_small_kernel<NP><<<1, 1024, 0, s>>>(logits, T, E, k, extra, gemv_rows, tile_m, max_tiles, idx, w, \
+                                              counts, offsets, sorted, pos, glist, tiles, hdr, x, H, x16)
     if (nper <= 1) MOE_ROUTE_SMALL(1);
     else if (nper <= 2) MOE_ROUTE_SMALL(2);
     else if (nper <= 5) MOE_ROUTE_SMALL(5);

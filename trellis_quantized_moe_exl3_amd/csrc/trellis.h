@@ -187,6 +187,31 @@ MOE_DEV u32x2 frag_decode_fp8(uint32_t D0, uint32_t D1, int q, uint32_t m_lo, ui
     return out;
 }
 
+// Fragment -> the eight decoded values as fp16 pairs of 2v + 1532 (exact:
+// integers in [1020, 2044]), the operand of the decode-fused GEMV's
+// v_dot2_f32_f16 (which subtracts 1532 * sum(x) once per output).  mcg: the
+// low half from v_sad_u8 on base 0x64006400, the high half from v_sad_hi_u8;
+// E4M3: 128 * c8 + 1532 (128 * c8 is an even integer: E4M3 keeps 4
+// significant bits of the integer v).
+template <int K, int CB>
+MOE_DEV void frag_biased_pairs(uint32_t D0, uint32_t D1, int q, uint32_t m_lo, uint32_t m_hi, f16x2 wp[4])
+{
+    uint32_t st[8];
+    frag_states<K>(D0, D1, q, st);
+#pragma unroll
+    for (int t = 0; t < 8; t += 2) {
+        if (CB == CB_MCG) {
+            const uint32_t ra = field_sum2(mcg_hash(st[t], m_lo, m_hi), 0x64006400u);
+            const uint32_t rb = __builtin_amdgcn_sad_hi_u8(mcg_hash(st[t + 1], m_lo, m_hi) & 0xFEFEFEFEu, 0u, ra);
+            wp[t / 2] = __builtin_bit_cast(f16x2, rb);
+        } else {
+            const float a = e4m3_value2(value2_f32(st[t], m_lo, m_hi)) + 1532.0f;
+            const float b = e4m3_value2(value2_f32(st[t + 1], m_lo, m_hi)) + 1532.0f;
+            wp[t / 2] = (f16x2){(f16)a, (f16)b};
+        }
+    }
+}
+
 // Fragment -> eight fp32 values of 2v (or 128 * E4M3(v/64)).
 template <int K, int CB>
 MOE_DEV void frag_decode_f32(uint32_t D0, uint32_t D1, int q, uint32_t m_lo, uint32_t m_hi, float out[8])
