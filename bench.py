@@ -4,9 +4,14 @@ Workload (one step = one whole layer, every launch of the hot path): the
 7168-token prefill chunk at GLM-5.3-Flash shapes (hidden 4096, expert
 intermediate 2048, 288 experts top-8 with a skewing router bias, K = 2 mcg
 codes, fp16 shared expert), seeded synthetic inputs already resident in HBM.
-`value` is tokens per second of that layer.  The 8-token decode step is timed
-as well (code HBM GB/s and us per layer, with rotating copies of the codes so
-the 256 MB last-level cache cannot hold them).
+`value` is tokens per second of that layer.  Also timed, each in an object of
+the same JSON line: the 8-token decode step at K = 2, 3, 4 (code HBM GB/s, us
+per layer and the VALU-implied bound, with rotating copies of the codes so the
+256 MB last-level cache cannot hold them); the 1-, 2-, 4- and 8-token verify
+batches replayed from HIP graphs; the 2048-token prefill at K = 3 and K = 4;
+the 16384-token E4M3-codebook layer on fp16 and fp8 MFMA; the format variants
+(per-tensor K3/K4 widths, and the rotated exlr8 layout with a trellis shared
+expert); the achievable HBM read bandwidth; and the CPU oracle per workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
@@ -36,7 +41,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_FP16_TFLOPS = 2500.0      # MI355X dense fp16/bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 PEAK_HBM_GBPS = 8000.0
+# VALU lane operations per second: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+PEAK_VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9
+VALU_FILE = os.path.join(ROOT, "profiles", "pmc_valu_gemv_decode.md")
 GEMV_ROWS = 2                  # default per-expert row count up to which the GEMV path runs
 SHARED_GEMV_TOKENS = 16        # above this many tokens the shared expert's 16-bit MFMA tiles run inside
                                # the routed gate/up and down launches
@@ -102,21 +111,45 @@ class Hip:
 
 
 def setup(cfg, copies=1, shared=True, extra_flags=0):
+    """Device inputs of a workload: `copies` copies of the codes (rotated by
+    the decode legs), the descriptor and one weights struct per copy.  Format
+    variants: per-tensor widths (one code pool per projection and a table of
+    tensor addresses), sign vectors, a trellis shared expert."""
     import trellis_quantized_moe_exl3_amd as M
     import workloads as W
     inp = W.gen_layer(cfg)
-    codes = [[_dev(c) for c in inp.codes] for _ in range(copies)]
+    flags = extra_flags
+    tabs = []
+    if inp.ktab is not None:
+        flags |= M.PER_TENSOR_K
+        codes = []
+        for _ in range(copies):
+            pools = [_dev(np.concatenate(c)) for c in inp.codes]
+            addr = np.zeros((3, cfg.n_trellis), dtype=np.int64)
+            for p in range(3):
+                off = 0
+                for e in range(cfg.n_trellis):
+                    addr[p, e] = pools[p].data_ptr() + 2 * off
+                    off += cfg.words_of(p, e, inp.ktab)
+            codes.append(pools)
+            tabs.append(_dev(addr))
+        ktab = _dev(np.ascontiguousarray(inp.ktab, dtype=np.int32))
+    else:
+        codes = [[_dev(c) for c in inp.codes] for _ in range(copies)]
+        ktab = None
     suh = [_dev(s) for s in inp.suh]
     svh = [_dev(s) for s in inp.svh]
     rw = _dev(inp.router_w)
     bias = _dev(inp.router_bias) if inp.router_bias is not None else None
     sh = [_dev(s) for s in inp.shared] if (shared and inp.shared is not None) else None
-    flags = (M.HAS_SHARED if sh is not None else 0) | (M.HAS_ROUTER_BIAS if bias is not None else 0)
-    flags |= extra_flags
+    signs = _dev(inp.signs) if inp.signs is not None else None
+    flags |= (M.HAS_SHARED if sh is not None else 0) | (M.HAS_ROUTER_BIAS if bias is not None else 0)
+    flags |= (M.HADAMARD if signs is not None else 0) | (M.SHARED_TRELLIS if cfg.shared_trellis else 0)
     desc = M.make_desc(cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k, cfg.K, cfg.codebook,
                        cfg.mcg, cfg.act_dtype, flags, 0)
-    weights = [M.make_weights(c, suh, svh, rw, bias, sh) for c in codes]
-    keep = (codes, suh, svh, rw, bias, sh)
+    weights = [M.make_weights(c, suh, svh, rw, bias, sh, signs, tabs[i] if tabs else None, ktab)
+               for i, c in enumerate(codes)]
+    keep = (codes, suh, svh, rw, bias, sh, signs, tabs, ktab)
     return inp, desc, weights, keep
 
 
@@ -213,21 +246,203 @@ def routing_counts(desc, weights, x, cfg):
     return counts.cpu().numpy()
 
 
-def cpu_baseline(cfg, n_tokens):
+def per_layer_percentiles(desc, weights_list, x, steps, hip):
+    """Median, p10 and p90 of the device time of single layers: each layer of
+    a separate pass sits between two events of its own (an event adds a few
+    microseconds, which the plain pass's mean does not contain)."""
+    import torch
+    import trellis_quantized_moe_exl3_amd as M
+    out = torch.empty_like(x)
+    ws = torch.empty(M.workspace_size(desc, x.shape[0]), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    evs = [hip.event() for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    assert hip.l.hipEventRecord(evs[0], stream) == 0
+    for i in range(steps):
+        M.layer(desc, weights_list[i % len(weights_list)], x, out, ws)
+        assert hip.l.hipEventRecord(evs[i + 1], stream) == 0
+    torch.cuda.synchronize()
+    t = np.array([hip.ms(evs[i], evs[i + 1]) for i in range(steps)])
+    for e in evs:
+        hip.destroy(e)
+    return {"median_ms": float(np.median(t)), "p10_ms": float(np.percentile(t, 10)),
+            "p90_ms": float(np.percentile(t, 90)), "layers": steps}
+
+
+def expert_flops(cfg, T):
+    """Algorithmic flops of the expert contractions: gate, up and down of every
+    routed row (T * k) and of the shared expert (T rows when there is one)."""
+    rows = T * cfg.top_k + (T if (cfg.shared or cfg.shared_trellis) else 0)
+    return 6.0 * cfg.hidden * cfg.inter * rows
+
+
+def recorded_valu_per_weight():
+    """VALU lane instructions per routed weight of the decode GEMVs, from the
+    committed counter summary (None when missing)."""
+    try:
+        with open(VALU_FILE) as f:
+            for line in f:
+                if line.startswith("VALU lane instructions per routed weight"):
+                    return float(line.split("=")[-1].split(",")[0].strip())
+    except (OSError, ValueError):
+        pass
+    return None
+
+
+def decode_leg(W, M, hip, K, steps, copies=4):
+    """The 8-token decode step at width K with `copies` rotating code copies:
+    us per layer (plain and graph replay), the routed kernels' code GB/s and
+    the VALU-implied bound of those kernels."""
+    import torch
+    dcfg = W.BY_NAME["decode"].replace(K=K)
+    dinp, ddesc, dweights, dkeep = setup(dcfg, copies=copies)
+    dx = _dev(dinp.x)
+    dms, dper, ddev, _, _ = time_layer(ddesc, dweights, dx, steps, 5, hip)
+    dgraph = time_layer_graph(ddesc, dweights, dx, steps, hip)
+    pct = per_layer_percentiles(ddesc, dweights, dx, steps, hip)
+    dcounts = routing_counts(ddesc, dweights[0], dx, dcfg)
+    touched = int((dcounts > 0).sum())
+    weights_n = touched * 3 * dcfg.hidden * dcfg.inter
+    code_bytes = weights_n * K // 8
+    dstep = {n: float(dper[:, i].mean()) for i, n in enumerate(M.STEPS)}
+    routed_ms = dstep["gemv_gateup"] + dstep["mfma_gateup"] + dstep["gemv_down"] + dstep["mfma_down"]
+    code_gbps = code_bytes / (routed_ms * 1e-3) / 1e9
+    vpw = recorded_valu_per_weight()
+    bound_us = weights_n * vpw / PEAK_VALU_LANE_OPS * 1e6 if vpw else None
+    print(f"[bench] decode K={K} {ddev * 1000:.1f} us/layer ({dgraph * 1000:.1f} from graph replays), "
+          f"code {code_gbps:.0f} GB/s; steps {json.dumps({k: round(v * 1000, 1) for k, v in dstep.items()})}",
+          file=sys.stderr, flush=True)
+    del dkeep, dweights
+    torch.cuda.empty_cache()
+    return {"workload": f"decode-8: T=8, K={K}, no router bias, {copies} rotating code copies",
+            "us_per_layer": ddev * 1000, "us_per_layer_graph_replay": dgraph * 1000,
+            "us_median": pct["median_ms"] * 1000, "us_p10": pct["p10_ms"] * 1000, "us_p90": pct["p90_ms"] * 1000,
+            "host_ms_per_step": dms, "touched_experts": touched, "routed_weights": weights_n,
+            "code_bytes": code_bytes, "routed_kernels_us": routed_ms * 1000, "code_GBps": code_gbps,
+            "code_hbm_frac": code_gbps / PEAK_HBM_GBPS,
+            "valu_per_weight": vpw, "valu_per_weight_source": "profiles/pmc_valu_gemv_decode.md (K=2)",
+            "valu_bound_us": bound_us,
+            "valu_bound_frac": (bound_us / (routed_ms * 1000)) if bound_us else None,
+            "step_us": {k: v * 1000 for k, v in dstep.items()}}
+
+
+def verify_batches(W, M, hip, steps):
+    """us per layer of the 1-, 2-, 4- and 8-token verify batches, each layer
+    replayed from a HIP graph with 4 rotating code copies (the decode-latency
+    regime of speculative decoding)."""
+    import torch
+    res = {}
+    for T in (1, 2, 4, 8):
+        cfg = W.BY_NAME["decode"].replace(tokens=T)
+        inp, desc, weights, keep = setup(cfg, copies=4)
+        x = _dev(inp.x)
+        res[str(T)] = time_layer_graph(desc, weights, x, steps, hip) * 1000
+        del keep, weights
+        torch.cuda.empty_cache()
+    print(f"[bench] verify batches us/layer (graph replay) {json.dumps({k: round(v, 1) for k, v in res.items()})}",
+          file=sys.stderr, flush=True)
+    return {"workload": "decode shapes at T = 1, 2, 4, 8, K=2, graph replay, 4 rotating code copies",
+            "us_per_layer_graph_replay": res}
+
+
+def prefill_leg(W, M, hip, name, steps, flags=0, label=None):
+    """One prefill-sized workload: ms per layer, per-step split, layer-level
+    expert MFMA utilisation and expert weights decoded per second."""
+    import torch
+    cfg = W.BY_NAME[name]
+    inp, desc, weights, keep = setup(cfg, extra_flags=flags)
+    x = _dev(inp.x)
+    ms, per, dev_ms, _, _ = time_layer(desc, weights, x, steps, 2, hip)
+    step = {n: float(per[:, i].mean()) for i, n in enumerate(M.STEPS)}
+    counts = routing_counts(desc, weights[0], x, cfg)
+    touched = int((counts > 0).sum()) + (1 if cfg.shared_trellis else 0)
+    fl = expert_flops(cfg, cfg.tokens)
+    res = {"ms_per_step": ms, "device_ms_per_step": dev_ms, "tokens_per_s": cfg.tokens / (ms * 1e-3),
+           "expert_tflop": fl / 1e12, "mfma_util_fp16_peak": fl / (ms * 1e-3) / (PEAK_FP16_TFLOPS * 1e12),
+           "touched_trellis_experts": touched,
+           "expert_weights_per_s": touched * 3 * cfg.hidden * cfg.inter / (ms * 1e-3), "step_ms": step}
+    print(f"[bench] {label or name} flags={flags} {ms:.3f} ms/step; steps "
+          f"{json.dumps({k: round(v, 4) for k, v in step.items()})}", file=sys.stderr, flush=True)
+    del keep, weights, x
+    torch.cuda.empty_cache()
+    return cfg, res
+
+
+def stream_read_bandwidth(hip, gib=4, reps=10):
+    """Achievable HBM read bandwidth: the probe kernel streaming `gib` GiB,
+    timed with events (best of `reps` passes)."""
+    import torch
+    path = os.path.join(ROOT, "trellis_quantized_moe_exl3_amd", "libmoe_exl3_bw.so")
+    if not os.path.exists(path):
+        return None
+    l = C.CDLL(path)
+    l.moe_exl3_bw_stream_read.argtypes = [C.c_void_p, C.c_int64, C.c_void_p, C.c_int, C.c_void_p]
+    n = gib << 30
+    buf = torch.ones(n // 4, dtype=torch.int32, device="cuda")
+    blocks = 256 * 16
+    sink = torch.zeros(blocks, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    best = 0.0
+    for _ in range(reps):
+        a, b = hip.event(), hip.event()
+        assert hip.l.hipEventRecord(a, stream) == 0
+        assert l.moe_exl3_bw_stream_read(buf.data_ptr(), n, sink.data_ptr(), blocks, stream) == 0
+        assert hip.l.hipEventRecord(b, stream) == 0
+        torch.cuda.synchronize()
+        best = max(best, n / (hip.ms(a, b) * 1e-3) / 1e9)
+        hip.destroy(a)
+        hip.destroy(b)
+    del buf
+    torch.cuda.empty_cache()
+    print(f"[bench] streaming read {best:.0f} GB/s", file=sys.stderr, flush=True)
+    return best
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(cfg, n_tokens, threads=None):
     import oracle
     import workloads as W
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    threads = threads or int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     inp = W.gen_layer(cfg, experts=[])
     sample = list(range(n_tokens))
     idx, _ = oracle.route_tokens(inp, sample)
-    ex = sorted(set(idx.ravel().tolist()))
-    codes = [W.gen_codes(cfg, p, ex) for p in range(3)]
+    ex = sorted(set(idx.ravel().tolist()) | ({cfg.n_experts} if cfg.shared_trellis else set()))
+    codes = [W.gen_codes(cfg, p, ex, inp.ktab) for p in range(3)]
     t0 = time.perf_counter()
     oracle.layer(inp, sample, nthreads=threads, codes=codes, present=set(ex))
     dt = time.perf_counter() - t0
     return {"value": n_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {n_tokens} tokens of the 7168-token prefill layer "
+            "sample": f"first {n_tokens} tokens of the {cfg.tokens}-token {cfg.name} layer "
                       f"({len(ex)} distinct experts decoded), fp64 oracle, {dt:.1f} s"}
+
+
+def oracle_per_config():
+    """The oracle on a bounded sample of each workload (all host threads, and
+    one thread for the two small ones): tokens/s and ms per sampled layer."""
+    import workloads as W
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    plan = [("tiny", 64, True), ("decode", 8, True), ("mixed_k3", 8, False), ("mixed_k4", 8, False),
+            ("fp8", 8, False)]
+    out = {"cpu_model": cpu_model(), "threads": threads}
+    for name, n, single in plan:
+        cfg = W.BY_NAME[name]
+        r = cpu_baseline(cfg, n, threads)
+        ent = {"tokens_per_s": r["value"], "sample": r["sample"]}
+        if single:
+            ent["tokens_per_s_1_thread"] = cpu_baseline(cfg, n, 1)["value"]
+        out[name] = ent
+        print(f"[bench] oracle {name}: {json.dumps(ent)}", file=sys.stderr, flush=True)
+    return out
 
 
 def main():
@@ -239,7 +454,10 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=80)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true", help="skip the 16384-token E4M3 workload")
+    ap.add_argument("--quick", action="store_true",
+                    help="headline prefill and K=2 decode only (no other legs, no oracle)")
     ap.add_argument("--profile-layer", default=None, help="run this workload's layer --reps times and exit")
+    ap.add_argument("--profile-flags", type=int, default=0, help="extra descriptor flags for --profile-layer")
     ap.add_argument("--reps", type=int, default=2)
     ap.add_argument("--copy-calibration", type=int, default=0, help="copy this many MiB 4 times and exit")
     args = ap.parse_args()
@@ -265,7 +483,7 @@ def main():
         return
     if args.profile_layer:
         pcfg = W.BY_NAME[args.profile_layer]
-        pinp, pdesc, pweights, pkeep = setup(pcfg)
+        pinp, pdesc, pweights, pkeep = setup(pcfg, extra_flags=args.profile_flags)
         px = _dev(pinp.x)
         pout = torch.empty_like(px)
         pws = torch.empty(M.workspace_size(pdesc, px.shape[0]), dtype=torch.uint8, device="cuda")
@@ -281,6 +499,7 @@ def main():
     x = _dev(inp.x)
     print(f"[bench] prefill inputs ready (T={cfg.tokens})", file=sys.stderr, flush=True)
     ms, per, total, _, _ = time_layer(desc, weights, x, args.steps, args.warmup, hip)
+    pct = per_layer_percentiles(desc, weights, x, args.steps, hip)
     counts = routing_counts(desc, weights[0], x, cfg)
     mfma_rows = int(counts[counts > GEMV_ROWS].sum())
     step_ms = {n: float(per[:, i].mean()) for i, n in enumerate(M.STEPS)}
@@ -289,48 +508,59 @@ def main():
     shared_rows = cfg.tokens if (cfg.shared and cfg.tokens > SHARED_GEMV_TOKENS) else 0
     gu_flops = 2.0 * 2 * cfg.hidden * cfg.inter * (mfma_rows + shared_rows)
     achieved = gu_flops / (gu_ms * 1e-3) / 1e12
+    layer_flops = expert_flops(cfg, cfg.tokens)
     print(f"[bench] prefill {ms:.3f} ms/step; steps {json.dumps({k: round(v, 4) for k, v in step_ms.items()})}",
           file=sys.stderr, flush=True)
     del keep, weights, x
     torch.cuda.empty_cache()
 
-    # ---- decode: 8 tokens, rotating code copies
-    dcfg = W.BY_NAME["decode"]
-    dinp, ddesc, dweights, dkeep = setup(dcfg, copies=4)
-    dx = _dev(dinp.x)
-    dms, dper, ddev, _, _ = time_layer(ddesc, dweights, dx, args.decode_steps, 5, hip)
-    dgraph = time_layer_graph(ddesc, dweights, dx, args.decode_steps, hip)
-    dcounts = routing_counts(ddesc, dweights[0], dx, dcfg)
-    touched = int((dcounts > 0).sum())
-    code_bytes = touched * 3 * (dcfg.hidden * dcfg.inter * dcfg.K // 8)
-    dstep = {n: float(dper[:, i].mean()) for i, n in enumerate(M.STEPS)}
-    routed_ms = dstep["gemv_gateup"] + dstep["mfma_gateup"] + dstep["gemv_down"] + dstep["mfma_down"]
-    code_gbps = code_bytes / (routed_ms * 1e-3) / 1e9
-    print(f"[bench] decode {ddev * 1000:.1f} us/layer ({dgraph * 1000:.1f} from graph replays), code {code_gbps:.0f} GB/s; "
-          f"steps {json.dumps({k: round(v * 1000, 1) for k, v in dstep.items()})}", file=sys.stderr, flush=True)
-    del dkeep, dweights
-    torch.cuda.empty_cache()
+    # ---- decode: 8 tokens, rotating copies, K = 2 (and 3, 4)
+    decode = decode_leg(W, M, hip, 2, args.decode_steps)
+    extra = {}
+    if not args.quick:
+        extra["decode_k3"] = decode_leg(W, M, hip, 3, args.decode_steps)
+        extra["decode_k4"] = decode_leg(W, M, hip, 4, args.decode_steps)
+        extra["verify_batches"] = verify_batches(W, M, hip, args.decode_steps)
+        # config 4: the 2048-token prefill at K = 3 and K = 4
+        mixed = {"workload": "prefill-2048 at K=3 and K=4 (same seeds), router bias, fp16 shared expert"}
+        for name in ("mixed_k3", "mixed_k4"):
+            _, mixed[name] = prefill_leg(W, M, hip, name, min(args.steps, 10))
+        extra["mixed_width"] = mixed
+        # format variants
+        var = {}
+        _, var["per_tensor_k34"] = prefill_leg(W, M, hip, "mixed_k34", min(args.steps, 10))
+        var["per_tensor_k34"]["workload"] = "prefill-2048, every tensor K3 or K4 (per-tensor widths)"
+        _, var["exlr8_prefill"] = prefill_leg(W, M, hip, "exlr8_prefill", min(args.steps, 10))
+        var["exlr8_prefill"]["workload"] = ("prefill-2048, K4 E4M3 codebook, rotated experts, trellis shared "
+                                            "expert (exlr8 layout)")
+        _, var["exlr8_prefill_fp8"] = prefill_leg(W, M, hip, "exlr8_prefill", min(args.steps, 10), M.FP8_MFMA,
+                                                  "exlr8_prefill fp8")
+        extra["format_variants"] = var
+        extra["hbm_read_GBps_achievable"] = stream_read_bandwidth(hip)
 
     # ---- 16384-token prefill with the E4M3 codebook: fp16 and fp8 MFMA
     fp8 = None
-    if not args.no_fp8:
-        fcfg = W.BY_NAME["fp8"]
+    if not args.no_fp8 and not args.quick:
         fp8 = {"workload": "prefill-16384: T=16384, K=4, E4M3-rounded mcg codebook, bf16 activations"}
         for name, fl in (("fp16_mfma", 0), ("fp8_mfma", M.FP8_MFMA)):
-            finp, fdesc, fweights, fkeep = setup(fcfg, extra_flags=fl)
-            fx = _dev(finp.x)
-            fms, fper, _, _, _ = time_layer(fdesc, fweights, fx, min(args.steps, 10), 2, hip)
-            fstep = {n: float(fper[:, i].mean()) for i, n in enumerate(M.STEPS)}
-            fp8[name] = {"ms_per_step": fms, "tokens_per_s": fcfg.tokens / (fms * 1e-3), "step_ms": fstep}
-            print(f"[bench] fp8 workload {name} {fms:.3f} ms/step; steps "
-                  f"{json.dumps({k: round(v, 4) for k, v in fstep.items()})}", file=sys.stderr, flush=True)
-            del fkeep, fweights, fx
-            torch.cuda.empty_cache()
+            fcfg, fp8[name] = prefill_leg(W, M, hip, "fp8", min(args.steps, 10), fl, f"fp8 workload {name}")
+        # layer-level utilisation: routed flops on the fp8 peak, shared on fp16
+        routed = 6.0 * fcfg.hidden * fcfg.inter * fcfg.tokens * fcfg.top_k
+        shared = 6.0 * fcfg.hidden * fcfg.inter * fcfg.tokens
+        t = fp8["fp8_mfma"]["ms_per_step"] * 1e-3
+        fp8["fp8_mfma"]["mfma_util_mixed_peak"] = (routed / (PEAK_FP8_TFLOPS * 1e12) +
+                                                   shared / (PEAK_FP16_TFLOPS * 1e12)) / t
 
     cpu = None
+    oracle_cfgs = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, args.cpu_tokens)
+        cpu["cpu_model"] = cpu_model()
+        if not args.quick:
+            oracle_cfgs = oracle_per_config()
 
+    hbm = extra.get("hbm_read_GBps_achievable")
+    decode["code_frac_of_achievable"] = decode["code_GBps"] / hbm if hbm else None
     rec = {
         "metric": "MoE-layer tokens/s @7168-tok prefill; us/layer @8-tok decode; code HBM GB/s",
         "value": cfg.tokens / (ms * 1e-3),
@@ -350,16 +580,18 @@ def main():
         "roofline": {"kernel": "mfma_gateup (group_gemm_kernel<0,2,0>)", "bound": "mfma",
                      "achieved": achieved, "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_FP16_TFLOPS, "traffic": recorded_traffic(),
+                     "traffic_source": "recorded: profiles/pmc_traffic_mfma_gateup_prefill.md "
+                                       "(null when the kernel sources changed since)",
                      "launch_ms": gu_ms, "flops_per_launch": gu_flops},
+        "layer_mfma_util": {"expert_tflop": layer_flops / 1e12,
+                            "frac_of_fp16_peak": layer_flops / (ms * 1e-3) / (PEAK_FP16_TFLOPS * 1e12)},
+        "prefill_percentiles": pct,
         "step_ms": step_ms,
-        "decode": {"workload": "decode-8: T=8, same layer, no router bias", "us_per_layer": ddev * 1000,
-                   "us_per_layer_graph_replay": dgraph * 1000,
-                   "host_ms_per_step": dms, "touched_experts": touched, "code_bytes": code_bytes,
-                   "routed_kernels_us": routed_ms * 1000, "code_GBps": code_gbps,
-                   "code_hbm_frac": code_gbps / PEAK_HBM_GBPS,
-                   "step_us": {k: v * 1000 for k, v in dstep.items()}},
+        "decode": decode,
+        **extra,
         "e4m3_prefill": fp8,
         "cpu_baseline": cpu,
+        "oracle_per_config": oracle_cfgs,
     }
     print(json.dumps(rec))
 

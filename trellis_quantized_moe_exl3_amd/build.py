@@ -19,6 +19,9 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmoe_exl3.so")
 SOURCES = ["route.hip", "decode.hip", "gemv.hip", "mfma.hip", "mfma8.hip", "moe_exl3.cpp"]
+# the benchmark's streaming-read probe (achievable HBM bandwidth), a library of its own
+BW_SOURCE = "bw_probe.hip"
+BW_LIB = os.path.join(HERE, "libmoe_exl3_bw.so")
 ARCH = "gfx950"
 
 
@@ -65,6 +68,10 @@ def build(verbose: bool = False) -> str:
         cmd = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp_lib]
         subprocess.check_call(cmd)
         os.replace(tmp_lib, LIB)
+        tmp_bw = BW_LIB + ".tmp"
+        subprocess.check_call([cc, *flags(), "-shared", os.path.join(CSRC, BW_SOURCE), "-o", tmp_bw],
+                              stderr=subprocess.DEVNULL if not verbose else None)
+        os.replace(tmp_bw, BW_LIB)
     finally:
         shutil.rmtree(tmpdir, ignore_errors=True)
     return LIB
