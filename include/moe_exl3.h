@@ -219,6 +219,25 @@ int moe_exl3_layer(const moe_exl3_desc *desc, const moe_exl3_weights *weights, c
                    int64_t T, void *out, void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * moe_exl3_layer for callers that cannot allocate memory (code under HIP
+ * graph capture, serving loops or harnesses that forbid hipMalloc): the
+ * workspace is a device array of MOE_EXL3_SCRATCH_BYTES inside the library,
+ * one per GPU, held from the first call on that GPU until the process ends.
+ * The call itself allocates and frees nothing.  Every call on one GPU uses
+ * the same array, so calls that overlap on one GPU (other streams, other
+ * threads) race and must be ordered by the caller; the layer needs nothing
+ * of the array's previous contents.  Returns MOE_EXL3_ERR_WORKSPACE when
+ * moe_exl3_workspace_size(desc, T) exceeds MOE_EXL3_SCRATCH_BYTES (about 500
+ * tokens at hidden 4096, inter 2048, top-8), MOE_EXL3_ERR_HIP when the array's
+ * address cannot be taken; otherwise the same contract as moe_exl3_layer.
+ * The status word sits at MOE_EXL3_STATUS_OFFSET of the array and is not
+ * readable by the caller.
+ */
+#define MOE_EXL3_SCRATCH_BYTES (64u << 20)
+int moe_exl3_layer_noalloc(const moe_exl3_desc *desc, const moe_exl3_weights *weights, const void *x,
+                           int64_t T, void *out, void *stream);
+
+/*
  * Routing and segment tables only (the layer's first steps, exposed for
  * bit-exact checks).  Outputs are device buffers:
  *   idx [T][k] int32, w [T][k] fp32 (softmax over the chosen logits),

@@ -28,7 +28,8 @@ STATUS_OFFSET = 8
 # every symbol the header declares
 EXPORTS = ("moe_exl3_version", "moe_exl3_strerror", "moe_exl3_workspace_size",
            "moe_exl3_layer", "moe_exl3_layer_profiled", "moe_exl3_route", "moe_exl3_decode",
-           "moe_exl3_repack", "moe_exl3_expand_block_scales")
+           "moe_exl3_repack", "moe_exl3_expand_block_scales", "moe_exl3_layer_noalloc")
+SCRATCH_BYTES = 64 << 20
 ORDER_ROWMAJOR, ORDER_COLMAJOR, ORDER_COLGROUPS128 = 0, 1, 2
 # launch steps of moe_exl3_layer_profiled (events[i] is recorded before step i)
 STEPS = ("route_logits", "topk", "segments", "convert_x", "gemv_gateup", "mfma_gateup",
@@ -81,12 +82,15 @@ def lib():
                                      C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
         l.moe_exl3_decode.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_uint32,
                                       C.c_int32, C.c_void_p, C.c_int32, C.c_void_p]
+        l.moe_exl3_layer_noalloc.argtypes = [C.POINTER(Desc), C.POINTER(Weights), C.c_void_p, C.c_int64,
+                                             C.c_void_p, C.c_void_p]
         l.moe_exl3_repack.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
                                       C.c_int32, C.c_void_p]
         l.moe_exl3_expand_block_scales.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_int32,
                                                    C.POINTER(C.c_void_p), C.POINTER(C.c_void_p), C.c_void_p]
         for f in ("moe_exl3_workspace_size", "moe_exl3_layer", "moe_exl3_layer_profiled",
-                  "moe_exl3_route", "moe_exl3_decode", "moe_exl3_repack", "moe_exl3_expand_block_scales"):
+                  "moe_exl3_route", "moe_exl3_decode", "moe_exl3_repack", "moe_exl3_expand_block_scales",
+                  "moe_exl3_layer_noalloc"):
             getattr(l, f).restype = C.c_int
         _lib = l
     return _lib
@@ -187,6 +191,15 @@ def layer(desc: Desc, weights: Weights, x, out, workspace, stream=None) -> None:
     _check(lib().moe_exl3_layer(C.byref(desc), C.byref(weights), _ptr(x), T, _ptr(out),
                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
                                 _stream(stream)), "moe_exl3_layer")
+
+
+def layer_noalloc(desc: Desc, weights: Weights, x, out, stream=None) -> None:
+    """layer() with the library's own per-GPU scratch array as the workspace
+    (moe_exl3_layer_noalloc): allocates nothing."""
+    _check_acts(desc, "layer_noalloc", x, out)
+    T = x.shape[0]
+    _check(lib().moe_exl3_layer_noalloc(C.byref(desc), C.byref(weights), _ptr(x), T, _ptr(out),
+                                        _stream(stream)), "moe_exl3_layer_noalloc")
 
 
 def layer_profiled(desc: Desc, weights: Weights, x, out, workspace, events, stream=None) -> None:

@@ -5,10 +5,17 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "internal.h"
 
 using namespace moe;
+
+// Workspace of moe_exl3_layer_noalloc: a device array of the library, one
+// copy per GPU, held until the process ends.  Its name is a host-side stand-in
+// in host code; only the address hipGetSymbolAddress returns for the current
+// device may reach a kernel or a copy.
+static __device__ __align__(256) unsigned char scratch[MOE_EXL3_SCRATCH_BYTES];
 
 namespace {
 
@@ -240,6 +247,27 @@ int run_route(const moe_exl3_desc &d, const moe_exl3_weights &w, const void *x, 
                         at<int32_t>(ws, p.tiles), hdr, s) != hipSuccess ||
         !checks())
         return MOE_EXL3_ERR_HIP;
+    return MOE_EXL3_OK;
+}
+
+// Device address of `scratch` on the current device, taken once per device.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices];
+
+int scratch_of_current_device(void **ptr)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return MOE_EXL3_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return MOE_EXL3_ERR_HIP;
+        g_scratch[dev] = p;
+    }
+    *ptr = g_scratch[dev];
     return MOE_EXL3_OK;
 }
 
@@ -480,6 +508,29 @@ int moe_exl3_layer(const moe_exl3_desc *desc, const moe_exl3_weights *weights, c
                    int64_t T, void *out, void *workspace, size_t ws_bytes, void *stream)
 {
     return run_layer(desc, weights, x, T, out, workspace, ws_bytes, stream, nullptr);
+}
+
+int moe_exl3_layer_noalloc(const moe_exl3_desc *desc, const moe_exl3_weights *weights, const void *x, int64_t T,
+                           void *out, void *stream)
+{
+    int rc = check_desc(desc);
+    if (rc)
+        return rc;
+    if (T < 0)
+        return MOE_EXL3_ERR_INVALID_ARG;
+    if (T == 0)
+        return MOE_EXL3_OK;
+    size_t need = 0;
+    rc = moe_exl3_workspace_size(desc, T, &need);
+    if (rc)
+        return rc;
+    if (need > (size_t)MOE_EXL3_SCRATCH_BYTES)
+        return MOE_EXL3_ERR_WORKSPACE;
+    void *ws = nullptr;
+    rc = scratch_of_current_device(&ws);
+    if (rc)
+        return rc;
+    return run_layer(desc, weights, x, T, out, ws, (size_t)MOE_EXL3_SCRATCH_BYTES, stream, nullptr);
 }
 
 int moe_exl3_layer_profiled(const moe_exl3_desc *desc, const moe_exl3_weights *weights,
