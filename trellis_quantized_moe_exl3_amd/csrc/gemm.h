@@ -51,34 +51,55 @@ MOE_DEV void frag_pos_rt(int K, int c, int h, int &d0, int &d1, int &q)
     d1 = (d0 + 1 == 8 * K) ? 0 : d0 + 1;
 }
 
-// The code words of tensor (p, e), an [n_in/16][n_out/16] tile grid.  K > 0:
-// every tensor has width K and is slice e of codes[p].  K = 0: the address
-// and width come from the per-tensor tables; a width outside {2, 3, 4} sets
-// the status bit and the tensor is read through an empty range (as zero
-// words, at width 2).
+// The code words of tensor (p, e), an [n_in/16][n_out/16] tile grid.
+//   K > 0, no tables:   every tensor has width K and is slice e of codes[p].
+//   K > 0, tables:      the tensor's own address; its table width must be K
+//                       (the caller dispatched on it), otherwise the width
+//                       was invalid.
+//   K = 0 (tables):     the address and the width from the tables.
+// An invalid width sets the status bit and the tensor is read through an
+// empty range (as zero words, at width 2).
 struct TensorCodes {
     const uint32_t *base;
     uint32_t bytes;   // of the tensor (0: nothing may be read)
     int K;
 };
 
+// A wave-uniform 64-bit address as such: values loaded from memory are not
+// known to be uniform, and a buffer descriptor built from a non-uniform base
+// turns every load through it into a waterfall loop.
+MOE_DEV const uint32_t *uniform_ptr(const void *p)
+{
+    const uint64_t v = (uint64_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const uint32_t *)(((uint64_t)hi << 32) | lo);
+}
+
+MOE_DEV int table_width(const GroupArgs &a, int p, int e)
+{
+    const int kw = a.k_tab[p * a.E + e];
+    return (kw >= 2 && kw <= 4) ? kw : 0;
+}
+
 template <int K>
 MOE_DEV TensorCodes tensor_codes(const GroupArgs &a, int p, int e, int n_in, int n_out)
 {
     TensorCodes t;
-    if constexpr (K > 0) {
+    const uint32_t grid_bytes = (uint32_t)((n_in / 16) * (n_out / 16) * 32);
+    if (!a.code_tab) {
         t.K = K;
-        t.bytes = (uint32_t)((n_in / 16) * (n_out / 16) * 32 * K);
-        t.base = (const uint32_t *)((const char *)a.codes[p] + (int64_t)e * t.bytes);
-    } else {
-        const int kw = a.k_tab[p * a.E + e];
-        const bool ok = kw >= 2 && kw <= 4;
-        if (!ok)
-            atomicOr((unsigned *)&const_cast<WsHeader *>(a.hdr)->status, MOE_EXL3_STATUS_BAD_WIDTH);
-        t.K = ok ? kw : 2;
-        t.bytes = ok ? (uint32_t)((n_in / 16) * (n_out / 16) * 32 * kw) : 0u;
-        t.base = (const uint32_t *)a.code_tab[p * a.E + e];
+        t.bytes = grid_bytes * K;
+        t.base = uniform_ptr((const char *)a.codes[p] + (int64_t)e * t.bytes);
+        return t;
     }
+    const int kw = table_width(a, p, e);
+    const bool ok = K > 0 ? kw == K : kw != 0;
+    if (!ok)
+        atomicOr((unsigned *)&const_cast<WsHeader *>(a.hdr)->status, MOE_EXL3_STATUS_BAD_WIDTH);
+    t.K = __builtin_amdgcn_readfirstlane(K > 0 ? K : (ok ? kw : 2));
+    t.bytes = __builtin_amdgcn_readfirstlane(ok ? grid_bytes * t.K : 0u);
+    t.base = uniform_ptr((const void *)a.code_tab[p * a.E + e]);
     return t;
 }
 

@@ -174,28 +174,24 @@ struct GemmTile {
 
     // B fragment (k-step kt, column group cm) before the suh scaling: 8 exact
     // values of 2v (fp16 for gate/up, bf16 for down), or dense weights
+    // K = 0 (per-tensor widths): the wavefront's width kw is a run-time,
+    // wave-uniform value; only the state windows depend on it
     template <int KK>
     MOE_DEV u32x4 decode_k(uint32_t D0, uint32_t D1) const
     {
         if constexpr (MODE == GATEUP_TRELLIS)
-            return __builtin_bit_cast(u32x4, frag_decode_f16<KK, CB>(D0, D1, q, m_lo, m_hi));
+            return __builtin_bit_cast(u32x4, frag_decode_f16<KK, CB>(D0, D1, q, m_lo, m_hi, kw));
         else
-            return __builtin_bit_cast(u32x4, frag_decode_bf16<KK, CB>(D0, D1, q, m_lo, m_hi));
+            return __builtin_bit_cast(u32x4, frag_decode_bf16<KK, CB>(D0, D1, q, m_lo, m_hi, kw));
     }
 
-    // K = 0: the wavefront's tensor width kw selects the decoder (a
-    // wavefront-uniform branch with no barrier inside).
     template <int CM>
     MOE_DEV u32x4 decode(const BRaw<CM> &br, int kt, int cm) const
     {
         if constexpr (!TR::kTrellis)
             return br.d[kt][cm];
-        else if constexpr (K > 0)
-            return decode_k<K>(br.c[kt][cm][0], br.c[kt][cm][1]);
         else
-            return kw == 4 ? decode_k<4>(br.c[kt][cm][0], br.c[kt][cm][1])
-                 : kw == 3 ? decode_k<3>(br.c[kt][cm][0], br.c[kt][cm][1])
-                           : decode_k<2>(br.c[kt][cm][0], br.c[kt][cm][1]);
+            return decode_k<K>(br.c[kt][cm][0], br.c[kt][cm][1]);
     }
 
     // Interleave the MFMAs of one fragment with the VALU work scheduled next

@@ -77,6 +77,37 @@ MOE_DEV void frag_states(uint32_t D0, uint32_t D1, int q, uint32_t st[8])
     }
 }
 
+// frag_states at a run-time width kw (2, 3 or 4, wave-uniform), for kernels
+// whose width comes from a per-tensor table.  States 0..4 start at most 16
+// bits into the fragment (K * t <= 16) and come from the first permute for
+// every width; states 5..7 come from the second permute (one or two bytes
+// further) where K * t > 16, which costs one select each.
+MOE_DEV void frag_states_rt(uint32_t D0, uint32_t D1, int q, int kw, uint32_t st[8])
+{
+    const int kC = kw == 4 ? 2 : 1;
+    const int b = q >> 3;
+    const uint32_t A = __builtin_amdgcn_perm(D0, D1, frag_sel(b));
+    const uint32_t C = __builtin_amdgcn_perm(D0, D1, frag_sel(b + kC));
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const int o = kw * t;
+        if (t < 5)
+            st[t] = __builtin_amdgcn_ubfe(A, 16 - o, 16);
+        else
+            st[t] = o <= 16 ? __builtin_amdgcn_ubfe(A, 16 - o, 16) : __builtin_amdgcn_ubfe(C, 16 + 8 * kC - o, 16);
+    }
+}
+
+// frag_states<K> for K > 0, frag_states_rt(kw) for K = 0.
+template <int K>
+MOE_DEV void frag_states_k(uint32_t D0, uint32_t D1, int q, int kw, uint32_t st[8])
+{
+    if constexpr (K > 0)
+        frag_states<K>(D0, D1, q, st);
+    else
+        frag_states_rt(D0, D1, q, kw, st);
+}
+
 // (mcg * s) mod 2^32 for a 16-bit state s (upper bits clear): one full-rate
 // 32-bit multiply on gfx950.
 MOE_DEV uint32_t mcg_hash(uint32_t s, uint32_t m_lo, uint32_t m_hi)
@@ -116,60 +147,81 @@ MOE_DEV float e4m3_value2(float v2)
 
 enum { CB_MCG = 0, CB_MCG_E4M3 = 1 };
 
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+// Two states -> the fp16 pair (2v0 + 1532, 2v1 + 1532), exact: bits 0x6400 + n
+// are the half 1024 + n (n < 1024); the low half gets 0x6400 + 2 (field sum
+// of s0) from v_sad_u8, the high half 0x6400 + 2 (field sum of s1) from
+// v_sad_hi_u8, which adds its sum shifted left by 16 (no carry: 0x6400 + 508
+// < 2^16).
+MOE_DEV uint32_t value2_pair_biased(uint32_t s0, uint32_t s1, uint32_t m_lo, uint32_t m_hi)
+{
+    const uint32_t ra = field_sum2(mcg_hash(s0, m_lo, m_hi), 0x64006400u);
+    return __builtin_amdgcn_sad_hi_u8(mcg_hash(s1, m_lo, m_hi) & 0xFEFEFEFEu, 0u, ra);
+}
+
+// The fp16 pair (2v0, 2v1), exact.
+MOE_DEV f16x2 value2_pair_f16(uint32_t s0, uint32_t s1, uint32_t m_lo, uint32_t m_hi)
+{
+    return __builtin_bit_cast(f16x2, value2_pair_biased(s0, s1, m_lo, m_hi)) - (f16x2){(f16)1532.0f, (f16)1532.0f};
+}
+
+// E4M3 rounding of a pair c = 2v / 128: both values to FP8 E4M3 (nearest
+// even; |c| < 4, far from saturation) with one scaled convert, which divides
+// by 128, and back with one that multiplies by 128: the fp16 pair
+// 128 * E4M3(c), exact (even integers of at most 4 significant bits).
+MOE_DEV f16x2 e4m3_pair_f16(f16x2 v2)
+{
+    const s16x2 b = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16((s16x2){0, 0}, v2, 128.0f, false);
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(__builtin_bit_cast(uint32_t, b), 128.0f, false);
+}
+
 // Fragment -> eight exact fp16 values of 2v (or 128 * E4M3(v/64)).
 template <int K, int CB>
-MOE_DEV f16x8 frag_decode_f16(uint32_t D0, uint32_t D1, int q, uint32_t m_lo, uint32_t m_hi)
+MOE_DEV f16x8 frag_decode_f16(uint32_t D0, uint32_t D1, int q, uint32_t m_lo, uint32_t m_hi, int kw = K)
 {
     uint32_t st[8];
-    frag_states<K>(D0, D1, q, st);
+    frag_states_k<K>(D0, D1, q, kw, st);
     f16x8 out;
-    if (CB == CB_MCG) {
 #pragma unroll
-        for (int t = 0; t < 8; t += 2) {
-            // bits 0x6400 + n are the half 1024 + n (n < 1024): the low half
-            // gets 0x6400 + 2 (field sum of state t) from v_sad_u8, the high
-            // half 0x6400 + 2 (field sum of state t+1) from v_sad_hi_u8, which
-            // adds its sum shifted left by 16 (no carry: 0x6400 + 508 < 2^16)
-            const uint32_t ra = field_sum2(mcg_hash(st[t], m_lo, m_hi), 0x64006400u);
-            const uint32_t rb = __builtin_amdgcn_sad_hi_u8(mcg_hash(st[t + 1], m_lo, m_hi) & 0xFEFEFEFEu, 0u, ra);
-            const f16x2 p = __builtin_bit_cast(f16x2, rb);
-            const f16x2 v = p - (f16x2){(f16)1532.0f, (f16)1532.0f};   // 1024 + 508
-            out[t] = v[0];
-            out[t + 1] = v[1];
-        }
-    } else {
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-            out[t] = (f16)e4m3_value2(value2_f32(st[t], m_lo, m_hi));
+    for (int t = 0; t < 8; t += 2) {
+        f16x2 v = value2_pair_f16(st[t], st[t + 1], m_lo, m_hi);
+        if (CB == CB_MCG_E4M3)
+            v = e4m3_pair_f16(v);
+        out[t] = v[0];
+        out[t + 1] = v[1];
     }
     return out;
 }
 
 // Fragment -> eight exact bf16 values of 2v (or 128 * E4M3(v/64)).
 template <int K, int CB>
-MOE_DEV bf16x8 frag_decode_bf16(uint32_t D0, uint32_t D1, int q, uint32_t m_lo, uint32_t m_hi)
+MOE_DEV bf16x8 frag_decode_bf16(uint32_t D0, uint32_t D1, int q, uint32_t m_lo, uint32_t m_hi, int kw = K)
 {
     uint32_t st[8];
-    frag_states<K>(D0, D1, q, st);
+    frag_states_k<K>(D0, D1, q, kw, st);
     u32x4 pk;
 #pragma unroll
     for (int t = 0; t < 8; t += 2) {
-        float a = value2_f32(st[t], m_lo, m_hi);
-        float b = value2_f32(st[t + 1], m_lo, m_hi);
         if (CB == CB_MCG_E4M3) {
-            a = e4m3_value2(a);
-            b = e4m3_value2(b);
+            // E4M3 bytes of the pair, widened to bf16 with the factor 128
+            const s16x2 b = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(
+                (s16x2){0, 0}, value2_pair_f16(st[t], st[t + 1], m_lo, m_hi), 128.0f, false);
+            pk[t / 2] = __builtin_bit_cast(
+                uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(__builtin_bit_cast(uint32_t, b), 128.0f, false));
+        } else {
+            const float a = value2_f32(st[t], m_lo, m_hi);
+            const float b = value2_f32(st[t + 1], m_lo, m_hi);
+            // |2v| <= 512 has at most 8 significant bits: truncation is exact
+            pk[t / 2] = __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
         }
-        // |2v| <= 512 has at most 8 significant bits: truncation is exact
-        pk[t / 2] = __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
     }
     return __builtin_bit_cast(bf16x8, pk);
 }
 
 // Fragment -> eight FP8 E4M3 bytes of c = v / 64 (nearest-even, saturating;
 // the E4M3 codebook value itself), state t in byte t % 4 of dword t / 4.
-// v_cvt_scalef32_pk_fp8_f32 divides by its scale: E4M3(2v / 128).
-typedef short s16x2 __attribute__((ext_vector_type(2)));
+// The scaled convert divides the fp16 pair 2v by 128 before rounding.
 template <int K>
 MOE_DEV u32x2 frag_decode_fp8(uint32_t D0, uint32_t D1, int q, uint32_t m_lo, uint32_t m_hi)
 {
@@ -178,10 +230,11 @@ MOE_DEV u32x2 frag_decode_fp8(uint32_t D0, uint32_t D1, int q, uint32_t m_lo, ui
     u32x2 out;
 #pragma unroll
     for (int d = 0; d < 2; ++d) {
-        s16x2 w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32((s16x2){0, 0}, value2_f32(st[4 * d], m_lo, m_hi),
-                                                            value2_f32(st[4 * d + 1], m_lo, m_hi), 128.0f, false);
-        w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, value2_f32(st[4 * d + 2], m_lo, m_hi),
-                                                      value2_f32(st[4 * d + 3], m_lo, m_hi), 128.0f, true);
+        s16x2 w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16((s16x2){0, 0},
+                                                           value2_pair_f16(st[4 * d], st[4 * d + 1], m_lo, m_hi),
+                                                           128.0f, false);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(w, value2_pair_f16(st[4 * d + 2], st[4 * d + 3], m_lo, m_hi),
+                                                     128.0f, true);
         out[d] = __builtin_bit_cast(uint32_t, w);
     }
     return out;
@@ -190,9 +243,8 @@ MOE_DEV u32x2 frag_decode_fp8(uint32_t D0, uint32_t D1, int q, uint32_t m_lo, ui
 // Fragment -> the eight decoded values as fp16 pairs of 2v + 1532 (exact:
 // integers in [1020, 2044]), the operand of the decode-fused GEMV's
 // v_dot2_f32_f16 (which subtracts 1532 * sum(x) once per output).  mcg: the
-// low half from v_sad_u8 on base 0x64006400, the high half from v_sad_hi_u8;
-// E4M3: 128 * c8 + 1532 (128 * c8 is an even integer: E4M3 keeps 4
-// significant bits of the integer v).
+// biased pair straight from the field sums; E4M3: 128 * c8 + 1532 (128 * c8
+// is an even integer: E4M3 keeps 4 significant bits of the integer v).
 template <int K, int CB>
 MOE_DEV void frag_biased_pairs(uint32_t D0, uint32_t D1, int q, uint32_t m_lo, uint32_t m_hi, f16x2 wp[4])
 {
@@ -200,15 +252,11 @@ MOE_DEV void frag_biased_pairs(uint32_t D0, uint32_t D1, int q, uint32_t m_lo, u
     frag_states<K>(D0, D1, q, st);
 #pragma unroll
     for (int t = 0; t < 8; t += 2) {
-        if (CB == CB_MCG) {
-            const uint32_t ra = field_sum2(mcg_hash(st[t], m_lo, m_hi), 0x64006400u);
-            const uint32_t rb = __builtin_amdgcn_sad_hi_u8(mcg_hash(st[t + 1], m_lo, m_hi) & 0xFEFEFEFEu, 0u, ra);
-            wp[t / 2] = __builtin_bit_cast(f16x2, rb);
-        } else {
-            const float a = e4m3_value2(value2_f32(st[t], m_lo, m_hi)) + 1532.0f;
-            const float b = e4m3_value2(value2_f32(st[t + 1], m_lo, m_hi)) + 1532.0f;
-            wp[t / 2] = (f16x2){(f16)a, (f16)b};
-        }
+        if (CB == CB_MCG)
+            wp[t / 2] = __builtin_bit_cast(f16x2, value2_pair_biased(st[t], st[t + 1], m_lo, m_hi));
+        else
+            wp[t / 2] = e4m3_pair_f16(value2_pair_f16(st[t], st[t + 1], m_lo, m_hi)) +
+                        (f16x2){(f16)1532.0f, (f16)1532.0f};
     }
 }
 
