@@ -458,6 +458,8 @@ def main():
                     help="headline prefill and K=2 decode only (no other legs, no oracle)")
     ap.add_argument("--profile-layer", default=None, help="run this workload's layer --reps times and exit")
     ap.add_argument("--profile-flags", type=int, default=0, help="extra descriptor flags for --profile-layer")
+    ap.add_argument("--copies", type=int, default=1,
+                    help="--profile-layer: rotate this many copies of the codes (the decode leg uses 4)")
     ap.add_argument("--reps", type=int, default=2)
     ap.add_argument("--copy-calibration", type=int, default=0, help="copy this many MiB 4 times and exit")
     args = ap.parse_args()
@@ -483,12 +485,12 @@ def main():
         return
     if args.profile_layer:
         pcfg = W.BY_NAME[args.profile_layer]
-        pinp, pdesc, pweights, pkeep = setup(pcfg, extra_flags=args.profile_flags)
+        pinp, pdesc, pweights, pkeep = setup(pcfg, copies=args.copies, extra_flags=args.profile_flags)
         px = _dev(pinp.x)
         pout = torch.empty_like(px)
         pws = torch.empty(M.workspace_size(pdesc, px.shape[0]), dtype=torch.uint8, device="cuda")
-        for _ in range(args.reps):
-            M.layer(pdesc, pweights[0], px, pout, pws)
+        for i in range(args.reps):
+            M.layer(pdesc, pweights[i % len(pweights)], px, pout, pws)
         torch.cuda.synchronize()
         print(f"[bench] ran the {args.profile_layer} layer {args.reps} times", file=sys.stderr, flush=True)
         return
