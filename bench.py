@@ -368,6 +368,37 @@ def prefill_leg(W, M, hip, name, steps, flags=0, label=None):
     return cfg, res
 
 
+def tile_classes(W, M, hip, steps):
+    """Expert MFMA rates per row-tile class: the gate/up and down launches'
+    event-timed TFLOP/s on routings whose tiles are all full (256 rows), mostly
+    33-96 rows, or all at most 32 rows (no shared expert, every expert on the
+    MFMA kernels)."""
+    import torch
+    res = {}
+    for name in ("tiles_full", "tiles_mid", "tiles_small"):
+        cfg = W.BY_NAME[name]
+        inp, desc, weights, keep = setup(cfg)
+        x = _dev(inp.x)
+        ms, per, _, _, _ = time_layer(desc, weights, x, steps, 2, hip)
+        step = {n: float(per[:, i].mean()) for i, n in enumerate(M.STEPS)}
+        counts = routing_counts(desc, weights[0], x, cfg)
+        on = counts[counts > GEMV_ROWS]
+        rows, tiles = int(on.sum()), int(((on + 255) // 256).sum())
+        gu, dn = step["mfma_gateup"], step["mfma_down"]
+        fl = 2.0 * cfg.hidden * cfg.inter * rows
+        res[name] = {"tokens": cfg.tokens, "rows_on_mfma": rows, "row_tiles": tiles,
+                     "rows_per_tile": rows / tiles, "layer_ms": ms,
+                     "gateup_ms": gu, "gateup_tflops": 2 * fl / (gu * 1e-3) / 1e12,
+                     "gateup_us_per_tile": gu * 1000 / tiles,
+                     "down_ms": dn, "down_tflops": fl / (dn * 1e-3) / 1e12,
+                     "down_us_per_tile": dn * 1000 / tiles}
+        print(f"[bench] {name}: {json.dumps({k: round(v, 3) for k, v in res[name].items()})}",
+              file=sys.stderr, flush=True)
+        del keep, weights, x
+        torch.cuda.empty_cache()
+    return res
+
+
 def stream_read_bandwidth(hip, gib=4, reps=10):
     """Achievable HBM read bandwidth: the probe kernel streaming `gib` GiB,
     timed with events (best of `reps` passes)."""
@@ -379,7 +410,7 @@ def stream_read_bandwidth(hip, gib=4, reps=10):
     l.moe_exl3_bw_stream_read.argtypes = [C.c_void_p, C.c_int64, C.c_void_p, C.c_int, C.c_void_p]
     n = gib << 30
     buf = torch.ones(n // 4, dtype=torch.int32, device="cuda")
-    blocks = 256 * 16
+    blocks = 256 * 64
     sink = torch.zeros(blocks, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
     best = 0.0
@@ -538,6 +569,7 @@ def main():
         _, var["exlr8_prefill_fp8"] = prefill_leg(W, M, hip, "exlr8_prefill", min(args.steps, 10), M.FP8_MFMA,
                                                   "exlr8_prefill fp8")
         extra["format_variants"] = var
+        extra["tile_classes"] = tile_classes(W, M, hip, min(args.steps, 10))
         extra["hbm_read_GBps_achievable"] = stream_read_bandwidth(hip)
 
     # ---- 16384-token prefill with the E4M3 codebook: fp16 and fp8 MFMA

@@ -219,6 +219,14 @@ def test_mixed_width_sampled(name):
     _sampled(name)
 
 
+@pytest.mark.parametrize("name,n_min", [("tiles_full", 64), ("tiles_mid", 24), ("tiles_small", 24)])
+def test_tile_class_routings_sampled(name, n_min):
+    # the routings that isolate one row-tile class for measurement: every
+    # tile full (4096 tokens on 8 experts), every tile 35-79 rows, every tile
+    # 5-31 rows
+    _sampled(name, n_min=n_min, n_full=1)
+
+
 def test_e4m3_codebook_sampled():
     _sampled("fp8")
 

@@ -69,6 +69,9 @@ class LayerConfig:
     hadamard: bool = False
     # a trellis-coded shared expert stored after the routed ones (index E)
     shared_trellis: bool = False
+    # with router_bias: a bias that makes experts 0 .. hot_experts-1 win for
+    # every token (shapes the row tiles for per-tile-class measurements)
+    hot_experts: int = 0
 
     @property
     def side_scale(self) -> float:
@@ -117,7 +120,17 @@ VARIANTS: List[LayerConfig] = [
     LayerConfig("exlr8_prefill", 6, 2048, 4096, 2048, 288, 8, 4, CB_MCG_E4M3, DT_BF16, True, False,
                 hadamard=True, shared_trellis=True),
 ]
-BY_NAME: Dict[str, LayerConfig] = {c.name: c for c in CONFIGS + VARIANTS}
+# Routings that isolate one class of MFMA row tile, for per-class timing and
+# counters: every tile full (4096 tokens on 8 experts, 16 tiles of 256 rows
+# each), tiles of at most 32 rows (512 tokens over 288 experts, run with
+# every expert on the MFMA kernels), and tiles of mostly 33-96 rows (2048
+# tokens over 288 experts).
+TILE_CLASSES: List[LayerConfig] = [
+    LayerConfig("tiles_full", 7, 4096, 4096, 2048, 288, 8, 2, CB_MCG, DT_BF16, True, False, hot_experts=8),
+    LayerConfig("tiles_small", 8, 512, 4096, 2048, 288, 8, 2, CB_MCG, DT_BF16, False, False),
+    LayerConfig("tiles_mid", 9, 2048, 4096, 2048, 288, 8, 2, CB_MCG, DT_BF16, False, False),
+]
+BY_NAME: Dict[str, LayerConfig] = {c.name: c for c in CONFIGS + VARIANTS + TILE_CLASSES}
 
 
 def _rng(seed: int, tag: str, *idx: int) -> np.random.Generator:
@@ -165,6 +178,10 @@ def gen_router_w(cfg: LayerConfig) -> np.ndarray:
 def gen_router_bias(cfg: LayerConfig) -> Optional[np.ndarray]:
     if not cfg.router_bias:
         return None
+    if cfg.hot_experts:
+        b = np.zeros(cfg.n_experts, dtype=np.float32)
+        b[:cfg.hot_experts] = 64.0    # router logits are about N(0, 1.3)
+        return b
     return _rng(cfg.seed, "router_bias").standard_normal(cfg.n_experts).astype(np.float32)
 
 
