@@ -54,9 +54,9 @@
  *               after the routed ones, added with weight 1 in the experts'
  *               basis
  *
- * Precision: routing decides integers, so logits are fp32 in the fixed order
- * (every bf16*fp16 or fp16*fp16 product is exact in fp32).  Everything after
- * routing is carried in fp64.
+ * Precision: routing decides integers, so logits are fp32 in the fixed order,
+ * every step a fused multiply-add (the exact product added to the partial sum
+ * with one rounding to fp32).  Everything after routing is carried in fp64.
  */
 #include <math.h>
 #include <stdint.h>
@@ -259,11 +259,24 @@ void orc_expand_block_scales(const uint16_t *block, int EA, int H, int I, uint16
     }
 }
 
+/* One accumulation step of a router partial sum: p + x * w with a single
+ * rounding to fp32 (a fused multiply-add).  The product of a bf16 or fp16
+ * activation and an fp16 weight has at most 22 significant bits, so it is
+ * exact in double.  The double sum is then either exact (the leading bits of
+ * the two terms lie within 28 places of each other) or the smaller term is
+ * below 2^-3 of half an fp32 ulp of the larger, which is itself an fp32 number;
+ * in both cases rounding the double sum to float gives
+ * the correctly rounded fp32 value of p + x * w.  Where the product is a normal
+ * fp32 number it is exact in fp32 as well, and the step equals a separate
+ * multiply and add; the two differ only for products below fp32's normal
+ * range. */
+static float fused_step(float p, float x, float w) { return (float)((double)p + (double)x * (double)w); }
+
 /* Router logits in fp32 ([p1] "Recipe" and [p4] "Intended use": routers stay
  * in source precision because routing is sensitive).  For each (t, e): 64
  * partial sums p[l] accumulate x[t][64i+l] * Wr[e][64i+l] for i = 0, 1, ...
- * in order; then p[l] += p[l+d] for d = 32, 16, 8, 4, 2, 1; logit = p[0]
- * (+ bias[e]).  Each product is exact in fp32. */
+ * in order, one fused step each; then p[l] += p[l+d] for d = 32, 16, 8, 4,
+ * 2, 1; logit = p[0] (+ bias[e]). */
 void orc_router_logits(const uint16_t *x, int x_dtype, int64_t T, int H, const uint16_t *Wr,
                        const float *bias, int E, float *logits)
 {
@@ -281,12 +294,9 @@ void orc_router_logits(const uint16_t *x, int x_dtype, int64_t T, int H, const u
             float p[64];
             for (int l = 0; l < 64; ++l)
                 p[l] = 0.0f;
-            for (int i = 0; i < H / 64; ++i) {
-                for (int l = 0; l < 64; ++l) {
-                    float prod = xf[64 * i + l] * we[64 * i + l];
-                    p[l] = p[l] + prod;
-                }
-            }
+            for (int i = 0; i < H / 64; ++i)
+                for (int l = 0; l < 64; ++l)
+                    p[l] = fused_step(p[l], xf[64 * i + l], we[64 * i + l]);
             for (int d = 32; d >= 1; d /= 2)
                 for (int l = 0; l < d; ++l)
                     p[l] = p[l] + p[l + d];

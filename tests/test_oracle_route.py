@@ -42,6 +42,79 @@ def test_fixed_order_hand_cases(dt, one, tiny):
     assert lg[0, 0] == np.float32(1.5)
 
 
+def _libm_fmaf():
+    import ctypes
+    import ctypes.util
+    libm = ctypes.CDLL(ctypes.util.find_library("m"))
+    f = libm.fmaf
+    f.restype = ctypes.c_float
+    f.argtypes = [ctypes.c_float] * 3
+    return f
+
+
+@pytest.mark.parametrize("dt", [W.DT_BF16, W.DT_F16])
+def test_fused_steps_match_libm_fmaf(dt):
+    # Every accumulation step is one fused multiply-add.  Reference: the C
+    # library's fmaf (correctly rounded x * w + p) in the same order, then the
+    # fp32 halving tree, on activations and weights that make products normal,
+    # fp32-subnormal (where a separately rounded product would differ),
+    # overflowing, infinite and NaN.
+    fmaf = _libm_fmaf()
+    rng = np.random.default_rng(11)
+    H, E = 128, 5
+    xf = rng.standard_normal((6, H)).astype(np.float32)
+    xf[1] *= np.float32(2.0 ** -120 if dt == W.DT_BF16 else 2.0 ** -12)
+    xf[2] *= np.float32(2.0 ** -130 if dt == W.DT_BF16 else 2.0 ** -14)
+    xf[3] *= np.float32(2.0 ** 100 if dt == W.DT_BF16 else 2.0 ** 10)
+    if dt == W.DT_BF16:
+        x = W.f32_to_bf16_bits(xf)
+        inf, nan = 0x7F80, 0x7FC0
+    else:
+        x = xf.astype(np.float16).view(np.uint16).copy()
+        inf, nan = 0x7C00, 0x7E00
+    x[4, 17] = inf
+    x[5, 90] = nan
+    Wr = (rng.standard_normal((E, H)) * 0.02).astype(np.float16)
+    Wr[1] = (Wr[1].astype(np.float32) * np.float32(2.0 ** -12)).astype(np.float16)   # fp16 subnormals
+    Wr[2, ::3] = np.float16(65504.0)
+    lg = oracle.router_logits(x, dt, Wr, None)
+    xv = W.act_bits_to_f32(x, dt)
+    wv = Wr.astype(np.float32)
+    ref = np.zeros_like(lg)
+    differs = 0
+    for t in range(x.shape[0]):
+        for e in range(E):
+            p = [0.0] * 64
+            q = np.zeros(64, dtype=np.float32)   # separately rounded product, for contrast
+            for i in range(H // 64):
+                for l in range(64):
+                    a, b = float(xv[t, 64 * i + l]), float(wv[e, 64 * i + l])
+                    p[l] = fmaf(a, b, p[l])
+                    with np.errstate(all="ignore"):
+                        q[l] = np.float32(q[l] + np.float32(np.float32(a) * np.float32(b)))
+            v = np.array(p, dtype=np.float32)
+            d = 32
+            while d >= 1:
+                with np.errstate(all="ignore"):
+                    v[:d] = v[:d] + v[d:2 * d]
+                    q[:d] = q[:d] + q[d:2 * d]
+                d //= 2
+            ref[t, e] = v[0]
+            differs += int(not (np.isnan(q[0]) and np.isnan(v[0])) and q[0].view(np.uint32) != v[0].view(np.uint32))
+    nan = np.isnan(ref)
+    np.testing.assert_array_equal(np.isnan(lg), nan)
+    np.testing.assert_array_equal(lg[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+    assert nan.any() and np.isinf(ref).any()
+    if dt == W.DT_BF16:
+        # bf16 activations reach products below fp32's normal range, where a
+        # separately rounded product parts from the fused step
+        assert differs > 0
+    else:
+        # fp16 x fp16 products are at least 2^-48: always exact in fp32, so
+        # the two readings coincide
+        assert differs == 0
+
+
 def test_logits_close_to_exact_dot():
     cfg = W.CONFIGS[1]
     x = W.gen_x(cfg)[:4]
