@@ -79,9 +79,21 @@ def test_route_deterministic():
 # The routing entry leaves the fp32 logits in its workspace right after the
 # 256-byte header (an internal layout this test reads on purpose).  They must
 # equal the oracle's fixed-order sums bit for bit: up to 64 tokens on the
-# 32-lanes-per-pair kernel, above that on the register-tiled one; bf16
+# 32-lanes-per-pair kernel, above that on the matrix-core one (16 x 16
+# tiles, ragged in tokens and, in the tiny config, in experts); bf16
 # activations at the real shapes, fp16 in the tiny config.
 _LOGITS_AT = 256
+
+
+def _device_logits(dl, T):
+    cfg = dl.inp.cfg
+    k, E = cfg.top_k, cfg.n_experts
+    outs = [torch.empty(T * k, dtype=dt, device="cuda") for dt in (torch.int32, torch.float32)]
+    tabs = [torch.empty(n, dtype=torch.int32, device="cuda") for n in (E, E + 1, T * k, T * k)]
+    ws = dl.workspace(T)
+    M.route(dl.desc, dl.weights, dl.x, *outs, *tabs, ws)
+    torch.cuda.synchronize()
+    return ws[_LOGITS_AT:_LOGITS_AT + 4 * T * E].cpu().numpy().view(np.float32).reshape(T, E)
 
 
 @pytest.mark.parametrize("T", [1, 8, 13, 64, 65, 300])
@@ -90,13 +102,58 @@ def test_route_logits_bit_exact(name, T):
     cfg = W.BY_NAME[name].replace(tokens=T, router_bias=True)
     inp = W.gen_layer(cfg, experts=[])
     dl = DevLayer(inp)
-    k, E = cfg.top_k, cfg.n_experts
-    outs = [torch.empty(T * k, dtype=dt, device="cuda")
-            for dt in (torch.int32, torch.float32)]
-    tabs = [torch.empty(n, dtype=torch.int32, device="cuda") for n in (E, E + 1, T * k, T * k)]
-    ws = dl.workspace(T)
-    M.route(dl.desc, dl.weights, dl.x, *outs, *tabs, ws)
-    torch.cuda.synchronize()
-    got = ws[_LOGITS_AT:_LOGITS_AT + 4 * T * E].cpu().numpy().view(np.float32).reshape(T, E)
+    got = _device_logits(dl, T)
     ref = oracle.router_logits(inp.x, cfg.act_dtype, inp.router_w, inp.router_bias)
     assert got.view(np.uint32).tolist() == ref.view(np.uint32).tolist()
+
+
+@pytest.mark.parametrize("name", ["prefill", "mixed_k3"])
+def test_route_logits_bit_exact_prefill_shapes(name):
+    # every logit of the 7168- and 2048-token layers (448 and 128 token tiles,
+    # 18 expert tiles)
+    inp = W.gen_layer(W.BY_NAME[name], experts=[])
+    dl = DevLayer(inp)
+    got = _device_logits(dl, inp.cfg.tokens)
+    ref = oracle.router_logits(inp.x, inp.cfg.act_dtype, inp.router_w, inp.router_bias)
+    np.testing.assert_array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def _edge_inputs(T):
+    """bf16 activations and fp16 router weights at the edges of the number
+    formats: products in fp32's subnormal range, fp16 subnormal weights,
+    products that overflow, infinities and NaN."""
+    cfg = W.BY_NAME["decode"].replace(tokens=T)     # no bias: the sums are the logits
+    inp = W.gen_layer(cfg, experts=[])
+    rng = np.random.default_rng(5)
+    H = cfg.hidden
+    xf = W.bf16_bits_to_f32(inp.x).copy()
+    xf[0:4] *= np.float32(2.0 ** -128)          # x * w far below fp32's normal range
+    xf[4:6] *= np.float32(2.0 ** -100)
+    xf[6:8] *= np.float32(2.0 ** 110)           # x * w beyond fp32's range for large w
+    x = W.f32_to_bf16_bits(xf)
+    x[8, rng.integers(0, H)] = 0x7F80           # +inf
+    x[9, rng.integers(0, H)] = 0xFF80           # -inf
+    x[10, rng.integers(0, H)] = 0x7FC0          # NaN
+    x[11, :] = 0x8000                           # -0
+    inp.x = x
+    w = inp.router_w.copy()
+    w[0:3] = (w[0:3].astype(np.float32) * np.float32(2.0 ** -10)).astype(np.float16)   # subnormal fp16
+    w[3, :] = np.float16(65504.0)
+    w[4, ::2] = np.float16(-65504.0)
+    inp.router_w = w
+    return inp
+
+
+@pytest.mark.parametrize("T", [40, 96])
+def test_route_logits_edge_values(T):
+    # T = 40: the few-token kernel; T = 96: the matrix-core kernel.  Equal bit
+    # for bit where the oracle's logit is a number, NaN where it is NaN.
+    inp = _edge_inputs(T)
+    got = _device_logits(DevLayer(inp), T)
+    ref = oracle.router_logits(inp.x, inp.cfg.act_dtype, inp.router_w, inp.router_bias)
+    nan = np.isnan(ref)
+    sub = (ref != 0) & (np.abs(ref) < np.finfo(np.float32).tiny)
+    assert nan.any() and np.isinf(ref).any() and sub.sum() > 100
+    print(f"T={T}: {int(nan.sum())} NaN, {int(np.isinf(ref).sum())} inf, {int(sub.sum())} subnormal logits")
+    np.testing.assert_array_equal(np.isnan(got), nan)
+    np.testing.assert_array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))

@@ -5,6 +5,7 @@
 #include <algorithm>
 
 #include "common.h"
+#include "gemm.h"
 #include "internal.h"
 
 namespace moe {
@@ -206,6 +207,114 @@ __global__ __launch_bounds__(256) void route_logits_pairs_kernel(const uint16_t 
     }
 }
 
+// Many tokens, on the matrix cores.  One wavefront (one block) computes a tile
+// of 16 tokens x 16 experts and holds all 64 partial sums of every pair of it
+// at once: v_mfma_f32_16x16x1_4b_f32 has k = 1, so each instruction adds
+// exactly one product to each of its accumulators, and its four 16x16 blocks
+// carry four of the 64 partial-sum chains.  Instruction q (q = 0..15) of a
+// 64-channel chunk i adds x[64i + l] * w[64i + l] to chains l = q + 16b of
+// block b = 0..3; the lanes of block b supply token (A) and expert (B) rows
+// 0..15 and load channels 64i + 16b .. + 15, 32 contiguous bytes per row.  As
+// in the VALU kernels the product is exact in fp32, so every accumulation
+// step rounds once, the order over i is the plain one, and the halving tree
+// over l runs on the finished chains: chains q, q + 16, q + 32, q + 48 of a
+// (token, expert) pair sit in one lane (block b in registers 4b .. 4b + 3,
+// lane 16 (row / 4) + column, register row % 4), so the whole tree is
+// in-lane adds.  256 accumulator registers: one wavefront per SIMD.
+constexpr int kRouteTile = 16;
+constexpr int kRouteSets = 4;
+
+template <bool BF16>
+MOE_DEV float act_elem(const u32x4 (&v)[2], int q)
+{
+    const uint32_t d = v[q >> 3][(q >> 1) & 3];
+    if (BF16)
+        return __uint_as_float((q & 1) ? (d & 0xFFFF0000u) : (d << 16));
+    return f16_to_f32((uint16_t)((q & 1) ? (d >> 16) : (d & 0xFFFFu)));
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void route_logits_mfma_kernel(
+    const uint16_t *__restrict__ x, int64_t T, int H, const uint16_t *__restrict__ Wr,
+    const float *__restrict__ bias, int E, float *__restrict__ logits, WsHeader *hdr, int n_tt, int n_et)
+{
+    clear_status(hdr);
+    int tt, et;
+    xcd_map((int)blockIdx.x, n_et, tt, et);   // the expert tiles of a token tile share one XCD's L2
+    if (tt >= n_tt)
+        return;
+    const int l = threadIdx.x, b = l >> 4, c = l & 15;
+    // the tile's token rows and expert rows through two buffer resources whose
+    // range ends at the last token / expert: rows past it load zeros and their
+    // sums are never stored
+    const int64_t t0 = (int64_t)tt * kRouteTile;
+    const int e0 = et * kRouteTile;
+    const int nt = (int)std::min<int64_t>(kRouteTile, T - t0), ne = std::min(kRouteTile, E - e0);
+    const __amdgpu_buffer_rsrc_t xs = buf_rsrc(x + t0 * H, (uint32_t)(nt * H * 2));
+    const __amdgpu_buffer_rsrc_t ws = buf_rsrc(Wr + (int64_t)e0 * H, (uint32_t)(ne * H * 2));
+    const uint32_t off = (uint32_t)(c * H + 16 * b) * 2;
+    f32x16 acc[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+        acc[q] = (f32x16){};
+    // Four register sets rotate: the loads of chunk i + 4 go out right after
+    // chunk i's MFMAs and have three chunks' MFMAs (48 x 32 cycles) to land.
+    // Loads past the last chunk fall outside the range and return zeros; they
+    // are never used.  The scheduling barriers keep every load group where it
+    // is written (the compiler would otherwise sink it to its first use).
+    const int n = H / 64;   // a multiple of kRouteSets
+    u32x4 xv[kRouteSets][2], wv[kRouteSets][2];
+    // (the chunk offset goes into the per-lane offset, which the range check
+    // covers, so a load past the range returns zeros and touches no memory)
+    auto load = [&](int i, int j) {
+        const uint32_t o = off + (uint32_t)i * 128u;
+        xv[j][0] = __builtin_amdgcn_raw_buffer_load_b128(xs, o, 0, 0);
+        xv[j][1] = __builtin_amdgcn_raw_buffer_load_b128(xs, o + 16, 0, 0);
+        wv[j][0] = __builtin_amdgcn_raw_buffer_load_b128(ws, o, 0, 0);
+        wv[j][1] = __builtin_amdgcn_raw_buffer_load_b128(ws, o + 16, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+#pragma unroll
+    for (int j = 0; j < kRouteSets; ++j)
+        load(j, j);
+    for (int i = 0; i < n; i += kRouteSets) {
+#pragma unroll
+        for (int j = 0; j < kRouteSets; ++j) {
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const uint32_t d = wv[j][q >> 3][(q >> 1) & 3];
+                const float wq = f16_to_f32((uint16_t)((q & 1) ? (d >> 16) : (d & 0xFFFFu)));
+                acc[q] = __builtin_amdgcn_mfma_f32_16x16x1f32(act_elem<BF16>(xv[j], q), wq, acc[q], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            load(i + kRouteSets + j, j);
+        }
+    }
+    // tree: d = 32 (blocks 0 + 2, 1 + 3), d = 16 (their sums), then d = 8 .. 1
+    // over q
+    f32x4 u[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            u[q][r] = (acc[q][r] + acc[q][8 + r]) + (acc[q][4 + r] + acc[q][12 + r]);
+#pragma unroll
+    for (int d = 8; d >= 1; d >>= 1)
+#pragma unroll
+        for (int q = 0; q < d; ++q)
+            u[q] = u[q] + u[q + d];
+    const int e = et * kRouteTile + c;
+    if (e < E) {
+        const float be = bias ? bias[e] : 0.0f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t t = (int64_t)tt * kRouteTile + 4 * b + r;
+            if (t < T)
+                logits[t * E + e] = bias ? u[0][r] + be : u[0][r];
+        }
+    }
+}
+
 template <bool BF16, int TPL, int EPL, int NTQ>
 static void route_launch(const uint16_t *x, int64_t T, int H, const uint16_t *Wr, const float *bias,
                          int E, float *logits, WsHeader *hdr, hipStream_t s)
@@ -218,10 +327,18 @@ static void route_launch(const uint16_t *x, int64_t T, int H, const uint16_t *Wr
 hipError_t launch_route_logits(const uint16_t *x, bool bf16, int64_t T, int H, const uint16_t *Wr,
                                const float *bias, int E, float *logits, WsHeader *hdr, hipStream_t s)
 {
-    // many tokens: 2 tokens x 4 experts per lane (8 tokens x 32 experts per
-    // block); few tokens: one (token, expert) pair per 32 lanes so that
-    // enough wavefronts stream the router weights
-    if (T > 64) {
+    // many tokens: 16 x 16 tiles on the matrix cores (hidden sizes in whole
+    // 256-channel rounds), else on the VALU with 2 tokens x 4 experts per
+    // lane (8 tokens x 32 experts per block); few tokens: one (token, expert)
+    // pair per 32 lanes so that enough wavefronts stream the router weights
+    if (T > 64 && H % (64 * kRouteSets) == 0) {
+        const int n_tt = (int)((T + kRouteTile - 1) / kRouteTile), n_et = (E + kRouteTile - 1) / kRouteTile;
+        const unsigned grid = (unsigned)(((n_tt + 7) / 8) * 8 * n_et);
+        if (bf16)
+            route_logits_mfma_kernel<true><<<grid, 64, 0, s>>>(x, T, H, Wr, bias, E, logits, hdr, n_tt, n_et);
+        else
+            route_logits_mfma_kernel<false><<<grid, 64, 0, s>>>(x, T, H, Wr, bias, E, logits, hdr, n_tt, n_et);
+    } else if (T > 64) {
         if (bf16) route_launch<true, 2, 4, 4>(x, T, H, Wr, bias, E, logits, hdr, s);
         else route_launch<false, 2, 4, 4>(x, T, H, Wr, bias, E, logits, hdr, s);
     } else {
