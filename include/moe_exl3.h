@@ -89,7 +89,8 @@ extern "C" {
                                                tiles, and with hidden > 8192 (the GEMV's LDS
                                                limit) every expert does */
 #define MOE_EXL3_FORCE_MFMA (1u << 3)       /* every routed expert on the MFMA path */
-#define MOE_EXL3_FP8_MFMA (1u << 4)         /* routed MFMA GEMMs in fp8 (needs CB_MCG_E4M3 and hidden, inter % 256 == 0) */
+#define MOE_EXL3_FP8_MFMA (1u << 4)         /* routed MFMA GEMMs in fp8 (needs CB_MCG_E4M3, hidden and
+                                               inter % 256 == 0 and hidden <= 8192) */
 #define MOE_EXL3_DEBUG_CHECKS (1u << 5)     /* extra launches that check the routing tables and
                                                the finiteness of x into the status word */
 #define MOE_EXL3_DETERMINISTIC_COMBINE (1u << 6) /* accepted, always in effect: the k slot rows of

@@ -26,6 +26,9 @@ constexpr int kGemvDefaultRows = 2;
 // (4 I bytes).
 constexpr int kGemvMaxHidden = 8192;
 constexpr int kGemvMaxInter = 16384;
+// The fp8 path's activation quantizer holds a row's x and two suh rows in
+// registers, one wavefront per row: hidden sizes up to this.
+constexpr int kQuantMaxHidden = 8192;
 // Tokens up to which one block runs the whole routing tail (top-k, segment
 // tables, activation copy) in a single launch.
 constexpr int kSmallRouteTokens = 64;
@@ -90,6 +93,7 @@ struct GroupArgs {
     const int32_t *k_tab;
     uint32_t mcg;
     const int32_t *counts, *offsets, *sorted, *glist, *tiles;
+    const int32_t *idx;      // top-k expert of every routed slot [T*k]
     const WsHeader *hdr;
     const float *w;          // routing weights [T*k]
     const uint16_t *x16;     // fp16 activations [T][H]

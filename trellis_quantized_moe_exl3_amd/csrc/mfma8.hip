@@ -418,19 +418,6 @@ hipError_t launch_mfma8_down(const GroupArgs &a, int max_tiles, hipStream_t s)
 }
 
 // ------------------------------------------------------------ row quantizers
-// Deterministic block max (256 threads) of one non-negative float per thread.
-MOE_DEV float block_max256(float v, float *part)
-{
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
-        v = fmaxf(v, __shfl_xor(v, off, 64));
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0)
-        part[threadIdx.x >> 6] = v;
-    __syncthreads();
-    return fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
-}
-
 // Row scale: the least power of two s with amax / s <= 448 (the largest
 // finite E4M3 value), found exactly from amax = m 2^e, m in [0.5, 1), and
 // 448 = 0.875 2^9.  The scaled convert below takes its scale as a power of
@@ -460,105 +447,160 @@ MOE_DEV u32x2 e4m3_pack8(const float v[8], float s)
     return o;
 }
 
-// One block per routed row p (sorted order): x[t] * suh_p[e] for gate and up,
-// each scaled by its row amax / 448 and rounded to E4M3.
+// Wave-wide maximum of a non-negative float (all 64 lanes hold the result).
+MOE_DEV float wave_max64(float v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        v = fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+// One wavefront per routed row p (sorted order), four rows per block:
+// x[t] * suh_p[e] for gate and up, each scaled by its row amax / 448 and
+// rounded to E4M3.  The row's expert is its slot's top-k expert (for the
+// trellis shared expert's slots past the routed ones, the last expert).  Lane
+// l holds the 16-byte pieces l, l + 64, ... of the three rows (at most NC of
+// them: H <= 512 NC) between the amax reduction and the conversion; the
+// products are exact in fp32 and formed again for the conversion.
+template <int NC>
 __global__ __launch_bounds__(256) void quant_gateup_kernel(GroupArgs a, int64_t n)
 {
-    __shared__ float part[4];
-    const int64_t p = blockIdx.x;
+    const int64_t p = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (p >= n)
         return;
-    const int H = a.H;
-    const int64_t t = slot_token(a.sorted[p], a.nr, a.k);
-    // expert of row p: the last e with offsets[e] <= p
-    int lo = 0, hi = a.E;
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (a.offsets[mid] <= p)
-            lo = mid;
-        else
-            hi = mid;
-    }
-    const int e = lo;
-    const f16 *xr = (const f16 *)a.x16 + (int64_t)t * H;
-    const f16 *sg = (const f16 *)a.suh[0] + (int64_t)e * H;
-    const f16 *su = (const f16 *)a.suh[1] + (int64_t)e * H;
-    float mg = 0.0f, mu = 0.0f;
-    for (int ch = threadIdx.x; ch < H / 8; ch += 256) {
-        const f16x8 xv = *(const f16x8 *)(xr + 8 * ch);
-        const f16x8 gv = *(const f16x8 *)(sg + 8 * ch), uv = *(const f16x8 *)(su + 8 * ch);
+    const int l = threadIdx.x & 63, H = a.H;
+    const int64_t slot = a.sorted[p];
+    const int64_t t = slot_token(slot, a.nr, a.k);
+    // (clamped: an index outside the table, which the segment kernels flag
+    // in the status word, still reads inside the side-vector arrays)
+    const int e = slot < a.nr ? min(max(a.idx[slot], 0), a.E - 1) : a.E - 1;
+    const f16x8 *xr = (const f16x8 *)(a.x16 + t * H);
+    const f16x8 *sg = (const f16x8 *)(a.suh[0] + (int64_t)e * H);
+    const f16x8 *su = (const f16x8 *)(a.suh[1] + (int64_t)e * H);
+    const int np = H / 8;   // 16-byte pieces per row
+    f16x8 xv[NC], gv[NC], uv[NC];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            mg = fmaxf(mg, fabsf((float)xv[j] * (float)gv[j]));
-            mu = fmaxf(mu, fabsf((float)xv[j] * (float)uv[j]));
-        }
+    for (int c = 0; c < NC; ++c) {
+        const int q = 64 * c + l < np ? 64 * c + l : np - 1;   // in bounds; past np never used
+        xv[c] = xr[q];
+        gv[c] = sg[q];
+        uv[c] = su[q];
     }
-    const float s_g = e4m3_row_scale(block_max256(mg, part));
-    const float s_u = e4m3_row_scale(block_max256(mu, part));
-    for (int ch = threadIdx.x; ch < H / 8; ch += 256) {
-        const f16x8 xv = *(const f16x8 *)(xr + 8 * ch);
-        const f16x8 gv = *(const f16x8 *)(sg + 8 * ch), uv = *(const f16x8 *)(su + 8 * ch);
+    float mg = 0.0f, mu = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (64 * c + l < np) {
+            mg = fmaxf(mg, fabsf((float)xv[c][j] * (float)gv[c][j]));
+            mu = fmaxf(mu, fabsf((float)xv[c][j] * (float)uv[c][j]));
+        }
+    const float s_g = e4m3_row_scale(wave_max64(mg));
+    const float s_u = e4m3_row_scale(wave_max64(mu));
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        if (64 * c + l >= np)
+            break;
         float vg[8], vu[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            vg[j] = (float)xv[j] * (float)gv[j];
-            vu[j] = (float)xv[j] * (float)uv[j];
+            vg[j] = (float)xv[c][j] * (float)gv[c][j];
+            vu[j] = (float)xv[c][j] * (float)uv[c][j];
         }
-        *(u32x2 *)(a.a8g + p * H + 8 * ch) = e4m3_pack8(vg, s_g);
-        *(u32x2 *)(a.a8u + p * H + 8 * ch) = e4m3_pack8(vu, s_u);
+        *(u32x2 *)(a.a8g + p * H + 8 * (64 * c + l)) = e4m3_pack8(vg, s_g);
+        *(u32x2 *)(a.a8u + p * H + 8 * (64 * c + l)) = e4m3_pack8(vu, s_u);
     }
-    if (threadIdx.x == 0) {
+    if (l == 0) {
         a.sg8[p] = s_g;
         a.su8[p] = s_u;
     }
 }
 
-// One block per routed row p: h[p] (bf16, already times suh_down) scaled by
-// its amax / 448 and rounded to E4M3.
+// One wavefront per routed row p, four rows per block: h[p] (bf16, already
+// times suh_down; I <= 512 NC) scaled by its amax / 448 and rounded to E4M3.
+template <int NC>
 __global__ __launch_bounds__(256) void quant_h_kernel(GroupArgs a, int64_t n)
 {
-    __shared__ float part[4];
-    const int64_t p = blockIdx.x;
+    const int64_t p = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (p >= n)
         return;
-    const int I = a.I;
-    const uint16_t *hr = a.hbuf + p * I;
+    const int l = threadIdx.x & 63, I = a.I;
+    const u32x4 *hr = (const u32x4 *)(a.hbuf + p * I);
+    const int np = I / 8;
+    u32x4 raw[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+        raw[c] = hr[64 * c + l < np ? 64 * c + l : np - 1];
     float m = 0.0f;
-    for (int ch = threadIdx.x; ch < I / 8; ch += 256) {
-        const u32x4 raw = *(const u32x4 *)(hr + 8 * ch);
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            m = fmaxf(m, fmaxf(fabsf(__uint_as_float(raw[j] << 16)), fabsf(__uint_as_float(raw[j] & 0xFFFF0000u))));
-    }
-    const float s = e4m3_row_scale(block_max256(m, part));
-    for (int ch = threadIdx.x; ch < I / 8; ch += 256) {
-        const u32x4 raw = *(const u32x4 *)(hr + 8 * ch);
+            if (64 * c + l < np)
+                m = fmaxf(m, fmaxf(fabsf(__uint_as_float(raw[c][j] << 16)),
+                               fabsf(__uint_as_float(raw[c][j] & 0xFFFF0000u))));
+    const float s = e4m3_row_scale(wave_max64(m));
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        if (64 * c + l >= np)
+            break;
         float v[8];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            v[2 * j] = __uint_as_float(raw[j] << 16);
-            v[2 * j + 1] = __uint_as_float(raw[j] & 0xFFFF0000u);
+            v[2 * j] = __uint_as_float(raw[c][j] << 16);
+            v[2 * j + 1] = __uint_as_float(raw[c][j] & 0xFFFF0000u);
         }
-        *(u32x2 *)(a.h8 + p * I + 8 * ch) = e4m3_pack8(v, s);
+        *(u32x2 *)(a.h8 + p * I + 8 * (64 * c + l)) = e4m3_pack8(v, s);
     }
-    if (threadIdx.x == 0)
+    if (l == 0)
         a.sh8[p] = s;
 }
 
-hipError_t launch_quant_gateup(const GroupArgs &a, int64_t n, hipStream_t s)
+// Rows of `width` channels (a multiple of 8, at most 512 * 16 for gate/up and
+// 512 * 32 for h): NC = pieces per lane, rounded up to a power of two.
+template <template <int> class KERNEL>
+static hipError_t launch_rows(const GroupArgs &a, int64_t n, int width, int max_nc, hipStream_t s)
 {
     if (n <= 0)
         return hipSuccess;
-    quant_gateup_kernel<<<(unsigned)n, 256, 0, s>>>(a, n);
+    const int need = (width / 8 + 63) / 64;
+    if (width % 8 || need > max_nc)
+        return hipErrorInvalidValue;
+    const unsigned grid = (unsigned)((n + 3) / 4);
+    if (need <= 1) KERNEL<1>::launch(grid, a, n, s);
+    else if (need <= 2) KERNEL<2>::launch(grid, a, n, s);
+    else if (need <= 4) KERNEL<4>::launch(grid, a, n, s);
+    else if (need <= 8) KERNEL<8>::launch(grid, a, n, s);
+    else if (need <= 16) KERNEL<16>::launch(grid, a, n, s);
+    else KERNEL<32>::launch(grid, a, n, s);
     return hipGetLastError();
+}
+
+template <int NC>
+struct QuantGateup {
+    static void launch(unsigned grid, const GroupArgs &a, int64_t n, hipStream_t s)
+    {
+        if constexpr (NC <= 16)   // (three rows of 32 pieces per lane would not fit in registers)
+            quant_gateup_kernel<NC><<<grid, 256, 0, s>>>(a, n);
+    }
+};
+template <int NC>
+struct QuantH {
+    static void launch(unsigned grid, const GroupArgs &a, int64_t n, hipStream_t s)
+    {
+        quant_h_kernel<NC><<<grid, 256, 0, s>>>(a, n);
+    }
+};
+
+hipError_t launch_quant_gateup(const GroupArgs &a, int64_t n, hipStream_t s)
+{
+    return launch_rows<QuantGateup>(a, n, a.H, kQuantMaxHidden / 512, s);
 }
 
 hipError_t launch_quant_h(const GroupArgs &a, int64_t n, hipStream_t s)
 {
-    if (n <= 0)
-        return hipSuccess;
-    quant_h_kernel<<<(unsigned)n, 256, 0, s>>>(a, n);
-    return hipGetLastError();
+    return launch_rows<QuantH>(a, n, a.I, 32, s);
 }
 
 }  // namespace moe

@@ -65,7 +65,7 @@ int check_desc(const moe_exl3_desc *d)
     // fp8 MFMA: only the E4M3 codebook (its values are exact in E4M3), and
     // whole 4-stage pipeline rounds of 64 input channels
     if ((d->flags & MOE_EXL3_FP8_MFMA) &&
-        (d->codebook != MOE_EXL3_CB_MCG_E4M3 || d->hidden % 256 || d->inter % 256))
+        (d->codebook != MOE_EXL3_CB_MCG_E4M3 || d->hidden % 256 || d->inter % 256 || d->hidden > kQuantMaxHidden))
         return MOE_EXL3_ERR_UNSUPPORTED;
     if ((d->flags & MOE_EXL3_FORCE_GEMV) && (d->flags & MOE_EXL3_FORCE_MFMA))
         return MOE_EXL3_ERR_INVALID_ARG;
@@ -426,6 +426,7 @@ static int run_layer(const moe_exl3_desc *desc, const moe_exl3_weights *weights,
     ga.counts = at<int32_t>(ws, p.counts);
     ga.offsets = at<int32_t>(ws, p.offsets);
     ga.sorted = at<int32_t>(ws, p.sorted);
+    ga.idx = at<int32_t>(ws, p.idx);
     ga.glist = at<int32_t>(ws, p.glist);
     ga.tiles = at<int32_t>(ws, p.tiles);
     ga.hdr = at<WsHeader>(ws, p.hdr);
