@@ -281,6 +281,109 @@ struct GemmTile {
         }
         wait_vmcnt<0>();   // the trailing zero-range loads still write LDS
     }
+
+    // ---- the down projections' pipeline: the A fragments of a stage's first
+    // k-step are read during the previous stage, so no MFMA waits for an LDS
+    // read right after the barrier.  That barrier must then also cover the
+    // next stage's loads, which leaves them two stages to land instead of
+    // three: enough for the contiguous h rows of the down kernels, too little
+    // for the gathered activation rows of gate/up (measured slower there).
+
+    // A fragments (and, gate/up trellis, this wave's suh piece) of k-step kt
+    // of the stage held in ring slot rg
+    template <int NMB>
+    MOE_DEV void read_a(const LDS_AS uint16_t *rg, int kt, u32x4 (&af)[NMB], f16x8 &su) const
+    {
+        if constexpr (MODE == GATEUP_TRELLIS)
+            su = *(const LDS_AS f16x8 *)(rg + kStageHalves + 128 * (4 * pr + 2 * kt + h));
+#pragma unroll
+        for (int i = 0; i < NMB; ++i)
+            af[i] = *(const LDS_AS u32x4 *)((const LDS_AS char *)rg + aread[kt] + i * 32 * kBK * 2);
+    }
+
+    // MFMAs of k-step kt (all CM column groups) on the fragments af, the
+    // decode of the next fragment running beside each group's MFMAs
+    template <int NMB, int CM>
+    MOE_DEV void kstep(int kt, const u32x4 (&af)[NMB], f16x8 su, const BRaw<CM> &bcur, const BRaw<CM> &bnext,
+                       u32x4 &dcur, f32x16 acc[kMB])
+    {
+#pragma unroll
+        for (int cm = 0; cm < CM; ++cm) {
+            const int f = kt * CM + cm;
+            u32x4 b = dcur;
+            if constexpr (MODE == GATEUP_TRELLIS)
+                b = __builtin_bit_cast(u32x4, __builtin_bit_cast(f16x8, dcur) * su);
+            if (f + 1 < kKT * CM)
+                dcur = decode<CM>(bcur, (f + 1) / CM, (f + 1) % CM);
+            else
+                dcur = decode<CM>(bnext, 0, 0);
+#pragma unroll
+            for (int i = 0; i < NMB; ++i)
+                acc[cm * NMB + i] = mfma_step<MODE>(af[i], b, acc[cm * NMB + i]);
+            if constexpr (TR::kTrellis)
+                interleave<NMB>();
+        }
+    }
+
+    // One stage s of the down pipeline (slot rg = s % 4, the next stage's slot
+    // rgn, the slot rgp that stage s + 3 refills): wait for this wave's loads
+    // of stage s + 1, barrier (every wave's loads of stage s + 1 landed, every
+    // wave is done with rgp, last read during stage s - 1), prefetch stage
+    // s + 3; k-step 0 runs on fragments read during stage s - 1 while k-step
+    // 1's are read, and k-step 1 while k-step 0 of stage s + 1 is read from
+    // rgn (carried in af0 / su0).  "At most NA + NB loads outstanding" (those
+    // of stage s + 2) proves that the loads of stage s + 1 are done.
+    template <int NMB, int CM>
+    MOE_DEV void stage_ahead(int s, int nst, const LDS_AS uint16_t *rg, const LDS_AS uint16_t *rgn,
+                             LDS_AS uint16_t *rgp, const BRaw<CM> &bcur, const BRaw<CM> &bnext, BRaw<CM> &bpf,
+                             u32x4 &dk0, u32x4 (&af0)[NMB], f16x8 &su0, f32x16 acc[kMB])
+    {
+        static_assert(kKT == 2, "two k-steps per stage");
+        constexpr int NA = TR::kNA, NB = TR::kNB * CM;
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<NA + NB>();
+        __builtin_amdgcn_s_barrier();
+        load_a(s + 3, nst, rgp);
+        load_b<CM>(s + 3, nst, bpf);
+        u32x4 af1[NMB];
+        f16x8 su1;
+        read_a<NMB>(rg, 1, af1, su1);
+        u32x4 dcur = dk0;
+        kstep<NMB, CM>(0, af0, su0, bcur, bnext, dcur, acc);
+        read_a<NMB>(rgn, 0, af0, su0);
+        kstep<NMB, CM>(1, af1, su1, bcur, bnext, dcur, acc);
+        dk0 = dcur;
+    }
+
+    template <int NMB, int CM>
+    MOE_DEV void run_ahead(LDS_AS uint16_t *r0, LDS_AS uint16_t *r1, LDS_AS uint16_t *r2, LDS_AS uint16_t *r3,
+                           f32x16 acc[kMB])
+    {
+        constexpr int NA = TR::kNA, NB = TR::kNB * CM;
+        const int nst = Kdim / kBK;   // a multiple of 4
+        BRaw<CM> b0, b1, b2, b3;
+        load_a(0, nst, r0);
+        load_b<CM>(0, nst, b0);
+        load_a(1, nst, r1);
+        load_b<CM>(1, nst, b1);
+        load_a(2, nst, r2);
+        load_b<CM>(2, nst, b2);
+        // stage 0's data (every wave's loads) before its first fragments
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<2 * (NA + NB)>();
+        __builtin_amdgcn_s_barrier();
+        u32x4 af0[NMB];
+        f16x8 su0;
+        read_a<NMB>(r0, 0, af0, su0);
+        u32x4 dk0 = decode<CM>(b0, 0, 0);
+        for (int s = 0; s < nst; s += 4) {
+            stage_ahead<NMB, CM>(s, nst, r0, r1, r3, b0, b1, b3, dk0, af0, su0, acc);
+            stage_ahead<NMB, CM>(s + 1, nst, r1, r2, r0, b1, b2, b0, dk0, af0, su0, acc);
+            stage_ahead<NMB, CM>(s + 2, nst, r2, r3, r1, b2, b3, b1, dk0, af0, su0, acc);
+            stage_ahead<NMB, CM>(s + 3, nst, r3, r0, r2, b3, b0, b2, dk0, af0, su0, acc);
+        }
+        wait_vmcnt<0>();   // the trailing zero-range loads still write LDS
+    }
 };
 
 // Column groups per wavefront for a tile of NMB 32-row blocks: small tiles
@@ -342,7 +445,10 @@ MOE_DEV void tile_body(GemmTile<MODE, K, CB> &g, const GemmArgs &args, int n0,
 #pragma unroll
     for (int i = 0; i < kMB; ++i)
         acc[i] = (f32x16){};
-    g.template run<NMB, CM>(R0, R1, R2, R3, acc);
+    if constexpr (TR::kGateUp)
+        g.template run<NMB, CM>(R0, R1, R2, R3, acc);
+    else
+        g.template run_ahead<NMB, CM>(R0, R1, R2, R3, acc);
     __syncthreads();   // every wave is done with the rings (reused below)
 
     // ---- epilogue.  Accumulator block b = cm * NMB + i covers rows 32 i + ..
