@@ -125,6 +125,68 @@ MOE_DEV void gemv_stream_k(int kw, __amdgpu_buffer_rsrc_t rs, uint32_t v0, uint3
     }
 }
 
+// The same stream with the dot products on the matrix cores: the lane's
+// fragment (eight input rows kk + 8h .. + 7 of column 16 ts + c) is exactly
+// its B operand of v_mfma_f32_32x32x16_f16 (column l % 32, k-half l / 32),
+// and its A operand is the same eight inputs of activation row l % 32, read
+// from LDS at arow + kk (arow: the lane's row, already offset by 8h).  Rows
+// past the pass's routed rows carry any in-range data: their output rows are
+// never read.  The accumulator d holds, in lanes 0..31, the column's sum for
+// activation row r in register r (r < 4); the MFMA adds both k-halves.
+template <int K, int CB>
+MOE_DEV void gemv_stream_mfma(__amdgpu_buffer_rsrc_t rs, uint32_t v0, uint32_t v1, uint32_t rowb, int tk0, int tk1,
+                              int q, uint32_t m_lo, uint32_t m_hi, const f16 *arow, f32x16 &d)
+{
+    uint32_t A[kGemvU][2], B[kGemvU][2];
+    auto load = [&](uint32_t(&buf)[kGemvU][2], int g) {
+#pragma unroll
+        for (int u = 0; u < kGemvU; ++u) {
+            const int so = (g + u) * (int)rowb;
+            buf[u][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, v0, so, 0);
+            buf[u][1] = __builtin_amdgcn_raw_buffer_load_b32(rs, v1, so, 0);
+        }
+    };
+    auto run = [&](const uint32_t(&buf)[kGemvU][2], int g) {
+#pragma unroll
+        for (int u = 0; u < kGemvU; ++u) {
+            f16x2 wp[4];
+            frag_biased_pairs<K, CB>(buf[u][0], buf[u][1], q, m_lo, m_hi, wp);
+            const f16x8 av = *(const f16x8 *)(arow + 16 * (g + u));
+            d = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, __builtin_bit_cast(f16x8, wp), d, 0, 0, 0);
+        }
+    };
+    // as in gemv_stream: every load unconditional, the last group reloaded
+    // past the wave's range
+    const int glast = tk1 - kGemvU;
+    int g = tk0;
+    load(A, g);
+    load(B, min(g + kGemvU, glast));
+    for (; g + 2 * kGemvU <= tk1; g += 2 * kGemvU) {
+        run(A, g);
+        load(A, min(g + 2 * kGemvU, glast));
+        run(B, g + kGemvU);
+        load(B, min(g + 3 * kGemvU, glast));
+    }
+    if (g < tk1)
+        run(A, g);
+}
+
+template <int K, int CB>
+MOE_DEV void gemv_stream_mfma_k(int kw, __amdgpu_buffer_rsrc_t rs, uint32_t v0, uint32_t v1, uint32_t rowb, int tk0,
+                                int tk1, int q, uint32_t m_lo, uint32_t m_hi, const f16 *arow, f32x16 &d)
+{
+    if constexpr (K > 0) {
+        gemv_stream_mfma<K, CB>(rs, v0, v1, rowb, tk0, tk1, q, m_lo, m_hi, arow, d);
+    } else {
+        if (kw == 4)
+            gemv_stream_mfma<4, CB>(rs, v0, v1, rowb, tk0, tk1, q, m_lo, m_hi, arow, d);
+        else if (kw == 3)
+            gemv_stream_mfma<3, CB>(rs, v0, v1, rowb, tk0, tk1, q, m_lo, m_hi, arow, d);
+        else
+            gemv_stream_mfma<2, CB>(rs, v0, v1, rowb, tk0, tk1, q, m_lo, m_hi, arow, d);
+    }
+}
+
 // ------------------------------------------------------------ shared expert GEMV
 // Dense fp16 weights in nn.Linear layout [out][in]; one wavefront per weight
 // row (gate/up: the gate and the up row of one channel), four per block.  The
@@ -411,27 +473,16 @@ __global__ __launch_bounds__(256, 4) void gemv_gateup_kernel(GroupArgs a, int ma
                 rsum[i / kGemvPass][i % kGemvPass] = sums[i];
         __syncthreads();
 
-        float acc[kGemvPass] = {};
-        const f16 *xsp = xs + (size_t)pr * kGemvPass * H + 8 * h;
-        auto dot = [&](int r, int kk, const f16x2 wp[4], float s) {
-            const f16x8 v = *(const f16x8 *)(xsp + (size_t)r * H + kk);
+        // lane l's activation row: l % 32 for the pass's rows, the last one
+        // for the rest (in range; their output rows are not read)
+        const int ar = min(l & 31, nr - 1);
+        const f16 *arow = xs + ((size_t)pr * kGemvPass + ar) * H + 8 * h;
+        f32x16 d = {};
+        gemv_stream_mfma_k<K, CB>(kw, rs, v0, v1, rowb, tk0, tk1, q, m_lo, m_hi, arow, d);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                s = __builtin_amdgcn_fdot2(wp[j], (f16x2){v[2 * j], v[2 * j + 1]}, s, false);
-            return s;
-        };
-        // nr is the same for the whole block: branch once, not per fragment
-        if (__builtin_amdgcn_readfirstlane(nr) == 2)
-            gemv_stream_k<K, CB, 2>(kw, rs, v0, v1, rowb, tk0, tk1, q, m_lo, m_hi, dot, acc);
-        else
-            gemv_stream_k<K, CB, 1>(kw, rs, v0, v1, rowb, tk0, tk1, q, m_lo, m_hi, dot, acc);
-        // the two k-halves of a tile row sit in lanes l and l ^ 32
-#pragma unroll
-        for (int r = 0; r < kGemvPass; ++r) {
-            const float tot = acc[r] + __shfl_xor(acc[r], 32, 64);
+        for (int r = 0; r < kGemvPass; ++r)
             if (r < nr && h == 0)
-                psum[pr][kh][r][32 * cp + 16 * ts + c] = tot;
-        }
+                psum[pr][kh][r][32 * cp + 16 * ts + c] = d[r];
         __syncthreads();
         if (threadIdx.x < nr * kGuCols) {
             const int r = threadIdx.x / kGuCols, cc = threadIdx.x % kGuCols;
@@ -551,28 +602,15 @@ __global__ __launch_bounds__(256, 4) void gemv_down_kernel(GroupArgs a, int max_
             }
         __syncthreads();
 
-        float acc[kGemvPass] = {};
-        const f16 *hsp = hs + 8 * h;
-        auto dot = [&](int r, int kk, const f16x2 wp[4], float s) {
-            const f16x8 v = *(const f16x8 *)(hsp + (size_t)r * I + kk);
+        const int ar = min(l & 31, nr - 1);
+        const f16 *arow = hs + (size_t)ar * I + 8 * h;
+        f32x16 d = {};
+        if (kr < S)
+            gemv_stream_mfma_k<K, CB>(kw, rs, v0, v1, rowb, tk0, tk1, q, m_lo, m_hi, arow, d);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                s = __builtin_amdgcn_fdot2(wp[j], (f16x2){v[2 * j], v[2 * j + 1]}, s, false);
-            return s;
-        };
-        if (kr < S) {
-            // nr is the same for the whole block: branch once, not per fragment
-            if (__builtin_amdgcn_readfirstlane(nr) == 2)
-                gemv_stream_k<K, CB, 2>(kw, rs, v0, v1, rowb, tk0, tk1, q, m_lo, m_hi, dot, acc);
-            else
-                gemv_stream_k<K, CB, 1>(kw, rs, v0, v1, rowb, tk0, tk1, q, m_lo, m_hi, dot, acc);
-        }
-#pragma unroll
-        for (int r = 0; r < kGemvPass; ++r) {
-            const float tot = acc[r] + __shfl_xor(acc[r], 32, 64);
+        for (int r = 0; r < kGemvPass; ++r)
             if (kr < S && r < nr && h == 0)
-                psum[kr][r][32 * cp + 16 * ts + c] = tot;
-        }
+                psum[kr][r][32 * cp + 16 * ts + c] = d[r];
         __syncthreads();
         if (threadIdx.x < nr * kDownCols) {
             const int r = threadIdx.x / kDownCols, cc = threadIdx.x % kDownCols;
