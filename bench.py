@@ -110,7 +110,7 @@ class Hip:
         self.l.hipEventDestroy(e)
 
 
-def setup(cfg, copies=1, shared=True, extra_flags=0):
+def setup(cfg, copies=1, shared=True, extra_flags=0, gemv_rows=0):
     """Device inputs of a workload: `copies` copies of the codes (rotated by
     the decode legs), the descriptor and one weights struct per copy.  Format
     variants: per-tensor widths (one code pool per projection and a table of
@@ -146,7 +146,7 @@ def setup(cfg, copies=1, shared=True, extra_flags=0):
     flags |= (M.HAS_SHARED if sh is not None else 0) | (M.HAS_ROUTER_BIAS if bias is not None else 0)
     flags |= (M.HADAMARD if signs is not None else 0) | (M.SHARED_TRELLIS if cfg.shared_trellis else 0)
     desc = M.make_desc(cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k, cfg.K, cfg.codebook,
-                       cfg.mcg, cfg.act_dtype, flags, 0)
+                       cfg.mcg, cfg.act_dtype, flags, gemv_rows)
     weights = [M.make_weights(c, suh, svh, rw, bias, sh, signs, tabs[i] if tabs else None, ktab)
                for i, c in enumerate(codes)]
     keep = (codes, suh, svh, rw, bias, sh, signs, tabs, ktab)
@@ -368,6 +368,29 @@ def prefill_leg(W, M, hip, name, steps, flags=0, label=None):
     return cfg, res
 
 
+def gemv_threshold_sweep(W, M, hip, steps):
+    """Layer time against the per-expert row threshold between the GEMV and
+    the MFMA paths (the descriptor's gemv_max_rows, at most 8; 0 is the
+    default: 8 up to 8 tokens, else 2), on the 7168-token prefill layer and
+    the 8-token step (4 rotating code copies)."""
+    import torch
+    res = {}
+    for name, copies, rows in (("prefill", 1, (1, 2, 4, 8)), ("decode", 4, (1, 2, 4, 8))):
+        cfg = W.BY_NAME[name]
+        out = {}
+        for g in rows:
+            inp, desc, weights, keep = setup(cfg, copies=copies, gemv_rows=g)
+            x = _dev(inp.x)
+            _, _, dev_ms, _, _ = time_layer(desc, weights, x, steps, 2, hip)
+            out[str(g)] = dev_ms
+            del keep, weights, x
+            torch.cuda.empty_cache()
+        res[name] = {"ms_per_layer_by_gemv_max_rows": out}
+        print(f"[bench] gemv threshold {name}: {json.dumps({k: round(v, 4) for k, v in out.items()})}",
+              file=sys.stderr, flush=True)
+    return res
+
+
 def tile_classes(W, M, hip, steps):
     """Expert MFMA rates per row-tile class: the gate/up and down launches'
     event-timed TFLOP/s on routings whose tiles are all full (256 rows), mostly
@@ -570,6 +593,18 @@ def main():
                                                   "exlr8_prefill fp8")
         extra["format_variants"] = var
         extra["tile_classes"] = tile_classes(W, M, hip, min(args.steps, 10))
+        extra["gemv_threshold"] = gemv_threshold_sweep(W, M, hip, min(args.steps, 10))
+        # one tensor-parallel rank's share of the prefill layer (I split in two)
+        _, extra["tp2_rank_prefill"] = prefill_leg(W, M, hip, "prefill_tp2", min(args.steps, 10))
+        extra["tp2_rank_prefill"]["workload"] = ("prefill-7168 at I = 1024: the intermediate half that one of "
+                                                 "two tensor-parallel ranks holds")
+        # the 64-token correctness layer, for its latency
+        tcfg = W.BY_NAME["tiny"]
+        tinp, tdesc, tweights, tkeep = setup(tcfg)
+        _, _, tdev, _, _ = time_layer(tdesc, tweights, _dev(tinp.x), args.decode_steps, 5, hip)
+        extra["tiny"] = {"workload": "tiny: T=64, H=256, I=128, E=8, top-2, K=2", "us_per_layer": tdev * 1000}
+        print(f"[bench] tiny {tdev * 1000:.1f} us/layer", file=sys.stderr, flush=True)
+        del tkeep, tweights
         extra["hbm_read_GBps_achievable"] = stream_read_bandwidth(hip)
 
     # ---- 16384-token prefill with the E4M3 codebook: fp16 and fp8 MFMA

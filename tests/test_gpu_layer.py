@@ -219,6 +219,11 @@ def test_mixed_width_sampled(name):
     _sampled(name)
 
 
+def test_tp2_rank_prefill_sampled():
+    # the 7168-token layer at I = 1024, one tensor-parallel rank's share
+    _sampled("prefill_tp2", n_min=32, n_full=2)
+
+
 @pytest.mark.parametrize("name,n_min", [("tiles_full", 64), ("tiles_mid", 24), ("tiles_small", 24)])
 def test_tile_class_routings_sampled(name, n_min):
     # the routings that isolate one row-tile class for measurement: every

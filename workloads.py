@@ -130,7 +130,12 @@ TILE_CLASSES: List[LayerConfig] = [
     LayerConfig("tiles_small", 8, 512, 4096, 2048, 288, 8, 2, CB_MCG, DT_BF16, False, False),
     LayerConfig("tiles_mid", 9, 2048, 4096, 2048, 288, 8, 2, CB_MCG, DT_BF16, False, False),
 ]
-BY_NAME: Dict[str, LayerConfig] = {c.name: c for c in CONFIGS + VARIANTS + TILE_CLASSES}
+# One tensor-parallel rank's share of the prefill layer: the intermediate
+# dimension split in two (each rank holds half of every expert's channels).
+TP_SHARES: List[LayerConfig] = [
+    LayerConfig("prefill_tp2", 2, 7168, 4096, 1024, 288, 8, 2, CB_MCG, DT_BF16, True, True),
+]
+BY_NAME: Dict[str, LayerConfig] = {c.name: c for c in CONFIGS + VARIANTS + TILE_CLASSES + TP_SHARES}
 
 
 def _rng(seed: int, tag: str, *idx: int) -> np.random.Generator:
