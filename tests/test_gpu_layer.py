@@ -256,6 +256,21 @@ def test_tiny_fp8_mfma(T):
         assert err <= TOL_FP8 and np.isfinite(out).all()
 
 
+@pytest.mark.parametrize("T", [37, 300])
+def test_tiny_fp8_mfma_with_fp16_shared_expert(T):
+    # above 16 tokens the dense fp16 shared expert's tiles run on the 16-bit
+    # MFMA path inside the fp8 launches (300 tokens: two 256-row dense tiles,
+    # the second ragged)
+    inp = W.gen_layer(_tiny_e4m3(T).replace(shared=True))
+    assert inp.shared is not None
+    out = DevLayer(inp, flags=M.FORCE_MFMA | M.FP8_MFMA).run()
+    _, _, ref = oracle.layer(inp)
+    err = rel_err(out, ref)
+    print(f"tiny fp8 + fp16 shared T={T} err={err:.3e}")
+    record(f"tiny fp8 + fp16 shared T={T}", err, TOL_FP8)
+    assert err <= TOL_FP8 and np.isfinite(out).all()
+
+
 def test_tiny_fp8_one_expert_takes_every_token():
     # 600 slots on expert 3: the fp8 GEMMs run three row tiles, the last one
     # ragged (88 rows), for the same expert
