@@ -76,6 +76,9 @@ extern "C" {
 #define MOE_EXL3_DT_FP8 3   /* OCP E4M3FN bit patterns, one byte per value */
 #define MOE_EXL3_DT_GEMV_F16 4   /* moe_exl3_decode only: fp16 128*c + 1532, the
                                     decode-fused GEMV's dot-product operand */
+#define MOE_EXL3_DT_MFMA_BIASED_F16 5   /* moe_exl3_decode only, CB_MCG only: fp16
+                                    128*c + 1532 from the gate/up MFMA's decoder
+                                    of one-block (at most 32-row) tiles */
 
 /* codebooks */
 #define MOE_EXL3_CB_MCG 0
@@ -286,6 +289,9 @@ int moe_exl3_layer_profiled(const moe_exl3_desc *desc, const moe_exl3_weights *w
  *   FP8       dst = E4M3FN bits of c, from the fp8 MFMA's decoder (exact for
  *             the E4M3 codebook; CB_MCG values are rounded to E4M3)
  *   GEMV_F16  dst = 128 c + 1532 in fp16, the decode-fused GEMV's operand (exact)
+ *   MFMA_BIASED_F16  dst = 128 c + 1532 in fp16, from the gate/up MFMA's decoder
+ *             of one-block tiles (exact; CB_MCG only, else UNSUPPORTED: with
+ *             the E4M3 codebook those tiles use the F16 decoder)
  *   F32       dst = c in fp32 (exact)
  * codes: device [n_in/16][n_out/16][16K] uint16; dst: device, row-major.
  * n_in and n_out are positive multiples of 16.

@@ -84,6 +84,7 @@ int main()
     CHECK(moe_exl3_decode(c, 15, 16, 2, 1u, 0, out, MOE_EXL3_DT_F32, nullptr) == MOE_EXL3_ERR_INVALID_ARG);
     CHECK(moe_exl3_decode(c, 16, 16, 5, 1u, 0, out, MOE_EXL3_DT_F32, nullptr) == MOE_EXL3_ERR_UNSUPPORTED);
     CHECK(moe_exl3_decode(c, 16, 16, 2, 1u, 0, out, 9, nullptr) == MOE_EXL3_ERR_UNSUPPORTED);
+    CHECK(moe_exl3_decode(c, 16, 16, 2, 1u, 1, out, MOE_EXL3_DT_MFMA_BIASED_F16, nullptr) == MOE_EXL3_ERR_UNSUPPORTED);
     CHECK(moe_exl3_decode(c, 16, 16, 2, 1u, 0, (char *)out + 1, MOE_EXL3_DT_F32, nullptr) == MOE_EXL3_ERR_MISALIGNED);
     uint16_t *dst = (uint16_t *)(fake + 2048);
     CHECK(moe_exl3_repack(c, dst, 0, 16, 16, 2, 0, nullptr) == MOE_EXL3_ERR_INVALID_ARG);

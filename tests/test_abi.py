@@ -119,3 +119,5 @@ def test_route_and_decode_argument_checks():
     assert l.moe_exl3_decode(0x1000, 40, 64, 2, 1, 0, 0x2000, 0, None) == M.ERR_INVALID_ARG
     assert l.moe_exl3_decode(0x1000, 48, 64, 2, 1, 0, 0x2004, 0, None) == M.ERR_MISALIGNED
     assert l.moe_exl3_decode(0x1000, 48, 64, 2, 1, 0, 0x2000, 9, None) == M.ERR_UNSUPPORTED
+    # the one-block MFMA operand mode exists for the mcg codebook only
+    assert l.moe_exl3_decode(0x1000, 48, 64, 2, 1, 1, 0x2000, M.DT_MFMA_BIASED_F16, None) == M.ERR_UNSUPPORTED

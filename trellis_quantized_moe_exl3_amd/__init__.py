@@ -15,7 +15,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_exl3.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_MISALIGNED, ERR_HIP = 0, -1, -2, -3, -4, -5
-DT_F32, DT_F16, DT_BF16, DT_FP8, DT_GEMV_F16 = 0, 1, 2, 3, 4
+DT_F32, DT_F16, DT_BF16, DT_FP8, DT_GEMV_F16, DT_MFMA_BIASED_F16 = 0, 1, 2, 3, 4, 5
 CB_MCG, CB_MCG_E4M3 = 0, 1
 HAS_SHARED, HAS_ROUTER_BIAS, FORCE_GEMV, FORCE_MFMA, FP8_MFMA = 1, 2, 4, 8, 16
 DEBUG_CHECKS, DETERMINISTIC_COMBINE = 32, 64

@@ -6,8 +6,10 @@
 //   F16       frag_decode_f16  (the gate/up MFMA B operand, 2v in fp16)
 //   BF16      frag_decode_bf16 (the down MFMA B operand, 2v in bf16)
 //   FP8       frag_decode_fp8  (the fp8 MFMA B operand, E4M3 bytes of c)
-//   GEMV_F16  frag_biased_pairs (the decode-fused GEMV dot-product operand,
+//   GEMV_F16  frag_biased_pairs (the decode-fused GEMV's MFMA operand,
 //             fp16 2v + 1532, stored as is)
+//   MFMA_BIASED_F16  frag_decode_f16_biased (the gate/up MFMA operand on
+//             one-block tiles, mcg codebook: fp16 2v + 1532, stored as is)
 //   F32       frag_decode_f32  (2v in fp32)
 // The 16-bit and fp32 modes store c = 2v / 128; the division is by a power
 // of two and exact in every one of these types.
@@ -17,7 +19,7 @@
 
 namespace moe {
 
-enum { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_FP8 = 3, DT_GEMV_F16 = 4 };
+enum { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_FP8 = 3, DT_GEMV_F16 = 4, DT_MFMA_BIASED_F16 = 5 };
 
 // 256 threads = 8 tiles; thread -> (tile, column c, k-half h).
 template <int K, int CB, int DT>
@@ -60,6 +62,11 @@ __global__ __launch_bounds__(256) void decode_kernel(const uint32_t *__restrict_
 #pragma unroll
         for (int t = 0; t < 8; ++t)
             ((f16 *)dst)[at(t)] = wp[t / 2][t & 1];
+    } else if constexpr (DT == DT_MFMA_BIASED_F16) {
+        const f16x8 v = frag_decode_f16_biased<K>(D0, D1, q, m_lo, m_hi);
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+            ((f16 *)dst)[at(t)] = v[t];
     } else {
         float v2[8];
         frag_decode_f32<K, CB>(D0, D1, q, m_lo, m_hi, v2);
@@ -82,6 +89,9 @@ static hipError_t decode_dt(const uint16_t *codes, int n_in, int n_out, uint32_t
     case DT_F16: decode_kernel<K, CB, DT_F16><<<grid, 256, 0, s>>>(c32, n_in, n_out, lo, hi, dst); break;
     case DT_BF16: decode_kernel<K, CB, DT_BF16><<<grid, 256, 0, s>>>(c32, n_in, n_out, lo, hi, dst); break;
     case DT_GEMV_F16: decode_kernel<K, CB, DT_GEMV_F16><<<grid, 256, 0, s>>>(c32, n_in, n_out, lo, hi, dst); break;
+    case DT_MFMA_BIASED_F16:
+        decode_kernel<K, CB, DT_MFMA_BIASED_F16><<<grid, 256, 0, s>>>(c32, n_in, n_out, lo, hi, dst);
+        break;
     default: decode_kernel<K, CB, DT_FP8><<<grid, 256, 0, s>>>(c32, n_in, n_out, lo, hi, dst); break;
     }
     return hipGetLastError();

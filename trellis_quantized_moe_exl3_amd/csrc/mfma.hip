@@ -176,23 +176,38 @@ struct GemmTile {
     // values of 2v (fp16 for gate/up, bf16 for down), or dense weights
     // K = 0 (per-tensor widths): the wavefront's width kw is a run-time,
     // wave-uniform value; only the state windows depend on it
-    template <int KK>
+    // (BIASED: the mcg gate/up values as 2v + 1532, see kBiasB)
+    template <int KK, bool BIASED>
     MOE_DEV u32x4 decode_k(uint32_t D0, uint32_t D1) const
     {
-        if constexpr (MODE == GATEUP_TRELLIS)
+        if constexpr (MODE == GATEUP_TRELLIS && BIASED)
+            return __builtin_bit_cast(u32x4, frag_decode_f16_biased<KK>(D0, D1, q, m_lo, m_hi, kw));
+        else if constexpr (MODE == GATEUP_TRELLIS)
             return __builtin_bit_cast(u32x4, frag_decode_f16<KK, CB>(D0, D1, q, m_lo, m_hi, kw));
         else
             return __builtin_bit_cast(u32x4, frag_decode_bf16<KK, CB>(D0, D1, q, m_lo, m_hi, kw));
     }
 
-    template <int CM>
+    template <int CM, bool BIASED = false>
     MOE_DEV u32x4 decode(const BRaw<CM> &br, int kt, int cm) const
     {
         if constexpr (!TR::kTrellis)
             return br.d[kt][cm];
         else
-            return decode_k<K>(br.c[kt][cm][0], br.c[kt][cm][1]);
+            return decode_k<K, BIASED>(br.c[kt][cm][0], br.c[kt][cm][1]);
     }
+
+    // Gate/up tiles of one 32-row block (NMB = 1): suh multiplies the A
+    // fragment, which serves all CM column groups, instead of every B
+    // fragment.  With the mcg codebook B also stays biased (2v + 1532, the
+    // GEMV's form, without the re-centring subtraction), and one more MFMA
+    // per A fragment against a B of ones sums its row into dsum, of which the
+    // epilogue takes off 1532 times.  Tiles of more blocks keep suh on B: an
+    // A fragment there serves one MFMA, a B fragment NMB.
+    template <int NMB>
+    static constexpr bool kSuhA = MODE == GATEUP_TRELLIS && NMB == 1;
+    template <int NMB>
+    static constexpr bool kBiasB = kSuhA<NMB> && CB == CB_MCG;
 
     // Interleave the MFMAs of one fragment with the VALU work scheduled next
     // to them (the decode of the following fragment): one MFMA occupies the
@@ -220,9 +235,10 @@ struct GemmTile {
     // s + 1 and s + 2) proves that the loads of stage s are done.
     template <int NMB, int CM, int SLOT>
     MOE_DEV void stage(int s, int nst, LDS_AS uint16_t *rg, LDS_AS uint16_t *rgp, const BRaw<CM> &bcur,
-                       const BRaw<CM> &bnext, BRaw<CM> &bpf, u32x4 &dk0, f32x16 acc[kMB])
+                       const BRaw<CM> &bnext, BRaw<CM> &bpf, u32x4 &dk0, f32x16 acc[kMB], f32x16 &dsum)
     {
         constexpr int NA = TR::kNA, NB = TR::kNB * CM;
+        constexpr bool SA = kSuhA<NMB>, BB = kBiasB<NMB>;
         __builtin_amdgcn_sched_barrier(0);
         wait_vmcnt<2 * (NA + NB)>();
         __builtin_amdgcn_s_barrier();
@@ -240,17 +256,29 @@ struct GemmTile {
 #pragma unroll
             for (int i = 0; i < NMB; ++i)
                 af[kt][i] = *(const LDS_AS u32x4 *)((const LDS_AS char *)rg + aread[kt] + i * 32 * kBK * 2);
+        if constexpr (SA) {
+#pragma unroll
+            for (int kt = 0; kt < kKT; ++kt)
+                af[kt][0] = __builtin_bit_cast(u32x4, __builtin_bit_cast(f16x8, af[kt][0]) * su[kt]);
+        }
         u32x4 dcur = dk0;
 #pragma unroll
         for (int f = 0; f < kKT * CM; ++f) {
             const int kt = f / CM, cm = f % CM;
             u32x4 b = dcur;
-            if constexpr (MODE == GATEUP_TRELLIS)
+            if constexpr (MODE == GATEUP_TRELLIS && !SA)
                 b = __builtin_bit_cast(u32x4, __builtin_bit_cast(f16x8, dcur) * su[kt]);
             if (f + 1 < kKT * CM)
-                dcur = decode<CM>(bcur, (f + 1) / CM, (f + 1) % CM);
+                dcur = decode<CM, BB>(bcur, (f + 1) / CM, (f + 1) % CM);
             else
-                dcur = decode<CM>(bnext, 0, 0);
+                dcur = decode<CM, BB>(bnext, 0, 0);
+            if constexpr (BB) {
+                if (cm == 0) {
+                    const f16x8 ones = {(f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f,
+                                        (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f};
+                    dsum = mfma_step<MODE>(af[kt][0], __builtin_bit_cast(u32x4, ones), dsum);
+                }
+            }
 #pragma unroll
             for (int i = 0; i < NMB; ++i)
                 acc[cm * NMB + i] = mfma_step<MODE>(af[kt][i], b, acc[cm * NMB + i]);
@@ -262,7 +290,7 @@ struct GemmTile {
 
     template <int NMB, int CM>
     MOE_DEV void run(LDS_AS uint16_t *r0, LDS_AS uint16_t *r1, LDS_AS uint16_t *r2, LDS_AS uint16_t *r3,
-                     f32x16 acc[kMB])
+                     f32x16 acc[kMB], f32x16 &dsum)
     {
         const int nst = Kdim / kBK;   // a multiple of 4
         BRaw<CM> b0, b1, b2, b3;
@@ -272,12 +300,12 @@ struct GemmTile {
         load_b<CM>(1, nst, b1);
         load_a(2, nst, r2);
         load_b<CM>(2, nst, b2);
-        u32x4 dk0 = decode<CM>(b0, 0, 0);
+        u32x4 dk0 = decode<CM, kBiasB<NMB>>(b0, 0, 0);
         for (int s = 0; s < nst; s += 4) {
-            stage<NMB, CM, 0>(s, nst, r0, r3, b0, b1, b3, dk0, acc);
-            stage<NMB, CM, 1>(s + 1, nst, r1, r0, b1, b2, b0, dk0, acc);
-            stage<NMB, CM, 2>(s + 2, nst, r2, r1, b2, b3, b1, dk0, acc);
-            stage<NMB, CM, 3>(s + 3, nst, r3, r2, b3, b0, b2, dk0, acc);
+            stage<NMB, CM, 0>(s, nst, r0, r3, b0, b1, b3, dk0, acc, dsum);
+            stage<NMB, CM, 1>(s + 1, nst, r1, r0, b1, b2, b0, dk0, acc, dsum);
+            stage<NMB, CM, 2>(s + 2, nst, r2, r1, b2, b3, b1, dk0, acc, dsum);
+            stage<NMB, CM, 3>(s + 3, nst, r3, r2, b3, b0, b2, dk0, acc, dsum);
         }
         wait_vmcnt<0>();   // the trailing zero-range loads still write LDS
     }
@@ -445,12 +473,20 @@ MOE_DEV void tile_body(GemmTile<MODE, K, CB> &g, const GemmArgs &args, int n0,
 #pragma unroll
     for (int i = 0; i < kMB; ++i)
         acc[i] = (f32x16){};
+    f32x16 dsum = {};
     if constexpr (TR::kGateUp)
-        g.template run<NMB, CM>(R0, R1, R2, R3, acc);
+        g.template run<NMB, CM>(R0, R1, R2, R3, acc, dsum);
     else
         g.template run_ahead<NMB, CM>(R0, R1, R2, R3, acc);
     __syncthreads();   // every wave is done with the rings (reused below)
 
+    // the biased gate/up accumulators of one-block tiles: 1532 x row sum off
+    auto accv = [&](int b, int r) -> float {
+        if constexpr (GemmTile<MODE, K, CB>::template kBiasB<NMB>)
+            return acc[b][r] - 1532.0f * dsum[r];
+        else
+            return acc[b][r];
+    };
     // ---- epilogue.  Accumulator block b = cm * NMB + i covers rows 32 i + ..
     // of column group cm; its D register r holds row 32i + 8(r/4) + 4h + r%4.
     constexpr int NB = NMB * CM;
@@ -480,7 +516,7 @@ MOE_DEV void tile_body(GemmTile<MODE, K, CB> &g, const GemmArgs &args, int n0,
                                      : f16_to_f32(a.svh[g.pr][(int64_t)e * I + col]) * (1.0f / 128.0f);
 #pragma unroll
                     for (int r = 0; r < 16; ++r)
-                        ex[((b & 3) * 16 + r) * 64 + g.l] = acc[b][r] * sc;
+                        ex[((b & 3) * 16 + r) * 64 + g.l] = accv(b, r) * sc;
                 }
             }
             __syncthreads();
@@ -500,8 +536,8 @@ MOE_DEV void tile_body(GemmTile<MODE, K, CB> &g, const GemmArgs &args, int n0,
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const float other = ex[((b & 3) * 16 + r) * 64 + g.l];
-                        const float gv = g.pr == 0 ? acc[b][r] * sg : other;
-                        const float uv = g.pr == 0 ? other : acc[b][r] * su;
+                        const float gv = g.pr == 0 ? accv(b, r) * sg : other;
+                        const float uv = g.pr == 0 ? other : accv(b, r) * su;
                         hv[r] = silu_f(gv) * uv * sd;
                     }
 #pragma unroll

@@ -553,7 +553,8 @@ int moe_exl3_decode(const uint16_t *codes, int32_t n_in, int32_t n_out, int32_t 
     if (!codes || !dst || n_in <= 0 || n_out <= 0 || n_in % 16 || n_out % 16)
         return MOE_EXL3_ERR_INVALID_ARG;
     if (K < 2 || K > 4 || (codebook != MOE_EXL3_CB_MCG && codebook != MOE_EXL3_CB_MCG_E4M3) ||
-        dst_dtype < MOE_EXL3_DT_F32 || dst_dtype > MOE_EXL3_DT_GEMV_F16)
+        dst_dtype < MOE_EXL3_DT_F32 || dst_dtype > MOE_EXL3_DT_MFMA_BIASED_F16 ||
+        (dst_dtype == MOE_EXL3_DT_MFMA_BIASED_F16 && codebook != MOE_EXL3_CB_MCG))
         return MOE_EXL3_ERR_UNSUPPORTED;
     if (!aligned16(codes) || !aligned16(dst))
         return MOE_EXL3_ERR_MISALIGNED;

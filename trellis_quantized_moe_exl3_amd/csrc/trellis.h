@@ -194,6 +194,21 @@ MOE_DEV f16x8 frag_decode_f16(uint32_t D0, uint32_t D1, int q, uint32_t m_lo, ui
     return out;
 }
 
+// Fragment -> eight fp16 values of 2v + 1532 (mcg codebook; exact integers
+// in [1020, 2044]) at the run-time window width kw when K = 0: the biased
+// form whose bias the MFMA gate/up kernel takes off per row.
+template <int K>
+MOE_DEV f16x8 frag_decode_f16_biased(uint32_t D0, uint32_t D1, int q, uint32_t m_lo, uint32_t m_hi, int kw = K)
+{
+    uint32_t st[8];
+    frag_states_k<K>(D0, D1, q, kw, st);
+    u32x4 pk;
+#pragma unroll
+    for (int t = 0; t < 8; t += 2)
+        pk[t / 2] = value2_pair_biased(st[t], st[t + 1], m_lo, m_hi);
+    return __builtin_bit_cast(f16x8, pk);
+}
+
 // Fragment -> eight exact bf16 values of 2v (or 128 * E4M3(v/64)).
 template <int K, int CB>
 MOE_DEV bf16x8 frag_decode_bf16(uint32_t D0, uint32_t D1, int q, uint32_t m_lo, uint32_t m_hi, int kw = K)
