@@ -969,7 +969,10 @@ hipError_t launch_rotate_x(const uint16_t *x, bool bf16, int64_t T, int H, const
 // weight 1), are summed in fp32 in that fixed order: deterministic.  With
 // sign vectors the sum is rotated back (R, then s1) before the fp16 shared
 // expert's fp32 row is added; then the cast to the activation dtype.  8
-// outputs per thread (16 threads per 128-channel block when rotating).
+// outputs per thread (16 threads per 128-channel block when rotating).  Slot
+// rows and shared rows are read once, with nontemporal loads: the 7168-token
+// layer's combine went 0.121 -> 0.098 ms with them (the rate of a plain
+// streaming read).
 template <bool BF16, bool ROT>
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict__ ybuf,
                                                       const float *__restrict__ sy, int64_t T, int H,
@@ -992,9 +995,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j) {
         if (j < k)
-            v[j] = *(const u32x4 *)(ybuf + (t * k + j) * H + m);
+            v[j] = __builtin_nontemporal_load((const u32x4 *)(ybuf + (t * k + j) * H + m));
         else if (j == k && extra)
-            v[j] = *(const u32x4 *)(ybuf + (T * k + t) * H + m);
+            v[j] = __builtin_nontemporal_load((const u32x4 *)(ybuf + (T * k + t) * H + m));
     }
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j)
@@ -1015,7 +1018,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
         }
     }
     if (sy) {
-        const f32x4 a = *(const f32x4 *)(sy + t * H + m), b = *(const f32x4 *)(sy + t * H + m + 4);
+        const f32x4 a = __builtin_nontemporal_load((const f32x4 *)(sy + t * H + m)),
+                    b = __builtin_nontemporal_load((const f32x4 *)(sy + t * H + m + 4));
         s[0] += a[0]; s[1] += a[1]; s[2] += a[2]; s[3] += a[3];
         s[4] += b[0]; s[5] += b[1]; s[6] += b[2]; s[7] += b[3];
     }
