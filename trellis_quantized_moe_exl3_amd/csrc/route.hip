@@ -207,71 +207,73 @@ __global__ __launch_bounds__(256) void route_logits_pairs_kernel(const uint16_t 
     }
 }
 
-// Many tokens, on the matrix cores.  One wavefront (one block) computes a tile
-// of 16 tokens x 16 experts and holds all 64 partial sums of every pair of it
-// at once: v_mfma_f32_16x16x1_4b_f32 has k = 1, so each instruction adds
+// Many tokens, on the matrix cores.  One block of two wavefronts computes a
+// tile of 16 tokens x 16 experts and holds all 64 partial sums of every pair
+// of it at once: v_mfma_f32_16x16x1_4b_f32 has k = 1, so each instruction adds
 // exactly one product to each of its accumulators, and its four 16x16 blocks
 // carry four of the 64 partial-sum chains.  Instruction q (q = 0..15) of a
 // 64-channel chunk i adds x[64i + l] * w[64i + l] to chains l = q + 16b of
-// block b = 0..3; the lanes of block b supply token (A) and expert (B) rows
-// 0..15 and load channels 64i + 16b .. + 15, 32 contiguous bytes per row.  As
-// in the VALU kernels the product is exact in fp32, so every accumulation
-// step rounds once, the order over i is the plain one, and the halving tree
-// over l runs on the finished chains: chains q, q + 16, q + 32, q + 48 of a
-// (token, expert) pair sit in one lane (block b in registers 4b .. 4b + 3,
-// lane 16 (row / 4) + column, register row % 4), so the whole tree is
-// in-lane adds.  256 accumulator registers: one wavefront per SIMD.
+// block b = 0..3; wavefront h issues instructions q = 8h .. 8h + 7, and the
+// lanes of block b supply token (A) and expert (B) rows 0..15 from channels
+// 64i + 16b + 8h .. + 7, 16 contiguous bytes per row.  As in the VALU kernels
+// the product is exact in fp32, so every accumulation step rounds once, the
+// order over i is the plain one, and the halving tree over l runs on the
+// finished chains: chains q, q + 16, q + 32, q + 48 of a (token, expert) pair
+// sit in one lane of one wavefront (block b in registers 4b .. 4b + 3, lane
+// 16 (row / 4) + column, register row % 4), so the steps d = 32, 16 are
+// in-lane adds, the step d = 8 adds wavefront 1's sums to wavefront 0's
+// through LDS, and d = 4, 2, 1 are in-lane again.  128 accumulator registers
+// per wavefront: two wavefronts per SIMD, which measured 3% faster than one
+// wavefront holding all 16 instructions' chains (256 registers).
 constexpr int kRouteTile = 16;
 constexpr int kRouteSets = 4;
 
+// element q (0..7) of 8 activations packed in 16 bytes, widened to fp32
 template <bool BF16>
-MOE_DEV float act_elem(const u32x4 (&v)[2], int q)
+MOE_DEV float act_elem(const u32x4 &v, int q)
 {
-    const uint32_t d = v[q >> 3][(q >> 1) & 3];
+    const uint32_t d = v[q >> 1];
     if (BF16)
         return __uint_as_float((q & 1) ? (d & 0xFFFF0000u) : (d << 16));
     return f16_to_f32((uint16_t)((q & 1) ? (d >> 16) : (d & 0xFFFFu)));
 }
 
 template <bool BF16>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void route_logits_mfma_kernel(
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) void route_logits_mfma_kernel(
     const uint16_t *__restrict__ x, int64_t T, int H, const uint16_t *__restrict__ Wr,
     const float *__restrict__ bias, int E, float *__restrict__ logits, WsHeader *hdr, int n_tt, int n_et)
 {
+    __shared__ f32x4 xch[8][64];
     clear_status(hdr);
     int tt, et;
     xcd_map((int)blockIdx.x, n_et, tt, et);   // the expert tiles of a token tile share one XCD's L2
     if (tt >= n_tt)
         return;
-    const int l = threadIdx.x, b = l >> 4, c = l & 15;
-    // the tile's token rows and expert rows through two buffer resources whose
-    // range ends at the last token / expert: rows past it load zeros and their
-    // sums are never stored
+    // wavefront h carries instructions q = 8h .. 8h + 7 of every chunk; rows
+    // past the last token / expert load zeros through the buffer ranges and
+    // their sums are never stored
+    const int h = threadIdx.x >> 6, l = threadIdx.x & 63, b = l >> 4, c = l & 15;
     const int64_t t0 = (int64_t)tt * kRouteTile;
     const int e0 = et * kRouteTile;
     const int nt = (int)std::min<int64_t>(kRouteTile, T - t0), ne = std::min(kRouteTile, E - e0);
     const __amdgpu_buffer_rsrc_t xs = buf_rsrc(x + t0 * H, (uint32_t)(nt * H * 2));
     const __amdgpu_buffer_rsrc_t ws = buf_rsrc(Wr + (int64_t)e0 * H, (uint32_t)(ne * H * 2));
-    const uint32_t off = (uint32_t)(c * H + 16 * b) * 2;
-    f32x16 acc[16];
+    const uint32_t off = (uint32_t)(c * H + 16 * b + 8 * h) * 2;
+    f32x16 acc[8];
 #pragma unroll
-    for (int q = 0; q < 16; ++q)
+    for (int q = 0; q < 8; ++q)
         acc[q] = (f32x16){};
-    // Four register sets rotate: the loads of chunk i + 4 go out right after
-    // chunk i's MFMAs and have three chunks' MFMAs (48 x 32 cycles) to land.
-    // Loads past the last chunk fall outside the range and return zeros; they
-    // are never used.  The scheduling barriers keep every load group where it
-    // is written (the compiler would otherwise sink it to its first use).
     const int n = H / 64;   // a multiple of kRouteSets
-    u32x4 xv[kRouteSets][2], wv[kRouteSets][2];
-    // (the chunk offset goes into the per-lane offset, which the range check
-    // covers, so a load past the range returns zeros and touches no memory)
+    // Four register sets rotate: the loads of chunk i + 4 go out right after
+    // chunk i's MFMAs.  Loads past the last chunk fall outside the range and
+    // return zeros (the chunk offset is in the per-lane offset, which the range
+    // check covers); they are never used.  The scheduling barriers keep every
+    // load group where it is written.
+    u32x4 xv[kRouteSets], wv[kRouteSets];
     auto load = [&](int i, int j) {
         const uint32_t o = off + (uint32_t)i * 128u;
-        xv[j][0] = __builtin_amdgcn_raw_buffer_load_b128(xs, o, 0, 0);
-        xv[j][1] = __builtin_amdgcn_raw_buffer_load_b128(xs, o + 16, 0, 0);
-        wv[j][0] = __builtin_amdgcn_raw_buffer_load_b128(ws, o, 0, 0);
-        wv[j][1] = __builtin_amdgcn_raw_buffer_load_b128(ws, o + 16, 0, 0);
+        xv[j] = __builtin_amdgcn_raw_buffer_load_b128(xs, o, 0, 0);
+        wv[j] = __builtin_amdgcn_raw_buffer_load_b128(ws, o, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
     };
 #pragma unroll
@@ -281,8 +283,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 #pragma unroll
         for (int j = 0; j < kRouteSets; ++j) {
 #pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                const uint32_t d = wv[j][q >> 3][(q >> 1) & 3];
+            for (int q = 0; q < 8; ++q) {
+                const uint32_t d = wv[j][q >> 1];
                 const float wq = f16_to_f32((uint16_t)((q & 1) ? (d >> 16) : (d & 0xFFFFu)));
                 acc[q] = __builtin_amdgcn_mfma_f32_16x16x1f32(act_elem<BF16>(xv[j], q), wq, acc[q], 0, 0, 0);
             }
@@ -290,16 +292,25 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
             load(i + kRouteSets + j, j);
         }
     }
-    // tree: d = 32 (blocks 0 + 2, 1 + 3), d = 16 (their sums), then d = 8 .. 1
-    // over q
-    f32x4 u[16];
+    f32x4 u[8];
 #pragma unroll
-    for (int q = 0; q < 16; ++q)
+    for (int q = 0; q < 8; ++q)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             u[q][r] = (acc[q][r] + acc[q][8 + r]) + (acc[q][4 + r] + acc[q][12 + r]);
+    if (h == 1) {
 #pragma unroll
-    for (int d = 8; d >= 1; d >>= 1)
+        for (int q = 0; q < 8; ++q)
+            xch[q][l] = u[q];
+    }
+    __syncthreads();
+    if (h == 1)
+        return;
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+        u[q] = u[q] + xch[q][l];
+#pragma unroll
+    for (int d = 4; d >= 1; d >>= 1)
 #pragma unroll
         for (int q = 0; q < d; ++q)
             u[q] = u[q] + u[q + d];
@@ -335,9 +346,9 @@ hipError_t launch_route_logits(const uint16_t *x, bool bf16, int64_t T, int H, c
         const int n_tt = (int)((T + kRouteTile - 1) / kRouteTile), n_et = (E + kRouteTile - 1) / kRouteTile;
         const unsigned grid = (unsigned)(((n_tt + 7) / 8) * 8 * n_et);
         if (bf16)
-            route_logits_mfma_kernel<true><<<grid, 64, 0, s>>>(x, T, H, Wr, bias, E, logits, hdr, n_tt, n_et);
+            route_logits_mfma_kernel<true><<<grid, 128, 0, s>>>(x, T, H, Wr, bias, E, logits, hdr, n_tt, n_et);
         else
-            route_logits_mfma_kernel<false><<<grid, 64, 0, s>>>(x, T, H, Wr, bias, E, logits, hdr, n_tt, n_et);
+            route_logits_mfma_kernel<false><<<grid, 128, 0, s>>>(x, T, H, Wr, bias, E, logits, hdr, n_tt, n_et);
     } else if (T > 64) {
         if (bf16) route_launch<true, 2, 4, 4>(x, T, H, Wr, bias, E, logits, hdr, s);
         else route_launch<false, 2, 4, 4>(x, T, H, Wr, bias, E, logits, hdr, s);
