@@ -5,9 +5,9 @@
 // per-lane window loads with a deep prefetch).
 //
 // Each lane decodes eight consecutive input rows of one output column from
-// two code dwords into packed fp16 pairs for v_dot2_f32_f16, so a wavefront
-// streams a pair of 16-column tiles and every output column stays in one
-// lane.  The code stream is read once per pass of up to two routed rows (once
+// two code dwords into packed fp16 pairs, which are its B operand of one
+// v_mfma_f32_32x32x16_f16 per tile row, so a wavefront streams a pair of
+// 16-column tiles and every output column stays in one lane.  The code stream is read once per pass of up to two routed rows (once
 // per expert at the default split); it is the only large HBM traffic of a
 // decode-sized step.  The dense shared expert's decode-sized GEMV lives here
 // too, as blocks of its own launches or of the routed ones.
@@ -22,6 +22,7 @@ namespace moe {
 
 constexpr int kGemvU = 4;      // tile rows per prefetch group
 constexpr int kGemvPass = 2;   // routed rows per pass over the codes
+constexpr int kNontemporal = 2;   // buffer-load cache policy: the nt bit
 
 // 1532 * (row sum), the re-centring of the biased decoded values.
 constexpr float kBias2 = 1532.0f;
@@ -53,83 +54,16 @@ MOE_DEV void block_reduce256(float v[N], float (*part)[4])
 }
 
 // Stream tile rows [tk0, tk1) of the lane's fragment and accumulate
-// x . (2v + 1532) for NR routed rows.  The codes come in through a buffer
+// x . (2v + 1532) on the matrix cores.  The codes come in through a buffer
 // resource over the wavefront's 16-column tile pair: the lane's two dwords
 // sit at fixed byte offsets v0, v1 inside a tile row and the tile row at a
 // scalar offset, so a load costs no vector address arithmetic.  Two register
 // sets of kGemvU tile rows alternate, one decoding while the other fills.
-// DOT(r, kk, wp, acc) adds the lane's 8 products of row r at input rows
-// kk + 8h .. kk + 8h + 7.
-template <int K, int CB, int NR, class DOT>
-MOE_DEV void gemv_stream(__amdgpu_buffer_rsrc_t rs, uint32_t v0, uint32_t v1, uint32_t rowb, int tk0, int tk1,
-                         int q, uint32_t m_lo, uint32_t m_hi, DOT dot, float acc[NR])
-{
-    uint32_t A[kGemvU][2], B[kGemvU][2];
-    auto load = [&](uint32_t(&buf)[kGemvU][2], int g) {
-#pragma unroll
-        for (int u = 0; u < kGemvU; ++u) {
-            const int so = (g + u) * (int)rowb;
-            buf[u][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, v0, so, 0);
-            buf[u][1] = __builtin_amdgcn_raw_buffer_load_b32(rs, v1, so, 0);
-        }
-    };
-    auto run = [&](const uint32_t(&buf)[kGemvU][2], int g) {
-#pragma unroll
-        for (int u = 0; u < kGemvU; ++u) {
-            f16x2 wp[4];
-            frag_biased_pairs<K, CB>(buf[u][0], buf[u][1], q, m_lo, m_hi, wp);
-            const int kk = 16 * (g + u);
-#pragma unroll
-            for (int r = 0; r < NR; ++r)
-                acc[r] = dot(r, kk, wp, acc[r]);
-        }
-    };
-    // tk0, tk1 are wavefront-uniform: every branch below is scalar.
-    // tk1 - tk0 is a positive multiple of kGemvU (an even one for every
-    // shape the library accepts, so the single-group tail below is kept only
-    // for generality).  Every load is issued
-    // unconditionally: a group past the wave's range reloads its last group
-    // (in range, just read, never used), so no load sits behind a branch and
-    // the two register sets need no copies to merge loaded and kept values.
-    const int glast = tk1 - kGemvU;
-    int g = tk0;
-    load(A, g);
-    load(B, min(g + kGemvU, glast));
-    for (; g + 2 * kGemvU <= tk1; g += 2 * kGemvU) {
-        run(A, g);
-        load(A, min(g + 2 * kGemvU, glast));
-        run(B, g + kGemvU);
-        load(B, min(g + 3 * kGemvU, glast));
-    }
-    if (g < tk1)
-        run(A, g);
-}
-
-// gemv_stream at the tensor's width: K > 0 fixes it at compile time; K = 0
-// (per-tensor widths) dispatches on the wavefront-uniform run-time width kw.
-// No barrier lies inside, so wavefronts of one block may take different
-// widths.
-template <int K, int CB, int NR, class DOT>
-MOE_DEV void gemv_stream_k(int kw, __amdgpu_buffer_rsrc_t rs, uint32_t v0, uint32_t v1, uint32_t rowb, int tk0,
-                           int tk1, int q, uint32_t m_lo, uint32_t m_hi, DOT dot, float acc[NR])
-{
-    if constexpr (K > 0) {
-        gemv_stream<K, CB, NR>(rs, v0, v1, rowb, tk0, tk1, q, m_lo, m_hi, dot, acc);
-    } else {
-        if (kw == 4)
-            gemv_stream<4, CB, NR>(rs, v0, v1, rowb, tk0, tk1, q, m_lo, m_hi, dot, acc);
-        else if (kw == 3)
-            gemv_stream<3, CB, NR>(rs, v0, v1, rowb, tk0, tk1, q, m_lo, m_hi, dot, acc);
-        else
-            gemv_stream<2, CB, NR>(rs, v0, v1, rowb, tk0, tk1, q, m_lo, m_hi, dot, acc);
-    }
-}
-
-// The same stream with the dot products on the matrix cores: the lane's
-// fragment (eight input rows kk + 8h .. + 7 of column 16 ts + c) is exactly
-// its B operand of v_mfma_f32_32x32x16_f16 (column l % 32, k-half l / 32),
-// and its A operand is the same eight inputs of activation row l % 32, read
-// from LDS at arow + kk (arow: the lane's row, already offset by 8h).  Rows
+// The lane's fragment (eight input rows kk + 8h .. + 7 of column 16 ts + c) is
+// exactly its B operand of v_mfma_f32_32x32x16_f16 (column l % 32, k-half
+// l / 32), and its A operand is the same eight inputs of activation row
+// l % 32, read from LDS at arow + kk (arow: the lane's row, already offset by
+// 8h).  Rows
 // past the pass's routed rows carry any in-range data: their output rows are
 // never read.  The accumulator d holds, in lanes 0..31, the column's sum for
 // activation row r in register r (r < 4); the MFMA adds both k-halves.
@@ -137,13 +71,16 @@ template <int K, int CB>
 MOE_DEV void gemv_stream_mfma(__amdgpu_buffer_rsrc_t rs, uint32_t v0, uint32_t v1, uint32_t rowb, int tk0, int tk1,
                               int q, uint32_t m_lo, uint32_t m_hi, const f16 *arow, f32x16 &d)
 {
+    // The code stream is read once per pass and never again in the call:
+    // the loads carry the nontemporal hint (cache policy 2), which measured
+    // 1% (K = 2) and 2% (K = 4) off the 8-token layer.
     uint32_t A[kGemvU][2], B[kGemvU][2];
     auto load = [&](uint32_t(&buf)[kGemvU][2], int g) {
 #pragma unroll
         for (int u = 0; u < kGemvU; ++u) {
             const int so = (g + u) * (int)rowb;
-            buf[u][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, v0, so, 0);
-            buf[u][1] = __builtin_amdgcn_raw_buffer_load_b32(rs, v1, so, 0);
+            buf[u][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, v0, so, kNontemporal);
+            buf[u][1] = __builtin_amdgcn_raw_buffer_load_b32(rs, v1, so, kNontemporal);
         }
     };
     auto run = [&](const uint32_t(&buf)[kGemvU][2], int g) {
@@ -155,8 +92,13 @@ MOE_DEV void gemv_stream_mfma(__amdgpu_buffer_rsrc_t rs, uint32_t v0, uint32_t v
             d = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, __builtin_bit_cast(f16x8, wp), d, 0, 0, 0);
         }
     };
-    // as in gemv_stream: every load unconditional, the last group reloaded
-    // past the wave's range
+    // tk0, tk1 are wavefront-uniform: every branch below is scalar.
+    // tk1 - tk0 is a positive multiple of kGemvU (an even one for every
+    // shape the library accepts, so the single-group tail below is kept only
+    // for generality).  Every load is issued unconditionally: a group past
+    // the wave's range reloads its last group (in range, just read, never
+    // used), so no load sits behind a branch and the two register sets need
+    // no copies to merge loaded and kept values.
     const int glast = tk1 - kGemvU;
     int g = tk0;
     load(A, g);
@@ -398,7 +340,7 @@ MOE_DEV bool shared_in_gemv(const GroupArgs &a, const SharedArgs &sa, int max_li
 // for both projections; wavefront w = 2p + j streams projection p, over
 // input half j (one tile pair) or over all inputs for tile pair j (two).
 // Rows are processed kGemvPass at a time: x * suh of the pass's rows in LDS
-// (fp16, both projections), one v_dot2_f32_f16 per pair of weights and row.
+// (fp16, both projections), one MFMA per tile row for all of the pass's rows.
 // The partial sums of the two halves meet in LDS and are added in a fixed
 // order.
 // Two tile pairs per block measured faster than one (longer streams per
@@ -504,8 +446,8 @@ __global__ __launch_bounds__(256, 4) void gemv_gateup_kernel(GroupArgs a, int ma
 // streams range w / kDownCP of tile pair w % kDownCP.  The pass's h rows sit
 // in LDS as fp16, each scaled by a power of two that brings its largest
 // magnitude into [2^14, 2^15): every bf16 value within 2^28 of the row
-// maximum converts exactly, so one v_dot2_f32_f16 per pair of weights and
-// row serves here as in gate/up, and the scale comes off the finished sum.
+// maximum converts exactly, so the fp16 MFMA serves here as in gate/up, and
+// the scale comes off the finished sum.
 // Range sums meet in LDS and are added in a fixed order.
 // Four tile pairs per block (each wavefront streams every input row of its
 // pair) measured faster than one or two.

@@ -256,8 +256,8 @@ MOE_DEV u32x2 frag_decode_fp8(uint32_t D0, uint32_t D1, int q, uint32_t m_lo, ui
 }
 
 // Fragment -> the eight decoded values as fp16 pairs of 2v + 1532 (exact:
-// integers in [1020, 2044]), the operand of the decode-fused GEMV's
-// v_dot2_f32_f16 (which subtracts 1532 * sum(x) once per output).  mcg: the
+// integers in [1020, 2044]), the B operand of the decode-fused GEMV's MFMA
+// (which subtracts 1532 * sum(x) once per output).  mcg: the
 // biased pair straight from the field sums; E4M3: 128 * c8 + 1532 (128 * c8
 // is an even integer: E4M3 keeps 4 significant bits of the integer v).
 template <int K, int CB>
