@@ -95,6 +95,9 @@ class Hip:
         self.l.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
         self.l.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
         self.l.hipEventDestroy.argtypes = [C.c_void_p]
+        # events and streams are pointers: without the declaration ctypes
+        # would pass the handles as 32-bit ints
+        self.l.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
 
     def event(self):
         e = C.c_void_p()
@@ -208,7 +211,6 @@ def time_layer(desc, weights_list, x, steps, warmup, hip):
     ws = torch.empty(M.workspace_size(desc, x.shape[0]), dtype=torch.uint8, device="cuda")
     nw = len(weights_list)
     stream = torch.cuda.current_stream().cuda_stream
-    hip.l.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
     for i in range(warmup):
         M.layer(desc, weights_list[i % nw], x, out, ws)
     a, b = hip.event(), hip.event()

@@ -121,3 +121,18 @@ def test_route_and_decode_argument_checks():
     assert l.moe_exl3_decode(0x1000, 48, 64, 2, 1, 0, 0x2000, 9, None) == M.ERR_UNSUPPORTED
     # the one-block MFMA operand mode exists for the mcg codebook only
     assert l.moe_exl3_decode(0x1000, 48, 64, 2, 1, 1, 0x2000, M.DT_MFMA_BIASED_F16, None) == M.ERR_UNSUPPORTED
+
+
+def test_bench_event_helper_declares_pointer_arguments():
+    # the benchmark's HIP event calls take event and stream handles; without
+    # declared argument types ctypes passes a Python int as a 32-bit C int,
+    # which truncates the handles (a graph-timing call made before any eager
+    # timing call crashed that way)
+    import bench
+    try:
+        hip = bench.Hip()
+    except OSError:
+        pytest.skip("HIP runtime library not loadable here")
+    assert hip.l.hipEventRecord.argtypes == [C.c_void_p, C.c_void_p]
+    assert hip.l.hipEventElapsedTime.argtypes == [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+    assert hip.l.hipEventDestroy.argtypes == [C.c_void_p]

@@ -128,6 +128,30 @@ def test_decode_step_code_widths(K, codebook):
     assert np.isfinite(out).all() and np.isfinite(out_r).all()
 
 
+@pytest.mark.parametrize("T", [1, 2, 3, 4])
+@pytest.mark.parametrize("name,K,codebook", [("decode", 2, W.CB_MCG), ("decode", 4, W.CB_MCG_E4M3),
+                                             ("mixed_k34", None, None)])
+def test_verify_batch_sizes(name, K, codebook, T):
+    # 1-4 tokens at the real shapes (the verify batches of speculative
+    # decoding): so few experts that the GEMV launches split each expert's
+    # columns into narrower blocks and its input rows into ranges, to fill
+    # the GPU; every token checked, routed-only and with the shared expert
+    cfg = W.BY_NAME[name].replace(tokens=T)
+    if K is not None:
+        cfg = cfg.replace(K=K, codebook=codebook)
+    inp = W.gen_layer(cfg)
+    routed = _routed_only(inp)
+    out_r = DevLayer(routed).run()
+    _, _, ref_r = oracle.layer(routed)
+    out = DevLayer(inp).run()
+    _, _, ref = oracle.layer(inp)
+    err_r, err = rel_err(out_r, ref_r), rel_err(out, ref)
+    print(f"verify batch {name} T={T} K={cfg.K} cb={cfg.codebook} routed err={err_r:.3e} full err={err:.3e}")
+    record(f"verify batch {name} T={T} K={cfg.K} cb={cfg.codebook} routed", err_r, TOL)
+    assert err_r <= TOL and err <= TOL
+    assert np.isfinite(out).all() and np.isfinite(out_r).all()
+
+
 def routing_sample(dl, gemv_rows=2, n_min=64, seed=0):
     """Tokens chosen from the layer's own segment tables so that the sample
     reaches every kernel path: the first and last token; in the heaviest
