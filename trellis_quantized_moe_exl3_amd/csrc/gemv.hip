@@ -12,6 +12,7 @@
 // decode-sized step.  The dense shared expert's decode-sized GEMV lives here
 // too, as blocks of its own launches or of the routed ones.
 #include <algorithm>
+#include <initializer_list>
 
 #include "common.h"
 #include "gemm.h"
@@ -336,23 +337,20 @@ MOE_DEV bool shared_in_gemv(const GroupArgs &a, const SharedArgs &sa, int max_li
     return true;
 }
 
-// gate/up + SwiGLU.  Block = kGuCP pairs of 16-column tiles of one expert
-// for both projections; wavefront w = 2p + j streams projection p, over
-// input half j (one tile pair) or over all inputs for tile pair j (two).
+// gate/up + SwiGLU.  Block = CP pairs of 16-column tiles of one expert for
+// both projections; wavefront w = 2p + j streams projection p, over input
+// half j (CP = 1: one tile pair) or over all inputs for tile pair j (CP = 2).
 // Rows are processed kGemvPass at a time: x * suh of the pass's rows in LDS
 // (fp16, both projections), one MFMA per tile row for all of the pass's rows.
 // The partial sums of the two halves meet in LDS and are added in a fixed
-// order.
-// Two tile pairs per block measured faster than one (longer streams per
-// wavefront amortise the staging of x * suh).
-constexpr int kGuCP = 2;
-constexpr int kGuCols = 32 * kGuCP;
-constexpr int kGuKH = 2 / kGuCP;
-static_assert(kGuCP == 1 || kGuCP == 2, "gate/up tile pairs per block");
-
-template <int K, int CB>
+// order.  The launch takes CP = 2 (longer streams per wavefront amortise the
+// staging of x * suh) unless that leaves fewer routed blocks than the GPU
+// holds at once; then CP = 1 doubles the blocks.
+template <int K, int CB, int CP>
 __global__ __launch_bounds__(256, 4) void gemv_gateup_kernel(GroupArgs a, int max_list, SharedArgs sa)
 {
+    static_assert(CP == 1 || CP == 2, "gate/up tile pairs per block");
+    constexpr int kGuCols = 32 * CP, kGuKH = 2 / CP;
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ float part[2 * kGemvPass][4];
     __shared__ float rsum[2][kGemvPass];
@@ -372,7 +370,7 @@ __global__ __launch_bounds__(256, 4) void gemv_gateup_kernel(GroupArgs a, int ma
     f16 *xs = (f16 *)smem;   // [2][kGemvPass][H]
 
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
-    const int pr = w >> 1, kh = kGuKH == 2 ? (w & 1) : 0, cp = kGuCP == 2 ? (w & 1) : 0;
+    const int pr = w >> 1, kh = kGuKH == 2 ? (w & 1) : 0, cp = CP == 2 ? (w & 1) : 0;
     const int c = l & 15, ts = (l >> 4) & 1, h = l >> 5;
     // the block's tile pair in every tile row of expert e's projection pr
     const TensorCodes tcs = tensor_codes<K>(a, pr, e, H, I);
@@ -440,24 +438,24 @@ __global__ __launch_bounds__(256, 4) void gemv_gateup_kernel(GroupArgs a, int ma
     }
 }
 
-// down + routing weight.  Block = kDownCP pairs of 16-column tiles of one
-// expert; the input rows are split into S = 4 / kDownCP (fewer for small
-// inter sizes) ranges of a multiple of kGemvU tile rows, and wavefront w
-// streams range w / kDownCP of tile pair w % kDownCP.  The pass's h rows sit
+// down + routing weight.  Block = CP pairs of 16-column tiles of one
+// expert; the input rows are split into S = 4 / CP (fewer for small inter
+// sizes) ranges of a multiple of kGemvU tile rows, and wavefront w streams
+// range w / CP of tile pair w % CP.  The pass's h rows sit
 // in LDS as fp16, each scaled by a power of two that brings its largest
 // magnitude into [2^14, 2^15): every bf16 value within 2^28 of the row
 // maximum converts exactly, so the fp16 MFMA serves here as in gate/up, and
 // the scale comes off the finished sum.
-// Range sums meet in LDS and are added in a fixed order.
-// Four tile pairs per block (each wavefront streams every input row of its
-// pair) measured faster than one or two.
-constexpr int kDownCP = 4;
-constexpr int kDownCols = 32 * kDownCP;
-constexpr int kDownS = 4 / kDownCP;
-
-template <int K, int CB>
+// Range sums meet in LDS and are added in a fixed order.  The launch takes
+// CP = 4 (each wavefront streams every input row of its pair; faster than
+// one or two when the grid fills the GPU) unless that leaves fewer routed
+// blocks than the GPU holds at once; then the smallest CP (2 or 1) that
+// fills it, or 1.
+template <int K, int CB, int CP>
 __global__ __launch_bounds__(256, 4) void gemv_down_kernel(GroupArgs a, int max_list, SharedArgs sa)
 {
+    static_assert(CP == 1 || CP == 2 || CP == 4, "down tile pairs per block");
+    constexpr int kDownCP = CP, kDownCols = 32 * CP, kDownS = 4 / CP;
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ float part[2 * kGemvPass][4];
     __shared__ float rsum[kGemvPass];
@@ -584,22 +582,80 @@ static size_t shared_lds_of(const SharedArgs *sh, int64_t T)
     return sh ? sizeof(f16) * tt * kShSlab : 0;
 }
 
+// Blocks of 256 threads the GPU holds at once at four wavefronts per SIMD.
+constexpr int kResidentBlocks = 1024;
+
+template <int K, int CB, int CP>
+struct GateupKernel {
+    static void go(dim3 grid, size_t lds, hipStream_t s, const GroupArgs &a, int max_list, const SharedArgs &sa)
+    {
+        gemv_gateup_kernel<K, CB, CP><<<grid, 256, lds, s>>>(a, max_list, sa);
+    }
+};
+template <int K, int CB, int CP>
+struct DownKernel {
+    static void go(dim3 grid, size_t lds, hipStream_t s, const GroupArgs &a, int max_list, const SharedArgs &sa)
+    {
+        gemv_down_kernel<K, CB, CP><<<grid, 256, lds, s>>>(a, max_list, sa);
+    }
+};
+
+// the kernel instance for the call's width and codebook
+template <template <int, int, int> class KERNEL, int CP>
+static void gemv_dispatch(dim3 grid, size_t lds, hipStream_t s, const GroupArgs &a, int max_list,
+                          const SharedArgs &sa)
+{
+    if (a.code_tab && a.cb == 0) KERNEL<0, 0, CP>::go(grid, lds, s, a, max_list, sa);
+    else if (a.code_tab) KERNEL<0, 1, CP>::go(grid, lds, s, a, max_list, sa);
+    else if (a.K == 2 && a.cb == 0) KERNEL<2, 0, CP>::go(grid, lds, s, a, max_list, sa);
+    else if (a.K == 3 && a.cb == 0) KERNEL<3, 0, CP>::go(grid, lds, s, a, max_list, sa);
+    else if (a.K == 4 && a.cb == 0) KERNEL<4, 0, CP>::go(grid, lds, s, a, max_list, sa);
+    else if (a.K == 2) KERNEL<2, 1, CP>::go(grid, lds, s, a, max_list, sa);
+    else if (a.K == 3) KERNEL<3, 1, CP>::go(grid, lds, s, a, max_list, sa);
+    else KERNEL<4, 1, CP>::go(grid, lds, s, a, max_list, sa);
+}
+
+// Tile pairs per block: the largest of `cps` (descending) whose routed grid
+// of max_list experts fills the resident blocks, else the smallest.
+static int gemv_cp(int max_list, int ncols, std::initializer_list<int> cps)
+{
+    int cp = 1;
+    for (int c : cps) {
+        cp = c;
+        if ((int64_t)max_list * (ncols / (32 * c)) >= kResidentBlocks)
+            break;
+    }
+    return cp;
+}
+
+template <int CP>
+static void gateup_cp(const GroupArgs &a, int max_list, const SharedArgs *sh, hipStream_t s)
+{
+    // I % 128 == 0: whole blocks of 4 shared rows
+    const unsigned nx = (unsigned)(a.I / (32 * CP));
+    dim3 grid(nx, max_list + shared_rows_of(sh, a.I, (int)nx));
+    const size_t lds = std::max(sizeof(f16) * 2 * kGemvPass * a.H, shared_lds_of(sh, a.T));
+    gemv_dispatch<GateupKernel, CP>(grid, lds, s, a, max_list, sh ? *sh : SharedArgs{});
+}
+
+template <int CP>
+static void down_cp(const GroupArgs &a, int max_list, const SharedArgs *sh, hipStream_t s)
+{
+    // H % 256 == 0: whole blocks of 4 shared rows
+    const unsigned nx = (unsigned)(a.H / (32 * CP));
+    dim3 grid(nx, max_list + shared_rows_of(sh, a.H, (int)nx));
+    const size_t lds = std::max(sizeof(f16) * kGemvPass * a.I, shared_lds_of(sh, a.T));
+    gemv_dispatch<DownKernel, CP>(grid, lds, s, a, max_list, sh ? *sh : SharedArgs{});
+}
+
 hipError_t launch_gemv_gateup(const GroupArgs &a, int max_list, const SharedArgs *sh, hipStream_t s)
 {
     if (max_list <= 0)
         return hipSuccess;
-    // I % 128 == 0: whole blocks of 4 shared rows
-    dim3 grid(a.I / kGuCols, max_list + shared_rows_of(sh, a.I, a.I / kGuCols));
-    const size_t lds = std::max(sizeof(f16) * 2 * kGemvPass * a.H, shared_lds_of(sh, a.T));
-    const SharedArgs sa = sh ? *sh : SharedArgs{};
-    if (a.code_tab && a.cb == 0) gemv_gateup_kernel<0, 0><<<grid, 256, lds, s>>>(a, max_list, sa);
-    else if (a.code_tab) gemv_gateup_kernel<0, 1><<<grid, 256, lds, s>>>(a, max_list, sa);
-    else if (a.K == 2 && a.cb == 0) gemv_gateup_kernel<2, 0><<<grid, 256, lds, s>>>(a, max_list, sa);
-    else if (a.K == 3 && a.cb == 0) gemv_gateup_kernel<3, 0><<<grid, 256, lds, s>>>(a, max_list, sa);
-    else if (a.K == 4 && a.cb == 0) gemv_gateup_kernel<4, 0><<<grid, 256, lds, s>>>(a, max_list, sa);
-    else if (a.K == 2) gemv_gateup_kernel<2, 1><<<grid, 256, lds, s>>>(a, max_list, sa);
-    else if (a.K == 3) gemv_gateup_kernel<3, 1><<<grid, 256, lds, s>>>(a, max_list, sa);
-    else gemv_gateup_kernel<4, 1><<<grid, 256, lds, s>>>(a, max_list, sa);
+    if (gemv_cp(max_list, a.I, {2, 1}) == 2)
+        gateup_cp<2>(a, max_list, sh, s);
+    else
+        gateup_cp<1>(a, max_list, sh, s);
     return hipGetLastError();
 }
 
@@ -607,18 +663,13 @@ hipError_t launch_gemv_down(const GroupArgs &a, int max_list, const SharedArgs *
 {
     if (max_list <= 0)
         return hipSuccess;
-    // H % 256 == 0: whole blocks of 4 shared rows
-    dim3 grid(a.H / kDownCols, max_list + shared_rows_of(sh, a.H, a.H / kDownCols));
-    const size_t lds = std::max(sizeof(f16) * kGemvPass * a.I, shared_lds_of(sh, a.T));
-    const SharedArgs sa = sh ? *sh : SharedArgs{};
-    if (a.code_tab && a.cb == 0) gemv_down_kernel<0, 0><<<grid, 256, lds, s>>>(a, max_list, sa);
-    else if (a.code_tab) gemv_down_kernel<0, 1><<<grid, 256, lds, s>>>(a, max_list, sa);
-    else if (a.K == 2 && a.cb == 0) gemv_down_kernel<2, 0><<<grid, 256, lds, s>>>(a, max_list, sa);
-    else if (a.K == 3 && a.cb == 0) gemv_down_kernel<3, 0><<<grid, 256, lds, s>>>(a, max_list, sa);
-    else if (a.K == 4 && a.cb == 0) gemv_down_kernel<4, 0><<<grid, 256, lds, s>>>(a, max_list, sa);
-    else if (a.K == 2) gemv_down_kernel<2, 1><<<grid, 256, lds, s>>>(a, max_list, sa);
-    else if (a.K == 3) gemv_down_kernel<3, 1><<<grid, 256, lds, s>>>(a, max_list, sa);
-    else gemv_down_kernel<4, 1><<<grid, 256, lds, s>>>(a, max_list, sa);
+    const int cp = gemv_cp(max_list, a.H, {4, 2, 1});
+    if (cp == 4)
+        down_cp<4>(a, max_list, sh, s);
+    else if (cp == 2)
+        down_cp<2>(a, max_list, sh, s);
+    else
+        down_cp<1>(a, max_list, sh, s);
     return hipGetLastError();
 }
 
