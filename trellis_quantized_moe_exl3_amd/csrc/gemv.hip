@@ -23,10 +23,19 @@ namespace moe {
 
 constexpr int kGemvU = 4;      // tile rows per prefetch group
 constexpr int kGemvPass = 2;   // routed rows per pass over the codes
+constexpr int kStageIt = 2;    // 16-byte pieces per thread and row in one staging round
 constexpr int kNontemporal = 2;   // buffer-load cache policy: the nt bit
 
 // 1532 * (row sum), the re-centring of the biased decoded values.
 constexpr float kBias2 = 1532.0f;
+
+// A wavefront-uniform value of a routing table an earlier launch wrote, read
+// through the scalar cache (the tables are read-only here): its wait does
+// not hold up the vector loads in flight, as a vector load's would.
+MOE_DEV int32_t ld_uniform(const int32_t *p)
+{
+    return *(const __attribute__((address_space(4))) int32_t *)p;
+}
 
 // Deterministic block reduction (256 threads) of N floats per thread, all
 // in one pair of barriers: entry i is summed, or maximised where bit i of
@@ -54,36 +63,57 @@ MOE_DEV void block_reduce256(float v[N], float (*part)[4])
                                      : ((part[i][0] + part[i][1]) + part[i][2]) + part[i][3];
 }
 
-// Stream tile rows [tk0, tk1) of the lane's fragment and accumulate
-// x . (2v + 1532) on the matrix cores.  The codes come in through a buffer
-// resource over the wavefront's 16-column tile pair: the lane's two dwords
-// sit at fixed byte offsets v0, v1 inside a tile row and the tile row at a
-// scalar offset, so a load costs no vector address arithmetic.  Two register
-// sets of kGemvU tile rows alternate, one decoding while the other fills.
-// The lane's fragment (eight input rows kk + 8h .. + 7 of column 16 ts + c) is
-// exactly its B operand of v_mfma_f32_32x32x16_f16 (column l % 32, k-half
-// l / 32), and its A operand is the same eight inputs of activation row
-// l % 32, read from LDS at arow + kk (arow: the lane's row, already offset by
-// 8h).  Rows
-// past the pass's routed rows carry any in-range data: their output rows are
-// never read.  The accumulator d holds, in lanes 0..31, the column's sum for
-// activation row r in register r (r < 4); the MFMA adds both k-halves.
-template <int K, int CB>
-MOE_DEV void gemv_stream_mfma(__amdgpu_buffer_rsrc_t rs, uint32_t v0, uint32_t v1, uint32_t rowb, int tk0, int tk1,
-                              int q, uint32_t m_lo, uint32_t m_hi, const f16 *arow, f32x16 &d)
-{
-    // The code stream is read once per pass and never again in the call:
-    // the loads carry the nontemporal hint (cache policy 2), which measured
-    // 1% (K = 2) and 2% (K = 4) off the 8-token layer.
+// The code stream of one wavefront: tile rows [tk0, tk1) of the lane's
+// fragment, through a buffer resource over the wavefront's 16-column tile
+// pair: the lane's two dwords sit at fixed byte offsets v0, v1 inside a tile
+// row and the tile row at a scalar offset, so a load costs no vector address
+// arithmetic.  Two register sets of kGemvU tile rows alternate, one decoding
+// while the other fills.  The loads do not depend on the width, so the first
+// two groups can go out (prime) as soon as the expert is known, ahead of the
+// staging of the pass's activations.  The stream is read once per pass and
+// never again in the call: the loads carry the nontemporal hint (cache
+// policy 2), which measured 1% (K = 2) and 2% (K = 4) off the 8-token layer.
+struct GemvCodes {
+    __amdgpu_buffer_rsrc_t rs;
+    uint32_t v0, v1, rowb;
+    int tk0, tk1;
     uint32_t A[kGemvU][2], B[kGemvU][2];
-    auto load = [&](uint32_t(&buf)[kGemvU][2], int g) {
+
+    MOE_DEV void load(uint32_t (&buf)[kGemvU][2], int g)
+    {
 #pragma unroll
         for (int u = 0; u < kGemvU; ++u) {
             const int so = (g + u) * (int)rowb;
             buf[u][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, v0, so, kNontemporal);
             buf[u][1] = __builtin_amdgcn_raw_buffer_load_b32(rs, v1, so, kNontemporal);
         }
-    };
+    }
+    // tk0, tk1 are wavefront-uniform: every branch of the stream is scalar.
+    // tk1 - tk0 is a positive multiple of kGemvU (an even one for every
+    // shape the library accepts, so the single-group tail is kept only for
+    // generality).  Every load is issued unconditionally: a group past the
+    // wave's range reloads its last group (in range, just read, never used),
+    // so no load sits behind a branch and the two register sets need no
+    // copies to merge loaded and kept values.
+    MOE_DEV void prime()
+    {
+        load(A, tk0);
+        load(B, min(tk0 + kGemvU, tk1 - kGemvU));
+    }
+};
+
+// Accumulate x . (2v + 1532) of the primed stream on the matrix cores.  The
+// lane's fragment (eight input rows kk + 8h .. + 7 of column 16 ts + c) is
+// exactly its B operand of v_mfma_f32_32x32x16_f16 (column l % 32, k-half
+// l / 32), and its A operand is the same eight inputs of activation row
+// l % 32, read from LDS at arow + kk (arow: the lane's row, already offset by
+// 8h).  Rows past the pass's routed rows carry any in-range data: their
+// output rows are never read.  The accumulator d holds, in lanes 0..31, the
+// column's sum for activation row r in register r (r < 4); the MFMA adds both
+// k-halves.
+template <int K, int CB>
+MOE_DEV void gemv_stream_mfma(GemvCodes &cs, int q, uint32_t m_lo, uint32_t m_hi, const f16 *arow, f32x16 &d)
+{
     auto run = [&](const uint32_t(&buf)[kGemvU][2], int g) {
 #pragma unroll
         for (int u = 0; u < kGemvU; ++u) {
@@ -93,40 +123,31 @@ MOE_DEV void gemv_stream_mfma(__amdgpu_buffer_rsrc_t rs, uint32_t v0, uint32_t v
             d = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, __builtin_bit_cast(f16x8, wp), d, 0, 0, 0);
         }
     };
-    // tk0, tk1 are wavefront-uniform: every branch below is scalar.
-    // tk1 - tk0 is a positive multiple of kGemvU (an even one for every
-    // shape the library accepts, so the single-group tail below is kept only
-    // for generality).  Every load is issued unconditionally: a group past
-    // the wave's range reloads its last group (in range, just read, never
-    // used), so no load sits behind a branch and the two register sets need
-    // no copies to merge loaded and kept values.
-    const int glast = tk1 - kGemvU;
-    int g = tk0;
-    load(A, g);
-    load(B, min(g + kGemvU, glast));
+    const int tk1 = cs.tk1, glast = tk1 - kGemvU;
+    int g = cs.tk0;
     for (; g + 2 * kGemvU <= tk1; g += 2 * kGemvU) {
-        run(A, g);
-        load(A, min(g + 2 * kGemvU, glast));
-        run(B, g + kGemvU);
-        load(B, min(g + 3 * kGemvU, glast));
+        run(cs.A, g);
+        cs.load(cs.A, min(g + 2 * kGemvU, glast));
+        run(cs.B, g + kGemvU);
+        cs.load(cs.B, min(g + 3 * kGemvU, glast));
     }
     if (g < tk1)
-        run(A, g);
+        run(cs.A, g);
 }
 
 template <int K, int CB>
-MOE_DEV void gemv_stream_mfma_k(int kw, __amdgpu_buffer_rsrc_t rs, uint32_t v0, uint32_t v1, uint32_t rowb, int tk0,
-                                int tk1, int q, uint32_t m_lo, uint32_t m_hi, const f16 *arow, f32x16 &d)
+MOE_DEV void gemv_stream_mfma_k(int kw, GemvCodes &cs, int q, uint32_t m_lo, uint32_t m_hi, const f16 *arow,
+                                f32x16 &d)
 {
     if constexpr (K > 0) {
-        gemv_stream_mfma<K, CB>(rs, v0, v1, rowb, tk0, tk1, q, m_lo, m_hi, arow, d);
+        gemv_stream_mfma<K, CB>(cs, q, m_lo, m_hi, arow, d);
     } else {
         if (kw == 4)
-            gemv_stream_mfma<4, CB>(rs, v0, v1, rowb, tk0, tk1, q, m_lo, m_hi, arow, d);
+            gemv_stream_mfma<4, CB>(cs, q, m_lo, m_hi, arow, d);
         else if (kw == 3)
-            gemv_stream_mfma<3, CB>(rs, v0, v1, rowb, tk0, tk1, q, m_lo, m_hi, arow, d);
+            gemv_stream_mfma<3, CB>(cs, q, m_lo, m_hi, arow, d);
         else
-            gemv_stream_mfma<2, CB>(rs, v0, v1, rowb, tk0, tk1, q, m_lo, m_hi, arow, d);
+            gemv_stream_mfma<2, CB>(cs, q, m_lo, m_hi, arow, d);
     }
 }
 
@@ -358,14 +379,13 @@ __global__ __launch_bounds__(256, 4) void gemv_gateup_kernel(GroupArgs a, int ma
     if (shared_in_gemv(a, sa, max_list, true, (f16 *)smem))
         return;
     // experts vary slowest: the blocks of the listed experts dispatch before
-    // those past the list's end, which only check the count and leave
+    // those past the list's end, which only check the count and leave (the
+    // list entry is read with the count: li < max_list is inside the list)
     const int li = blockIdx.y;
-    if (li >= a.hdr->n_gemv)
+    const int n_gemv = ld_uniform(&a.hdr->n_gemv), e = ld_uniform(a.glist + li);
+    if (li >= n_gemv)
         return;
     const int H = a.H, I = a.I;
-    const int e = a.glist[li];
-    const int R = a.counts[e];
-    const int p0 = a.offsets[e];
     const int n0 = blockIdx.x * kGuCols;
     f16 *xs = (f16 *)smem;   // [2][kGemvPass][H]
 
@@ -381,31 +401,85 @@ __global__ __launch_bounds__(256, 4) void gemv_gateup_kernel(GroupArgs a, int ma
     const __amdgpu_buffer_rsrc_t rs =
         buf_rsrc(tcs.base + (n0 / 16) * 8 * kw, tcs.bytes ? tcs.bytes - (uint32_t)(n0 / 16) * 32u * kw : 0u);
     const uint32_t tb = (uint32_t)(2 * cp + ts) * 8u * kw;
-    const uint32_t v0 = 4u * (tb + d0), v1 = 4u * (tb + d1);
     const uint32_t m_lo = a.mcg & 0xFFFFu, m_hi = a.mcg >> 16;
-    const int ntk = H / 16, tk0 = kh * (ntk / kGuKH), tk1 = tk0 + ntk / kGuKH;
+    const int ntk = H / 16;
+    GemvCodes cs;
+    cs.rs = rs;
+    cs.v0 = 4u * (tb + d0);
+    cs.v1 = 4u * (tb + d1);
+    cs.rowb = rowb;
+    cs.tk0 = kh * (ntk / kGuKH);
+    cs.tk1 = cs.tk0 + ntk / kGuKH;
+    const int R = ld_uniform(a.counts + e);
+    const int p0 = ld_uniform(a.offsets + e);
+    // one round of staging: the pieces ch = threadIdx.x + 256 (it0 + it)
+    auto load_suh = [&](f16x8 (&sv)[2][kStageIt], int it0) {
+#pragma unroll
+        for (int it = 0; it < kStageIt; ++it) {
+            const int ch = threadIdx.x + 256 * (it0 + it);
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp)
+                sv[pp][it] = ch < H / 8 ? *(const f16x8 *)(a.suh[pp] + (int64_t)e * H + 8 * ch) : (f16x8){};
+        }
+    };
 
     for (int r0 = 0; r0 < R; r0 += kGemvPass) {
         const int nr = min(kGemvPass, R - r0);
-        // x * suh of the pass's rows for both projections, and their sums
+        // x * suh of the pass's rows for both projections, and their sums.
+        // The rows' slot ids (rows past nr read the last row's) and the first
+        // round's suh pieces go out first, then the code stream's first
+        // groups, so the codes load while the slot -> token -> activation
+        // chain runs; every x piece of a round is loaded before the first
+        // product.
+        int32_t slot[kGemvPass];
+#pragma unroll
+        for (int r = 0; r < kGemvPass; ++r)
+            slot[r] = ld_uniform(a.sorted + p0 + r0 + min(r, nr - 1));
+        f16x8 sv0[2][kStageIt];
+        load_suh(sv0, 0);
+        cs.prime();
+        // (keeps the first use of the slot ids, and so their wait, below the
+        // code loads)
+        __builtin_amdgcn_sched_barrier(0);
+        int64_t tok[kGemvPass];
+#pragma unroll
+        for (int r = 0; r < kGemvPass; ++r)
+            tok[r] = slot_token(slot[r], a.nr, a.k);
         float sums[2 * kGemvPass] = {};
+        for (int it0 = 0; 256 * it0 < H / 8; it0 += kStageIt) {
+            f16x8 sv[2][kStageIt], xv[kGemvPass][kStageIt];
+            if (it0 == 0) {
 #pragma unroll
-        for (int pp = 0; pp < 2; ++pp)
+                for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
-            for (int r = 0; r < kGemvPass; ++r) {
-                if (r >= nr)
-                    continue;
-                const int64_t t = slot_token(a.sorted[p0 + r0 + r], a.nr, a.k);
-                for (int ch = threadIdx.x; ch < H / 8; ch += 256) {
-                    const f16x8 xv = *(const f16x8 *)(a.x16 + (int64_t)t * H + 8 * ch);
-                    const f16x8 sv = *(const f16x8 *)(a.suh[pp] + (int64_t)e * H + 8 * ch);
-                    const f16x8 pv = xv * sv;
-                    *(f16x8 *)(xs + ((size_t)pp * kGemvPass + r) * H + 8 * ch) = pv;
-#pragma unroll
-                    for (int j = 0; j < 8; ++j)
-                        sums[pp * kGemvPass + r] += (float)pv[j];
-                }
+                    for (int it = 0; it < kStageIt; ++it)
+                        sv[pp][it] = sv0[pp][it];
+            } else {
+                load_suh(sv, it0);
             }
+#pragma unroll
+            for (int it = 0; it < kStageIt; ++it) {
+                const int ch = threadIdx.x + 256 * (it0 + it);
+#pragma unroll
+                for (int r = 0; r < kGemvPass; ++r)
+                    xv[r][it] = ch < H / 8 && r < nr ? *(const f16x8 *)(a.x16 + tok[r] * H + 8 * ch) : (f16x8){};
+            }
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+                for (int r = 0; r < kGemvPass; ++r)
+#pragma unroll
+                    for (int it = 0; it < kStageIt; ++it) {
+                        const int ch = threadIdx.x + 256 * (it0 + it);
+                        if (r >= nr || ch >= H / 8)
+                            continue;
+                        const f16x8 pv = xv[r][it] * sv[pp][it];
+                        *(f16x8 *)(xs + ((size_t)pp * kGemvPass + r) * H + 8 * ch) = pv;
+#pragma unroll
+                        for (int j = 0; j < 8; ++j)
+                            sums[pp * kGemvPass + r] += (float)pv[j];
+                    }
+        }
         block_reduce256<2 * kGemvPass>(sums, part);
         if (threadIdx.x == 0)
 #pragma unroll
@@ -418,7 +492,7 @@ __global__ __launch_bounds__(256, 4) void gemv_gateup_kernel(GroupArgs a, int ma
         const int ar = min(l & 31, nr - 1);
         const f16 *arow = xs + ((size_t)pr * kGemvPass + ar) * H + 8 * h;
         f32x16 d = {};
-        gemv_stream_mfma_k<K, CB>(kw, rs, v0, v1, rowb, tk0, tk1, q, m_lo, m_hi, arow, d);
+        gemv_stream_mfma_k<K, CB>(kw, cs, q, m_lo, m_hi, arow, d);
 #pragma unroll
         for (int r = 0; r < kGemvPass; ++r)
             if (r < nr && h == 0)
@@ -464,12 +538,10 @@ __global__ __launch_bounds__(256, 4) void gemv_down_kernel(GroupArgs a, int max_
     if (shared_in_gemv(a, sa, max_list, false, (f16 *)smem))
         return;
     const int li = blockIdx.y;
-    if (li >= a.hdr->n_gemv)
+    const int n_gemv = ld_uniform(&a.hdr->n_gemv), e = ld_uniform(a.glist + li);
+    if (li >= n_gemv)
         return;
     const int H = a.H, I = a.I;
-    const int e = a.glist[li];
-    const int R = a.counts[e];
-    const int p0 = a.offsets[e];
     const int m0 = blockIdx.x * kDownCols;
     f16 *hs = (f16 *)smem;   // [kGemvPass][I]
 
@@ -484,31 +556,66 @@ __global__ __launch_bounds__(256, 4) void gemv_down_kernel(GroupArgs a, int max_
     const __amdgpu_buffer_rsrc_t rs =
         buf_rsrc(tcs.base + (m0 / 16) * 8 * kw, tcs.bytes ? tcs.bytes - (uint32_t)(m0 / 16) * 32u * kw : 0u);
     const uint32_t tb = (uint32_t)(2 * cp + ts) * 8u * kw;
-    const uint32_t v0 = 4u * (tb + d0), v1 = 4u * (tb + d1);
     const uint32_t m_lo = a.mcg & 0xFFFFu, m_hi = a.mcg >> 16;
     // I % 128 == 0, so ntk is a multiple of kGemvU and S = 1 always fits
     const int ntk = I / 16;
     const int S = (kDownS >= 4 && ntk % (4 * kGemvU) == 0) ? 4 : (kDownS >= 2 && ntk % (2 * kGemvU) == 0) ? 2 : 1;
-    const int tk0 = kr * (ntk / S), tk1 = tk0 + ntk / S;
+    GemvCodes cs;
+    cs.rs = rs;
+    cs.v0 = 4u * (tb + d0);
+    cs.v1 = 4u * (tb + d1);
+    cs.rowb = rowb;
+    // wavefronts past the S ranges (kr >= S) stream nothing; their primed
+    // loads read range 0 (in range, never used), so the prime needs no branch
+    cs.tk0 = kr < S ? kr * (ntk / S) : 0;
+    cs.tk1 = cs.tk0 + ntk / S;
+    const int R = ld_uniform(a.counts + e);
+    const int p0 = ld_uniform(a.offsets + e);
+    // one round of h pieces ch = threadIdx.x + 256 (it0 + it) of the pass's rows
+    auto load_h = [&](u32x4 (&raw)[kGemvPass][kStageIt], int r0, int nr, int it0) {
+#pragma unroll
+        for (int r = 0; r < kGemvPass; ++r)
+#pragma unroll
+            for (int it = 0; it < kStageIt; ++it) {
+                const int ch = threadIdx.x + 256 * (it0 + it);
+                raw[r][it] = r < nr && ch < I / 8 ? *(const u32x4 *)(a.hbuf + (int64_t)(p0 + r0 + r) * I + 8 * ch)
+                                                  : (u32x4){0u, 0u, 0u, 0u};
+            }
+    };
 
     for (int r0 = 0; r0 < R; r0 += kGemvPass) {
         const int nr = min(kGemvPass, R - r0);
-        // per row: the largest magnitude and the sum, in one reduction
+        // per row: the largest magnitude and the sum, in one reduction.  The
+        // first round's pieces (all of a row up to I = 256 * 8 * kStageIt)
+        // go out before the code stream's first groups and are kept for the
+        // conversion below.
         float red[2 * kGemvPass] = {};   // [2r] max |h|, [2r + 1] sum h
+        u32x4 held[kGemvPass][kStageIt];
+        load_h(held, r0, nr, 0);
+        cs.prime();
+        __builtin_amdgcn_sched_barrier(0);
+        for (int it0 = 0; 256 * it0 < I / 8; it0 += kStageIt) {
+            u32x4 raw[kGemvPass][kStageIt];
+            if (it0 == 0) {
 #pragma unroll
-        for (int r = 0; r < kGemvPass; ++r) {
-            if (r >= nr)
-                continue;
-            const uint16_t *hrow = a.hbuf + (int64_t)(p0 + r0 + r) * I;
-            for (int ch = threadIdx.x; ch < I / 8; ch += 256) {
-                const u32x4 raw = *(const u32x4 *)(hrow + 8 * ch);
+                for (int r = 0; r < kGemvPass; ++r)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float lo = __uint_as_float(raw[j] << 16), hi = __uint_as_float(raw[j] & 0xFFFF0000u);
-                    red[2 * r] = fmaxf(red[2 * r], fmaxf(fabsf(lo), fabsf(hi)));
-                    red[2 * r + 1] += lo + hi;
-                }
+                    for (int it = 0; it < kStageIt; ++it)
+                        raw[r][it] = held[r][it];
+            } else {
+                load_h(raw, r0, nr, it0);
             }
+#pragma unroll
+            for (int r = 0; r < kGemvPass; ++r)
+#pragma unroll
+                for (int it = 0; it < kStageIt; ++it)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float lo = __uint_as_float(raw[r][it][j] << 16),
+                                    hi = __uint_as_float(raw[r][it][j] & 0xFFFF0000u);
+                        red[2 * r] = fmaxf(red[2 * r], fmaxf(fabsf(lo), fabsf(hi)));
+                        red[2 * r + 1] += lo + hi;
+                    }
         }
         block_reduce256<2 * kGemvPass, 0x5u>(red, part);
         int ex[kGemvPass];
@@ -518,21 +625,34 @@ __global__ __launch_bounds__(256, 4) void gemv_down_kernel(GroupArgs a, int max_
             const float mx = red[2 * r];
             ex[r] = (mx > 0.0f && mx < __builtin_inff()) ? 15 - __builtin_amdgcn_frexp_expf(mx) : 0;
         }
+        // the scaled fp16 rows into LDS: the first round from the kept
+        // pieces, later rounds (I > 256 * 8 * kStageIt) loaded again
+        for (int it0 = 0; 256 * it0 < I / 8; it0 += kStageIt) {
+            u32x4 raw[kGemvPass][kStageIt];
+            if (it0 == 0) {
 #pragma unroll
-        for (int r = 0; r < kGemvPass; ++r) {
-            if (r >= nr)
-                continue;
-            const uint16_t *hrow = a.hbuf + (int64_t)(p0 + r0 + r) * I;
-            for (int ch = threadIdx.x; ch < I / 8; ch += 256) {
-                const u32x4 raw = *(const u32x4 *)(hrow + 8 * ch);
-                f16x8 hv;
+                for (int r = 0; r < kGemvPass; ++r)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    hv[2 * j] = (f16)__builtin_ldexpf(__uint_as_float(raw[j] << 16), ex[r]);
-                    hv[2 * j + 1] = (f16)__builtin_ldexpf(__uint_as_float(raw[j] & 0xFFFF0000u), ex[r]);
-                }
-                *(f16x8 *)(hs + (size_t)r * I + 8 * ch) = hv;
+                    for (int it = 0; it < kStageIt; ++it)
+                        raw[r][it] = held[r][it];
+            } else {
+                load_h(raw, r0, nr, it0);
             }
+#pragma unroll
+            for (int r = 0; r < kGemvPass; ++r)
+#pragma unroll
+                for (int it = 0; it < kStageIt; ++it) {
+                    const int ch = threadIdx.x + 256 * (it0 + it);
+                    if (r >= nr || ch >= I / 8)
+                        continue;
+                    f16x8 hv;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        hv[2 * j] = (f16)__builtin_ldexpf(__uint_as_float(raw[r][it][j] << 16), ex[r]);
+                        hv[2 * j + 1] = (f16)__builtin_ldexpf(__uint_as_float(raw[r][it][j] & 0xFFFF0000u), ex[r]);
+                    }
+                    *(f16x8 *)(hs + (size_t)r * I + 8 * ch) = hv;
+                }
         }
         if (threadIdx.x == 0)
 #pragma unroll
@@ -546,7 +666,7 @@ __global__ __launch_bounds__(256, 4) void gemv_down_kernel(GroupArgs a, int max_
         const f16 *arow = hs + (size_t)ar * I + 8 * h;
         f32x16 d = {};
         if (kr < S)
-            gemv_stream_mfma_k<K, CB>(kw, rs, v0, v1, rowb, tk0, tk1, q, m_lo, m_hi, arow, d);
+            gemv_stream_mfma_k<K, CB>(kw, cs, q, m_lo, m_hi, arow, d);
 #pragma unroll
         for (int r = 0; r < kGemvPass; ++r)
             if (kr < S && r < nr && h == 0)

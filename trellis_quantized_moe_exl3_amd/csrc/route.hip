@@ -804,8 +804,23 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
         const int64_t n8 = T * H / 8;
         const int first = split ? (int)threadIdx.x - 512 : (int)threadIdx.x, step = split ? 512 : 1024;
         bool over = false;
-        for (int64_t i = first; i < n8; i += step)
-            ((u32x4 *)x16)[i] = bf16x8_to_f16x8(((const u32x4 *)x)[i], over);
+        // all loads of a round of kCopyBatch pieces go out before its first
+        // store: one memory latency per round rather than one per piece
+        constexpr int kCopyBatch = 8;
+        for (int64_t i0 = first; i0 < n8; i0 += (int64_t)kCopyBatch * step) {
+            u32x4 v[kCopyBatch];
+#pragma unroll
+            for (int j = 0; j < kCopyBatch; ++j) {
+                const int64_t i = i0 + (int64_t)j * step;
+                v[j] = i < n8 ? ((const u32x4 *)x)[i] : (u32x4){0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int j = 0; j < kCopyBatch; ++j) {
+                const int64_t i = i0 + (int64_t)j * step;
+                if (i < n8)
+                    ((u32x4 *)x16)[i] = bf16x8_to_f16x8(v[j], over);
+            }
+        }
         if (over)
             flag_status(hdr, MOE_EXL3_STATUS_ACT_RANGE);
     }
