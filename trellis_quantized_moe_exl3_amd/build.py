@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmoe_exl3.so")
-SOURCES = ["route.hip", "decode.hip", "gemv.hip", "mfma.hip", "mfma8.hip", "moe_exl3.cpp"]
+SOURCES = ["route.hip", "decode.hip", "gemv.hip", "mfma.hip", "mfma8.hip", "combine.hip", "moe_exl3.cpp"]
 # the benchmark's streaming-read probe (achievable HBM bandwidth), a library of its own
 BW_SOURCE = "bw_probe.hip"
 BW_LIB = os.path.join(HERE, "libmoe_exl3_bw.so")
