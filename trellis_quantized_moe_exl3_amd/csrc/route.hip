@@ -502,8 +502,9 @@ hipError_t launch_topk(const float *logits, int64_t T, int E, int k, int32_t *id
 //  1. per-block expert histograms of kSegChunk consecutive slots;
 //  2. one block: per-expert running sums over blocks, counts, exclusive
 //     offsets, and the work lists (GEMV experts, MFMA row tiles);
-//  3. per block, slots in order: rank inside each 64-slot chunk from ballots,
-//     position = block base + rank.
+//  3. per block, slots in order: eight wavefronts each rank a span of the
+//     block's slots, inside each 64-slot chunk from ballots; position =
+//     block base + earlier spans' counts + rank.
 
 // An expert index outside [0, E) (impossible from topk_token; a guard against
 // a corrupted table) is left out of every table and flagged in the status word.
@@ -646,37 +647,63 @@ __global__ __launch_bounds__(1024) void seg_scan_kernel(int32_t *__restrict__ bh
         write_extra_slots(nr, T, sorted, pos, w);
 }
 
-__global__ __launch_bounds__(64) void seg_scatter_kernel(const int32_t *__restrict__ idx, int64_t n,
-                                                         int E, const int32_t *__restrict__ bhist,
-                                                         const int32_t *__restrict__ offsets,
-                                                         int32_t *__restrict__ sorted,
-                                                         int32_t *__restrict__ pos)
+// Scatter of one kSegChunk-slot block by kScatterWaves wavefronts, wavefront
+// w taking the block's slots w * kScatterSpan .. + kScatterSpan - 1 in order.
+// Each wavefront first counts its span per expert; the bases of wavefront w
+// are then the block's base plus the counts of wavefronts 0 .. w - 1, so the
+// spans rank independently and the order stays the stable one.
+constexpr int kScatterWaves = 8;
+constexpr int kScatterSpan = kSegChunk / kScatterWaves;   // a multiple of 64
+
+__global__ __launch_bounds__(64 * kScatterWaves) void seg_scatter_kernel(const int32_t *__restrict__ idx, int64_t n,
+                                                                        int E, const int32_t *__restrict__ bhist,
+                                                                        const int32_t *__restrict__ offsets,
+                                                                        int32_t *__restrict__ sorted,
+                                                                        int32_t *__restrict__ pos)
 {
-    extern __shared__ int32_t base[];
-    for (int e = threadIdx.x; e < E; e += 64)
-        base[e] = bhist[(int64_t)blockIdx.x * E + e] + offsets[e];
-    __syncthreads();
-    const int l = threadIdx.x;
-    const int64_t a0 = (int64_t)blockIdx.x * kSegChunk;
+    extern __shared__ int32_t base[];   // [kScatterWaves][E]
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    for (int i = threadIdx.x; i < kScatterWaves * E; i += 64 * kScatterWaves)
+        base[i] = 0;
+    const int64_t a0 = (int64_t)blockIdx.x * kSegChunk + (int64_t)w * kScatterSpan;
     int nbits = 0;
     while ((1 << nbits) < E)
         ++nbits;
     const uint64_t below = (l == 0) ? 0ull : (~0ull >> (64 - l));
-    // the chunk's expert ids are loaded up front (one round trip), the ranking
+    // the span's expert ids are loaded up front (one round trip), the ranking
     // below then runs on registers and LDS only
-    constexpr int kIter = kSegChunk / 64;
+    constexpr int kIter = kScatterSpan / 64;
     int ev[kIter];
 #pragma unroll
     for (int c = 0; c < kIter; ++c) {
         const int64_t a = a0 + 64 * c + l;
         ev[c] = a < n ? idx[a] : 0;
     }
-    const int64_t span = n - a0 < kSegChunk ? n - a0 : kSegChunk;   // slots of this block
+    __syncthreads();
+    int32_t *wb = base + w * E;
 #pragma unroll
     for (int c = 0; c < kIter; ++c) {
-        if (64 * c >= span)
-            break;
         const int64_t a = a0 + 64 * c + l;
+        if (a < n && valid_expert(ev[c], E))
+            atomicAdd(&wb[ev[c]], 1);
+    }
+    __syncthreads();
+    // counts -> bases: the block's base of expert e, then the wavefronts'
+    // spans in order
+    for (int e = threadIdx.x; e < E; e += 64 * kScatterWaves) {
+        int run = bhist[(int64_t)blockIdx.x * E + e] + offsets[e];
+        for (int v = 0; v < kScatterWaves; ++v) {
+            const int cnt = base[v * E + e];
+            base[v * E + e] = run;
+            run += cnt;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < kIter; ++c) {
+        const int64_t a = a0 + 64 * c + l;
+        if (a - l >= n)   // wavefront-uniform: the rest of the span is past the end
+            break;
         const int e = ev[c];
         const bool valid = a < n && valid_expert(e, E);
         uint64_t m = __ballot(valid);
@@ -685,16 +712,17 @@ __global__ __launch_bounds__(64) void seg_scatter_kernel(const int32_t *__restri
             const uint64_t bb = __ballot(bit);
             m &= bit ? bb : ~bb;
         }
+        // the wavefront's LDS operations run in order: every lane reads its
+        // expert's base before the last lane of that expert advances it
         if (valid) {
-            const int rank = __popcll(m & below);
-            const int p = base[e] + rank;
+            const int p = wb[e] + __popcll(m & below);
             sorted[p] = (int32_t)a;
             pos[a] = p;
         }
-        __syncthreads();
+        __builtin_amdgcn_wave_barrier();
         if (valid && (m >> l) == 1ull)   // last lane of its expert in this chunk
-            base[e] += __popcll(m);
-        __syncthreads();
+            wb[e] += __popcll(m);
+        __builtin_amdgcn_wave_barrier();
     }
 }
 
@@ -708,7 +736,7 @@ hipError_t launch_segments(const int32_t *idx, int64_t T, int k, int E, bool ext
     seg_hist_kernel<<<nblk, 256, lds, s>>>(idx, n, E, bhist, hdr);
     seg_scan_kernel<<<1, 1024, 0, s>>>(bhist, nblk, E, T, n, extra, gemv_rows, tile_m, max_tiles, counts,
                                        offsets, sorted, pos, w, glist, tiles, hdr);
-    seg_scatter_kernel<<<nblk, 64, lds, s>>>(idx, n, E, bhist, offsets, sorted, pos);
+    seg_scatter_kernel<<<nblk, 64 * kScatterWaves, kScatterWaves * lds, s>>>(idx, n, E, bhist, offsets, sorted, pos);
     return hipGetLastError();
 }
 
