@@ -40,8 +40,10 @@
  *   - Pointers marked "device" point to device memory of the current HIP
  *     device, are owned by the caller and must stay valid until the work
  *     queued on `stream` has finished.  The library never allocates, frees or
- *     synchronises; it keeps no mutable global state, so calls on different
- *     streams are independent as long as each call has its own workspace.
+ *     synchronises.  Apart from the per-GPU scratch array of
+ *     moe_exl3_layer_noalloc (see there) it keeps no mutable global state, so
+ *     calls on different streams are independent as long as each call has its
+ *     own workspace.
  *   - `stream` is a hipStream_t (NULL = the null stream).
  *   - Return value: 0 on success or a negative MOE_EXL3_ERR_* code.  All
  *     argument checks run before the first launch; on error nothing is
@@ -172,7 +174,9 @@ typedef struct moe_exl3_desc {
     int32_t act_dtype;      /* dtype of x and out */
     uint32_t flags;         /* MOE_EXL3_* flags */
     int32_t gemv_max_rows;  /* experts with at most this many routed rows use the
-                               GEMV path; 0 selects the default (2) */
+                               GEMV path (at most 8); 0 selects the default: 8 for
+                               calls of at most 8 tokens (every expert on the GEMV
+                               path), else 2 */
 } moe_exl3_desc;
 
 /*
