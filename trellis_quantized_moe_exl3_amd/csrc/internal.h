@@ -94,6 +94,7 @@ struct GroupArgs {
     uint32_t mcg;
     const int32_t *counts, *offsets, *sorted, *glist, *tiles;
     const int32_t *idx;      // top-k expert of every routed slot [T*k]
+    const int32_t *pos;      // inverse of sorted: the sorted position of slot a
     const WsHeader *hdr;
     const float *w;          // routing weights [T*k]
     const uint16_t *x16;     // fp16 activations [T][H]

@@ -456,9 +456,9 @@ MOE_DEV float wave_max64(float v)
     return v;
 }
 
-// One wavefront per routed row p (sorted order), four rows per block:
-// x[t] * suh_p[e] for gate and up, each scaled by its row amax / 448 and
-// rounded to E4M3.  The row's expert is its slot's top-k expert (for the
+// One wavefront per routed slot a (slot order, four per block), written as
+// row p = pos[a] of the sorted order: x[t] * suh_p[e] for gate and up, each
+// scaled by its row amax / 448 and rounded to E4M3.  The row's expert is its slot's top-k expert (for the
 // trellis shared expert's slots past the routed ones, the last expert).  Lane
 // l holds the 16-byte pieces l, l + 64, ... of the three rows (at most NC of
 // them: H <= 512 NC) between the amax reduction and the conversion; the
@@ -466,11 +466,18 @@ MOE_DEV float wave_max64(float v)
 template <int NC>
 __global__ __launch_bounds__(256) void quant_gateup_kernel(GroupArgs a, int64_t n)
 {
-    const int64_t p = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (p >= n)
+    // rows in slot order (the k slots of a token side by side, so its
+    // activation row is read once from memory), each written at its sorted
+    // position
+    const int64_t slot = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (slot >= n)
         return;
     const int l = threadIdx.x & 63, H = a.H;
-    const int64_t slot = a.sorted[p];
+    const int64_t p = a.pos[slot];
+    // a slot left out of the tables (an expert index outside [0, E), flagged
+    // in the status word) has no position: nothing is written for it
+    if ((uint64_t)p >= (uint64_t)n)
+        return;
     const int64_t t = slot_token(slot, a.nr, a.k);
     // (clamped: an index outside the table, which the segment kernels flag
     // in the status word, still reads inside the side-vector arrays)

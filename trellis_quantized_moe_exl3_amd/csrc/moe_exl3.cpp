@@ -427,6 +427,7 @@ static int run_layer(const moe_exl3_desc *desc, const moe_exl3_weights *weights,
     ga.offsets = at<int32_t>(ws, p.offsets);
     ga.sorted = at<int32_t>(ws, p.sorted);
     ga.idx = at<int32_t>(ws, p.idx);
+    ga.pos = at<int32_t>(ws, p.pos);
     ga.glist = at<int32_t>(ws, p.glist);
     ga.tiles = at<int32_t>(ws, p.tiles);
     ga.hdr = at<WsHeader>(ws, p.hdr);
