@@ -425,8 +425,9 @@ MOE_DEV void topk_token(const float *__restrict__ logits, int64_t t, int E, int 
         v[i] = lv != lv ? -INFINITY : lv;
         key[i] = ok ? e : kNoExpert;
     }
-    float selv[16];
-    int seli[16];
+    // lane j keeps pick j (k <= 16 lanes); the softmax then runs across lanes
+    float myv = -INFINITY, top = -INFINITY;
+    int myi = 0;
     for (int j = 0; j < k; ++j) {
         // the lane's best remaining: slots are in ascending expert order, so
         // the strict compare keeps the lowest expert among equal logits
@@ -446,8 +447,12 @@ MOE_DEV void topk_token(const float *__restrict__ logits, int64_t t, int E, int 
             win = __builtin_amdgcn_readlane(bi, __builtin_ctzll(tie));
         else
             win = wave_min(((tie >> l) & 1) ? bi : kNoExpert);
-        selv[j] = m;
-        seli[j] = win;
+        if (l == j) {
+            myv = m;
+            myi = win;
+        }
+        if (j == 0)
+            top = m;
         if ((win & 63) == l) {
 #pragma unroll
             for (int i = 0; i < NPER; ++i)
@@ -455,16 +460,19 @@ MOE_DEV void topk_token(const float *__restrict__ logits, int64_t t, int E, int 
                     key[i] = kNoExpert;
         }
     }
-    if (l == 0) {
-        float sum = 0.0f;
-        for (int j = 0; j < k; ++j)
-            sum += expf(selv[j] - selv[0]);
-        for (int j = 0; j < k; ++j) {
-            idx[t * k + j] = seli[j];
-            w[t * k + j] = expf(selv[j] - selv[0]) / sum;
-            if (sidx)
-                sidx[t * k + j] = seli[j];
-        }
+    // softmax over the k picks: one exponential per lane, the sum by a fixed
+    // butterfly over the wavefront (lanes past k add zero), then every pick
+    // stored by its own lane
+    const float ex = l < k ? expf(myv - top) : 0.0f;
+    float sum = ex;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        sum += __shfl_xor(sum, off, 64);
+    if (l < k) {
+        idx[t * k + l] = myi;
+        w[t * k + l] = ex / sum;
+        if (sidx)
+            sidx[t * k + l] = myi;
     }
 }
 
@@ -559,6 +567,40 @@ __device__ int block_exclusive_scan(int v, int *total)
     __syncthreads();
     *total = tot;
     return base + incl - v;
+}
+
+// Three block-wide exclusive scans at once (blockDim.x == 1024), for counts
+// whose block totals stay below 2^21: packed as 21-bit fields of one 64-bit
+// value, no carry crosses a field, so each field scans exactly.
+__device__ void block_exclusive_scan3(const int v[3], int ex[3], int tot[3])
+{
+    __shared__ uint64_t wsum3[16];
+    const int l = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const uint64_t p = (uint64_t)v[0] | ((uint64_t)v[1] << 21) | ((uint64_t)v[2] << 42);
+    uint64_t incl = p;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint64_t o = __shfl_up(incl, off, 64);
+        if (l >= off)
+            incl += o;
+    }
+    if (l == 63)
+        wsum3[wv] = incl;
+    __syncthreads();
+    uint64_t base = 0, all = 0;
+    for (int i = 0; i < 16; ++i) {
+        if (i < wv)
+            base += wsum3[i];
+        all += wsum3[i];
+    }
+    __syncthreads();
+    const uint64_t e = base + incl - p;
+    constexpr uint64_t kMask = (1ull << 21) - 1;
+#pragma unroll
+    for (int f = 0; f < 3; ++f) {
+        ex[f] = (int)((e >> (21 * f)) & kMask);
+        tot[f] = (int)((all >> (21 * f)) & kMask);
+    }
 }
 
 // The GEMV expert list and the MFMA tile list (expert, first row), written by
@@ -865,20 +907,21 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
     const int e = threadIdx.x;   // E + extra <= 1024
     const int EA = E + (extra ? 1 : 0);
     const int c = e < E ? hist[e] : e < EA ? (int)T : 0;
-    int tot;
-    const int off = block_exclusive_scan(c, &tot);
+    const bool gemv = e < EA && c > 0 && c <= gemv_rows;
+    const int nt = (e < EA && c > gemv_rows) ? (c + tile_m - 1) / tile_m : 0;
+    // offsets, GEMV list positions and tile list positions in one scan (every
+    // block total is at most T * k + T <= 2 kSegChunk < 2^21)
+    const int sv[3] = {c, gemv ? 1 : 0, nt};
+    int sx[3], st[3];
+    block_exclusive_scan3(sv, sx, st);
+    const int off = sx[0];
     if (e < EA) {
         counts[e] = c;
         offsets[e] = off;
     }
     if (e == 0)
-        offsets[EA] = tot;
-    const bool gemv = e < EA && c > 0 && c <= gemv_rows;
-    const int nt = (e < EA && c > gemv_rows) ? (c + tile_m - 1) / tile_m : 0;
-    int ng, ntt;
-    const int gpos = block_exclusive_scan(gemv ? 1 : 0, &ng);
-    const int tpos = block_exclusive_scan(nt, &ntt);
-    write_work_lists(e, gemv, gpos, ng, nt, tpos, ntt, tile_m, max_tiles, glist, tiles, hdr);
+        offsets[EA] = st[0];
+    write_work_lists(e, gemv, sx[1], st[1], nt, sx[2], st[2], tile_m, max_tiles, glist, tiles, hdr);
     if (extra)
         write_extra_slots((int64_t)n, T, sorted, pos, w);
     __syncthreads();
