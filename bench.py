@@ -520,8 +520,8 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, help="copy this many MiB 4 times and exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py: this build runs on one GPU only; multi-GPU scaling is not part of it "
-              "(see the sharding notes in DESIGN.md)", file=sys.stderr)
+        print("bench.py: the benchmark runs the layer on one GPU only; multi-GPU scaling is not "
+              "part of it", file=sys.stderr)
         sys.exit(2)
 
     import torch
