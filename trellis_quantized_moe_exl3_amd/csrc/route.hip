@@ -207,26 +207,41 @@ __global__ __launch_bounds__(256) void route_logits_pairs_kernel(const uint16_t 
     }
 }
 
-// Many tokens, on the matrix cores.  One block of two wavefronts computes a
-// tile of 16 tokens x 16 experts and holds all 64 partial sums of every pair
-// of it at once: v_mfma_f32_16x16x1_4b_f32 has k = 1, so each instruction adds
-// exactly one product to each of its accumulators, and its four 16x16 blocks
-// carry four of the 64 partial-sum chains.  Instruction q (q = 0..15) of a
-// 64-channel chunk i adds x[64i + l] * w[64i + l] to chains l = q + 16b of
-// block b = 0..3; wavefront h issues instructions q = 8h .. 8h + 7, and the
-// lanes of block b supply token (A) and expert (B) rows 0..15 from channels
-// 64i + 16b + 8h .. + 7, 16 contiguous bytes per row.  As in the VALU kernels
-// the product is exact in fp32, so every accumulation step rounds once, the
-// order over i is the plain one, and the halving tree over l runs on the
-// finished chains: chains q, q + 16, q + 32, q + 48 of a (token, expert) pair
-// sit in one lane of one wavefront (block b in registers 4b .. 4b + 3, lane
-// 16 (row / 4) + column, register row % 4), so the steps d = 32, 16 are
-// in-lane adds, the step d = 8 adds wavefront 1's sums to wavefront 0's
-// through LDS, and d = 4, 2, 1 are in-lane again.  128 accumulator registers
-// per wavefront: two wavefronts per SIMD, which measured 3% faster than one
-// wavefront holding all 16 instructions' chains (256 registers).
-constexpr int kRouteTile = 16;
-constexpr int kRouteSets = 4;
+// Many tokens, on the matrix cores.  v_mfma_f32_16x16x1_4b_f32 has k = 1: each
+// instruction adds exactly one product to each accumulator, and its four
+// 16 x 16 blocks carry four of the 64 partial-sum chains of every (token,
+// expert) pair of a 16 x 16 tile.  Instruction q (q = 0..15) of a 64-channel
+// chunk i adds x[64i + l] * w[64i + l] to chain l = q + 16b of block b = 0..3;
+// the lanes of block b supply token (A) and expert (B) rows 0..15.  The
+// product is exact in fp32, so every accumulation step rounds once, the order
+// over i is the plain one, and the halving tree over l runs on the finished
+// chains.
+//
+// A block of four wavefronts computes 16 tokens x 32 experts.  Wavefronts 2s
+// and 2s + 1 own experts 16s .. 16s + 15; wavefront 2s + h issues
+// instructions q = 8h .. 8h + 7 of every chunk, so its lane (b, row c) needs
+// channels 64i + 16b + 8h .. + 7 of token row c and of expert row 16s + c.
+// Chains q, q + 16, q + 32, q + 48 of a pair then sit in one lane of one
+// wavefront (block b in registers 4b .. 4b + 3, lane 16 (row / 4) + column,
+// register row % 4): the tree steps d = 32, 16 are in-lane adds, d = 8 adds
+// wavefront 2s + 1's sums to wavefront 2s's through LDS, and d = 4, 2, 1 are
+// in-lane again.  128 accumulator registers per wavefront, two wavefronts per
+// SIMD.
+//
+// Each step of 128 channels (two chunks) the block copies its 16 token rows
+// and 32 expert rows into one stage of an LDS ring with LDS-direct loads in
+// which 16 lanes read 256 contiguous bytes of one row, so every cache line a
+// load touches is used whole, and each staged activation row serves 32
+// experts.  (Loading the operands straight into registers touched 16 rows per
+// instruction and half of each line, and the texture addresser stalled.)
+// Piece p (16 bytes, channels 8p .. 8p + 7 of the step) of row r sits in slot
+// p ^ (r & 15) of the row's 16, so the 16 lanes that read one piece of 16
+// rows hit 16 distinct 4-bank groups.  The step's 32 operands are widened to
+// fp32 before its 16 MFMAs, which then issue back to back.
+constexpr int kRlTok = 16, kRlExp = 32;
+constexpr int kRlStages = 6;                      // ring depth; loads run 5 steps ahead
+constexpr int kRlSlots = (kRlTok + kRlExp) * 16;  // 16-byte slots per stage
+constexpr int kRlLoads = kRlSlots / 256;          // LDS-direct loads per lane per step
 
 // element q (0..7) of 8 activations packed in 16 bytes, widened to fp32
 template <bool BF16>
@@ -238,88 +253,129 @@ MOE_DEV float act_elem(const u32x4 &v, int q)
     return f16_to_f32((uint16_t)((q & 1) ? (d >> 16) : (d & 0xFFFFu)));
 }
 
+MOE_DEV float w_elem(const u32x4 &v, int q)
+{
+    const uint32_t d = v[q >> 1];
+    return f16_to_f32((uint16_t)((q & 1) ? (d >> 16) : (d & 0xFFFFu)));
+}
+
 template <bool BF16>
-__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) void route_logits_mfma_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void route_logits_mfma_kernel(
     const uint16_t *__restrict__ x, int64_t T, int H, const uint16_t *__restrict__ Wr,
     const float *__restrict__ bias, int E, float *__restrict__ logits, WsHeader *hdr, int n_tt, int n_et)
 {
-    __shared__ f32x4 xch[8][64];
+    __shared__ u32x4 ring_mem[kRlStages * kRlSlots];   // 72 KiB
+    LDS_AS u32x4 *ring = (LDS_AS u32x4 *)ring_mem;
     clear_status(hdr);
     int tt, et;
     xcd_map((int)blockIdx.x, n_et, tt, et);   // the expert tiles of a token tile share one XCD's L2
     if (tt >= n_tt)
         return;
-    // wavefront h carries instructions q = 8h .. 8h + 7 of every chunk; rows
-    // past the last token / expert load zeros through the buffer ranges and
-    // their sums are never stored
-    const int h = threadIdx.x >> 6, l = threadIdx.x & 63, b = l >> 4, c = l & 15;
-    const int64_t t0 = (int64_t)tt * kRouteTile;
-    const int e0 = et * kRouteTile;
-    const int nt = (int)std::min<int64_t>(kRouteTile, T - t0), ne = std::min(kRouteTile, E - e0);
+    const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), l = threadIdx.x & 63;
+    const int sx = w >> 1, h = w & 1, b = l >> 4, c = l & 15;
+    const int64_t t0 = (int64_t)tt * kRlTok;
+    const int e0 = et * kRlExp;
+    const int nt = (int)std::min<int64_t>(kRlTok, T - t0), ne = std::min(kRlExp, E - e0);
+    // rows past the last token / expert read zeros through the ranges; their
+    // sums are never stored
     const __amdgpu_buffer_rsrc_t xs = buf_rsrc(x + t0 * H, (uint32_t)(nt * H * 2));
     const __amdgpu_buffer_rsrc_t ws = buf_rsrc(Wr + (int64_t)e0 * H, (uint32_t)(ne * H * 2));
-    const uint32_t off = (uint32_t)(c * H + 16 * b + 8 * h) * 2;
+    const __amdgpu_buffer_rsrc_t none = buf_rsrc(x, 0);
+    // load k of wavefront w fills slots 64j .. 64j + 63 of a stage, j = 3w + k:
+    // stage row 4j + l / 16 (token rows 0..15, then expert rows), slot l % 16
+    // of that row, which holds piece (l % 16) ^ (row & 15)
+    uint32_t loff[kRlLoads];
+    __amdgpu_buffer_rsrc_t lrs[kRlLoads];
+#pragma unroll
+    for (int k = 0; k < kRlLoads; ++k) {
+        const int j = kRlLoads * w + k, r = 4 * j + (l >> 4);
+        const bool tok = 4 * j < kRlTok;   // the same for the whole wavefront
+        const int rr = tok ? r : r - kRlTok;
+        lrs[k] = tok ? xs : ws;
+        loff[k] = (uint32_t)(rr * H * 2 + 16 * ((l & 15) ^ (rr & 15)));
+    }
+    const int nst = H / 128;
+    // Every step issues the same loads; those past the last step go through a
+    // zero-range descriptor (no memory access) into a stage nobody reads, so
+    // one wait count holds on every path.
+    auto load = [&](int g, int slot) {
+        LDS_AS u32x4 *st = ring + slot * kRlSlots;
+#pragma unroll
+        for (int k = 0; k < kRlLoads; ++k) {
+            const __amdgpu_buffer_rsrc_t rs = g < nst ? lrs[k] : none;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void *)(st + 64 * (kRlLoads * w + k)), 16,
+                                                     loff[k] + 256u * (uint32_t)g, 0, 0, 0);
+        }
+    };
+    // the lane's operand slots: piece 8i + 2b + h (chunk i of the step) of
+    // token row c and of expert row 16 sx + c
+    const int xsl0 = 16 * c + ((2 * b + h) ^ c), xsl1 = 16 * c + ((8 + 2 * b + h) ^ c);
+    const int wsl0 = 16 * (kRlTok + 16 * sx) + xsl0, wsl1 = 16 * (kRlTok + 16 * sx) + xsl1;
     f32x16 acc[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q)
         acc[q] = (f32x16){};
-    const int n = H / 64;   // a multiple of kRouteSets
-    // Four register sets rotate: the loads of chunk i + 4 go out right after
-    // chunk i's MFMAs.  Loads past the last chunk fall outside the range and
-    // return zeros (the chunk offset is in the per-lane offset, which the range
-    // check covers); they are never used.  The scheduling barriers keep every
-    // load group where it is written.
-    u32x4 xv[kRouteSets], wv[kRouteSets];
-    auto load = [&](int i, int j) {
-        const uint32_t o = off + (uint32_t)i * 128u;
-        xv[j] = __builtin_amdgcn_raw_buffer_load_b128(xs, o, 0, 0);
-        wv[j] = __builtin_amdgcn_raw_buffer_load_b128(ws, o, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-    };
 #pragma unroll
-    for (int j = 0; j < kRouteSets; ++j)
+    for (int j = 0; j < kRlStages - 1; ++j)
         load(j, j);
-    for (int i = 0; i < n; i += kRouteSets) {
+    int cur = 0, prev = kRlStages - 1;
+    for (int g = 0; g < nst; ++g) {
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<(kRlStages - 2) * kRlLoads>();   // this step's loads are done
+        __builtin_amdgcn_s_barrier();     // ... for every wavefront, and nobody reads step g - 1 any more
+        load(g + kRlStages - 1, prev);    // into step g - 1's stage
+        const LDS_AS u32x4 *st = ring + cur * kRlSlots;
+        prev = cur;
+        cur = cur + 1 == kRlStages ? 0 : cur + 1;
+        const u32x4 xv0 = st[xsl0], wv0 = st[wsl0], xv1 = st[xsl1], wv1 = st[wsl1];
+        __builtin_amdgcn_sched_barrier(0);   // all four reads go out before the first MFMA
+        float a0[8], b0[8], a1[8], b1[8];
 #pragma unroll
-        for (int j = 0; j < kRouteSets; ++j) {
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const uint32_t d = wv[j][q >> 1];
-                const float wq = f16_to_f32((uint16_t)((q & 1) ? (d >> 16) : (d & 0xFFFFu)));
-                acc[q] = __builtin_amdgcn_mfma_f32_16x16x1f32(act_elem<BF16>(xv[j], q), wq, acc[q], 0, 0, 0);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            load(i + kRouteSets + j, j);
+        for (int q = 0; q < 8; ++q) {
+            a0[q] = act_elem<BF16>(xv0, q);
+            b0[q] = w_elem(wv0, q);
+            a1[q] = act_elem<BF16>(xv1, q);
+            b1[q] = w_elem(wv1, q);
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            acc[q] = __builtin_amdgcn_mfma_f32_16x16x1f32(a0[q], b0[q], acc[q], 0, 0, 0);
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            acc[q] = __builtin_amdgcn_mfma_f32_16x16x1f32(a1[q], b1[q], acc[q], 0, 0, 0);
     }
+    wait_vmcnt<0>();   // the trailing zero-range loads still write LDS
+    __syncthreads();   // the ring is free: it holds the exchange below
     f32x4 u[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             u[q][r] = (acc[q][r] + acc[q][8 + r]) + (acc[q][4 + r] + acc[q][12 + r]);
+    LDS_AS f32x4 *xch = (LDS_AS f32x4 *)ring + sx * 8 * 64;
     if (h == 1) {
 #pragma unroll
         for (int q = 0; q < 8; ++q)
-            xch[q][l] = u[q];
+            xch[64 * q + l] = u[q];
     }
     __syncthreads();
     if (h == 1)
         return;
 #pragma unroll
     for (int q = 0; q < 8; ++q)
-        u[q] = u[q] + xch[q][l];
+        u[q] = u[q] + xch[64 * q + l];
 #pragma unroll
     for (int d = 4; d >= 1; d >>= 1)
 #pragma unroll
         for (int q = 0; q < d; ++q)
             u[q] = u[q] + u[q + d];
-    const int e = et * kRouteTile + c;
+    const int e = e0 + 16 * sx + c;
     if (e < E) {
         const float be = bias ? bias[e] : 0.0f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int64_t t = (int64_t)tt * kRouteTile + 4 * b + r;
+            const int64_t t = t0 + 4 * b + r;
             if (t < T)
                 logits[t * E + e] = bias ? u[0][r] + be : u[0][r];
         }
@@ -338,17 +394,17 @@ static void route_launch(const uint16_t *x, int64_t T, int H, const uint16_t *Wr
 hipError_t launch_route_logits(const uint16_t *x, bool bf16, int64_t T, int H, const uint16_t *Wr,
                                const float *bias, int E, float *logits, WsHeader *hdr, hipStream_t s)
 {
-    // many tokens: 16 x 16 tiles on the matrix cores (hidden sizes in whole
-    // 256-channel rounds), else on the VALU with 2 tokens x 4 experts per
+    // many tokens: 16 x 32 tiles on the matrix cores (hidden sizes in whole
+    // 128-channel steps), else on the VALU with 2 tokens x 4 experts per
     // lane (8 tokens x 32 experts per block); few tokens: one (token, expert)
     // pair per 32 lanes so that enough wavefronts stream the router weights
-    if (T > 64 && H % (64 * kRouteSets) == 0) {
-        const int n_tt = (int)((T + kRouteTile - 1) / kRouteTile), n_et = (E + kRouteTile - 1) / kRouteTile;
+    if (T > 64 && H % 128 == 0) {
+        const int n_tt = (int)((T + kRlTok - 1) / kRlTok), n_et = (E + kRlExp - 1) / kRlExp;
         const unsigned grid = (unsigned)(((n_tt + 7) / 8) * 8 * n_et);
         if (bf16)
-            route_logits_mfma_kernel<true><<<grid, 128, 0, s>>>(x, T, H, Wr, bias, E, logits, hdr, n_tt, n_et);
+            route_logits_mfma_kernel<true><<<grid, 256, 0, s>>>(x, T, H, Wr, bias, E, logits, hdr, n_tt, n_et);
         else
-            route_logits_mfma_kernel<false><<<grid, 128, 0, s>>>(x, T, H, Wr, bias, E, logits, hdr, n_tt, n_et);
+            route_logits_mfma_kernel<false><<<grid, 256, 0, s>>>(x, T, H, Wr, bias, E, logits, hdr, n_tt, n_et);
     } else if (T > 64) {
         if (bf16) route_launch<true, 2, 4, 4>(x, T, H, Wr, bias, E, logits, hdr, s);
         else route_launch<false, 2, 4, 4>(x, T, H, Wr, bias, E, logits, hdr, s);
