@@ -482,41 +482,60 @@ __global__ __launch_bounds__(256) void quant_gateup_kernel(GroupArgs a, int64_t 
     // (clamped: an index outside the table, which the segment kernels flag
     // in the status word, still reads inside the side-vector arrays)
     const int e = slot < a.nr ? min(max(a.idx[slot], 0), a.E - 1) : a.E - 1;
+    // lane l takes 32-byte pieces 64c + l of the row (16 channels each: the
+    // fp8 path's hidden sizes are multiples of 256), so each projection's
+    // quantized piece leaves in one 16-byte store
+    constexpr int NP = (NC + 1) / 2;
     const f16x8 *xr = (const f16x8 *)(a.x16 + t * H);
     const f16x8 *sg = (const f16x8 *)(a.suh[0] + (int64_t)e * H);
     const f16x8 *su = (const f16x8 *)(a.suh[1] + (int64_t)e * H);
-    const int np = H / 8;   // 16-byte pieces per row
-    f16x8 xv[NC], gv[NC], uv[NC];
+    const int np = H / 16;
+    f16x8 xv[NP][2], gv[NP][2], uv[NP][2];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
+    for (int c = 0; c < NP; ++c) {
         const int q = 64 * c + l < np ? 64 * c + l : np - 1;   // in bounds; past np never used
-        xv[c] = xr[q];
-        gv[c] = sg[q];
-        uv[c] = su[q];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            xv[c][hh] = xr[2 * q + hh];
+            gv[c][hh] = sg[2 * q + hh];
+            uv[c][hh] = su[2 * q + hh];
+        }
     }
     float mg = 0.0f, mu = 0.0f;
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
+    for (int c = 0; c < NP; ++c)
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            if (64 * c + l < np) {
-            mg = fmaxf(mg, fabsf((float)xv[c][j] * (float)gv[c][j]));
-            mu = fmaxf(mu, fabsf((float)xv[c][j] * (float)uv[c][j]));
-        }
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (64 * c + l < np) {
+                    mg = fmaxf(mg, fabsf((float)xv[c][hh][j] * (float)gv[c][hh][j]));
+                    mu = fmaxf(mu, fabsf((float)xv[c][hh][j] * (float)uv[c][hh][j]));
+                }
     const float s_g = e4m3_row_scale(wave_max64(mg));
     const float s_u = e4m3_row_scale(wave_max64(mu));
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        if (64 * c + l >= np)
+    for (int c = 0; c < NP; ++c) {
+        const int q = 64 * c + l;
+        if (q >= np)
             break;
-        float vg[8], vu[8];
+        u32x4 og, ou;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            vg[j] = (float)xv[c][j] * (float)gv[c][j];
-            vu[j] = (float)xv[c][j] * (float)uv[c][j];
+        for (int hh = 0; hh < 2; ++hh) {
+            float vg[8], vu[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                vg[j] = (float)xv[c][hh][j] * (float)gv[c][hh][j];
+                vu[j] = (float)xv[c][hh][j] * (float)uv[c][hh][j];
+            }
+            const u32x2 pg = e4m3_pack8(vg, s_g), pu = e4m3_pack8(vu, s_u);
+            og[2 * hh] = pg[0];
+            og[2 * hh + 1] = pg[1];
+            ou[2 * hh] = pu[0];
+            ou[2 * hh + 1] = pu[1];
         }
-        *(u32x2 *)(a.a8g + p * H + 8 * (64 * c + l)) = e4m3_pack8(vg, s_g);
-        *(u32x2 *)(a.a8u + p * H + 8 * (64 * c + l)) = e4m3_pack8(vu, s_u);
+        __builtin_nontemporal_store(og, (u32x4 *)(a.a8g + p * H + 16 * q));
+        __builtin_nontemporal_store(ou, (u32x4 *)(a.a8u + p * H + 16 * q));
     }
     if (l == 0) {
         a.sg8[p] = s_g;
