@@ -11,36 +11,13 @@
 namespace moe {
 
 // ---------------------------------------------------------------- router logits
-// Fixed order (64 lane partial sums over h = 64i + l, each accumulated in
-// order of i, then the halving tree p[l] += p[l + d], d = 32 .. 1).  The
-// partial sums are spread over hardware lanes as follows: an 8-lane group
-// holds all 64 of them for its (token, expert) pairs, lane g of the group
-// owning l = 8g + j, j = 0..7, so every load is 16 contiguous bytes of a row.
-// Each lane keeps TPL tokens x EPL experts of partial sums; a wavefront is 8
-// groups = NTQ token quads x (8 / NTQ) expert quads, a block 4 wavefronts that
-// split the experts.  The tree then runs as three DPP row shifts across the
-// group (d = 32, 16, 8: lanes g+4, g+2, g+1) and three in-register steps
-// (d = 4, 2, 1).  Every x*w product is exact in fp32, so fma == add(product).
-template <int TPL, int EPL, int NTQ>
-struct RouteShape {
-    static constexpr int kNEQ = 8 / NTQ;
-    static constexpr int kTokens = NTQ * TPL;          // per block
-    static constexpr int kExpertsWave = kNEQ * EPL;
-    static constexpr int kExperts = 4 * kExpertsWave;  // per block
-};
-
-MOE_DEV float dpp_shl(float v, int n)
-{
-    // row_shl:n -- lane i of a 16-lane row reads lane i + n
-    const int ctrl = 0x100 + n;
-    int r;
-    switch (ctrl) {
-    case 0x104: r = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x104, 0xF, 0xF, false); break;
-    case 0x102: r = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x102, 0xF, 0xF, false); break;
-    default: r = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x101, 0xF, 0xF, false); break;
-    }
-    return __int_as_float(r);
-}
+// Fixed order: 64 partial sums p[l] over channels h = 64i + l, each
+// accumulated in order of i, then the halving tree p[l] += p[l + d],
+// d = 32 .. 1, and the bias.  Each step is one fused multiply-add (a single
+// rounding; a product of two 16-bit floats is exact in fp32 unless it falls
+// below fp32's normal range).  Two kernels compute it: one
+// (token, expert) pair per 32 lanes for few tokens, and tiles of pairs on the
+// matrix cores for many.
 
 // The first launch of every call clears the status word of the workspace
 // header; later launches only set bits in it.
@@ -48,106 +25,6 @@ MOE_DEV void clear_status(WsHeader *hdr)
 {
     if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
         hdr->status = 0;
-}
-
-template <bool BF16, int TPL, int EPL, int NTQ>
-__global__ __launch_bounds__(256) void route_logits_kernel(const uint16_t *__restrict__ x, int64_t T,
-                                                           int H, const uint16_t *__restrict__ Wr,
-                                                           const float *__restrict__ bias, int E,
-                                                           float *__restrict__ logits, WsHeader *hdr)
-{
-    clear_status(hdr);
-    using S = RouteShape<TPL, EPL, NTQ>;
-    const int w = threadIdx.x >> 6, L = threadIdx.x & 63;
-    const int g = L & 7, blk = L >> 3;
-    const int tq = blk / S::kNEQ, eq = blk % S::kNEQ;
-    const int64_t tb = (int64_t)blockIdx.x * S::kTokens + tq * TPL;
-    const int eb = blockIdx.y * S::kExperts + w * S::kExpertsWave + eq * EPL;
-    const uint16_t *xr[TPL];
-    bool tok_ok[TPL];
-#pragma unroll
-    for (int a = 0; a < TPL; ++a) {
-        tok_ok[a] = tb + a < T;
-        xr[a] = x + (tok_ok[a] ? tb + a : 0) * (int64_t)H + 8 * g;
-    }
-    const uint16_t *wr[EPL];
-    bool ex_ok[EPL];
-#pragma unroll
-    for (int b = 0; b < EPL; ++b) {
-        ex_ok[b] = eb + b < E;
-        wr[b] = Wr + (int64_t)(ex_ok[b] ? eb + b : 0) * H + 8 * g;
-    }
-    float p[TPL][EPL][8];
-#pragma unroll
-    for (int a = 0; a < TPL; ++a)
-#pragma unroll
-        for (int b = 0; b < EPL; ++b)
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                p[a][b][j] = 0.0f;
-    // rows past the last token or expert read row 0 (in bounds); their sums
-    // are never stored
-#pragma unroll 2
-    for (int i = 0; i < H / 64; ++i) {
-        float xv[TPL][8];
-#pragma unroll
-        for (int a = 0; a < TPL; ++a) {
-            const u32x4 raw = *(const u32x4 *)(xr[a] + 64 * i);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (BF16) {
-                    xv[a][2 * j] = __uint_as_float(raw[j] << 16);
-                    xv[a][2 * j + 1] = __uint_as_float(raw[j] & 0xFFFF0000u);
-                } else {
-                    xv[a][2 * j] = f16_to_f32((uint16_t)(raw[j] & 0xFFFFu));
-                    xv[a][2 * j + 1] = f16_to_f32((uint16_t)(raw[j] >> 16));
-                }
-            }
-        }
-#pragma unroll
-        for (int b = 0; b < EPL; ++b) {
-            const f16x8 wv = *(const f16x8 *)(wr[b] + 64 * i);
-#pragma unroll
-            for (int a = 0; a < TPL; ++a)
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    p[a][b][j] = __builtin_fmaf(xv[a][j], (float)wv[j], p[a][b][j]);
-        }
-    }
-    // tree: d = 32, 16, 8 across the group (lane g += lane g + d/8) ...
-#pragma unroll
-    for (int a = 0; a < TPL; ++a)
-#pragma unroll
-        for (int b = 0; b < EPL; ++b)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                float v = p[a][b][j];
-                v = v + dpp_shl(v, 4);
-                v = v + dpp_shl(v, 2);
-                v = v + dpp_shl(v, 1);
-                p[a][b][j] = v;
-            }
-    // ... then d = 4, 2, 1 inside lane g = 0
-    if (g == 0) {
-#pragma unroll
-        for (int a = 0; a < TPL; ++a)
-#pragma unroll
-            for (int b = 0; b < EPL; ++b) {
-                float r[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    r[j] = p[a][b][j];
-#pragma unroll
-                for (int d = 4; d >= 1; d >>= 1)
-#pragma unroll
-                    for (int j = 0; j < d; ++j)
-                        r[j] = r[j] + r[j + d];
-                if (tok_ok[a] && ex_ok[b]) {
-                    const int e = eb + b;
-                    logits[(tb + a) * E + e] = bias ? r[0] + bias[e] : r[0];
-                }
-            }
-    }
 }
 
 // Few tokens: 32 lanes per (token, expert) pair, lane m owning the partial
@@ -382,32 +259,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
 }
 
-template <bool BF16, int TPL, int EPL, int NTQ>
-static void route_launch(const uint16_t *x, int64_t T, int H, const uint16_t *Wr, const float *bias,
-                         int E, float *logits, WsHeader *hdr, hipStream_t s)
-{
-    using S = RouteShape<TPL, EPL, NTQ>;
-    dim3 grid((unsigned)((T + S::kTokens - 1) / S::kTokens), (unsigned)((E + S::kExperts - 1) / S::kExperts));
-    route_logits_kernel<BF16, TPL, EPL, NTQ><<<grid, 256, 0, s>>>(x, T, H, Wr, bias, E, logits, hdr);
-}
-
 hipError_t launch_route_logits(const uint16_t *x, bool bf16, int64_t T, int H, const uint16_t *Wr,
                                const float *bias, int E, float *logits, WsHeader *hdr, hipStream_t s)
 {
-    // many tokens: 16 x 32 tiles on the matrix cores (hidden sizes in whole
-    // 128-channel steps), else on the VALU with 2 tokens x 4 experts per
-    // lane (8 tokens x 32 experts per block); few tokens: one (token, expert)
-    // pair per 32 lanes so that enough wavefronts stream the router weights
-    if (T > 64 && H % 128 == 0) {
+    // many tokens: 16 x 32 tiles on the matrix cores, in 128-channel steps
+    // (the layer's hidden size is a multiple of 256); few tokens: one (token,
+    // expert) pair per 32 lanes so that enough wavefronts stream the router
+    // weights
+    if (H % 128)
+        return hipErrorInvalidValue;
+    if (T > 64) {
         const int n_tt = (int)((T + kRlTok - 1) / kRlTok), n_et = (E + kRlExp - 1) / kRlExp;
         const unsigned grid = (unsigned)(((n_tt + 7) / 8) * 8 * n_et);
         if (bf16)
             route_logits_mfma_kernel<true><<<grid, 256, 0, s>>>(x, T, H, Wr, bias, E, logits, hdr, n_tt, n_et);
         else
             route_logits_mfma_kernel<false><<<grid, 256, 0, s>>>(x, T, H, Wr, bias, E, logits, hdr, n_tt, n_et);
-    } else if (T > 64) {
-        if (bf16) route_launch<true, 2, 4, 4>(x, T, H, Wr, bias, E, logits, hdr, s);
-        else route_launch<false, 2, 4, 4>(x, T, H, Wr, bias, E, logits, hdr, s);
     } else {
         const unsigned grid = (unsigned)((T * E + 7) / 8);
         if (bf16) route_logits_pairs_kernel<true><<<grid, 256, 0, s>>>(x, T, H, Wr, bias, E, logits, hdr);
