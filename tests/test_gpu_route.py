@@ -79,9 +79,10 @@ def test_route_deterministic():
 # The routing entry leaves the fp32 logits in its workspace right after the
 # 256-byte header (an internal layout this test reads on purpose).  They must
 # equal the oracle's fixed-order sums bit for bit: up to 64 tokens on the
-# 32-lanes-per-pair kernel, above that on the matrix-core one (16 x 16
-# tiles, ragged in tokens and, in the tiny config, in experts); bf16
-# activations at the real shapes, fp16 in the tiny config.
+# 32-lanes-per-pair kernel, above that on the matrix-core one (16-token x
+# 32-expert tiles, ragged in tokens and, in the tiny config's 8 experts and
+# 256 channels, in experts and with fewer 128-channel steps than its LDS ring
+# has stages); bf16 activations at the real shapes, fp16 in the tiny config.
 _LOGITS_AT = 256
 
 
@@ -109,8 +110,8 @@ def test_route_logits_bit_exact(name, T):
 
 @pytest.mark.parametrize("name", ["prefill", "mixed_k3"])
 def test_route_logits_bit_exact_prefill_shapes(name):
-    # every logit of the 7168- and 2048-token layers (448 and 128 token tiles,
-    # 18 expert tiles)
+    # every logit of the 7168- and 2048-token layers (448 and 128 token tiles
+    # of 16, 9 expert tiles of 32)
     inp = W.gen_layer(W.BY_NAME[name], experts=[])
     dl = DevLayer(inp)
     got = _device_logits(dl, inp.cfg.tokens)
