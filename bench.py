@@ -18,6 +18,7 @@ expert); the achievable HBM read bandwidth; and the CPU oracle per workload.
 Helpers for rocprofv3 counter passes (each does one thing and exits):
 
     python bench.py --profile-layer prefill --reps 2   # the layer, N times
+    python bench.py --profile-layer decode --profile-tokens 1 --copies 4 --reps 100 --profile-graph
     python bench.py --copy-calibration 1024            # a plain 1 GiB copy, 4 times
 
 The roofline's `traffic` (HBM bytes per launch of the dominant kernel) is read
@@ -516,6 +517,10 @@ def main():
     ap.add_argument("--profile-flags", type=int, default=0, help="extra descriptor flags for --profile-layer")
     ap.add_argument("--copies", type=int, default=1,
                     help="--profile-layer: rotate this many copies of the codes (the decode leg uses 4)")
+    ap.add_argument("--profile-tokens", type=int, default=0,
+                    help="--profile-layer: this many tokens instead of the workload's own")
+    ap.add_argument("--profile-graph", action="store_true",
+                    help="--profile-layer: replay the layers from HIP graphs, as the verify-batch leg does")
     ap.add_argument("--reps", type=int, default=2)
     ap.add_argument("--copy-calibration", type=int, default=0, help="copy this many MiB 4 times and exit")
     args = ap.parse_args()
@@ -541,14 +546,22 @@ def main():
         return
     if args.profile_layer:
         pcfg = W.BY_NAME[args.profile_layer]
+        if args.profile_tokens > 0:
+            pcfg = pcfg.replace(tokens=args.profile_tokens)
         pinp, pdesc, pweights, pkeep = setup(pcfg, copies=args.copies, extra_flags=args.profile_flags)
         px = _dev(pinp.x)
+        if args.profile_graph:
+            us = time_layer_graph(pdesc, pweights, px, args.reps, hip) * 1000
+            print(f"[bench] replayed the {args.profile_layer} layer (T={pcfg.tokens}) {args.reps} times "
+                  f"from graphs: {us:.1f} us/layer", file=sys.stderr, flush=True)
+            return
         pout = torch.empty_like(px)
         pws = torch.empty(M.workspace_size(pdesc, px.shape[0]), dtype=torch.uint8, device="cuda")
         for i in range(args.reps):
             M.layer(pdesc, pweights[i % len(pweights)], px, pout, pws)
         torch.cuda.synchronize()
-        print(f"[bench] ran the {args.profile_layer} layer {args.reps} times", file=sys.stderr, flush=True)
+        print(f"[bench] ran the {args.profile_layer} layer (T={pcfg.tokens}) {args.reps} times", file=sys.stderr,
+              flush=True)
         return
 
     # ---- prefill: the headline workload
