@@ -108,6 +108,19 @@ def test_route_logits_bit_exact(name, T):
     assert got.view(np.uint32).tolist() == ref.view(np.uint32).tolist()
 
 
+@pytest.mark.parametrize("T", [79, 80, 81, 129])
+@pytest.mark.parametrize("E,H", [(40, 512), (296, 1024)])
+def test_route_logits_bit_exact_ragged_tiles(E, H, T):
+    # the matrix-core router's ragged edges: 40 experts = one full 32-expert
+    # tile and one of 8, 296 = nine full tiles and one of 8; token counts on
+    # both sides of a 16-token tile boundary; 4 and 8 128-channel steps
+    cfg = W.BY_NAME["decode"].replace(tokens=T, n_experts=E, hidden=H, router_bias=True)
+    inp = W.gen_layer(cfg, experts=[])
+    got = _device_logits(DevLayer(inp), T)
+    ref = oracle.router_logits(inp.x, cfg.act_dtype, inp.router_w, inp.router_bias)
+    np.testing.assert_array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
 @pytest.mark.parametrize("name", ["prefill", "mixed_k3"])
 def test_route_logits_bit_exact_prefill_shapes(name):
     # every logit of the 7168- and 2048-token layers (448 and 128 token tiles
